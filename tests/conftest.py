@@ -1,0 +1,15 @@
+"""Shared pytest configuration.
+
+Tests marked ``gpu`` need an MI355X and the built HIP library; everything else
+runs on the CPU (oracle pins, host allocator/planner, C-ABI symbol checks).
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
