@@ -215,14 +215,15 @@ def _zero_last_above(C, p, tag=None):
     zero-out tag of Zipage Alg. 3. Modifies C in place.
     """
     rows, cols = C.shape
-    for j in range(cols):
-        if tag is not None and tag[j]:
-            continue
-        above = np.nonzero(C[:, j] > p)[0]
-        if above.size:
-            C[above[-1], j] = 0.0
-            if tag is not None:
-                tag[j] = True
+    above = C > p
+    has = above.any(axis=0)
+    if tag is not None:
+        has &= ~tag
+    last = rows - 1 - np.argmax(above[::-1, :], axis=0)   # highest row above p
+    j = np.nonzero(has)[0]
+    C[last[j], j] = 0.0
+    if tag is not None:
+        tag[j] = True
     return C
 
 
