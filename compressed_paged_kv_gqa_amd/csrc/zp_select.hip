@@ -1,0 +1,338 @@
+// Top-k selection and in-order compaction of K, V and F (gfx950).
+//
+// Zipage (arXiv 2603.08743): Sec. 4.2 (keep the k = (N_max - 1) b entries with
+// the highest scores; the window carries +inf), App. C.6 (top-k tag, then a
+// two-pointer move that packs the kept entries densely and in order; the
+// global-score cache F moves with K and V, one element per token instead of
+// d), Sec. 4.4 (the packed entries go to target blocks, fresh ones for shared
+// prefix blocks).
+//
+// One workgroup per (kv-head, request, layer):
+//  1. radix select over order-preserving 32-bit keys of the fp32 scores
+//     (4 passes of 8 bits, LDS histogram) finds the k-th largest key;
+//  2. ties at that key go to the highest token indices (a backward block
+//     scan), giving a selection bitmap in LDS;
+//  3. a forward block scan turns the bitmap into the ascending kept list;
+//  4. the kept rows are moved in chunks: every thread loads its rows, the
+//     workgroup waits until all loads of the chunk have completed, then
+//     stores. Destination slot j <= source slot kept[j] and targets are
+//     either the same block or a fresh one, so no chunk reads a slot that an
+//     earlier chunk wrote, and no chunk writes a slot a later chunk still
+//     has to read before that read has completed.
+#include "zp_device.h"
+#include "zp_internal.h"
+
+namespace zp {
+
+constexpr int kKeepMax = 8192;
+constexpr int kSelMaxTokens = 65536;
+
+struct SelectParams {
+  const float* scores;
+  void* kc;
+  void* vc;
+  float* gscore;
+  const int32_t* src_tables;
+  const int32_t* num_blocks;
+  const int32_t* dst_tables;
+  int32_t* kept_out;
+  uint32_t* err;
+  int64_t scores_stride;
+  int64_t kv_layer_elems, f_layer_elems;
+  int32_t src_stride, dst_stride;
+  int32_t layer_begin, nreq, h_kv, b, num_blocks_total, max_blocks, keep;
+  uint32_t flags;
+};
+
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+// -0 is folded onto +0 and NaN onto the smallest key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 0u;
+  if (f == 0.f) f = 0.f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over the 256 threads of the workgroup.
+__device__ int block_inclusive_scan(int v, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wv] = v;
+  __syncthreads();
+  for (int i = 0; i < wv; ++i) v += wsum[i];
+  return v;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bitmap[kSelMaxTokens / 32];
+  __shared__ int32_t kept[kKeepMax];
+  __shared__ int wsum[4];
+  __shared__ uint32_t sh_prefix, sh_krem;
+  __shared__ int sh_bad;
+
+  const int h = blockIdx.x, r = blockIdx.y, li = blockIdx.z;
+  const int z = li * P.nreq + r;
+  const int layer = P.layer_begin + li;
+  const int tid = threadIdx.x;
+  const int N = P.num_blocks[r];
+  if (N <= 0) return;
+  if (N > P.max_blocks || N > P.src_stride) {
+    if (tid == 0) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
+    return;
+  }
+  const int n = N * P.b;
+  const int keep = P.keep;
+  if (keep > n) {
+    if (tid == 0) flag_error(P.err, ZP_DEVERR_KEEP);
+    return;
+  }
+  const int32_t* stab = P.src_tables + (int64_t)r * P.src_stride;
+  const int32_t* dtab = P.dst_tables + (int64_t)r * P.dst_stride;
+  const bool compact = !(P.flags & ZP_SELECT_NO_COMPACT);
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  // Validate every block id the move will touch before touching anything.
+  for (int i = tid; i < N; i += 256) {
+    const int pg = stab[i];
+    if (pg < 0 || pg >= P.num_blocks_total) sh_bad = 1;
+  }
+  if (compact)
+    for (int i = tid; i < (keep + P.b - 1) / P.b; i += 256) {
+      const int pg = dtab[i];
+      if (pg < 0 || pg >= P.num_blocks_total) sh_bad = 1;
+    }
+  __syncthreads();
+  if (sh_bad) {
+    if (tid == 0) flag_error(P.err, ZP_DEVERR_BLOCK_ID);
+    return;
+  }
+
+  const float* sc = P.scores + ((int64_t)z * P.h_kv + h) * P.scores_stride;
+
+  // 1. Radix select of the keep-th largest key.
+  uint32_t prefix = 0, pmask = 0, krem = keep;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < n; t += 256) {
+      const uint32_t k = order_key(sc[t]);
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t cum = 0;
+      int sel = 0;
+      for (int v = 255; v >= 0; --v) {
+        if (cum + hist[v] >= krem) { sel = v; break; }
+        cum += hist[v];
+      }
+      sh_prefix = prefix | (uint32_t(sel) << shift);
+      sh_krem = krem - cum;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    krem = sh_krem;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;  // key of the keep-th largest score
+  // krem = how many of the keys equal to thr are kept (the highest indices).
+
+  // 2. Selection bitmap; equal keys counted from the end.
+  const int nchunks = (n + 255) / 256;
+  int carry = 0;  // equal keys already seen in later chunks
+  for (int c = nchunks - 1; c >= 0; --c) {
+    // Reverse the order inside the chunk so an inclusive scan counts later keys.
+    const int t = c * 256 + (255 - tid);
+    uint32_t k = 0;
+    int eq = 0;
+    if (t < n) {
+      k = order_key(sc[t]);
+      eq = k == thr;
+    }
+    const int incl = block_inclusive_scan(eq, wsum);
+    const int later = carry + incl - eq;  // equal keys with a higher index
+    const bool selected = t < n && (k > thr || (eq && later < (int)krem));
+    if (t < n) {
+      if (selected) atomicOr(&bitmap[t >> 5], 1u << (t & 31));
+      else atomicAnd(&bitmap[t >> 5], ~(1u << (t & 31)));
+    }
+    __syncthreads();
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+
+  // 3. Ascending kept list.
+  int base = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    const int t = c * 256 + tid;
+    const int sel = t < n ? (bitmap[t >> 5] >> (t & 31)) & 1 : 0;
+    const int incl = block_inclusive_scan(sel, wsum);
+    if (sel && base + incl - 1 < keep) kept[base + incl - 1] = t;
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  __syncthreads();
+  if (P.kept_out) {
+    int32_t* ko = P.kept_out + ((int64_t)z * P.h_kv + h) * keep;
+    for (int j = tid; j < keep; j += 256) ko[j] = kept[j];
+  }
+  if (!compact) return;
+
+  // 4. Ordered move of K, V (and F).
+  constexpr int EPL = Vec16<T>::N;
+  constexpr int LPR = D / EPL;          // lanes per token row
+  constexpr int RPR = 256 / LPR;        // rows per workgroup pass
+  constexpr int PASSES = 4;
+  constexpr int CHUNK = RPR * PASSES;   // rows per chunk
+  const int b = P.b;
+  T* kc = reinterpret_cast<T*>(P.kc) + layer * P.kv_layer_elems;
+  T* vc = reinterpret_cast<T*>(P.vc) + layer * P.kv_layer_elems;
+  float* fc = P.gscore ? P.gscore + layer * P.f_layer_elems : nullptr;
+  const int64_t page_elems = (int64_t)P.h_kv * b * D;
+  const int64_t head_off = (int64_t)h * b * D;
+  const int rr = tid / LPR, sub = tid % LPR;
+  for (int j0 = 0; j0 < keep; j0 += CHUNK) {
+    uint4 kv[PASSES], vv[PASSES];
+    float fv = 0.f;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int j = j0 + ps * RPR + rr;
+      if (j < keep) {
+        const int t = kept[j];
+        const int64_t off = (int64_t)stab[t / b] * page_elems + head_off + (int64_t)(t % b) * D +
+                            sub * EPL;
+        kv[ps] = ld16(kc + off);
+        vv[ps] = ld16(vc + off);
+      }
+    }
+    if (fc && tid < CHUNK && j0 + tid < keep) {
+      const int t = kept[j0 + tid];
+      fv = fc[((int64_t)stab[t / b] * P.h_kv + h) * b + (t % b)];
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every load of the chunk has returned
+    __syncthreads();
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int j = j0 + ps * RPR + rr;
+      if (j < keep) {
+        const int64_t off = (int64_t)dtab[j / b] * page_elems + head_off + (int64_t)(j % b) * D +
+                            sub * EPL;
+        st16(kc + off, kv[ps]);
+        st16(vc + off, vv[ps]);
+      }
+    }
+    if (fc && tid < CHUNK && j0 + tid < keep) {
+      const int j = j0 + tid;
+      fc[((int64_t)dtab[j / b] * P.h_kv + h) * b + (j % b)] = fv;
+    }
+  }
+}
+
+template <typename T, int D>
+static void launch_select(const SelectParams& P, int layer_count, hipStream_t s) {
+  dim3 grid(P.h_kv, P.nreq, layer_count);
+  hipLaunchKernelGGL((select_compact_kernel<T, D>), grid, dim3(256), 0, s, P);
+}
+
+}  // namespace zp
+
+using namespace zp;
+
+extern "C" size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_count,
+                                           int32_t nreq) {
+  if (validate_geom(geom, "zp_select_workspace_size") != ZP_OK || layer_count < 0 || nreq < 0)
+    return 0;
+  return kWsHeader;
+}
+
+extern "C" zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cache,
+                                       int32_t layer_begin, int32_t layer_count, int32_t nreq,
+                                       const float* scores, int64_t scores_stride,
+                                       const int32_t* src_tables, int32_t src_stride,
+                                       const int32_t* num_blocks, int32_t max_blocks,
+                                       const int32_t* dst_tables, int32_t dst_stride,
+                                       int32_t keep, int32_t* kept_idx, uint32_t flags,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  zp_status st = validate_geom(geom, "zp_select_compact");
+  if (st != ZP_OK) return st;
+  if (!cache || !cache->k || !cache->v) return fail(ZP_EINVAL, "zp_select_compact: cache NULL");
+  if (layer_begin < 0 || layer_count < 0 || layer_begin + layer_count > geom->num_layers)
+    return fail(ZP_EINVAL, "zp_select_compact: layer range outside the cache");
+  if (nreq < 0 || max_blocks < 0 || src_stride <= 0)
+    return fail(ZP_EINVAL, "zp_select_compact: bad nreq/max_blocks/src_stride");
+  if (flags & ~uint32_t(ZP_SELECT_NO_COMPACT))
+    return fail(ZP_EINVAL, "zp_select_compact: unknown flags 0x%x", flags);
+  if (keep < 1 || keep > kKeepMax)
+    return fail(ZP_EINVAL, "zp_select_compact: keep %d outside [1, %d]", keep, kKeepMax);
+  if (int64_t(max_blocks) * geom->block_size > kSelMaxTokens)
+    return fail(ZP_EINVAL, "zp_select_compact: max_blocks*b above %d tokens", kSelMaxTokens);
+  const bool compact = !(flags & ZP_SELECT_NO_COMPACT);
+  if (compact && (!dst_tables || dst_stride <= 0 || int64_t(dst_stride) * geom->block_size < keep))
+    return fail(ZP_EINVAL, "zp_select_compact: dst_tables must hold keep tokens");
+  if (nreq == 0 || layer_count == 0 || max_blocks == 0) return ZP_OK;
+  if (!scores || !src_tables || !num_blocks || !workspace)
+    return fail(ZP_EINVAL, "zp_select_compact: NULL buffer");
+  if (scores_stride < int64_t(max_blocks) * geom->block_size)
+    return fail(ZP_EINVAL, "zp_select_compact: scores_stride < max_blocks*b");
+  if (workspace_bytes < kWsHeader) return fail(ZP_EINVAL, "zp_select_compact: workspace too small");
+  if (nreq > 65535 || layer_count > 65535)
+    return fail(ZP_EINVAL, "zp_select_compact: nreq and layer_count must be <= 65535");
+
+  SelectParams P{};
+  P.scores = scores; P.scores_stride = scores_stride;
+  P.kc = cache->k; P.vc = cache->v; P.gscore = cache->gscore;
+  P.src_tables = src_tables; P.src_stride = src_stride; P.num_blocks = num_blocks;
+  P.dst_tables = dst_tables ? dst_tables : src_tables;
+  P.dst_stride = dst_tables ? dst_stride : src_stride;
+  P.kept_out = kept_idx;
+  P.err = static_cast<uint32_t*>(workspace);
+  const int64_t d = geom->head_dim;
+  P.kv_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size * d;
+  P.f_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size;
+  P.layer_begin = layer_begin; P.nreq = nreq; P.h_kv = geom->num_kv_heads;
+  P.b = geom->block_size; P.num_blocks_total = geom->num_blocks; P.max_blocks = max_blocks;
+  P.keep = keep; P.flags = flags;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (geom->dtype == ZP_DTYPE_BF16) {
+    if (d == 128) launch_select<bf16_t, 128>(P, layer_count, s);
+    else launch_select<bf16_t, 64>(P, layer_count, s);
+  } else {
+    if (d == 128) launch_select<float, 128>(P, layer_count, s);
+    else launch_select<float, 64>(P, layer_count, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZP_EHIP, "zp_select_compact: launch failed: %s", hipGetErrorString(e));
+  return ZP_OK;
+}
+
+extern "C" zp_status zp_workspace_errors(const void* workspace, uint32_t* flags, void* stream) {
+  if (!workspace || !flags) return fail(ZP_EINVAL, "zp_workspace_errors: NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(ZP_EHIP, "zp_workspace_errors: %s", hipGetErrorString(e));
+  return ZP_OK;
+}
+
+namespace zp {
+__global__ void clear_word_kernel(uint32_t* p) { *p = 0u; }
+}  // namespace zp
+
+extern "C" zp_status zp_workspace_clear_errors(void* workspace, void* stream) {
+  if (!workspace) return fail(ZP_EINVAL, "zp_workspace_clear_errors: NULL workspace");
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(workspace));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZP_EHIP, "zp_workspace_clear_errors: %s", hipGetErrorString(e));
+  return ZP_OK;
+}

@@ -1,0 +1,281 @@
+"""Host runtime around libzp: per-step decode of a batch of requests, the
+compression trigger, target planning, and asynchronous compression on a side
+HIP stream.
+
+Zipage (arXiv 2603.08743): Sec. 4.1 (cap of N_max blocks, trigger after a
+step that leaves N >= N_max full blocks, reserved N_max-th block), Sec. 4.2
+(query-cache slot per request), Sec. 4.4 (shared prefix blocks and their
+target blocks), Sec. 4.5 (decoding requests do not wait for compression; a
+compressing request rejoins decode once its compression has finished),
+App. C.1 (compression runs layer_stride layers per launch).
+
+Every numeric step runs in the library's kernels; this module only keeps
+block tables and per-request state and enqueues work (torch supplies device
+memory and streams). Scheduling policies (admission, preemption, hybrid query
+slots) are out of scope: requests are added explicitly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import zp
+
+
+@dataclass
+class Request:
+    sid: int
+    table: list
+    n: int                      # resident tokens
+    first: bool = True          # never compressed so far
+    compressing: bool = False
+    done: bool = False
+
+
+@dataclass
+class _Pending:
+    sids: list
+    plans: list                 # (old_table, dst, new_table)
+    event: torch.cuda.Event
+    buffers: list = field(default_factory=list)   # keep tensors alive until the event
+
+
+class DecodeEngine:
+    """Batch of requests decoding layer by layer over a paged cache."""
+
+    def __init__(self, geom: zp.CacheGeometry, params: zp.ScoreParams, max_seqs, table_cap,
+                 layer_stride=8, async_compress=True, with_global=True, device="cuda",
+                 cache_init=None, record=False):
+        self.geom = geom
+        self.params = params
+        self.B = max_seqs
+        self.cap = table_cap
+        self.layer_stride = max(1, min(layer_stride, geom.num_layers))
+        self.async_compress = async_compress
+        self.device = device
+        self.cache = zp.PagedKVCache(geom, device=device, with_global=with_global, init=cache_init)
+        self.alloc = zp.BlockAllocator(geom.num_blocks)
+        self.reqs: dict[int, Request] = {}
+        # Host master copies, staged through a ring of pinned buffers: a
+        # buffer is rewritten only after the copy that last read it finished.
+        self.tables_np = np.zeros((max_seqs, table_cap), np.int32)
+        self.lens_np = np.zeros(max_seqs, np.int32)
+        self._ring = [(torch.zeros((max_seqs, table_cap), dtype=torch.int32).pin_memory(),
+                       torch.zeros(max_seqs, dtype=torch.int32).pin_memory(),
+                       torch.cuda.Event()) for _ in range(4)]
+        self._ring_i = 0
+        self.tables_d = torch.zeros((max_seqs, table_cap), dtype=torch.int32, device=device)
+        self.lens_d = torch.zeros(max_seqs, dtype=torch.int32, device=device)
+        self.qslot_d = torch.arange(max_seqs, dtype=torch.int32, device=device)
+        self.max_seq_len = table_cap * geom.block_size
+        self.dec_ws = zp.new_workspace(zp.zp_decode_workspace_size(geom, max_seqs,
+                                                                    self.max_seq_len), device)
+        self.side = torch.cuda.Stream(device=device)
+        self.pending: list[_Pending] = []
+        self.compressions = 0
+        self.decoded_tokens = 0
+        # optional per-layer timing of the decode kernel (start, end) events
+        self.layer_events = None
+        # with record=True every compression keeps its scores and kept indices
+        # (device tensors, read by tests): list of (sids, first, scores, kept)
+        self.record = record
+        self.log = []
+
+    # ------------------------------------------------------------------ setup
+    def add_request(self, sid, n_tokens, prefix_table=None):
+        """Registers request `sid` holding n_tokens resident tokens. Blocks
+        are allocated here (after sharing `prefix_table`, if given); the
+        caller fills their contents. Returns the block table."""
+        assert 0 <= sid < self.B and sid not in self.reqs
+        b = self.geom.block_size
+        nb = -(-n_tokens // b)
+        table = []
+        if prefix_table:
+            self.alloc.share(prefix_table)
+            table = list(prefix_table)
+        table += self.alloc.alloc(nb - len(table))
+        assert len(table) <= self.cap
+        self.reqs[sid] = Request(sid, table, n_tokens)
+        return table
+
+    def write_tokens(self, sid, layer, start, k, v):
+        """Copies K/V rows [h_kv][t][d] of request `sid` into its pages from
+        logical position `start` (prompt ingest; plain device copies)."""
+        r = self.reqs[sid]
+        b = self.geom.block_size
+        t_total = k.shape[1]
+        t = 0
+        while t < t_total:
+            pos = start + t
+            blk, off = divmod(pos, b)
+            cnt = min(b - off, t_total - t)
+            pg = r.table[blk]
+            self.cache.k[layer, pg, :, off:off + cnt] = k[:, t:t + cnt]
+            self.cache.v[layer, pg, :, off:off + cnt] = v[:, t:t + cnt]
+            t += cnt
+
+    def write_window_queries(self, sid, layer, qw):
+        """Query-cache rows [h_kv][g][w][d] of request `sid` (prompt window)."""
+        self.cache.qwin[layer, sid] = qw
+
+    # ------------------------------------------------------------------ step
+    def active(self):
+        return [s for s, r in self.reqs.items() if not r.compressing and not r.done]
+
+    def prepare_step(self):
+        """Reserves a block for each active request's next token and uploads
+        tables and lengths. Returns the list of active sids."""
+        self.poll()
+        b = self.geom.block_size
+        act = self.active()
+        self.lens_np[:] = 0
+        for s in act:
+            r = self.reqs[s]
+            if r.n // b >= len(r.table):
+                r.table += self.alloc.alloc(1)
+            nt = len(r.table)
+            if not np.array_equal(self.tables_np[s, :nt], r.table):
+                self.tables_np[s, :nt] = r.table
+            self.lens_np[s] = r.n + 1
+        tab_h, len_h, ev = self._ring[self._ring_i]
+        self._ring_i = (self._ring_i + 1) % len(self._ring)
+        ev.synchronize()
+        np.copyto(tab_h.numpy(), self.tables_np)
+        np.copyto(len_h.numpy(), self.lens_np)
+        self.tables_d.copy_(tab_h, non_blocking=True)
+        self.lens_d.copy_(len_h, non_blocking=True)
+        ev.record()
+        return act
+
+    def decode_layer(self, layer, q, k_new, v_new, out, lse=None):
+        zp.zp_paged_decode(self.cache, layer, q, k_new, v_new, self.tables_d, self.lens_d,
+                           self.max_seq_len, self.qslot_d, out, lse, self.dec_ws)
+
+    def finish_step(self, act):
+        """Advances lengths and launches compressions that became due."""
+        for s in act:
+            self.reqs[s].n += 1
+        self.decoded_tokens += len(act)
+        due = [s for s in act if self._due(self.reqs[s])]
+        if due:
+            self.compress(due)
+
+    def step(self, q, k_new, v_new, out):
+        """One decode step of every active request through all layers.
+        q/out: [L][B][h_q][d]; k_new/v_new: [L][B][h_kv][d] (rows of requests
+        that are not active are ignored)."""
+        act = self.prepare_step()
+        for l in range(self.geom.num_layers):
+            ev = self.layer_events[l] if self.layer_events else None
+            if ev:
+                ev[0].record()
+            self.decode_layer(l, q[l], k_new[l], v_new[l], out[l])
+            if ev:
+                ev[1].record()
+        self.finish_step(act)
+        return act
+
+    # ------------------------------------------------------------ compression
+    def _due(self, r: Request):
+        b, n_max = self.geom.block_size, self.geom.n_max
+        N = -(-r.n // b)
+        return N >= n_max and r.n % b == 0 and r.n > 0
+
+    def compress_due_now(self):
+        """Compresses requests whose prompt already meets the trigger."""
+        due = [s for s, r in self.reqs.items()
+               if not r.compressing and not r.done and self._due(r)]
+        if due:
+            self.compress(due)
+
+    def compress(self, sids):
+        G = self.geom
+        b, n_max = G.block_size, G.n_max
+        keep = G.keep
+        plans, ok = [], []
+        for s in sids:
+            r = self.reqs[s]
+            try:
+                dst, new, _ = self.alloc.plan_compress(r.table, n_max)
+            except zp.NoBlocks:
+                continue          # stays uncompressed; a scheduler would preempt
+            plans.append((list(r.table), dst, new))
+            ok.append(s)
+            r.compressing = True
+        if not ok:
+            return
+        nreq = len(ok)
+        maxb = max(len(p[0]) for p in plans)
+        src = np.full((nreq, maxb), 0, np.int32)
+        for i, p in enumerate(plans):
+            src[i, :len(p[0])] = p[0]
+        dst = np.array([p[1] for p in plans], np.int32)
+        nblk = np.array([len(p[0]) for p in plans], np.int32)
+        qslot = np.array(ok, np.int32)
+        first = np.array([self.reqs[s].first for s in ok], np.uint8)
+        stream = self.side if self.async_compress else torch.cuda.current_stream()
+        ready = torch.cuda.Event()
+        ready.record()
+        bufs = []
+        with torch.cuda.stream(stream):
+            stream.wait_event(ready)
+            dv = lambda a: torch.from_numpy(a).to(self.device, non_blocking=False)
+            src_d, dst_d, nblk_d, qslot_d, first_d = dv(src), dv(dst), dv(nblk), dv(qslot), dv(first)
+            ls = self.layer_stride if not self.record else G.num_layers
+            scores = torch.empty((ls, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
+                                 device=self.device)
+            kept = (torch.empty((G.num_layers, nreq, G.num_kv_heads, keep), dtype=torch.int32,
+                                device=self.device) if self.record else None)
+            sws = zp.new_workspace(zp.zp_score_workspace_size(G, ls, nreq, maxb), self.device)
+            cws = zp.new_workspace(zp.zp_select_workspace_size(G, ls, nreq), self.device)
+            for lb in range(0, G.num_layers, ls):
+                lc = min(ls, G.num_layers - lb)
+                sc = scores[lb:lb + lc] if self.record else scores[:lc]
+                zp.zp_score_tokens(self.cache, self.params, lb, lc, src_d, nblk_d, maxb, qslot_d,
+                                   first_d, sc, sws, stream=stream)
+                zp.zp_select_compact(self.cache, lb, lc, sc, src_d, nblk_d, maxb, dst_d, keep,
+                                     kept[lb:lb + lc] if kept is not None else None, cws,
+                                     stream=stream)
+            done = torch.cuda.Event()
+            done.record(stream)
+            bufs = [src_d, dst_d, nblk_d, qslot_d, first_d, scores, sws, cws]
+            if self.record:
+                self.log.append((list(ok), first.copy(), scores, kept))
+        self.pending.append(_Pending(ok, plans, done, bufs))
+        self.compressions += nreq
+        if not self.async_compress:
+            self.poll(wait=True)
+
+    def poll(self, wait=False):
+        """Commits finished compressions (all of them if wait)."""
+        keep = self.geom.keep
+        still = []
+        for p in self.pending:
+            if wait:
+                p.event.synchronize()
+            elif not p.event.query():
+                still.append(p)
+                continue
+            for s, (old, _dst, new) in zip(p.sids, p.plans):
+                self.alloc.commit_compress(old, new)
+                r = self.reqs[s]
+                r.table = list(new)
+                r.n = keep
+                r.first = False
+                r.compressing = False
+        self.pending = still
+
+    def wait_compressions(self):
+        self.poll(wait=True)
+
+    def resident_kv(self, sid, layer, head):
+        """K, V rows [n][d] of a request read back through its block table
+        (test helper)."""
+        r = self.reqs[sid]
+        b = self.geom.block_size
+        idx = torch.tensor(r.table, device=self.device)
+        K = self.cache.k[layer, idx, head].reshape(-1, self.geom.head_dim)[:r.n]
+        V = self.cache.v[layer, idx, head].reshape(-1, self.geom.head_dim)[:r.n]
+        return K, V

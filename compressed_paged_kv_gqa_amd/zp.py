@@ -1,0 +1,397 @@
+"""ctypes binding of libzp (the C ABI declared in include/zp.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels. Functions keep the C names and take torch tensors for device
+buffers (PyTorch provides device memory and streams, nothing else). The
+library must be built (``python -m compressed_paged_kv_gqa_amd._build``);
+importing the binding without it raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzp.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "zp.h")
+
+ZP_OK, ZP_EINVAL, ZP_ENOBLOCKS, ZP_EHIP, ZP_ESTATE = 0, -1, -2, -3, -4
+ZP_DTYPE_F32, ZP_DTYPE_BF16 = 0, 1
+ZP_DEVERR_BLOCK_ID, ZP_DEVERR_SEQ_LEN, ZP_DEVERR_SLOT, ZP_DEVERR_KEEP = 1, 2, 4, 8
+ZP_SCORE_GLOBAL, ZP_SCORE_POOL, ZP_SCORE_POOL_FIRST_ONLY, ZP_SCORE_REDUNDANCY = 1, 2, 4, 8
+ZP_SELECT_NO_COMPACT = 1
+
+
+class ZpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"zp status {status}: {msg}")
+        self.status = status
+
+
+class NoBlocks(ZpError):
+    pass
+
+
+class Geom(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "num_layers", "num_blocks", "block_size", "num_kv_heads", "num_q_heads",
+        "head_dim", "window", "max_slots", "n_max", "dtype")]
+
+
+class Cache(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("qwin", C.c_void_p),
+                ("gscore", C.c_void_p)]
+
+
+class ScoreParamsC(C.Structure):
+    _fields_ = [("alpha", C.c_float), ("lambda_", C.c_float), ("tau", C.c_float),
+                ("sim_threshold", C.c_float), ("pool_kernel", C.c_int32),
+                ("flags", C.c_uint32)]
+
+
+_lib = None
+_P = C.c_void_p
+_I32P = C.POINTER(C.c_int32)
+
+
+def _declare(lib):
+    g, c, sp = C.POINTER(Geom), C.POINTER(Cache), C.POINTER(ScoreParamsC)
+    i32, i64, sz, u32 = C.c_int32, C.c_int64, C.c_size_t, C.c_uint32
+    sigs = {
+        "zp_last_error": (C.c_char_p, []),
+        "zp_version": (C.c_char_p, []),
+        "zp_decode_workspace_size": (sz, [g, i32, i32]),
+        "zp_paged_decode": (C.c_int, [g, c, i32, i32, _P, _P, _P, _P, i32, _P, i32, _P, _P,
+                                      _P, _P, sz, _P]),
+        "zp_score_workspace_size": (sz, [g, i32, i32, i32]),
+        "zp_score_tokens": (C.c_int, [g, c, sp, i32, i32, i32, _P, i32, _P, i32, _P, _P, _P,
+                                      i64, _P, sz, _P]),
+        "zp_select_workspace_size": (sz, [g, i32, i32]),
+        "zp_select_compact": (C.c_int, [g, c, i32, i32, i32, _P, i64, _P, i32, _P, i32, _P,
+                                        i32, i32, _P, u32, _P, sz, _P]),
+        "zp_workspace_errors": (C.c_int, [_P, C.POINTER(C.c_uint32), _P]),
+        "zp_workspace_clear_errors": (C.c_int, [_P, _P]),
+        "zp_alloc_create": (_P, [i32]),
+        "zp_alloc_destroy": (None, [_P]),
+        "zp_block_alloc": (C.c_int, [_P, i32, _I32P]),
+        "zp_block_free": (C.c_int, [_P, _I32P, i32]),
+        "zp_block_share": (C.c_int, [_P, _I32P, i32]),
+        "zp_block_refcount": (i32, [_P, i32]),
+        "zp_num_free": (i32, [_P]),
+        "zp_num_blocks": (i32, [_P]),
+        "zp_plan_compress": (C.c_int, [_P, _I32P, i32, i32, _I32P, _I32P, _I32P, _I32P]),
+        "zp_commit_compress": (C.c_int, [_P, _I32P, i32, _I32P, i32]),
+        "zp_abort_compress": (C.c_int, [_P, _I32P, i32, _I32P, i32]),
+        "zp_capacity": (C.c_int, [i64, i64, i64, i64, i32, C.POINTER(i64), C.POINTER(i64)]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+def lib():
+    """The loaded libzp (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m compressed_paged_kv_gqa_amd._build` (there is no fallback path)")
+        _lib = _declare(C.CDLL(LIB_PATH))
+    return _lib
+
+
+def header_symbols():
+    """Function names declared in include/zp.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zp_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status, what=""):
+    if status == ZP_OK:
+        return
+    msg = lib().zp_last_error().decode()
+    if status == ZP_ENOBLOCKS:
+        raise NoBlocks(status, msg)
+    raise ZpError(status, f"{what}: {msg}" if what else msg)
+
+
+# --------------------------------------------------------------------------
+# Geometry and caches
+# --------------------------------------------------------------------------
+
+@dataclass
+class CacheGeometry:
+    num_layers: int
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int
+    window: int
+    max_slots: int
+    n_max: int
+    dtype: str = "bf16"        # "bf16" or "f32"
+
+    @property
+    def group(self):
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def keep(self):
+        """Tokens kept per compression, k = (N_max - 1) b."""
+        return (self.n_max - 1) * self.block_size
+
+    def c(self):
+        return Geom(self.num_layers, self.num_blocks, self.block_size, self.num_kv_heads,
+                    self.num_q_heads, self.head_dim, self.window, self.max_slots, self.n_max,
+                    ZP_DTYPE_BF16 if self.dtype == "bf16" else ZP_DTYPE_F32)
+
+    def torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+class PagedKVCache:
+    """Device buffers of K, V, the window query cache and the global-score
+    cache F, in the layouts include/zp.h documents. Allocated with torch."""
+
+    def __init__(self, geom: CacheGeometry, device="cuda", with_global=True, init=None):
+        import torch
+        self.geom = geom
+        dt = geom.torch_dtype()
+        G = geom
+        shape = (G.num_layers, G.num_blocks, G.num_kv_heads, G.block_size, G.head_dim)
+        alloc = torch.zeros if init == "zeros" else torch.empty
+        self.k = alloc(shape, dtype=dt, device=device)
+        self.v = alloc(shape, dtype=dt, device=device)
+        self.qwin = alloc((G.num_layers, max(G.max_slots, 1), G.num_kv_heads, G.group,
+                           G.window, G.head_dim), dtype=dt, device=device)
+        self.gscore = (alloc((G.num_layers, G.num_blocks, G.num_kv_heads, G.block_size),
+                             dtype=torch.float32, device=device) if with_global else None)
+
+    def c(self):
+        return Cache(self.k.data_ptr(), self.v.data_ptr(), self.qwin.data_ptr(),
+                     self.gscore.data_ptr() if self.gscore is not None else None)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, dtype, name, device=True):
+    import torch
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+# --------------------------------------------------------------------------
+# GPU entry points
+# --------------------------------------------------------------------------
+
+def zp_decode_workspace_size(geom: CacheGeometry, batch, max_seq_len):
+    return lib().zp_decode_workspace_size(C.byref(geom.c()), batch, max_seq_len)
+
+
+def zp_score_workspace_size(geom: CacheGeometry, layer_count, nreq, max_blocks):
+    return lib().zp_score_workspace_size(C.byref(geom.c()), layer_count, nreq, max_blocks)
+
+
+def zp_select_workspace_size(geom: CacheGeometry, layer_count, nreq):
+    return lib().zp_select_workspace_size(C.byref(geom.c()), layer_count, nreq)
+
+
+def new_workspace(nbytes, device="cuda"):
+    """A zero-filled device workspace (uint8), as the ABI expects on first use."""
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def zp_paged_decode(cache: PagedKVCache, layer, q, k_new, v_new, block_tables, seq_lens,
+                    max_seq_len, qslot, out, lse, workspace, stream=None):
+    import torch
+    geom = cache.geom
+    dt = geom.torch_dtype()
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out")):
+        _need(t, dt, n)
+    _need(block_tables, torch.int32, "block_tables")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(qslot, torch.int32, "qslot")
+    _need(lse, torch.float32, "lse")
+    batch = q.shape[0]
+    _check(lib().zp_paged_decode(
+        C.byref(geom.c()), C.byref(cache.c()), layer, batch, q.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
+        int(max_seq_len), _ptr(qslot), out.data_ptr(), _ptr(lse), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "zp_paged_decode")
+
+
+@dataclass
+class ScoreParams:
+    """Scoring hyper-parameters (defaults: Zipage App. C.8's recommendation,
+    lambda 0.2, tau 0.4, alpha 0.8, pooling at the first compression only,
+    lightning redundancy; p and the pooling width are readings: 0.9 and 7)."""
+    alpha: float = 0.8
+    lam: float = 0.2
+    tau: float = 0.4
+    p: float = 0.9
+    pool_kernel: int = 7
+    use_global: bool = True
+    use_pool: bool = True
+    pool_first_only: bool = True
+    use_redundancy: bool = True
+
+    def c(self):
+        flags = ((ZP_SCORE_GLOBAL if self.use_global else 0)
+                 | (ZP_SCORE_POOL if self.use_pool else 0)
+                 | (ZP_SCORE_POOL_FIRST_ONLY if self.pool_first_only else 0)
+                 | (ZP_SCORE_REDUNDANCY if self.use_redundancy else 0))
+        return ScoreParamsC(self.alpha, self.lam, self.tau, self.p, self.pool_kernel, flags)
+
+
+def zp_score_tokens(cache: PagedKVCache, params: ScoreParams, layer_begin, layer_count,
+                    block_tables, num_blocks, max_blocks, qslot, first_compression, scores,
+                    workspace, stream=None):
+    import torch
+    _need(block_tables, torch.int32, "block_tables")
+    _need(num_blocks, torch.int32, "num_blocks")
+    _need(qslot, torch.int32, "qslot")
+    _need(first_compression, torch.uint8, "first_compression")
+    _need(scores, torch.float32, "scores")
+    nreq = block_tables.shape[0]
+    _check(lib().zp_score_tokens(
+        C.byref(cache.geom.c()), C.byref(cache.c()), C.byref(params.c()), layer_begin,
+        layer_count, nreq, block_tables.data_ptr(), block_tables.shape[1],
+        num_blocks.data_ptr(), int(max_blocks), qslot.data_ptr(), first_compression.data_ptr(),
+        scores.data_ptr(), scores.shape[-1], workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "zp_score_tokens")
+
+
+def zp_select_compact(cache: PagedKVCache, layer_begin, layer_count, scores, src_tables,
+                      num_blocks, max_blocks, dst_tables, keep, kept_idx, workspace,
+                      flags=0, stream=None):
+    import torch
+    _need(scores, torch.float32, "scores")
+    _need(src_tables, torch.int32, "src_tables")
+    _need(num_blocks, torch.int32, "num_blocks")
+    _need(dst_tables, torch.int32, "dst_tables")
+    _need(kept_idx, torch.int32, "kept_idx")
+    nreq = src_tables.shape[0]
+    _check(lib().zp_select_compact(
+        C.byref(cache.geom.c()), C.byref(cache.c()), layer_begin, layer_count, nreq,
+        scores.data_ptr(), scores.shape[-1], src_tables.data_ptr(), src_tables.shape[1],
+        num_blocks.data_ptr(), int(max_blocks), _ptr(dst_tables),
+        dst_tables.shape[1] if dst_tables is not None else 0, int(keep), _ptr(kept_idx),
+        int(flags), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "zp_select_compact")
+
+
+def zp_workspace_errors(workspace, stream=None):
+    flags = C.c_uint32(0)
+    _check(lib().zp_workspace_errors(workspace.data_ptr(), C.byref(flags), _stream(stream)),
+           "zp_workspace_errors")
+    return flags.value
+
+
+def zp_workspace_clear_errors(workspace, stream=None):
+    _check(lib().zp_workspace_clear_errors(workspace.data_ptr(), _stream(stream)),
+           "zp_workspace_clear_errors")
+
+
+# --------------------------------------------------------------------------
+# Host allocator and planner
+# --------------------------------------------------------------------------
+
+def _arr(xs):
+    xs = list(xs)
+    return (C.c_int32 * max(len(xs), 1))(*xs)
+
+
+class BlockAllocator:
+    """Refcounted block pool (zp_alloc_*, zp_block_*, zp_plan/commit/abort)."""
+
+    def __init__(self, num_blocks):
+        self._h = lib().zp_alloc_create(num_blocks)
+        if not self._h:
+            raise ZpError(ZP_EINVAL, lib().zp_last_error().decode())
+
+    def close(self):
+        if self._h:
+            lib().zp_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n):
+        ids = (C.c_int32 * max(n, 1))()
+        _check(lib().zp_block_alloc(self._h, n, ids), "zp_block_alloc")
+        return list(ids[:n])
+
+    def free(self, ids):
+        ids = list(ids)
+        _check(lib().zp_block_free(self._h, _arr(ids), len(ids)), "zp_block_free")
+
+    def share(self, ids):
+        ids = list(ids)
+        _check(lib().zp_block_share(self._h, _arr(ids), len(ids)), "zp_block_share")
+
+    def refcount(self, i):
+        return lib().zp_block_refcount(self._h, i)
+
+    @property
+    def num_free(self):
+        return lib().zp_num_free(self._h)
+
+    @property
+    def num_blocks(self):
+        return lib().zp_num_blocks(self._h)
+
+    def plan_compress(self, table, n_max):
+        """Returns (dst_table [n_max-1], new_table [n_max], release list)."""
+        table = list(table)
+        dst = (C.c_int32 * (n_max - 1))()
+        new = (C.c_int32 * n_max)()
+        rel = (C.c_int32 * max(len(table), 1))()
+        nrel = C.c_int32(0)
+        _check(lib().zp_plan_compress(self._h, _arr(table), len(table), n_max, dst, new, rel,
+                                      C.byref(nrel)), "zp_plan_compress")
+        return list(dst), list(new), list(rel[:nrel.value])
+
+    def commit_compress(self, old_table, new_table):
+        _check(lib().zp_commit_compress(self._h, _arr(old_table), len(old_table),
+                                        _arr(new_table), len(new_table)), "zp_commit_compress")
+
+    def abort_compress(self, old_table, new_table):
+        _check(lib().zp_abort_compress(self._h, _arr(old_table), len(old_table),
+                                       _arr(new_table), len(new_table)), "zp_abort_compress")
+
+
+def zp_capacity(m_avail, m_kv, m_f, m_q, n_max):
+    M = C.c_int64(0)
+    N = C.c_int64(0)
+    _check(lib().zp_capacity(m_avail, m_kv, m_f, m_q, n_max, C.byref(M), C.byref(N)),
+           "zp_capacity")
+    return M.value, N.value

@@ -1,0 +1,306 @@
+/*
+ * zp.h - C ABI of the compressed paged KV hot path for AMD Instinct MI355X
+ * (gfx950): grouped-query decode attention over block tables, per-token
+ * importance scoring, top-k selection with page compaction, and the host
+ * block allocator / compression planner.
+ *
+ * Method: "Zipage: Maintain High Request Concurrency for LLM Reasoning
+ * through Compressed PagedAttention" (Liao et al., arXiv 2603.08743), cited
+ * below as "Zipage" with section, algorithm, equation or figure.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Plain C types only. Pointers marked [device] must point to GPU memory
+ *    the caller owns (the library never allocates or frees device memory);
+ *    pointers marked [host] are ordinary host memory.
+ *  - GPU calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream). They return after enqueueing work. Argument
+ *    validation happens on the host before anything is enqueued: a call that
+ *    returns an error has enqueued nothing and changed nothing.
+ *  - No exception crosses the ABI. A failing call returns a negative
+ *    zp_status and zp_last_error() returns a message for the calling thread.
+ *  - Workspaces: every GPU call takes a caller-owned device workspace of at
+ *    least the size its *_workspace_size function returns. Its first 256
+ *    bytes are a header whose first uint32 collects device-side error bits
+ *    (ZP_DEVERR_*). The caller zero-fills a workspace once before first use;
+ *    the kernels leave every internal counter at zero when they finish, so a
+ *    workspace can be reused by later calls on the same stream. Calls that
+ *    share one workspace must not overlap in time.
+ *  - Device-side validation: kernels never read or write outside the buffers
+ *    the geometry describes. A block id outside [0, num_blocks), a sequence
+ *    longer than its table or than the launch bound, or a query slot outside
+ *    [0, max_slots) sets a ZP_DEVERR_* bit; the affected outputs are written
+ *    as NaN (decode) or left unmodified (scoring, compaction). Read the bits
+ *    with zp_workspace_errors().
+ *
+ * Cache layouts (row-major, innermost last)
+ * -----------------------------------------
+ *   K, V   [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ *   Qwin   [num_layers][max_slots][num_kv_heads][g][window][head_dim],
+ *          g = num_q_heads / num_kv_heads; query head j belongs to kv-head
+ *          j / g (contiguous grouping).
+ *   F      [num_layers][num_blocks][num_kv_heads][block_size] float32
+ * These hold the contents Zipage Sec. 3 (K, V), Sec. 4.2 (query cache) and
+ * App. C.3 (global score cache F) define; only the axis order differs: one
+ * (layer, block, kv-head) slice of K or V is contiguous.
+ */
+#ifndef ZP_H_
+#define ZP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Status                                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef enum zp_status {
+  ZP_OK = 0,
+  ZP_EINVAL = -1,     /* invalid argument or unsupported geometry            */
+  ZP_ENOBLOCKS = -2,  /* not enough free blocks; state unchanged             */
+  ZP_EHIP = -3,       /* a HIP runtime call failed                           */
+  ZP_ESTATE = -4      /* allocator misuse: double free, refcount underflow   */
+} zp_status;
+
+/* Device-side error bits (first uint32 of a workspace). */
+#define ZP_DEVERR_BLOCK_ID 0x1u  /* block id outside [0, num_blocks)          */
+#define ZP_DEVERR_SEQ_LEN 0x2u   /* sequence longer than its table / launch   */
+#define ZP_DEVERR_SLOT 0x4u      /* query slot outside [0, max_slots)         */
+#define ZP_DEVERR_KEEP 0x8u      /* keep > resident tokens of a request       */
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char* zp_last_error(void);
+const char* zp_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Geometry                                                                  */
+/* ------------------------------------------------------------------------ */
+
+typedef enum zp_dtype { ZP_DTYPE_F32 = 0, ZP_DTYPE_BF16 = 1 } zp_dtype;
+
+/* Shapes of the pre-allocated caches (Zipage Sec. 3 and Sec. 4.2).
+ * Supported: head_dim in {64, 128}; block_size a multiple of 16 in
+ * [16, 256]; num_q_heads a multiple of num_kv_heads with g in {1, 2, 4, 8};
+ * 1 <= window <= block_size and g * window a multiple of 16, at most 128;
+ * n_max >= 2. */
+typedef struct zp_geom {
+  int32_t num_layers;   /* L                                               */
+  int32_t num_blocks;   /* N_total blocks in the pool                      */
+  int32_t block_size;   /* b tokens per block                              */
+  int32_t num_kv_heads; /* h_kv                                            */
+  int32_t num_q_heads;  /* h_q                                             */
+  int32_t head_dim;     /* d                                               */
+  int32_t window;       /* w, observation window                           */
+  int32_t max_slots;    /* M, query-cache slots                            */
+  int32_t n_max;        /* N_max, blocks a request keeps after compression */
+  int32_t dtype;        /* zp_dtype of K, V, Qwin, q, k/v_new and outputs  */
+} zp_geom;
+
+/* Device buffers of the caches, all [device], caller-owned. */
+typedef struct zp_cache {
+  void* k;       /* K cache                                              */
+  void* v;       /* V cache                                              */
+  void* qwin;    /* query cache of the observation window                */
+  float* gscore; /* global score cache F, or NULL when it is not used    */
+} zp_cache;
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention (Zipage Sec. 3 block tables; Sec. 6: eviction leaves the */
+/* attention forward an ordinary softmax attention over resident tokens)     */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace zp_paged_decode needs for `batch` rows whose resident
+ * lengths are at most `max_seq_len`. */
+size_t zp_decode_workspace_size(const zp_geom* geom, int32_t batch, int32_t max_seq_len);
+
+/* One decode step of one layer for `batch` requests.
+ *
+ * For each row i with n = seq_lens[i] > 0 (n counts the token being decoded):
+ *   1. the token's k_new[i], v_new[i] are written to block
+ *      block_tables[i*table_stride + (n-1)/b], slot (n-1)%b of layer `layer`;
+ *   2. if qslot != NULL, qslot[i] >= 0 and (n-1)%b >= b-w, q[i] is written to
+ *      row (n-1)%b-(b-w) of query-cache slot qslot[i] (Zipage Sec. 4.2: the
+ *      window is the last w slots of the final block);
+ *   3. out[i][j] = sum_t softmax_t(q[i][j] . k_t / sqrt(d)) v_t over the n
+ *      resident tokens of kv-head j/g, and lse[i][j] = log sum_t exp(.) if
+ *      lse != NULL.
+ * Rows with seq_lens[i] <= 0 are skipped (nothing written).
+ *
+ *   q       [device] [batch][h_q][d] dtype
+ *   k_new   [device] [batch][h_kv][d] dtype;  v_new likewise
+ *   block_tables [device] int32 [batch][table_stride]
+ *   seq_lens     [device] int32 [batch], each <= max_seq_len [host value]
+ *   qslot        [device] int32 [batch] or NULL
+ *   out     [device] [batch][h_q][d] dtype
+ *   lse     [device] float32 [batch][h_q] or NULL
+ * Errors: ZP_EINVAL for bad geometry/arguments or a short workspace.
+ */
+zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t layer,
+                          int32_t batch, const void* q, const void* k_new, const void* v_new,
+                          const int32_t* block_tables, int32_t table_stride,
+                          const int32_t* seq_lens, int32_t max_seq_len, const int32_t* qslot,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Importance scores (Zipage Sec. 4.2; App. C.2 Alg. 1, C.3 Alg. 2, C.4,     */
+/* C.5 eq. (4), C.7 lightning redundancy, C.8 tempered softmax)              */
+/* ------------------------------------------------------------------------ */
+
+#define ZP_SCORE_GLOBAL 0x1u          /* decayed global score (Alg. 2)            */
+#define ZP_SCORE_POOL 0x2u            /* max pooling along the sequence (eq. (3)) */
+#define ZP_SCORE_POOL_FIRST_ONLY 0x4u /* pool only at a request's first compression */
+#define ZP_SCORE_REDUNDANCY 0x8u      /* lightning key redundancy, S - lambda R   */
+
+typedef struct zp_score_params {
+  float alpha;         /* decay of the global score                          */
+  float lambda_;       /* weight of the redundancy score                     */
+  float tau;           /* softmax temperature of the redundancy score (> 0)  */
+  float sim_threshold; /* p: cosine above which the last entry per column is
+                          zeroed; must be >= 0                               */
+  int32_t pool_kernel; /* odd pooling width >= 1                             */
+  uint32_t flags;      /* ZP_SCORE_* bits                                    */
+} zp_score_params;
+
+size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t nreq,
+                               int32_t max_blocks);
+
+/* Final per-token scores of `nreq` requests whose blocks are all full, for
+ * layers [layer_begin, layer_begin + layer_count) (the layer stride of
+ * Zipage App. C.1) and every kv-head. For request r with N = num_blocks[r]
+ * blocks (n = N*b tokens, N <= max_blocks) and window queries in query-cache
+ * slot qslot[r]:
+ *   S0 = mean over the window of the max over the g query heads of
+ *        softmax_t(q.k_t/sqrt(d)), the last block causally masked;
+ *   S1 = global score (F read and updated in place when ZP_SCORE_GLOBAL;
+ *        first_compression[r] != 0 means the request was never compressed);
+ *   S2 = max-pooled S1 (when ZP_SCORE_POOL, and first_compression[r] if
+ *        ZP_SCORE_POOL_FIRST_ONLY);
+ *   S3 = S2 - lambda * softmax_t(r_t / n / tau), r_t the lightning row sums,
+ *        when ZP_SCORE_REDUNDANCY;
+ *   scores = S3 with +inf on the last w positions.
+ *
+ *   block_tables [device] int32 [nreq][table_stride]
+ *   num_blocks   [device] int32 [nreq];  qslot [device] int32 [nreq]
+ *   first_compression [device] uint8 [nreq]
+ *   scores [device] float32 [layer_count][nreq][h_kv][scores_stride],
+ *          scores_stride >= max_blocks*b; entries past n are not written.
+ */
+zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
+                          const zp_score_params* params, int32_t layer_begin,
+                          int32_t layer_count, int32_t nreq, const int32_t* block_tables,
+                          int32_t table_stride, const int32_t* num_blocks, int32_t max_blocks,
+                          const int32_t* qslot, const uint8_t* first_compression, float* scores,
+                          int64_t scores_stride, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Top-k selection and compaction (Zipage Sec. 4.2, App. C.6 Alg. 4,         */
+/* Sec. 4.4 target blocks)                                                   */
+/* ------------------------------------------------------------------------ */
+
+#define ZP_SELECT_NO_COMPACT 0x1u /* only select; leave K, V, F untouched */
+
+size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t nreq);
+
+/* For every (layer, request, kv-head): keep the `keep` tokens with the
+ * highest score (ties go to the higher token index), and move their K, V and
+ * (if cache->gscore != NULL) F entries, in ascending token order, to logical
+ * slots 0..keep-1 of the target blocks dst_tables[r][0..]. keep is normally
+ * (N_max - 1) * b. kept_idx, if not NULL, receives the ascending token
+ * indices.
+ *
+ * Precondition (in-place safety): each target block dst_tables[r][i] is
+ * either src_tables[r][i] or a block that src_tables[r] does not contain.
+ * zp_plan_compress produces targets of this form.
+ *
+ *   scores   [device] float32 [layer_count][nreq][h_kv][scores_stride]
+ *   src_tables [device] int32 [nreq][src_stride]; num_blocks [device] int32 [nreq]
+ *   dst_tables [device] int32 [nreq][dst_stride], dst_stride*b >= keep
+ *   kept_idx [device] int32 [layer_count][nreq][h_kv][keep] or NULL
+ * keep must be in [1, 8192].
+ */
+zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cache, int32_t layer_begin,
+                            int32_t layer_count, int32_t nreq, const float* scores,
+                            int64_t scores_stride, const int32_t* src_tables, int32_t src_stride,
+                            const int32_t* num_blocks, int32_t max_blocks,
+                            const int32_t* dst_tables, int32_t dst_stride, int32_t keep,
+                            int32_t* kept_idx, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Waits for `stream`, then copies the workspace's device error bits to
+ * *flags [host]. */
+zp_status zp_workspace_errors(const void* workspace, uint32_t* flags, void* stream);
+/* Clears the workspace's device error bits (enqueued on `stream`). */
+zp_status zp_workspace_clear_errors(void* workspace, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator and compression planner (Zipage Sec. 3, Sec. 4.1,    */
+/* Sec. 4.4). Host-only; one handle is not thread-safe (callers serialise,   */
+/* like a single scheduler).                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct zp_alloc zp_alloc;
+
+/* Pool of block ids 0..num_blocks-1, all free. NULL on bad size. */
+zp_alloc* zp_alloc_create(int32_t num_blocks);
+void zp_alloc_destroy(zp_alloc* a);
+
+/* Takes n free blocks (refcount 1) into ids[0..n) [host], lowest ids first.
+ * All or nothing: ZP_ENOBLOCKS leaves the pool unchanged. */
+zp_status zp_block_alloc(zp_alloc* a, int32_t n, int32_t* ids);
+/* Drops one reference of each listed block; a block whose count reaches 0
+ * returns to the pool. ZP_ESTATE (state unchanged) if any listed block is
+ * already free or would be released twice by this call. */
+zp_status zp_block_free(zp_alloc* a, const int32_t* ids, int32_t n);
+/* Adds one reference to each listed (allocated) block: prefix sharing. */
+zp_status zp_block_share(zp_alloc* a, const int32_t* ids, int32_t n);
+/* Reference count of a block (0 = free), or -1 for an id out of range. */
+int32_t zp_block_refcount(const zp_alloc* a, int32_t id);
+int32_t zp_num_free(const zp_alloc* a);
+int32_t zp_num_blocks(const zp_alloc* a);
+
+/* Plans one compression of a request holding table[0..n_blocks) [host]
+ * (n_blocks >= n_max >= 2). Blocks with refcount > 1 are shared and must form
+ * a prefix of the table. Target rule (Zipage Sec. 4.4): with N_prefix shared
+ * blocks, if N_prefix >= n_max-1 all n_max-1 targets are new blocks, else the
+ * shared positions get new blocks and the other positions keep the request's
+ * own blocks; new blocks take the logical positions of the shared ones. The
+ * reserved n_max-th block (Sec. 4.1) is the first own block not used as a
+ * target, or a new block if there is none. Fresh blocks are allocated here,
+ * all or nothing (ZP_ENOBLOCKS leaves everything unchanged: the request
+ * stays uncompressed and the caller must wait or preempt).
+ *   dst_table [host] int32 [n_max-1]  targets for zp_select_compact
+ *   new_table [host] int32 [n_max]    table after the compression
+ *   release   [host] int32 [n_blocks] own blocks that commit will free
+ *   n_release [host] their count */
+zp_status zp_plan_compress(zp_alloc* a, const int32_t* table, int32_t n_blocks, int32_t n_max,
+                           int32_t* dst_table, int32_t* new_table, int32_t* release,
+                           int32_t* n_release);
+/* Finishes a planned compression once its compaction has completed on the
+ * GPU: every block of old_table that is not in new_table loses one reference
+ * (shared blocks drop by one, released own blocks return to the pool). */
+zp_status zp_commit_compress(zp_alloc* a, const int32_t* old_table, int32_t n_blocks,
+                             const int32_t* new_table, int32_t n_max);
+/* Abandons a planned compression: frees the fresh blocks of new_table (those
+ * not in old_table); the request keeps old_table. */
+zp_status zp_abort_compress(zp_alloc* a, const int32_t* old_table, int32_t n_blocks,
+                            const int32_t* new_table, int32_t n_max);
+
+/* Capacity (Zipage Sec. 4.2 eq. (1); App. C.3 eq. (2)): with m_blk = m_kv +
+ * m_f bytes per block (m_f = global-score bytes per block, 0 if unused) and
+ * m_q query-cache bytes per request,
+ *   M = floor(m_avail / (m_blk*n_max + m_q)),
+ *   N_total = floor(m_avail / (m_blk + m_q/n_max)). */
+zp_status zp_capacity(int64_t m_avail, int64_t m_kv, int64_t m_f, int64_t m_q, int32_t n_max,
+                      int64_t* max_concurrency, int64_t* num_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZP_H_ */

@@ -1,0 +1,128 @@
+"""GPU parity of zp_paged_decode against the float64 oracle.
+
+Zipage (arXiv 2603.08743) Sec. 3 / Sec. 6: decode attention over a block
+table is softmax attention over the resident tokens; Sec. 4.2: the query of
+each of the last w slots of a block goes to the query cache.
+Bar: max |out - ref| <= tol * max |ref| per (sequence, query head), tol 1e-5
+for fp32 and 2e-2 for bf16; appended K/V and captured queries bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_paged_kv_gqa_amd import synth, zp
+from oracle import zipage as Z
+
+from gpu_cases import HostCache, announce, dev_i32, random_tables, tol_for
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, d, h_q, h_kv, b, w, lens (resident after the append)
+    ("f32", 64, 4, 1, 16, 8, [1, 17, 208, 16, 300]),
+    ("bf16", 128, 32, 8, 256, 16, [1, 255, 256, 257, 1793, 2048, 3000, 4097]),
+    ("bf16", 64, 8, 8, 32, 16, [5, 64, 640]),
+    ("f32", 128, 16, 2, 64, 2, [70, 129, 1200]),
+    ("bf16", 128, 8, 4, 128, 8, [1, 1024, 2500]),
+]
+
+
+def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=()):
+    announce(f"decode dtype={dtype} d={d} hq={h_q} hkv={h_kv} b={b} lens={lens}")
+    B = len(lens)
+    nb = [-(-n // b) for n in lens]
+    stride = max(nb) + 1
+    pool = sum(nb) + 3
+    geom = zp.CacheGeometry(num_layers=2, num_blocks=pool, block_size=b, num_kv_heads=h_kv,
+                            num_q_heads=h_q, head_dim=d, window=w, max_slots=B, n_max=2,
+                            dtype=dtype)
+    hc = HostCache(geom, seed, 1)
+    tab = random_tables(seed, 1, nb, pool, stride)
+    g = synth.rng(seed, 1, layer, "step_q")
+    q = synth.cast(g.standard_normal((B, h_q, d)), dtype)
+    kn = synth.cast(g.standard_normal((B, h_kv, d)), dtype)
+    vn = synth.cast(g.standard_normal((B, h_kv, d)), dtype)
+    seq = np.array(lens, np.int32)
+    for r in skip_rows:
+        seq[r] = 0
+    qslot = np.arange(B, dtype=np.int32)
+    dt = geom.torch_dtype()
+    tq = torch.from_numpy(q).to(dt).cuda()
+    tk = torch.from_numpy(kn).to(dt).cuda()
+    tv = torch.from_numpy(vn).to(dt).cuda()
+    out = torch.full((B, h_q, d), 7.0, dtype=dt, device="cuda")
+    lse = torch.zeros((B, h_q), dtype=torch.float32, device="cuda")
+    max_len = max(lens)
+    ws = zp.new_workspace(zp.zp_decode_workspace_size(geom, B, max_len))
+    zp.zp_paged_decode(hc.dev, layer, tq, tk, tv, dev_i32(tab), dev_i32(seq), max_len,
+                       dev_i32(qslot), out, lse, ws)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(ws) == 0
+    out_h = out.float().cpu().numpy().astype(np.float64)
+    lse_h = lse.cpu().numpy()
+    tol = tol_for(dtype)
+    K_after = hc.dev.k.float().cpu().numpy()
+    V_after = hc.dev.v.float().cpu().numpy()
+    Q_after = hc.dev.qwin.float().cpu().numpy()
+    expK, expV, expQ = hc.K.copy(), hc.V.copy(), hc.Q.copy()
+    for r in range(B):
+        if seq[r] <= 0:
+            assert np.all(out_h[r] == 7.0)
+            continue
+        n = lens[r]
+        Kr = np.stack([Z.gather_sequence(hc.K[layer, :, h], tab[r], n - 1, b) for h in range(h_kv)])
+        Vr = np.stack([Z.gather_sequence(hc.V[layer, :, h], tab[r], n - 1, b) for h in range(h_kv)])
+        Kr = np.concatenate([Kr, kn[r][:, None, :].astype(np.float64)], axis=1)
+        Vr = np.concatenate([Vr, vn[r][:, None, :].astype(np.float64)], axis=1)
+        o_ref, lse_ref = Z.decode_attention(q[r], Kr, Vr)
+        for j in range(h_q):
+            err = np.abs(out_h[r, j] - o_ref[j]).max()
+            assert err <= tol * np.abs(o_ref[j]).max(), (r, j, err)
+        np.testing.assert_allclose(lse_h[r], lse_ref, atol=1e-4 if dtype == "bf16" else 2e-5)
+        pg, sl = tab[r][(n - 1) // b], (n - 1) % b
+        expK[layer, pg, :, sl] = kn[r]
+        expV[layer, pg, :, sl] = vn[r]
+        if sl >= b - w:
+            gq = h_q // h_kv
+            expQ[layer, r] = expQ[layer, r]
+            for j in range(h_q):
+                expQ[layer, r, j // gq, j % gq, sl - (b - w)] = q[r, j]
+    np.testing.assert_array_equal(K_after, expK)
+    np.testing.assert_array_equal(V_after, expV)
+    np.testing.assert_array_equal(Q_after, expQ)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2]//c[3]}-b{c[4]}" for c in CASES])
+def test_decode_parity(case):
+    _run_case(*case)
+
+
+def test_decode_skips_rows_with_zero_length():
+    _run_case("bf16", 128, 32, 8, 256, 16, [300, 1000, 2000], skip_rows=(1,))
+
+
+def test_decode_reports_bad_block_ids_without_faulting():
+    """A table entry outside the pool is masked out and flagged; the kernel
+    never dereferences it."""
+    announce("decode bad block id")
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=4, block_size=16, num_kv_heads=1,
+                            num_q_heads=4, head_dim=64, window=8, max_slots=1, n_max=2, dtype="f32")
+    hc = HostCache(geom, 5, 2)
+    tab = np.array([[0, 99, 2]], np.int32)
+    q = torch.randn(1, 4, 64, device="cuda")
+    k = torch.randn(1, 1, 64, device="cuda")
+    out = torch.zeros(1, 4, 64, device="cuda")
+    ws = zp.new_workspace(zp.zp_decode_workspace_size(geom, 1, 40))
+    zp.zp_paged_decode(hc.dev, 0, q, k, k.clone(), dev_i32(tab), dev_i32([40]), 40, None, out,
+                       None, ws)
+    assert zp.zp_workspace_errors(ws) & zp.ZP_DEVERR_BLOCK_ID
+    assert torch.isfinite(out).all()
+    zp.zp_workspace_clear_errors(ws)
+    assert zp.zp_workspace_errors(ws) == 0
+    # a length beyond the launch bound poisons the row and is flagged
+    zp.zp_paged_decode(hc.dev, 0, q, k, k.clone(), dev_i32(tab), dev_i32([41]), 40, None, out,
+                       None, ws)
+    assert zp.zp_workspace_errors(ws) & zp.ZP_DEVERR_SEQ_LEN
+    assert torch.isnan(out).all()

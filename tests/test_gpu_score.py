@@ -1,0 +1,148 @@
+"""GPU parity of zp_score_tokens against the float64 oracle.
+
+Zipage (arXiv 2603.08743): App. C.2 Alg. 1 (window logits, causal last block,
+softmax, GQA max, window mean), App. C.3 Alg. 2 (global score with F updated
+in place), App. C.4 (pooling), App. C.5 eq. (4) / C.7 / C.8 (lightning
+redundancy, tempered softmax), Sec. 4.2 (+inf window).
+
+Bar (derived in the design doc): the GPU accumulates in fp32 from inputs that both
+sides hold exactly, so |S_gpu - S_ref| <= 2e-5 * max|S_ref| over the finite
+entries, +inf exactly on the window, and F within the same bound. Cases with
+p below the planted-cluster cosines check the redundancy threshold logic
+where no cosine lies near p (the test asserts that margin on the oracle side).
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_paged_kv_gqa_amd import synth, zp
+from oracle import zipage as Z
+
+from gpu_cases import HostCache, announce, dev_i32, random_tables
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 2e-5
+
+
+def _oracle_params(sp: zp.ScoreParams):
+    return Z.ScoreParams(alpha=sp.alpha, lam=sp.lam, tau=sp.tau, p=sp.p,
+                         pool_kernel=sp.pool_kernel, use_global=sp.use_global,
+                         use_pool=sp.use_pool, pool_first_only=sp.pool_first_only,
+                         use_redundancy=sp.use_redundancy, redundancy="lightning")
+
+
+def _planted_keys(hc, seed):
+    """Replace every key by a positive multiple of one of eight basis
+    directions: in-block cosines are then exactly 0 (different directions,
+    disjoint support, exact on both sides) or 1 up to rounding, far from any
+    threshold p in [0, 0.99)."""
+    g = synth.rng(seed, 9, 0, "misc")
+    G = hc.geom
+    lab = g.integers(0, 8, hc.K.shape[:4])
+    sc = g.uniform(0.5, 3.0, hc.K.shape[:4])
+    K = np.zeros_like(hc.K)
+    np.put_along_axis(K, lab[..., None], sc[..., None], axis=-1)
+    hc.K = synth.cast(K, G.dtype)
+
+
+def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, layer_count=2,
+         seed=11, planted=False, heavy=True):
+    announce(f"score dtype={dtype} d={d} g={h_q // h_kv} b={b} w={w} N={nblocks} first={first} "
+             f"sp={sp}")
+    nreq = len(nblocks)
+    max_blocks = max(nblocks)
+    pool = sum(nblocks) + 2
+    geom = zp.CacheGeometry(num_layers=L, num_blocks=pool, block_size=b, num_kv_heads=h_kv,
+                            num_q_heads=h_q, head_dim=d, window=w, max_slots=nreq + 1, n_max=2,
+                            dtype=dtype)
+    hc = HostCache(geom, seed, 2)
+    if heavy:
+        hc.plant_heavy(seed, 2)
+    tab = random_tables(seed, 2, nblocks, pool, max_blocks + 1)
+    if planted:
+        _planted_keys(hc, seed)
+    hc.upload()
+    qslot = np.array([(r + 1) % (nreq + 1) for r in range(nreq)], np.int32)
+    firsts = np.array([first(r) for r in range(nreq)], np.uint8)
+    stride = max_blocks * b + 5
+    scores = torch.full((layer_count, nreq, h_kv, stride), -7.0, device="cuda")
+    ws = zp.new_workspace(zp.zp_score_workspace_size(geom, layer_count, nreq, max_blocks))
+    zp.zp_score_tokens(hc.dev, sp, layer_begin, layer_count, dev_i32(tab), dev_i32(nblocks),
+                       max_blocks, dev_i32(qslot), torch.from_numpy(firsts).cuda(), scores, ws)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(ws) == 0
+    S_gpu = scores.cpu().numpy()
+    F_gpu = hc.dev.gscore.cpu().numpy()
+    op = _oracle_params(sp)
+    worst = 0.0
+    for li in range(layer_count):
+        l = layer_begin + li
+        for r in range(nreq):
+            n = nblocks[r] * b
+            for h in range(h_kv):
+                K = Z.gather_sequence(hc.K[l, :, h], tab[r], n, b)
+                Fo = Z.gather_sequence(hc.F[l, :, h], tab[r], n, b)
+                S_ref, F_ref, parts = Z.score_tokens(hc.Q[l, qslot[r], h], K, Fo, bool(firsts[r]),
+                                                     b, op, return_parts=True)
+                if sp.use_redundancy and planted:
+                    # no cosine within 1e-3 of p: the threshold decision is robust
+                    for i in range(nblocks[r]):
+                        C = Z.cosine_matrix(K[i * b:(i + 1) * b], K[i * b:(i + 1) * b])
+                        np.fill_diagonal(C, 0)
+                        off = C[C != 0]
+                        assert off.size == 0 or np.min(np.abs(off - sp.p)) > 1e-3
+                got = S_gpu[li, r, h]
+                assert np.all(got[n:] == -7.0)          # nothing written past n
+                got = got[:n]
+                fin = np.isfinite(S_ref)
+                assert np.array_equal(np.isinf(got), ~fin) and np.all(got[~fin] > 0)
+                scale = np.abs(S_ref[fin]).max()
+                err = np.abs(got[fin] - S_ref[fin]).max() / scale
+                worst = max(worst, err)
+                assert err <= SCORE_TOL, (li, r, h, err)
+                if sp.use_global:
+                    Fg = Z.gather_sequence(F_gpu[l, :, h], tab[r], n, b)
+                    np.testing.assert_allclose(Fg, F_ref, atol=SCORE_TOL * np.abs(F_ref).max())
+    print(f"max relative score error {worst:.3e}", flush=True)
+
+
+DEFAULT = zp.ScoreParams()
+
+
+def test_score_tiny_fp32_first_compression():
+    _run("f32", 64, 4, 1, 16, 8, [13], lambda r: 1, DEFAULT, L=1, layer_begin=0, layer_count=1)
+
+
+def test_score_tiny_fp32_later_compression_every_part():
+    sp = zp.ScoreParams(pool_first_only=False)
+    _run("f32", 64, 4, 1, 16, 8, [4, 6, 5], lambda r: r == 1, sp)
+
+
+def test_score_qwen_shape_bf16_mixed_first():
+    _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, DEFAULT)
+
+
+@pytest.mark.parametrize("flags", [
+    dict(use_global=False, use_pool=False, use_redundancy=False),
+    dict(use_pool=False),
+    dict(use_redundancy=False),
+    dict(use_global=False, pool_kernel=3),
+])
+def test_score_flag_combinations(flags):
+    sp = zp.ScoreParams(**flags)
+    _run("bf16", 128, 32, 8, 256, 16, [8, 8], lambda r: r == 0, sp, L=2, layer_begin=0,
+         layer_count=2)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.5])
+def test_score_redundancy_threshold_sweep_planted(p):
+    sp = zp.ScoreParams(p=p, use_global=False, use_pool=False)
+    _run("bf16", 128, 16, 4, 64, 16, [4, 3], lambda r: 1, sp, planted=True, heavy=False)
+
+
+def test_score_other_shapes():
+    _run("bf16", 64, 8, 8, 32, 16, [5, 2], lambda r: 0, DEFAULT, L=1, layer_begin=0,
+         layer_count=1)
+    _run("f32", 128, 16, 2, 64, 2, [3, 4], lambda r: 1, DEFAULT, L=1, layer_begin=0,
+         layer_count=1)
