@@ -15,9 +15,13 @@
 //    K (or V) and the head-major page layout keeps the stream sequential;
 //  * q.k partial dot products are all-reduced inside each row group with DPP
 //    (no LDS), softmax is online in exp2 form per chunk of tokens;
-//  * the split partials (max, sum, unnormalised output) are merged by the
-//    last workgroup of each (sequence, kv-head) to finish (device-scope
-//    fence + counter), so one launch covers the whole step;
+//  * a sequence is split over several workgroups only when the (sequence,
+//    kv-head) items alone cannot fill the GPU; then a second small kernel
+//    merges the split partials (max, sum, unnormalised output). A device-wide
+//    fence per workgroup (to merge in the same launch) costs far more than
+//    that extra launch on this chip (measured);
+//  * the block ids a workgroup needs are staged in LDS first, so no K/V load
+//    waits behind a block-table load;
 //  * the token being decoded is taken from k_new / v_new directly by the
 //    split that covers it, which also writes it to its page: no other
 //    workgroup reads that slot, so append and attention need no extra launch.
@@ -41,12 +45,11 @@ struct DecodeParams {
   void* out;
   float* lse;
   float* part;        // [batch][h_kv][max_splits][G][D + 2]
-  int32_t* counters;  // [batch][h_kv]
   uint32_t* err;
   int64_t kv_layer_off;    // element offset of the layer in K / V
   int64_t qwin_layer_off;  // element offset of the layer in Qwin
   int32_t table_stride, num_blocks, b, h_kv, w, max_slots;
-  int32_t split_tokens, max_splits, max_seq_len;
+  int32_t split_tokens, max_splits, max_seq_len, log2b;
   float qk_scale;  // log2(e) / sqrt(d)
 };
 
@@ -55,21 +58,76 @@ struct DecodeCfg {
   static constexpr int EPL = Vec16<T>::N;  // elements per lane per 16-byte load
   static constexpr int LPR = D / EPL;      // lanes per token row
   static constexpr int RPW = 64 / LPR;     // token rows per wavefront load
-  static constexpr int U = 4;              // row loads in flight per lane (K and V each)
-  static constexpr int TILE = RPW * U;     // tokens per wavefront iteration
+  static constexpr int CHUNK = 16;         // tokens per wavefront chunk (never crosses a block)
+  static constexpr int U = CHUNK / RPW;    // row loads per lane per chunk (K and V each)
   static constexpr int WAVES = 4;
+  // waves per SIMD the register budget is sized for (no spills)
+  static constexpr int MIN_WAVES = (sizeof(T) == 2 && G <= 4) || (D == 64 && G <= 4) ? 3 : 2;
 };
 
+// Query registers of one lane: its EPL dims of the g query heads.
+template <typename T, int G>
+struct QRegs;
+
+template <int G>
+struct QRegs<bf16_t, G> {
+  uint32_t w[G][4];  // 8 bf16 per head, packed in pairs
+  __device__ void load(const bf16_t* q, int64_t head_stride) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4 v = ld16(q + h * head_stride);
+      w[h][0] = v.x; w[h][1] = v.y; w[h][2] = v.z; w[h][3] = v.w;
+    }
+  }
+  // q_h . k over this lane's 8 dims (bf16 pairs, fp32 accumulation)
+  __device__ float dot(int h, const uint4& k) const {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w[h][0]),
+                                              __builtin_bit_cast(bf2, k.x), 0.f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w[h][1]),
+                                        __builtin_bit_cast(bf2, k.y), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w[h][2]),
+                                        __builtin_bit_cast(bf2, k.z), a, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w[h][3]),
+                                           __builtin_bit_cast(bf2, k.w), a, false);
+  }
+};
+
+template <int G>
+struct QRegs<float, G> {
+  float w[G][4];
+  __device__ void load(const float* q, int64_t head_stride) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) Vec16<float>::unpack(ld16(q + h * head_stride), w[h]);
+  }
+  __device__ float dot(int h, const uint4& k) const {
+    float a = w[h][0] * __uint_as_float(k.x);
+    a = fmaf(w[h][1], __uint_as_float(k.y), a);
+    a = fmaf(w[h][2], __uint_as_float(k.z), a);
+    return fmaf(w[h][3], __uint_as_float(k.w), a);
+  }
+};
+
+// Online-softmax state of one lane for its token-row group. Rescaling is
+// lazy: a chunk rescales only when its maximum exceeds the running one by
+// more than kLazy (log2 units), so p = exp2(s - m) stays below 2^kLazy.
+constexpr float kLazy = 8.0f;
+// Upper bound on the blocks one split covers (decode_split_tokens keeps
+// split_tokens <= kMaxSplitPages * block_size).
+constexpr int kMaxSplitPages = 1024;
+constexpr float kNoMax = -1.0e30f;  // finite "nothing seen yet"
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_decode_kernel(
+    DecodeParams P) {
   using C = DecodeCfg<T, D, G>;
-  constexpr int EPL = C::EPL, LPR = C::LPR, RPW = C::RPW, U = C::U, TILE = C::TILE;
+  constexpr int EPL = C::EPL, LPR = C::LPR, RPW = C::RPW, U = C::U, CHUNK = C::CHUNK;
   constexpr int WAVES = C::WAVES;
 
   __shared__ float sm_m[WAVES][G];
   __shared__ float sm_l[WAVES][G];
   __shared__ float sm_o[WAVES][G][D];
-  __shared__ int sm_last;
+  __shared__ int sm_pages[kMaxSplitPages];
 
   const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int n = P.seq_lens[seq];
@@ -94,128 +152,141 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams P) {
   const int t1 = min(n, t0 + P.split_tokens);
   const int row = lane / LPR;
   const int sub = lane % LPR;
+  const int b = P.b;
   const int32_t* tab = P.tables + (int64_t)seq * P.table_stride;
-  const T* kc = reinterpret_cast<const T*>(P.kc) + P.kv_layer_off;
-  const T* vc = reinterpret_cast<const T*>(P.vc) + P.kv_layer_off;
+  T* kc = reinterpret_cast<T*>(P.kc) + P.kv_layer_off;
+  T* vc = reinterpret_cast<T*>(P.vc) + P.kv_layer_off;
   const T* knew = reinterpret_cast<const T*>(P.k_new) + ((int64_t)seq * P.h_kv + kvh) * D + sub * EPL;
   const T* vnew = reinterpret_cast<const T*>(P.v_new) + ((int64_t)seq * P.h_kv + kvh) * D + sub * EPL;
-  const int64_t head_off = (int64_t)kvh * P.b * D + sub * EPL;  // within a page
-  const int64_t page_elems = (int64_t)P.h_kv * P.b * D;
+  const int64_t lane_off = (int64_t)kvh * b * D + (int64_t)row * D + sub * EPL;  // within a page
+  const int64_t page_elems = (int64_t)P.h_kv * b * D;
 
-  // Query rows of the group, this lane's EPL dims, in fp32.
-  float qf[G][EPL];
-  {
-    const T* qp = reinterpret_cast<const T*>(P.q) + out_row * D + sub * EPL;
-#pragma unroll
-    for (int h = 0; h < G; ++h) Vec16<T>::unpack(ld16(qp + (int64_t)h * D), qf[h]);
-  }
+  QRegs<T, G> q;
+  q.load(reinterpret_cast<const T*>(P.q) + out_row * D + sub * EPL, D);
+
+  // Block ids of this split (at most kMaxSplitPages by construction).
+  const int pg0 = t0 >> P.log2b;
+  const int npg = ((t1 - 1) >> P.log2b) - pg0 + 1;
+  for (int i = tid; i < npg; i += 256) sm_pages[i] = tab[pg0 + i];
+  __syncthreads();
 
   float m[G], l[G], o[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
+    m[h] = kNoMax;
     l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
   }
 
-  for (int base = t0 + wv * TILE; base < t1; base += WAVES * TILE) {
-    uint4 kr[U], vr[U];
-    bool valid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = base + u * RPW + row;
-      valid[u] = t < t1;
-      const int tt = valid[u] ? t : t0;
-      const T* kp;
-      const T* vp;
-      if (tt == n - 1) {
-        kp = knew;
-        vp = vnew;
-      } else {
-        const int page = tab[tt / P.b];
-        const bool ok = page >= 0 && page < P.num_blocks;
-        if (!ok) {
-          if (valid[u] && sub == 0) flag_error(P.err, ZP_DEVERR_BLOCK_ID);
-          valid[u] = false;
-        }
-        const int64_t off = (ok ? page : 0) * page_elems + head_off + (int64_t)(tt % P.b) * D;
-        kp = kc + off;
-        vp = vc + off;
-      }
-      kr[u] = ld16(kp);
-      vr[u] = ld16(vp);
-    }
+  const int nchunks = (t1 - t0 + CHUNK - 1) / CHUNK;
 
-    // Logits, pre-multiplied by log2(e)/sqrt(d).
-    float s[G][U];
+  // Element offset of this lane's row 0 in chunk c, or -1 for a bad block id.
+  auto chunk_offset = [&](int c) -> int64_t {
+    const int base = t0 + c * CHUNK;
+    const int page = sm_pages[(base >> P.log2b) - pg0];
+    if (page < 0 || page >= P.num_blocks) return -1;
+    return (int64_t)page * page_elems + lane_off + (int64_t)(base & (b - 1)) * D;
+  };
+  auto load_chunk = [&](int c, uint4 (&kr)[U], uint4 (&vr)[U]) -> int64_t {
+    const int64_t off = chunk_offset(c);
+    const int64_t safe = off < 0 ? lane_off : off;  // a valid address; the chunk is masked
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float kf[EPL];
-      Vec16<T>::unpack(kr[u], kf);
+      kr[u] = ld16(kc + safe + (int64_t)u * RPW * D);
+      vr[u] = ld16(vc + safe + (int64_t)u * RPW * D);
+    }
+    return off;
+  };
+  auto process = [&](int c, uint4 (&kr)[U], uint4 (&vr)[U], int64_t off) {
+    const int base = t0 + c * CHUNK;
+    if (off < 0 && lane == 0) flag_error(P.err, ZP_DEVERR_BLOCK_ID);
+    if (base <= n - 1 && n - 1 < base + CHUNK) {
+      // The token being decoded: take it from k_new / v_new and append it.
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[h][e], kf[e], acc);
-        s[h][u] = acc;
+      for (int u = 0; u < U; ++u) {
+        if (base + u * RPW + row == n - 1) {
+          kr[u] = ld16(knew);
+          vr[u] = ld16(vnew);
+          if (off >= 0) {
+            st16(kc + off + (int64_t)u * RPW * D, kr[u]);
+            st16(vc + off + (int64_t)u * RPW * D, vr[u]);
+          }
+        }
       }
     }
+    float s[G][U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float v = group_sum<LPR>(s[h][u]) * P.qk_scale;
-        s[h][u] = valid[u] ? v : -INFINITY;
-      }
-
-    // Online softmax update per head over this chunk.
-    float vf[U][EPL];
+      for (int h = 0; h < G; ++h) s[h][u] = group_sum<LPR>(q.dot(h, kr[u])) * P.qk_scale;
+    if (base + CHUNK > t1 || off < 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) Vec16<T>::unpack(vr[u], vf[u]);
+      for (int u = 0; u < U; ++u) {
+        const bool valid = off >= 0 && base + u * RPW + row < t1;
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[h][u] = valid ? s[h][u] : -INFINITY;
+      }
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float cm = s[h][0];
 #pragma unroll
       for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[h][u]);
-      cm = across_groups_max<LPR>(cm);
-      const float mn = fmaxf(m[h], cm);
-      if (mn == -INFINITY) continue;  // nothing visible yet
-      const float alpha = exp2f(m[h] - mn);
-      m[h] = mn;
-      l[h] *= alpha;
+      if (cm > m[h] + kLazy) {
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - cm);
+        l[h] *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+        for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+        m[h] = cm;
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = exp2f(s[h][u] - mn);
-        l[h] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p, vf[u][e], o[h][e]);
+        s[h][u] = __builtin_amdgcn_exp2f(s[h][u] - m[h]);  // p, in place
+        l[h] += s[h][u];
       }
     }
-
-    // Append the decoded token to its page (only the split holding n-1).
+    // o += p v, one V row at a time (keeps few unpacked values live).
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = base + u * RPW + row;
-      if (t == n - 1 && t < t1) {
-        const int page = tab[t / P.b];
-        if (page >= 0 && page < P.num_blocks) {
-          const int64_t off = (int64_t)page * page_elems + head_off + (int64_t)(t % P.b) * D;
-          st16(const_cast<T*>(kc) + off, kr[u]);
-          st16(const_cast<T*>(vc) + off, vr[u]);
-        }
-      }
+      float vf[EPL];
+      Vec16<T>::unpack(vr[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(s[h][u], vf[e], o[h][e]);
+    }
+  };
+
+  // Chunks c = wv, wv + 4, ...; the next chunk's loads are issued before the
+  // current chunk is processed (two register buffers).
+  {
+    uint4 ka[U], va[U], kb[U], vb[U];
+    int c = wv;
+    int64_t offa = 0, offb = 0;
+    if (c < nchunks) offa = load_chunk(c, ka, va);
+    while (c < nchunks) {
+      int cn = c + WAVES;
+      if (cn < nchunks) offb = load_chunk(cn, kb, vb);
+      process(c, ka, va, offa);
+      c = cn;
+      if (c >= nchunks) break;
+      cn = c + WAVES;
+      if (cn < nchunks) offa = load_chunk(cn, ka, va);
+      process(c, kb, vb, offb);
+      c = cn;
     }
   }
 
-  // Merge the row groups of the wavefront (m is already wavefront-uniform).
+  // Merge the token-row groups of the wavefront.
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    l[h] = across_groups_sum<LPR>(l[h]);
+    const float M = across_groups_max<LPR>(m[h]);
+    const float sc = __builtin_amdgcn_exp2f(m[h] - M);
+    l[h] = across_groups_sum<LPR>(l[h] * sc);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = across_groups_sum<LPR>(o[h][e]);
+    for (int e = 0; e < EPL; ++e) o[h][e] = across_groups_sum<LPR>(o[h][e] * sc);
+    m[h] = M;
   }
   if (lane < LPR) {
 #pragma unroll
@@ -259,20 +330,18 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams P) {
 #pragma unroll
   for (int k = 0; k < (PAIRS + 255) / 256; ++k) {
     const int i = tid + k * 256;
-    Mw[k] = -INFINITY; Lw[k] = 0.f; Ow[k] = 0.f;
+    Mw[k] = kNoMax; Lw[k] = 0.f; Ow[k] = 0.f;
     if (i < PAIRS) {
       const int h = i / D, e = i % D;
       float M = sm_m[0][h];
 #pragma unroll
       for (int w2 = 1; w2 < WAVES; ++w2) M = fmaxf(M, sm_m[w2][h]);
       float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
 #pragma unroll
-        for (int w2 = 0; w2 < WAVES; ++w2) {
-          const float sc = exp2f(sm_m[w2][h] - M);
-          L += sm_l[w2][h] * sc;
-          O += sm_o[w2][h][e] * sc;
-        }
+      for (int w2 = 0; w2 < WAVES; ++w2) {
+        const float sc = __builtin_amdgcn_exp2f(sm_m[w2][h] - M);
+        L += sm_l[w2][h] * sc;
+        O += sm_o[w2][h][e] * sc;
       }
       Mw[k] = M; Lw[k] = L; Ow[k] = O;
     }
@@ -292,7 +361,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams P) {
     return;
   }
 
-  // Several splits: publish this split's partial, the last one merges.
+  // Several splits: publish this split's partial; zp_decode_merge_kernel
+  // combines them.
   const int64_t item = (int64_t)seq * P.h_kv + kvh;
   float* mypart = P.part + (item * P.max_splits + split) * G * (D + 2);
 #pragma unroll
@@ -307,39 +377,43 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams P) {
       }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&P.counters[item], 1);
-    sm_last = (prev == nsplit - 1);
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
+}
+
+// Merges the split partials of every (sequence, kv-head) row that was split.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams P) {
+  const int kvh = blockIdx.x, seq = blockIdx.y;
+  const int n = P.seq_lens[seq];
+  if (n <= 0 || n > P.max_seq_len || n > (int64_t)P.table_stride * P.b) return;
+  const int nsplit = (n + P.split_tokens - 1) / P.split_tokens;
+  if (nsplit <= 1) return;  // written directly by the decode kernel
+  const int64_t item = (int64_t)seq * P.h_kv + kvh;
+  const int64_t out_row = (int64_t)seq * P.h_kv * G + (int64_t)kvh * G;
   const float* parts = P.part + item * P.max_splits * G * (D + 2);
-  for (int i = tid; i < PAIRS; i += 256) {
+  T* out = reinterpret_cast<T*>(P.out);
+  for (int i = threadIdx.x; i < G * D; i += 256) {
     const int h = i / D, e = i % D;
-    float M = -INFINITY;
+    float M = kNoMax;
     for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, parts[(s2 * G + h) * (D + 2)]);
     float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int s2 = 0; s2 < nsplit; ++s2) {
-        const float* pp = parts + (s2 * G + h) * (D + 2);
-        const float sc = exp2f(pp[0] - M);
-        L += pp[1] * sc;
-        O += pp[2 + e] * sc;
-      }
+    for (int s2 = 0; s2 < nsplit; ++s2) {
+      const float* pp = parts + (s2 * G + h) * (D + 2);
+      const float sc = __builtin_amdgcn_exp2f(pp[0] - M);
+      L += pp[1] * sc;
+      O += pp[2 + e] * sc;
     }
     out[(out_row + h) * D + e] = from_f32<T>(O / L);
     if (P.lse && e == 0) P.lse[out_row + h] = (M + log2f(L)) * kLn2;
   }
-  if (tid == 0) P.counters[item] = 0;  // leave the workspace reusable
 }
 
 template <typename T, int D, int G>
 static void launch_decode(const DecodeParams& P, int batch, hipStream_t stream) {
   dim3 grid(P.max_splits, P.h_kv, batch);
   hipLaunchKernelGGL((paged_decode_kernel<T, D, G>), grid, dim3(256), 0, stream, P);
+  if (P.max_splits > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(P.h_kv, batch), dim3(256), 0, stream,
+                       P);
 }
 
 template <typename T, int D>
@@ -353,15 +427,12 @@ static void dispatch_group(int g, const DecodeParams& P, int batch, hipStream_t 
 }
 
 static size_t decode_ws_layout(const zp_geom* g, int32_t batch, int32_t max_seq_len,
-                               size_t* counters_off, size_t* part_off, int32_t* split_tokens,
-                               int32_t* max_splits) {
+                               size_t* part_off, int32_t* split_tokens, int32_t* max_splits) {
   const int32_t st = decode_split_tokens(g, batch, max_seq_len);
   const int32_t ms = std::max<int32_t>(1, (std::max<int32_t>(max_seq_len, 1) + st - 1) / st);
   const size_t items = size_t(batch) * g->num_kv_heads;
-  const size_t c_off = kWsHeader;
-  const size_t p_off = round_up(c_off + items * sizeof(int32_t), 256);
-  const size_t total = p_off + items * ms * group_size(g) * (g->head_dim + 2) * sizeof(float);
-  if (counters_off) *counters_off = c_off;
+  const size_t p_off = kWsHeader;
+  const size_t total = p_off + (ms > 1 ? items * ms * group_size(g) * (g->head_dim + 2) * sizeof(float) : 0);
   if (part_off) *part_off = p_off;
   if (split_tokens) *split_tokens = st;
   if (max_splits) *max_splits = ms;
@@ -376,7 +447,7 @@ extern "C" size_t zp_decode_workspace_size(const zp_geom* geom, int32_t batch,
                                            int32_t max_seq_len) {
   if (validate_geom(geom, "zp_decode_workspace_size") != ZP_OK || batch < 0 || max_seq_len < 0)
     return 0;
-  return decode_ws_layout(geom, batch, max_seq_len, nullptr, nullptr, nullptr, nullptr);
+  return decode_ws_layout(geom, batch, max_seq_len, nullptr, nullptr, nullptr);
 }
 
 extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t layer,
@@ -397,10 +468,9 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
   if (!q || !k_new || !v_new || !block_tables || !seq_lens || !out || !workspace)
     return fail(ZP_EINVAL, "zp_paged_decode: NULL buffer");
   if (qslot && !cache->qwin) return fail(ZP_EINVAL, "zp_paged_decode: qslot given but qwin NULL");
-  size_t c_off, p_off;
+  size_t p_off;
   int32_t split_tokens, max_splits;
-  const size_t need =
-      decode_ws_layout(geom, batch, max_seq_len, &c_off, &p_off, &split_tokens, &max_splits);
+  const size_t need = decode_ws_layout(geom, batch, max_seq_len, &p_off, &split_tokens, &max_splits);
   if (workspace_bytes < need)
     return fail(ZP_EINVAL, "zp_paged_decode: workspace %zu bytes, need %zu", workspace_bytes, need);
 
@@ -411,7 +481,6 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
   P.out = out; P.lse = lse;
   char* ws = static_cast<char*>(workspace);
   P.err = reinterpret_cast<uint32_t*>(ws);
-  P.counters = reinterpret_cast<int32_t*>(ws + c_off);
   P.part = reinterpret_cast<float*>(ws + p_off);
   const int64_t d = geom->head_dim;
   P.kv_layer_off = int64_t(layer) * geom->num_blocks * geom->num_kv_heads * geom->block_size * d;
@@ -420,6 +489,7 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
   P.h_kv = geom->num_kv_heads; P.w = geom->window; P.max_slots = geom->max_slots;
   P.split_tokens = split_tokens; P.max_splits = max_splits; P.max_seq_len = max_seq_len;
   P.qk_scale = kLog2e / std::sqrt(float(d));
+  P.log2b = __builtin_ctz(unsigned(geom->block_size));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int g = group_size(geom);

@@ -259,8 +259,8 @@ zp_status zp::validate_geom(const zp_geom* g, const char* who) {
     return fail(ZP_EINVAL, "%s: unsupported dtype %d", who, g->dtype);
   if (g->head_dim != 64 && g->head_dim != 128)
     return fail(ZP_EINVAL, "%s: head_dim must be 64 or 128 (got %d)", who, g->head_dim);
-  if (g->block_size < 16 || g->block_size > 256 || g->block_size % 16 != 0)
-    return fail(ZP_EINVAL, "%s: block_size must be a multiple of 16 in [16, 256] (got %d)", who,
+  if (g->block_size < 16 || g->block_size > 256 || (g->block_size & (g->block_size - 1)) != 0)
+    return fail(ZP_EINVAL, "%s: block_size must be a power of two in [16, 256] (got %d)", who,
                 g->block_size);
   if (g->num_q_heads % g->num_kv_heads != 0)
     return fail(ZP_EINVAL, "%s: num_q_heads must be a multiple of num_kv_heads", who);
@@ -281,10 +281,18 @@ zp_status zp::validate_geom(const zp_geom* g, const char* who) {
 }
 
 int32_t zp::decode_split_tokens(const zp_geom* g, int32_t batch, int32_t max_seq_len) {
-  const int64_t items = int64_t(batch) * g->num_kv_heads;
-  const int64_t want_splits = std::max<int64_t>(1, (4096 + items - 1) / std::max<int64_t>(items, 1));
-  int64_t s = (std::max<int32_t>(max_seq_len, 1) + want_splits - 1) / want_splits;
-  s = std::max<int64_t>(256, std::min<int64_t>(1024, s));
+  // One workgroup per (sequence, kv-head) when those items fill the GPU
+  // (>= 1536 of them: two rounds of 3 resident workgroups on 256 CUs);
+  // otherwise split so that about 2048 workgroups run, with at least 512
+  // tokens each. A split covers at most ~1000 blocks (kMaxSplitPages = 1024).
+  const int64_t items = std::max<int64_t>(1, int64_t(batch) * g->num_kv_heads);
+  const int64_t len = std::max<int32_t>(max_seq_len, 1);
+  int64_t s = len;
+  if (items < 1536) {
+    const int64_t want = (2048 + items - 1) / items;
+    s = std::max<int64_t>(512, (len + want - 1) / want);
+  }
+  s = std::min<int64_t>(s, int64_t(1000) * g->block_size);
   s = (s + 63) / 64 * 64;
   return static_cast<int32_t>(s);
 }

@@ -208,21 +208,34 @@ class DecodeEngine:
             return
         nreq = len(ok)
         maxb = max(len(p[0]) for p in plans)
-        src = np.full((nreq, maxb), 0, np.int32)
+        nd = n_max - 1
+        # one pinned int32 staging buffer: src tables | dst tables | N | slot | first
+        meta = torch.zeros(nreq * (maxb + nd + 3), dtype=torch.int32).pin_memory()
+        m = meta.numpy()
+        src = m[:nreq * maxb].reshape(nreq, maxb)
+        dst = m[nreq * maxb:nreq * (maxb + nd)].reshape(nreq, nd)
+        tail = m[nreq * (maxb + nd):].reshape(3, nreq)
         for i, p in enumerate(plans):
             src[i, :len(p[0])] = p[0]
-        dst = np.array([p[1] for p in plans], np.int32)
-        nblk = np.array([len(p[0]) for p in plans], np.int32)
-        qslot = np.array(ok, np.int32)
-        first = np.array([self.reqs[s].first for s in ok], np.uint8)
+            dst[i] = p[1]
+        tail[0] = [len(p[0]) for p in plans]
+        tail[1] = ok
+        tail[2] = [1 if self.reqs[s].first else 0 for s in ok]
+        first = tail[2].astype(np.uint8)
         stream = self.side if self.async_compress else torch.cuda.current_stream()
         ready = torch.cuda.Event()
         ready.record()
-        bufs = []
+        bufs = [meta]
         with torch.cuda.stream(stream):
             stream.wait_event(ready)
-            dv = lambda a: torch.from_numpy(a).to(self.device, non_blocking=False)
-            src_d, dst_d, nblk_d, qslot_d, first_d = dv(src), dv(dst), dv(nblk), dv(qslot), dv(first)
+            meta_d = meta.to(self.device, non_blocking=True)
+            o = nreq * maxb
+            src_d = meta_d[:o].view(nreq, maxb)
+            dst_d = meta_d[o:o + nreq * nd].view(nreq, nd)
+            o += nreq * nd
+            nblk_d = meta_d[o:o + nreq]
+            qslot_d = meta_d[o + nreq:o + 2 * nreq]
+            first_d = meta_d[o + 2 * nreq:o + 3 * nreq].to(torch.uint8)
             ls = self.layer_stride if not self.record else G.num_layers
             scores = torch.empty((ls, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
                                  device=self.device)
@@ -240,7 +253,7 @@ class DecodeEngine:
                                      stream=stream)
             done = torch.cuda.Event()
             done.record(stream)
-            bufs = [src_d, dst_d, nblk_d, qslot_d, first_d, scores, sws, cws]
+            bufs += [meta_d, first_d, scores, sws, cws]
             if self.record:
                 self.log.append((list(ok), first.copy(), scores, kept))
         self.pending.append(_Pending(ok, plans, done, bufs))

@@ -83,7 +83,7 @@ const char* zp_version(void);
 typedef enum zp_dtype { ZP_DTYPE_F32 = 0, ZP_DTYPE_BF16 = 1 } zp_dtype;
 
 /* Shapes of the pre-allocated caches (Zipage Sec. 3 and Sec. 4.2).
- * Supported: head_dim in {64, 128}; block_size a multiple of 16 in
+ * Supported: head_dim in {64, 128}; block_size a power of two in
  * [16, 256]; num_q_heads a multiple of num_kv_heads with g in {1, 2, 4, 8};
  * 1 <= window <= block_size and g * window a multiple of 16, at most 128;
  * n_max >= 2. */

@@ -46,12 +46,12 @@ def test_bad_geometry_is_rejected_on_the_host(bad):
 def test_short_workspace_and_null_buffers_are_rejected():
     g = _geom().c()
     cache = zp.Cache(1, 1, 1, None)
-    need = zp.lib().zp_decode_workspace_size(C.byref(g), 2, 300)
-    assert need > 256
-    st = zp.lib().zp_paged_decode(C.byref(g), C.byref(cache), 0, 2, 1, 1, 1, 1, 1, 1, 300, None,
+    need = zp.lib().zp_decode_workspace_size(C.byref(g), 2, 3000)
+    assert need > 256                       # split partials of long rows
+    st = zp.lib().zp_paged_decode(C.byref(g), C.byref(cache), 0, 2, 1, 1, 1, 1, 1, 1, 3000, None,
                                   1, None, 1, need - 1, None)
     assert st == zp.ZP_EINVAL and "workspace" in zp.lib().zp_last_error().decode()
-    st = zp.lib().zp_paged_decode(C.byref(g), C.byref(cache), 3, 2, 1, 1, 1, 1, 1, 1, 300, None,
+    st = zp.lib().zp_paged_decode(C.byref(g), C.byref(cache), 3, 2, 1, 1, 1, 1, 1, 1, 3000, None,
                                   1, None, 1, need, None)
     assert st == zp.ZP_EINVAL  # layer out of range
     sp = zp.ScoreParams(tau=0.0).c()

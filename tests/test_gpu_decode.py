@@ -126,3 +126,53 @@ def test_decode_reports_bad_block_ids_without_faulting():
                        None, ws)
     assert zp.zp_workspace_errors(ws) & zp.ZP_DEVERR_SEQ_LEN
     assert torch.isnan(out).all()
+
+
+def test_decode_bench_launch_configuration_sampled():
+    """256 sequences x 8 kv-heads with 1793..2048 resident tokens (one layer of
+    the timed workload, one workgroup per (sequence, kv-head)); eight rows
+    are checked against the oracle one by one."""
+    announce("decode 256x8 bench configuration")
+    B, h_q, h_kv, d, b = 256, 32, 8, 128, 256
+    g = synth.rng(5, 3, 0, "lengths")
+    lens = (7 * b + g.integers(1, b + 1, B)).astype(np.int32)
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=B * 8 + 4, block_size=b,
+                            num_kv_heads=h_kv, num_q_heads=h_q, head_dim=d, window=16,
+                            max_slots=B, n_max=8, dtype="bf16")
+    cache = zp.PagedKVCache(geom, with_global=False)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    cache.k.normal_(generator=gen)
+    cache.v.normal_(generator=gen)
+    perm = torch.from_numpy(g.permutation(B * 8).astype(np.int32)).cuda()
+    tab = perm.view(B, 8).contiguous()
+    q = torch.randn(B, h_q, d, generator=gen, device="cuda").to(torch.bfloat16)
+    kn = torch.randn(B, h_kv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(B, h_kv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    # host snapshot of the inputs before the kernel touches the cache
+    rows = [0, 1, 77, 128, 200, 254, 255, int(np.argmax(lens))]
+    tab_h = tab.cpu().numpy()
+    snap = {r: (cache.k[0, tab[r].long()].float().cpu().numpy(),
+                cache.v[0, tab[r].long()].float().cpu().numpy()) for r in rows}
+    out = torch.empty(B, h_q, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, h_q, device="cuda")
+    ws = zp.new_workspace(zp.zp_decode_workspace_size(geom, B, 8 * b))
+    assert ws.numel() == 256                     # no split partials at this width
+    zp.zp_paged_decode(cache, 0, q, kn, vn, tab, dev_i32(lens), 8 * b, None, out, lse, ws)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(ws) == 0
+    qh, kh, vh = q.float().cpu().numpy(), kn.float().cpu().numpy(), vn.float().cpu().numpy()
+    oh, lh = out.float().cpu().numpy(), lse.cpu().numpy()
+    for r in rows:
+        n = int(lens[r])
+        Kp, Vp = snap[r]                          # [8 pages][h_kv][b][d]
+        K = Kp.transpose(1, 0, 2, 3).reshape(h_kv, 8 * b, d)[:, :n].astype(np.float64)
+        V = Vp.transpose(1, 0, 2, 3).reshape(h_kv, 8 * b, d)[:, :n].astype(np.float64)
+        K[:, n - 1] = kh[r]
+        V[:, n - 1] = vh[r]
+        o_ref, lse_ref = Z.decode_attention(qh[r], K, V)
+        for j in range(h_q):
+            assert np.abs(oh[r, j] - o_ref[j]).max() <= 2e-2 * np.abs(o_ref[j]).max(), (r, j)
+        np.testing.assert_allclose(lh[r], lse_ref, atol=1e-4)
+        pg, sl = tab_h[r][(n - 1) // b], (n - 1) % b
+        np.testing.assert_array_equal(cache.k[0, pg, :, sl].float().cpu().numpy(), kh[r])
