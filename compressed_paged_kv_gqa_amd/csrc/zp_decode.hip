@@ -193,8 +193,8 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
     const int64_t safe = off < 0 ? lane_off : off;  // a valid address; the chunk is masked
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      kr[u] = ld16(kc + safe + (int64_t)u * RPW * D);
-      vr[u] = ld16(vc + safe + (int64_t)u * RPW * D);
+      kr[u] = ld16_nt(kc + safe + (int64_t)u * RPW * D);
+      vr[u] = ld16_nt(vc + safe + (int64_t)u * RPW * D);
     }
     return off;
   };
@@ -215,11 +215,12 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
         }
       }
     }
+    // Raw q.k (unscaled); the 1/sqrt(d) * log2(e) factor enters the exp.
     float s[G][U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h][u] = group_sum<LPR>(q.dot(h, kr[u])) * P.qk_scale;
+      for (int h = 0; h < G; ++h) s[h][u] = group_sum<LPR>(q.dot(h, kr[u]));
     if (base + CHUNK > t1 || off < 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -228,11 +229,13 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
         for (int h = 0; h < G; ++h) s[h][u] = valid ? s[h][u] : -INFINITY;
       }
     }
+    const float sc2 = P.qk_scale;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float cm = s[h][0];
 #pragma unroll
       for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[h][u]);
+      cm *= sc2;
       if (cm > m[h] + kLazy) {
         const float alpha = __builtin_amdgcn_exp2f(m[h] - cm);
         l[h] *= alpha;
@@ -241,20 +244,52 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
         m[h] = cm;
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        s[h][u] = __builtin_amdgcn_exp2f(s[h][u] - m[h]);  // p, in place
-        l[h] += s[h][u];
-      }
+      for (int u = 0; u < U; ++u) s[h][u] = __builtin_amdgcn_exp2f(fmaf(s[h][u], sc2, -m[h]));  // p
     }
-    // o += p v, one V row at a time (keeps few unpacked values live).
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[EPL];
-      Vec16<T>::unpack(vr[u], vf);
+    if constexpr (sizeof(T) == 2) {
+      // o += p v over token pairs (u, u+1) with packed-bf16 dot products:
+      // the weights enter the numerator rounded to bf16 (the normaliser l
+      // keeps the fp32 values), V of the two tokens interleaved per
+      // dimension with v_perm.
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(s[h][u], vf[e], o[h][e]);
+        for (int u = 0; u < U; ++u) l[h] += s[h][u];
+#pragma unroll
+      for (int u = 0; u < U; u += 2) {
+        b2 pp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pp[h] = __builtin_convertvector(f2{s[h][u], s[h][u + 1]}, b2);
+        const uint32_t a[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+        const uint32_t bb[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const b2 lo = __builtin_bit_cast(b2, __builtin_amdgcn_perm(bb[j], a[j], 0x05040100u));
+          const b2 hi = __builtin_bit_cast(b2, __builtin_amdgcn_perm(bb[j], a[j], 0x07060302u));
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            o[h][2 * j] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], lo, o[h][2 * j], false);
+            o[h][2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], hi, o[h][2 * j + 1], false);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int u = 0; u < U; ++u) l[h] += s[h][u];
+      // o += p v, one V row at a time (keeps few unpacked values live).
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float vf[EPL];
+        Vec16<T>::unpack(vr[u], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(s[h][u], vf[e], o[h][e]);
+      }
     }
   };
 
