@@ -17,7 +17,7 @@
 //     of exp2) and the block's Gram matrix (b x b) -> lightning row sums.
 //  B  page_s0: per block again, merges the row statistics into log-sum-exp,
 //     recomputes the logits, forms S0 (group max, window mean) and applies
-//     the global score (reads / writes F).
+//     the global score (reads F, writes the updated history to f_new).
 //  C  finalize: per (request, kv-head): pooling, redundancy softmax over the
 //     sequence, S - lambda R, +inf window -> scores.
 // The window QK^T and the Gram are dense contractions (bf16 inputs, fp32
@@ -114,6 +114,7 @@ struct ScoreParams {
   const int32_t* qslot;
   const uint8_t* first;
   float* scores;
+  float* f_new;  // updated global score (S1) per token, same layout as scores
   float* stats;  // [items][h_kv][max_blocks][R][2]  (max, sum) in the exp2 domain
   float* rbuf;   // [items][h_kv][max_blocks * b]     lightning row sums / n
   float* s1buf;  // [items][h_kv][max_blocks * b]     S1
@@ -388,9 +389,10 @@ __global__ __launch_bounds__(256) void score_page_s0_kernel(ScoreParams P) {
       s0 /= (float)P.w;
       float s1 = s0;
       if (P.flags & ZP_SCORE_GLOBAL) {
-        float* f = P.gscore + layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col;
-        if (!first && !last) s1 = fmaxf(P.alpha * *f, s0);
-        *f = s1;
+        // F is read only: blocks may be shared by several requests.
+        if (!first && !last)
+          s1 = fmaxf(P.alpha * P.gscore[layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col], s0);
+        P.f_new[zh * P.scores_stride + (int64_t)pidx * b + col] = s1;
       }
       P.s1buf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + col] = s1;
     }
@@ -533,8 +535,8 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
                                      const int32_t* block_tables, int32_t table_stride,
                                      const int32_t* num_blocks, int32_t max_blocks,
                                      const int32_t* qslot, const uint8_t* first_compression,
-                                     float* scores, int64_t scores_stride, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     float* scores, float* f_new, int64_t scores_stride,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   zp_status st = validate_geom(geom, "zp_score_tokens");
   if (st != ZP_OK) return st;
   if (!cache || !cache->k || !cache->qwin || !params)
@@ -551,8 +553,8 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
     return fail(ZP_EINVAL, "zp_score_tokens: scores_stride %lld < max_blocks*b",
                 (long long)scores_stride);
   const zp_score_params& sp = *params;
-  if ((sp.flags & ZP_SCORE_GLOBAL) && !cache->gscore)
-    return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL needs cache->gscore");
+  if ((sp.flags & ZP_SCORE_GLOBAL) && (!cache->gscore || !f_new))
+    return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL needs cache->gscore and f_new");
   if (sp.flags & ~uint32_t(ZP_SCORE_GLOBAL | ZP_SCORE_POOL | ZP_SCORE_POOL_FIRST_ONLY |
                            ZP_SCORE_REDUNDANCY))
     return fail(ZP_EINVAL, "zp_score_tokens: unknown flags 0x%x", sp.flags);
@@ -573,7 +575,8 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   ScoreParams P{};
   P.kc = cache->k; P.qwin = cache->qwin; P.gscore = cache->gscore;
   P.tables = block_tables; P.num_blocks = num_blocks; P.qslot = qslot;
-  P.first = first_compression; P.scores = scores; P.scores_stride = scores_stride;
+  P.first = first_compression; P.scores = scores; P.f_new = f_new;
+  P.scores_stride = scores_stride;
   char* ws = static_cast<char*>(workspace);
   P.err = reinterpret_cast<uint32_t*>(ws);
   P.stats = reinterpret_cast<float*>(ws + so);

@@ -29,6 +29,7 @@ constexpr int kSelMaxTokens = 65536;
 
 struct SelectParams {
   const float* scores;
+  const float* f_new;  // updated global scores to move into F, or NULL
   void* kc;
   void* vc;
   float* gscore;
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
   }
 
   const float* sc = P.scores + ((int64_t)z * P.h_kv + h) * P.scores_stride;
+  const float* fnew = P.f_new ? P.f_new + ((int64_t)z * P.h_kv + h) * P.scores_stride : nullptr;
 
   // 1. Radix select of the keep-th largest key.
   uint32_t prefix = 0, pmask = 0, krem = keep;
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
     }
     if (fc && tid < CHUNK && j0 + tid < keep) {
       const int t = kept[j0 + tid];
-      fv = fc[((int64_t)stab[t / b] * P.h_kv + h) * b + (t % b)];
+      fv = fnew ? fnew[t] : fc[((int64_t)stab[t / b] * P.h_kv + h) * b + (t % b)];
     }
     __builtin_amdgcn_s_waitcnt(0);  // every load of the chunk has returned
     __syncthreads();
@@ -256,7 +258,8 @@ extern "C" size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_co
 
 extern "C" zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cache,
                                        int32_t layer_begin, int32_t layer_count, int32_t nreq,
-                                       const float* scores, int64_t scores_stride,
+                                       const float* scores, const float* f_new,
+                                       int64_t scores_stride,
                                        const int32_t* src_tables, int32_t src_stride,
                                        const int32_t* num_blocks, int32_t max_blocks,
                                        const int32_t* dst_tables, int32_t dst_stride,
@@ -288,7 +291,7 @@ extern "C" zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cach
     return fail(ZP_EINVAL, "zp_select_compact: nreq and layer_count must be <= 65535");
 
   SelectParams P{};
-  P.scores = scores; P.scores_stride = scores_stride;
+  P.scores = scores; P.f_new = f_new; P.scores_stride = scores_stride;
   P.kc = cache->k; P.vc = cache->v; P.gscore = cache->gscore;
   P.src_tables = src_tables; P.src_stride = src_stride; P.num_blocks = num_blocks;
   P.dst_tables = dst_tables ? dst_tables : src_tables;

@@ -239,21 +239,24 @@ class DecodeEngine:
             ls = self.layer_stride if not self.record else G.num_layers
             scores = torch.empty((ls, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
                                  device=self.device)
+            use_f = self.params.use_global and self.cache.gscore is not None
+            f_new = torch.empty_like(scores) if use_f else None
             kept = (torch.empty((G.num_layers, nreq, G.num_kv_heads, keep), dtype=torch.int32,
                                 device=self.device) if self.record else None)
             sws = zp.new_workspace(zp.zp_score_workspace_size(G, ls, nreq, maxb), self.device)
             cws = zp.new_workspace(zp.zp_select_workspace_size(G, ls, nreq), self.device)
             for lb in range(0, G.num_layers, ls):
                 lc = min(ls, G.num_layers - lb)
-                sc = scores[lb:lb + lc] if self.record else scores[:lc]
+                sl = slice(lb, lb + lc) if self.record else slice(0, lc)
+                sc, fn = scores[sl], (f_new[sl] if use_f else None)
                 zp.zp_score_tokens(self.cache, self.params, lb, lc, src_d, nblk_d, maxb, qslot_d,
-                                   first_d, sc, sws, stream=stream)
+                                   first_d, sc, fn, sws, stream=stream)
                 zp.zp_select_compact(self.cache, lb, lc, sc, src_d, nblk_d, maxb, dst_d, keep,
-                                     kept[lb:lb + lc] if kept is not None else None, cws,
-                                     stream=stream)
+                                     kept[sl] if kept is not None else None, cws,
+                                     stream=stream, f_new=fn)
             done = torch.cuda.Event()
             done.record(stream)
-            bufs += [meta_d, first_d, scores, sws, cws]
+            bufs += [meta_d, first_d, scores, f_new, sws, cws]
             if self.record:
                 self.log.append((list(ok), first.copy(), scores, kept))
         self.pending.append(_Pending(ok, plans, done, bufs))

@@ -44,7 +44,7 @@ def cast(x, dtype):
 class RequestInputs:
     prompt_k: np.ndarray   # [L][h_kv][n0][d]
     prompt_v: np.ndarray   # [L][h_kv][n0][d]
-    prompt_q: np.ndarray   # [L][h_q][n0][d] or None
+    prompt_q: np.ndarray   # [L][h_q][m][d]: queries of the last m prompt positions, or None
     steps_q: np.ndarray    # [T][L][h_q][d]
     steps_k: np.ndarray    # [T][L][h_kv][d]
     steps_v: np.ndarray    # [T][L][h_kv][d]
@@ -54,13 +54,14 @@ def request_inputs(seed, config, L, h_q, h_kv, d, n_prompt, n_steps, dtype="f32"
                    heavy_frac=0.02, heavy_scale=4.0, prompt_q_last=0):
     """Q/K/V ~ N(0, 1) for one request: its prompt and its decode steps.
 
-    ``prompt_q_last`` > 0 also draws queries for the last that many prompt
+    ``prompt_q_last`` = m > 0 also draws queries for the last m prompt
     positions (the observation window when compression fires right after the
-    prompt); other prompt queries are zero (never read).
+    prompt), shaped [L][h_q][m][d].
     """
     pk = np.empty((L, h_kv, n_prompt, d), np.float32)
     pv = np.empty_like(pk)
-    pq = np.zeros((L, h_q, n_prompt, d), np.float32) if prompt_q_last else None
+    m = min(prompt_q_last, n_prompt)
+    pq = np.zeros((L, h_q, m, d), np.float32) if prompt_q_last else None
     sq = np.empty((n_steps, L, h_q, d), np.float32)
     sk = np.empty((n_steps, L, h_kv, d), np.float32)
     sv = np.empty_like(sk)
@@ -70,17 +71,13 @@ def request_inputs(seed, config, L, h_q, h_kv, d, n_prompt, n_steps, dtype="f32"
         hv = rng(seed, config, l, "heavy").random((h_kv, n_prompt + n_steps)) < heavy_frac
         pk[l] *= np.where(hv[:, :n_prompt], heavy_scale, 1.0)[..., None]
         if prompt_q_last:
-            m = min(prompt_q_last, n_prompt)
-            pq[l, :, n_prompt - m:] = rng(seed, config, l, "prompt_q").standard_normal((h_q, m, d))
+            pq[l] = rng(seed, config, l, "prompt_q").standard_normal((h_q, m, d))
         sq[:, l] = rng(seed, config, l, "step_q").standard_normal((n_steps, h_q, d))
         sk[:, l] = rng(seed, config, l, "step_k").standard_normal((n_steps, h_kv, d))
         sv[:, l] = rng(seed, config, l, "step_v").standard_normal((n_steps, h_kv, d))
         sk[:, l] *= np.where(hv[:, n_prompt:].T, heavy_scale, 1.0)[..., None]
     c = lambda a: None if a is None else cast(a, dtype)
-    if pq is not None:
-        m = min(prompt_q_last, n_prompt)
-        pq[:, :, n_prompt - m:] = c(pq[:, :, n_prompt - m:])
-    return RequestInputs(c(pk), c(pv), pq, c(sq), c(sk), c(sv))
+    return RequestInputs(c(pk), c(pv), c(pq), c(sq), c(sk), c(sv))
 
 
 def scores_with_ties(seed, config, n, n_window, levels=None):

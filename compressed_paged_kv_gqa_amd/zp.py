@@ -67,9 +67,9 @@ def _declare(lib):
                                       _P, _P, sz, _P]),
         "zp_score_workspace_size": (sz, [g, i32, i32, i32]),
         "zp_score_tokens": (C.c_int, [g, c, sp, i32, i32, i32, _P, i32, _P, i32, _P, _P, _P,
-                                      i64, _P, sz, _P]),
+                                      _P, i64, _P, sz, _P]),
         "zp_select_workspace_size": (sz, [g, i32, i32]),
-        "zp_select_compact": (C.c_int, [g, c, i32, i32, i32, _P, i64, _P, i32, _P, i32, _P,
+        "zp_select_compact": (C.c_int, [g, c, i32, i32, i32, _P, _P, i64, _P, i32, _P, i32, _P,
                                         i32, i32, _P, u32, _P, sz, _P]),
         "zp_workspace_errors": (C.c_int, [_P, C.POINTER(C.c_uint32), _P]),
         "zp_workspace_clear_errors": (C.c_int, [_P, _P]),
@@ -270,27 +270,33 @@ class ScoreParams:
 
 def zp_score_tokens(cache: PagedKVCache, params: ScoreParams, layer_begin, layer_count,
                     block_tables, num_blocks, max_blocks, qslot, first_compression, scores,
-                    workspace, stream=None):
+                    f_new, workspace, stream=None):
     import torch
     _need(block_tables, torch.int32, "block_tables")
     _need(num_blocks, torch.int32, "num_blocks")
     _need(qslot, torch.int32, "qslot")
     _need(first_compression, torch.uint8, "first_compression")
     _need(scores, torch.float32, "scores")
+    _need(f_new, torch.float32, "f_new")
+    if f_new is not None and f_new.shape != scores.shape:
+        raise ValueError("f_new must have the shape of scores")
     nreq = block_tables.shape[0]
     _check(lib().zp_score_tokens(
         C.byref(cache.geom.c()), C.byref(cache.c()), C.byref(params.c()), layer_begin,
         layer_count, nreq, block_tables.data_ptr(), block_tables.shape[1],
         num_blocks.data_ptr(), int(max_blocks), qslot.data_ptr(), first_compression.data_ptr(),
-        scores.data_ptr(), scores.shape[-1], workspace.data_ptr(),
+        scores.data_ptr(), _ptr(f_new), scores.shape[-1], workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)), "zp_score_tokens")
 
 
 def zp_select_compact(cache: PagedKVCache, layer_begin, layer_count, scores, src_tables,
                       num_blocks, max_blocks, dst_tables, keep, kept_idx, workspace,
-                      flags=0, stream=None):
+                      flags=0, stream=None, f_new=None):
     import torch
     _need(scores, torch.float32, "scores")
+    _need(f_new, torch.float32, "f_new")
+    if f_new is not None and f_new.shape != scores.shape:
+        raise ValueError("f_new must have the shape of scores")
     _need(src_tables, torch.int32, "src_tables")
     _need(num_blocks, torch.int32, "num_blocks")
     _need(dst_tables, torch.int32, "dst_tables")
@@ -298,7 +304,8 @@ def zp_select_compact(cache: PagedKVCache, layer_begin, layer_count, scores, src
     nreq = src_tables.shape[0]
     _check(lib().zp_select_compact(
         C.byref(cache.geom.c()), C.byref(cache.c()), layer_begin, layer_count, nreq,
-        scores.data_ptr(), scores.shape[-1], src_tables.data_ptr(), src_tables.shape[1],
+        scores.data_ptr(), _ptr(f_new), scores.shape[-1], src_tables.data_ptr(),
+        src_tables.shape[1],
         num_blocks.data_ptr(), int(max_blocks), _ptr(dst_tables),
         dst_tables.shape[1] if dst_tables is not None else 0, int(keep), _ptr(kept_idx),
         int(flags), workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -176,8 +176,11 @@ size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t
  * slot qslot[r]:
  *   S0 = mean over the window of the max over the g query heads of
  *        softmax_t(q.k_t/sqrt(d)), the last block causally masked;
- *   S1 = global score (F read and updated in place when ZP_SCORE_GLOBAL;
- *        first_compression[r] != 0 means the request was never compressed);
+ *   S1 = global score (when ZP_SCORE_GLOBAL; first_compression[r] != 0
+ *        means the request was never compressed); the cache's F is only read,
+ *        the updated history (Alg. 2's new F, which equals S1) goes to f_new,
+ *        and zp_select_compact moves it into the target blocks, so blocks
+ *        shared between requests are never written;
  *   S2 = max-pooled S1 (when ZP_SCORE_POOL, and first_compression[r] if
  *        ZP_SCORE_POOL_FIRST_ONLY);
  *   S3 = S2 - lambda * softmax_t(r_t / n / tau), r_t the lightning row sums,
@@ -189,14 +192,16 @@ size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t
  *   first_compression [device] uint8 [nreq]
  *   scores [device] float32 [layer_count][nreq][h_kv][scores_stride],
  *          scores_stride >= max_blocks*b; entries past n are not written.
+ *   f_new  [device] float32, same layout as scores: S1 of every token; may be
+ *          NULL when ZP_SCORE_GLOBAL is off.
  */
 zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
                           const zp_score_params* params, int32_t layer_begin,
                           int32_t layer_count, int32_t nreq, const int32_t* block_tables,
                           int32_t table_stride, const int32_t* num_blocks, int32_t max_blocks,
                           const int32_t* qslot, const uint8_t* first_compression, float* scores,
-                          int64_t scores_stride, void* workspace, size_t workspace_bytes,
-                          void* stream);
+                          float* f_new, int64_t scores_stride, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Top-k selection and compaction (Zipage Sec. 4.2, App. C.6 Alg. 4,         */
@@ -209,16 +214,18 @@ size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_count, int32_
 
 /* For every (layer, request, kv-head): keep the `keep` tokens with the
  * highest score (ties go to the higher token index), and move their K, V and
- * (if cache->gscore != NULL) F entries, in ascending token order, to logical
- * slots 0..keep-1 of the target blocks dst_tables[r][0..]. keep is normally
- * (N_max - 1) * b. kept_idx, if not NULL, receives the ascending token
- * indices.
+ * (if cache->gscore != NULL) global-score entries, in ascending token order,
+ * to logical slots 0..keep-1 of the target blocks dst_tables[r][0..]. The
+ * global score written for kept token t is f_new[t] (zp_score_tokens'
+ * updated history) when f_new != NULL, else the cache's own F value of t.
+ * keep is normally (N_max - 1) * b. kept_idx, if not NULL, receives the
+ * ascending token indices.
  *
  * Precondition (in-place safety): each target block dst_tables[r][i] is
  * either src_tables[r][i] or a block that src_tables[r] does not contain.
  * zp_plan_compress produces targets of this form.
  *
- *   scores   [device] float32 [layer_count][nreq][h_kv][scores_stride]
+ *   scores, f_new [device] float32 [layer_count][nreq][h_kv][scores_stride]
  *   src_tables [device] int32 [nreq][src_stride]; num_blocks [device] int32 [nreq]
  *   dst_tables [device] int32 [nreq][dst_stride], dst_stride*b >= keep
  *   kept_idx [device] int32 [layer_count][nreq][h_kv][keep] or NULL
@@ -226,7 +233,8 @@ size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_count, int32_
  */
 zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cache, int32_t layer_begin,
                             int32_t layer_count, int32_t nreq, const float* scores,
-                            int64_t scores_stride, const int32_t* src_tables, int32_t src_stride,
+                            const float* f_new, int64_t scores_stride,
+                            const int32_t* src_tables, int32_t src_stride,
                             const int32_t* num_blocks, int32_t max_blocks,
                             const int32_t* dst_tables, int32_t dst_stride, int32_t keep,
                             int32_t* kept_idx, uint32_t flags, void* workspace,

@@ -438,12 +438,13 @@ def window_row(pos, b, w):
 # End-to-end logical simulation of one request (used for the small cases)
 # ---------------------------------------------------------------------------
 
-def simulate_request(prompt_K, prompt_V, prompt_Q, steps_q, steps_k, steps_v,
+def simulate_request(prompt_K, prompt_V, prompt_Q_tail, steps_q, steps_k, steps_v,
                      b, w, n_max, params: ScoreParams, scale=None):
     """Run one request through prompt, decode steps and compressions.
 
-    prompt_K/V: [L][h_kv][n0][d]; prompt_Q: [L][h_q][n0][d] or None (queries
-    of the prompt, needed only when the window falls inside the prompt);
+    prompt_K/V: [L][h_kv][n0][d]; prompt_Q_tail: [L][h_q][m][d] with the
+    queries of the last m prompt positions, or None (needed only when the
+    window falls inside the prompt);
     steps_q: [T][L][h_q][d]; steps_k/v: [T][L][h_kv][d]. Each decode step
     appends k/v to every layer, runs decode attention over the resident tokens
     and records the window query; after every step that leaves N >= N_max full
@@ -453,30 +454,36 @@ def simulate_request(prompt_K, prompt_V, prompt_Q, steps_q, steps_k, steps_v,
 
     Returns dict(outputs [T][L][h_q][d], events: list of per-event dicts with
     the kept indices [L][h_kv][k] and scores [L][h_kv][n], and the final
-    resident K, V, F).
+    resident K, V, F as lists [L][h_kv] of arrays).
     """
     prompt_K, prompt_V = _f64(prompt_K), _f64(prompt_V)
     L, h_kv, n0, d = prompt_K.shape
-    h_q = np.shape(steps_q)[2] if len(steps_q) else (np.shape(prompt_Q)[1])
+    T = len(steps_q)
+    h_q = np.shape(steps_q)[2] if T else np.shape(prompt_Q_tail)[1]
     g = h_q // h_kv
-    K = [[list(prompt_K[l, h]) for h in range(h_kv)] for l in range(L)]
-    V = [[list(prompt_V[l, h]) for h in range(h_kv)] for l in range(L)]
-    F = [[[0.0] * n0 for _ in range(h_kv)] for _ in range(L)]
+    cap = n0 + T
+    # resident tokens of every (layer, kv-head), in logical order, plus F
+    K = np.zeros((L, h_kv, cap, d))
+    V = np.zeros((L, h_kv, cap, d))
+    F = np.zeros((L, h_kv, cap))
+    K[:, :, :n0] = prompt_K
+    V[:, :, :n0] = prompt_V
+    n = n0
     qwin = np.zeros((L, h_kv, g, w, d), _F)
-    if prompt_Q is not None:
-        for pos in range(n0):
+    if prompt_Q_tail is not None:
+        m = np.shape(prompt_Q_tail)[2]
+        for pos in range(n0 - m, n0):
             row = window_row(pos, b, w)
             if row >= 0:
                 for l in range(L):
                     for j in range(h_q):
-                        qwin[l, j // g, j % g, row] = prompt_Q[l][j][pos]
+                        qwin[l, j // g, j % g, row] = prompt_Q_tail[l][j][pos - (n0 - m)]
     first = True
     events = []
-    outputs = []
+    outputs = np.zeros((T, L, h_q, d), _F)
 
     def maybe_compress():
-        nonlocal first, K, V, F
-        n = len(K[0][0])
+        nonlocal first, n
         if not should_compress(n, b, n_max):
             return
         keep = (n_max - 1) * b
@@ -484,39 +491,32 @@ def simulate_request(prompt_K, prompt_V, prompt_Q, steps_q, steps_k, steps_v,
                   scores=np.zeros((L, h_kv, n), _F), first=first)
         for l in range(L):
             for h in range(h_kv):
-                Kl = np.stack(K[l][h])
-                S, F_new = score_tokens(qwin[l, h], Kl, np.asarray(F[l][h]),
-                                        first, b, params, scale)
+                S, F_new = score_tokens(qwin[l, h], K[l, h, :n], F[l, h, :n], first, b,
+                                        params, scale)
                 kept = topk_keep(S, keep)
                 ev["kept"][l, h] = kept
                 ev["scores"][l, h] = S
-                K[l][h] = [K[l][h][t] for t in kept]
-                V[l][h] = [V[l][h][t] for t in kept]
-                Fl = F_new if F_new is not None else np.zeros(n)
-                F[l][h] = [float(Fl[t]) for t in kept]
+                K[l, h, :keep] = K[l, h, kept]
+                V[l, h, :keep] = V[l, h, kept]
+                F[l, h, :keep] = F_new[kept] if F_new is not None else 0.0
+        n = keep
         first = False
         events.append(ev)
 
     maybe_compress()
-    for s in range(len(steps_q)):
-        out_s = np.zeros((L, h_q, d), _F)
+    for s in range(T):
+        K[:, :, n] = steps_k[s]
+        V[:, :, n] = steps_v[s]
+        F[:, :, n] = 0.0
+        n += 1
         for l in range(L):
-            for h in range(h_kv):
-                K[l][h].append(_f64(steps_k[s][l][h]))
-                V[l][h].append(_f64(steps_v[s][l][h]))
-                F[l][h].append(0.0)
-            Kl = np.stack([np.stack(K[l][h]) for h in range(h_kv)])
-            Vl = np.stack([np.stack(V[l][h]) for h in range(h_kv)])
-            o, _ = decode_attention(steps_q[s][l], Kl, Vl, scale)
-            out_s[l] = o
-            pos = len(K[l][0]) - 1
-            row = window_row(pos, b, w)
+            outputs[s, l] = decode_attention(steps_q[s][l], K[l, :, :n], V[l, :, :n], scale)[0]
+            row = window_row(n - 1, b, w)
             if row >= 0:
                 for j in range(h_q):
                     qwin[l, j // g, j % g, row] = steps_q[s][l][j]
-        outputs.append(out_s)
         maybe_compress()
-    return dict(outputs=np.array(outputs), events=events,
-                K=[[np.stack(K[l][h]) for h in range(h_kv)] for l in range(L)],
-                V=[[np.stack(V[l][h]) for h in range(h_kv)] for l in range(L)],
-                F=[[np.asarray(F[l][h]) for h in range(h_kv)] for l in range(L)])
+    return dict(outputs=outputs, events=events,
+                K=[[K[l, h, :n].copy() for h in range(h_kv)] for l in range(L)],
+                V=[[V[l, h, :n].copy() for h in range(h_kv)] for l in range(L)],
+                F=[[F[l, h, :n].copy() for h in range(h_kv)] for l in range(L)])

@@ -50,60 +50,97 @@ def _compare_kept(kept_gpu, S_ref, keep):
     return outside, False
 
 
-def _run_requests(cfg, geom, sp, inputs, n_steps, sample, layer_stride=1, async_compress=True):
-    """Drives all requests on the GPU; compares `sample` of them with the
-    oracle simulation. `inputs[r]` is a synth.RequestInputs."""
+def _run_requests(cfg, geom, sp, inputs, n_steps, sample, layer_stride=1, async_compress=True,
+                  wait_each_step=True, prefix_len=0, check_prefix=None):
+    """Drives all requests on the GPU and compares `sample` of them with the
+    oracle simulation. `inputs[r]` is a synth.RequestInputs. Every request
+    consumes its own next decode input: with wait_each_step=False a
+    compressing request sits out decode steps until its side-stream event has
+    fired (Sec. 4.5), so requests drift apart in step count. With
+    prefix_len > 0 the first prefix_len prompt tokens of every request are
+    identical and their blocks are shared (Sec. 4.4)."""
     B = len(inputs)
     L, h_q, h_kv, d = geom.num_layers, geom.num_q_heads, geom.num_kv_heads, geom.head_dim
+    b, w = geom.block_size, geom.window
     dt = geom.torch_dtype()
-    cap = max(-(-(x.prompt_k.shape[2] + n_steps) // geom.block_size) for x in inputs) + 1
+    cap = max(-(-(x.prompt_k.shape[2] + n_steps) // b) for x in inputs) + 1
     eng = DecodeEngine(geom, sp, B, cap, layer_stride=layer_stride,
                        async_compress=async_compress, record=True)
+    prefix_table = None
     for r, x in enumerate(inputs):
         n0 = x.prompt_k.shape[2]
-        eng.add_request(r, n0)
+        share = prefix_table if (prefix_len and r > 0) else None
+        table = eng.add_request(r, n0, prefix_table=share)
+        if prefix_len and r == 0:
+            prefix_table = table[:prefix_len // b]
+        start = prefix_len if share else 0
         for l in range(L):
-            eng.write_tokens(r, l, 0, torch.from_numpy(x.prompt_k[l]).to(dt).cuda(),
-                             torch.from_numpy(x.prompt_v[l]).to(dt).cuda())
+            eng.write_tokens(r, l, start, torch.from_numpy(x.prompt_k[l][:, start:]).to(dt).cuda(),
+                             torch.from_numpy(x.prompt_v[l][:, start:]).to(dt).cuda())
             if x.prompt_q is not None:
-                b, w = geom.block_size, geom.window
-                # window rows of the prompt's last block (when that block is full)
                 qw = np.zeros((h_kv, h_q // h_kv, w, d), np.float32)
-                for pos in range(n0 - w, n0):
+                m = x.prompt_q.shape[2]
+                for pos in range(n0 - m, n0):
                     row = Z.window_row(pos, b, w)
                     if row >= 0:
-                        qw[:, :, row] = x.prompt_q[l, :, pos].reshape(h_kv, h_q // h_kv, d)
+                        qw[:, :, row] = x.prompt_q[l, :, pos - (n0 - m)].reshape(h_kv, h_q // h_kv, d)
                 eng.write_window_queries(r, l, torch.from_numpy(qw).to(dt).cuda())
+    if prefix_table is not None:
+        assert all(eng.alloc.refcount(p) == B for p in prefix_table)
+        prefix_k = eng.cache.k[:, prefix_table].clone()
     eng.compress_due_now()
+    if wait_each_step:
+        eng.wait_compressions()
+    # per-request decode inputs [B][T][L][...] on the device
+    q_req = torch.from_numpy(np.stack([x.steps_q for x in inputs])).to(dt).cuda()
+    k_req = torch.from_numpy(np.stack([x.steps_k for x in inputs])).to(dt).cuda()
+    v_req = torch.from_numpy(np.stack([x.steps_v for x in inputs])).to(dt).cuda()
+    outs = torch.zeros((B, n_steps, L, h_q, d), dtype=dt, device="cuda")
+    out_step = torch.empty((L, B, h_q, d), dtype=dt, device="cuda")
+    cnt = np.zeros(B, np.int64)
+    rows = torch.arange(B, device="cuda")
+    guard = 0
+    while cnt.min() < n_steps:
+        guard += 1
+        assert guard < 50 * n_steps, "requests stopped making progress"
+        for r in range(B):
+            eng.reqs[r].done = cnt[r] >= n_steps
+        act = eng.prepare_step()
+        if not act:
+            eng.poll(wait=True)
+            continue
+        idx = torch.from_numpy(np.minimum(cnt, n_steps - 1)).cuda()
+        q_s = q_req[rows, idx].transpose(0, 1).contiguous()      # [L][B][h_q][d]
+        k_s = k_req[rows, idx].transpose(0, 1).contiguous()
+        v_s = v_req[rows, idx].transpose(0, 1).contiguous()
+        for l in range(L):
+            eng.decode_layer(l, q_s[l], k_s[l], v_s[l], out_step[l])
+        a = torch.tensor(act, device="cuda")
+        outs[a, torch.from_numpy(cnt[act]).cuda()] = out_step[:, a].transpose(0, 1)
+        eng.finish_step(act)
+        cnt[act] += 1
+        if wait_each_step:
+            eng.wait_compressions()
     eng.wait_compressions()
-    outs = torch.zeros((n_steps, L, B, h_q, d), dtype=dt, device="cuda")
-    q_all = torch.stack([torch.from_numpy(np.stack([x.steps_q[:, l] for x in inputs], 1))
-                         for l in range(L)], 1).to(dt).cuda()            # [T][L][B][h_q][d]
-    k_all = torch.stack([torch.from_numpy(np.stack([x.steps_k[:, l] for x in inputs], 1))
-                         for l in range(L)], 1).to(dt).cuda()
-    v_all = torch.stack([torch.from_numpy(np.stack([x.steps_v[:, l] for x in inputs], 1))
-                         for l in range(L)], 1).to(dt).cuda()
-    for s in range(n_steps):
-        act = eng.step(q_all[s], k_all[s], v_all[s], outs[s])
-        assert len(act) == B
-        eng.wait_compressions()      # keep every request in every step
     torch.cuda.synchronize()
     assert zp.zp_workspace_errors(eng.dec_ws) == 0
+    if check_prefix is not None:
+        check_prefix(eng, prefix_table, prefix_k)
     outs_h = outs.float().cpu().numpy()
     op = _oracle_params(sp)
     tol = tol_for(geom.dtype)
     worst_out = 0.0
     for r in sample:
         x = inputs[r]
-        announce(f"{cfg}: oracle for request {r}")
+        announce(f"{cfg}: oracle for request {r} (prompt {x.prompt_k.shape[2]})")
         res = Z.simulate_request(x.prompt_k, x.prompt_v, x.prompt_q, x.steps_q, x.steps_k,
-                                 x.steps_v, geom.block_size, geom.window, geom.n_max, op)
-        # compression events of this request, in order
+                                 x.steps_v, b, w, geom.n_max, op)
         gpu_events = [(sids.index(r), first, sc, kept) for (sids, first, sc, kept) in eng.log
                       if r in sids]
-        assert len(gpu_events) == len(res["events"])
+        assert len(gpu_events) == len(res["events"]), (len(gpu_events), len(res["events"]))
         agree = True
         for (i, first, sc, kept), ev in zip(gpu_events, res["events"]):
+            assert bool(first[i]) == ev["first"]
             kept_h = kept.cpu().numpy()
             for l in range(L):
                 for h in range(h_kv):
@@ -118,7 +155,7 @@ def _run_requests(cfg, geom, sp, inputs, n_steps, sample, layer_stride=1, async_
             for l in range(L):
                 for j in range(h_q):
                     ref = res["outputs"][s, l, j]
-                    err = np.abs(outs_h[s, l, r, j] - ref).max() / np.abs(ref).max()
+                    err = np.abs(outs_h[r, s, l, j] - ref).max() / np.abs(ref).max()
                     worst_out = max(worst_out, err)
                     assert err <= tol, (cfg, r, s, l, j, err)
         for l in range(L):
@@ -166,3 +203,68 @@ def test_qwen_shape_prefill_compress_then_decode_sampled():
     for r in eng.reqs.values():
         assert r.n == 1792 + T and len(r.table) == 8 and not r.first
     assert eng.alloc.num_free == geom.num_blocks - 8 * B
+
+
+@pytest.mark.timeout(900)
+def test_shared_prefix_copy_on_compress_sampled():
+    """128 requests share one 1024-token prefix (4 blocks, refcount 128) and
+    have unique 512-token suffixes; 2048 decode steps, compressions every 256
+    steps from step 512. The first compression of each request writes its
+    kept tokens to 4 fresh blocks (copy-on-compress) and drops one reference
+    of each shared block; the shared blocks' contents never change. Requests
+    rejoin decode as their compressions finish (no waiting)."""
+    announce("e2e shared prefix 128 x (1024 + 512), 2048 steps")
+    B, pre, suf, T = 128, 1024, 512, 2048
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=4 + B * 8 + B * 4 + 8, block_size=256,
+                            num_kv_heads=8, num_q_heads=32, head_dim=128, window=16,
+                            max_slots=B, n_max=8, dtype="bf16")
+    base = synth.request_inputs(4, 4, 1, 32, 8, 128, pre, 0, dtype="bf16")
+    inputs = []
+    for r in range(B):
+        x = synth.request_inputs(4, 4000 + r, 1, 32, 8, 128, suf, T, dtype="bf16")
+        x.prompt_k = np.concatenate([base.prompt_k, x.prompt_k], axis=2)
+        x.prompt_v = np.concatenate([base.prompt_v, x.prompt_v], axis=2)
+        inputs.append(x)
+        if r % 32 == 31:
+            announce(f"generated {r + 1}/{B} requests")
+
+    def check_prefix(eng, prefix_table, prefix_k):
+        for p in prefix_table:
+            assert eng.alloc.refcount(p) == 0          # every request let go
+        # untouched by any compaction (no block was allocated after the first
+        # compression, so the freed prefix blocks still hold the prefix)
+        assert torch.equal(eng.cache.k[:, prefix_table], prefix_k)
+        for r in eng.reqs.values():
+            assert not set(r.table) & set(prefix_table) and len(r.table) == 8
+
+    eng = _run_requests("prefix", geom, zp.ScoreParams(), inputs, T, [0, 77, 127],
+                        wait_each_step=False, prefix_len=pre, check_prefix=check_prefix)
+    assert eng.compressions == B * 7
+
+
+@pytest.mark.timeout(900)
+def test_ragged_long_context_sampled():
+    """64 requests with prompts log-uniform in [2048, 32768] tokens, 256 decode
+    steps: prompts ending on a block boundary compress at once (up to
+    32768 -> 1792 tokens), the others when decode fills their last block,
+    while the rest keep decoding (no waiting)."""
+    announce("e2e ragged 64 x [2048, 32768], 256 steps")
+    B, T = 64, 256
+    lens = synth.log_uniform_lengths(5, 5, B, 2048, 32768)
+    lens[:4] = [2048, 8192, 32768, 4096]          # some prompts end on a block boundary
+    nblocks = sum(-(-(int(n) + T) // 256) for n in lens)
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=nblocks + 16, block_size=256,
+                            num_kv_heads=8, num_q_heads=32, head_dim=128, window=16,
+                            max_slots=B, n_max=8, dtype="bf16")
+    inputs = []
+    for r in range(B):
+        inputs.append(synth.request_inputs(5, 5000 + r, 1, 32, 8, 128, int(lens[r]), T,
+                                           dtype="bf16", prompt_q_last=16))
+        if r % 16 == 15:
+            announce(f"generated {r + 1}/{B} requests")
+    order = np.argsort(lens)
+    sample = [0, 2, int(order[0]), int(order[B // 2])]
+    eng = _run_requests("ragged", geom, zp.ScoreParams(), inputs, T, sample,
+                        wait_each_step=False)
+    for r in eng.reqs.values():
+        assert len(r.table) <= 8

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(dtype, d, h_kv, b, w, nblocks, keep, fresh_mask, levels, L=2, layer_begin=1,
-         layer_count=1, seed=21, with_global=True, no_compact=False):
+         layer_count=1, seed=21, with_global=True, no_compact=False, use_f_new=False):
     announce(f"select dtype={dtype} d={d} b={b} N={nblocks} keep={keep} fresh={fresh_mask} "
              f"levels={levels}")
     nreq = len(nblocks)
@@ -45,11 +45,13 @@ def _run(dtype, d, h_kv, b, w, nblocks, keep, fresh_mask, levels, L=2, layer_beg
             for h in range(h_kv):
                 n = nblocks[r] * b
                 S[li, r, h, :n] = synth.scores_with_ties(seed + 97 * li + 13 * h, r, n, w, levels)
+    FN = (synth.rng(seed, 3, 1, "gscore").random(S.shape) * 0.01).astype(np.float32)
     kept = torch.full((layer_count, nreq, h_kv, keep), -1, dtype=torch.int32, device="cuda")
     ws = zp.new_workspace(zp.zp_select_workspace_size(geom, layer_count, nreq))
     zp.zp_select_compact(hc.dev, layer_begin, layer_count, torch.from_numpy(S).cuda(),
                          dev_i32(tab), dev_i32(nblocks), max_blocks, dev_i32(dst), keep, kept, ws,
-                         flags=zp.ZP_SELECT_NO_COMPACT if no_compact else 0)
+                         flags=zp.ZP_SELECT_NO_COMPACT if no_compact else 0,
+                         f_new=torch.from_numpy(FN).cuda() if use_f_new else None)
     torch.cuda.synchronize()
     assert zp.zp_workspace_errors(ws) == 0
     kept_h = kept.cpu().numpy()
@@ -67,7 +69,12 @@ def _run(dtype, d, h_kv, b, w, nblocks, keep, fresh_mask, levels, L=2, layer_beg
                 tag[ref] = True
                 expK[l, :, h] = Z.compact_pages(expK[l, :, h], tab[r], n, dst[r], tag, b)
                 expV[l, :, h] = Z.compact_pages(expV[l, :, h], tab[r], n, dst[r], tag, b)
-                expF[l, :, h] = Z.compact_pages(expF[l, :, h], tab[r], n, dst[r], tag, b)
+                if use_f_new:
+                    # the updated history is moved instead of the cache's old F
+                    for j, t in enumerate(ref):
+                        expF[l, dst[r][j // b], h, j % b] = FN[li, r, h, t]
+                else:
+                    expF[l, :, h] = Z.compact_pages(expF[l, :, h], tab[r], n, dst[r], tag, b)
     np.testing.assert_array_equal(hc.dev.k.float().cpu().numpy(), expK)
     np.testing.assert_array_equal(hc.dev.v.float().cpu().numpy(), expV)
     if with_global:
@@ -79,8 +86,10 @@ def test_select_in_place_qwen_shape_with_ties():
 
 
 def test_select_fresh_targets_prefix_like():
-    # the first four target blocks are fresh (shared-prefix positions)
-    _run("bf16", 128, 8, 256, 16, [8, 10], 7 * 256, lambda r, i: i < 4, levels=None)
+    # the first four target blocks are fresh (shared-prefix positions); the
+    # updated global scores come from f_new
+    _run("bf16", 128, 8, 256, 16, [8, 10], 7 * 256, lambda r, i: i < 4, levels=None,
+         use_f_new=True)
 
 
 def test_select_long_context_to_budget():

@@ -205,3 +205,46 @@ def test_capacity_eq2_global_score_fraction():
     assert Fraction(m_kv + m_f) == (1 + Fraction(1, 2 * d)) * m_kv
     M, Nt = PL.capacity(10**11, m_kv, 10**6, 8, m_f)
     assert M == 10**11 // ((m_kv + m_f) * 8 + 10**6)
+
+
+# --- whole-request simulation ------------------------------------------------
+
+def test_simulation_without_compression_is_dense_decode():
+    """Budget above the context: every step is dense attention over prompt +
+    decoded tokens (Sec. 6), no event fires."""
+    rng = np.random.default_rng(30)
+    L, h_q, h_kv, d, n0, T, b = 2, 4, 2, 8, 10, 5, 4
+    pk, pv = rng.standard_normal((L, h_kv, n0, d)), rng.standard_normal((L, h_kv, n0, d))
+    sq = rng.standard_normal((T, L, h_q, d))
+    sk, sv = rng.standard_normal((T, L, h_kv, d)), rng.standard_normal((T, L, h_kv, d))
+    res = Z.simulate_request(pk, pv, None, sq, sk, sv, b, 2, n_max=8, params=Z.ScoreParams())
+    assert res["events"] == []
+    for s in range(T):
+        for l in range(L):
+            K = np.concatenate([pk[l], np.moveaxis(sk[:s + 1, l], 0, 1)], axis=1)
+            V = np.concatenate([pv[l], np.moveaxis(sv[:s + 1, l], 0, 1)], axis=1)
+            np.testing.assert_allclose(res["outputs"][s, l], Z.decode_attention(sq[s, l], K, V)[0],
+                                       atol=1e-13)
+
+
+def test_simulation_events_keep_budget_and_gather_kept_rows():
+    """An event keeps exactly (N_max - 1) b rows per (layer, kv-head), the
+    window among them, and the resident rows are the kept pre-event rows in
+    order; the next token lands in the reserved block."""
+    rng = np.random.default_rng(31)
+    L, h_q, h_kv, d, b, w, n_max = 1, 4, 2, 8, 4, 2, 3
+    n0, T = 10, 3           # 12 tokens = 3 full blocks after 2 steps -> event
+    pk, pv = rng.standard_normal((L, h_kv, n0, d)), rng.standard_normal((L, h_kv, n0, d))
+    sq = rng.standard_normal((T, L, h_q, d))
+    sk, sv = rng.standard_normal((T, L, h_kv, d)), rng.standard_normal((T, L, h_kv, d))
+    res = Z.simulate_request(pk, pv, None, sq, sk, sv, b, w, n_max, Z.ScoreParams())
+    assert len(res["events"]) == 1
+    ev = res["events"][0]
+    keep = (n_max - 1) * b
+    assert ev["n"] == 12 and ev["kept"].shape == (L, h_kv, keep)
+    full_K = np.concatenate([pk[0], np.moveaxis(sk[:2, 0], 0, 1)], axis=1)   # [h_kv][12][d]
+    for h in range(h_kv):
+        kept = ev["kept"][0, h]
+        assert {10, 11} <= set(kept.tolist())
+        np.testing.assert_array_equal(res["K"][0][h][:keep], full_K[h][kept])
+        np.testing.assert_array_equal(res["K"][0][h][keep], sk[2, 0, h])
