@@ -104,7 +104,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def setup(args, phases):
+def build_workload(phases, sync_compress=False, record=False):
+    """The timed workload: engine, filled caches and per-step inputs
+    (q/k/v: 4 variants [4][L][B][...] cycled over the steps; out [L][B][...])."""
     import torch
     from compressed_paged_kv_gqa_amd import zp
     from compressed_paged_kv_gqa_amd.engine import DecodeEngine
@@ -112,7 +114,7 @@ def setup(args, phases):
                             num_kv_heads=HKV, num_q_heads=HQ, head_dim=D, window=W,
                             max_slots=B, n_max=NMAX, dtype="bf16")
     eng = DecodeEngine(geom, zp.ScoreParams(), B, NMAX, layer_stride=8,
-                       async_compress=not args.sync_compress)
+                       async_compress=not sync_compress, record=record)
     log("filling the K/V cache")
     fill_cache(eng.cache, SEED)
     for s in range(B):
@@ -132,7 +134,7 @@ def setup(args, phases):
 
 def run_gpu(args, phases):
     import torch
-    eng, (q, k, v, out) = setup(args, phases)
+    eng, (q, k, v, out) = build_workload(phases, args.sync_compress)
     nvar = q.shape[0]
     for i in range(args.warmup):
         eng.step(q[i % nvar], k[i % nvar], v[i % nvar], out)

@@ -236,8 +236,9 @@ class DecodeEngine:
             nblk_d = meta_d[o:o + nreq]
             qslot_d = meta_d[o + nreq:o + 2 * nreq]
             first_d = meta_d[o + 2 * nreq:o + 3 * nreq].to(torch.uint8)
-            ls = self.layer_stride if not self.record else G.num_layers
-            scores = torch.empty((ls, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
+            ls = self.layer_stride
+            nl = G.num_layers if self.record else ls     # recording keeps every layer
+            scores = torch.empty((nl, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
                                  device=self.device)
             use_f = self.params.use_global and self.cache.gscore is not None
             f_new = torch.empty_like(scores) if use_f else None

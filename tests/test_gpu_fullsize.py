@@ -1,0 +1,143 @@
+"""Parity at full size, in the launch configuration bench.py times: 36 layers,
+256 sequences in steady state (1793..2048 resident tokens, every sequence
+compressed before), block 256, N_max 8, asynchronous compression with layer
+stride 8 (Zipage, arXiv 2603.08743, Sec. 4.1-4.5, App. C).
+
+The oracle sees only host snapshots of the seeded, torch-filled caches taken
+before any kernel ran, plus the per-step inputs: the resident K/V, window
+queries and global-score history of sampled sequences are rebuilt from those.
+Checked on sampled (sequence, layer) pairs: decode outputs at every step,
+scores and kept sets of the compression events, and the compacted K/V.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+from compressed_paged_kv_gqa_amd import synth
+from oracle import zipage as Z
+
+from gpu_cases import announce
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 2e-5
+LAYERS = [0, 17, 35]
+
+
+@pytest.mark.timeout(900)
+def test_bench_workload_sampled_decode_and_compression():
+    announce("full-size bench workload: 36 layers x 256 sequences")
+    B, BS, NMAX, W, HQ, HKV = bench.B, bench.BS, bench.NMAX, bench.W, bench.HQ, bench.HKV
+    g = HQ // HKV
+    phases = synth.rng(bench.SEED, 3, 0, "lengths").integers(0, BS, B)
+    eng, (q, k, v, out) = bench.build_workload(phases, record=True)
+    order = np.argsort(-phases, kind="stable")
+    samples = [int(order[0]), int(order[1]), int(order[B // 2])]   # 2 compress early
+    nvar = q.shape[0]
+    # --- host snapshots before any kernel of the library has run ------------
+    snap = {}
+    for s in samples:
+        r = eng.reqs[s]
+        idx = torch.tensor(r.table, device="cuda")
+        snap[s] = dict(
+            n0=r.n, table=list(r.table),
+            K=np.stack([eng.cache.k[l, idx].float().cpu().numpy() for l in LAYERS]),
+            V=np.stack([eng.cache.v[l, idx].float().cpu().numpy() for l in LAYERS]),
+            F=np.stack([eng.cache.gscore[l, idx].cpu().numpy() for l in LAYERS]),
+            Q=np.stack([eng.cache.qwin[l, s].float().cpu().numpy() for l in LAYERS]))
+    qh = q[:, LAYERS].float().cpu().numpy()        # [4][3][B][HQ][D]
+    kh = k[:, LAYERS].float().cpu().numpy()
+    vh = v[:, LAYERS].float().cpu().numpy()
+
+    # resident rows per (sample, layer idx, head), logical order
+    def rows(x, li, h, n):   # x: [3][8][HKV][b][d]
+        return x[li][:, h].reshape(NMAX * BS, -1)[:n].astype(np.float64)
+
+    state = {}
+    for s in samples:
+        sn = snap[s]
+        n0 = sn["n0"]
+        state[s] = dict(
+            n=n0,
+            K=[[list(rows(sn["K"], li, h, n0)) for h in range(HKV)] for li in range(len(LAYERS))],
+            V=[[list(rows(sn["V"], li, h, n0)) for h in range(HKV)] for li in range(len(LAYERS))],
+            F=[[list(sn["F"][li][:, h].reshape(-1)[:n0].astype(np.float64)) for h in range(HKV)]
+               for li in range(len(LAYERS))],
+            Q=sn["Q"].astype(np.float64).copy(), events=0)
+    params = Z.ScoreParams()
+    T = 12
+    logged = 0
+    for i in range(T):
+        act = eng.step(q[i % nvar], k[i % nvar], v[i % nvar], out)
+        o_h = out[LAYERS].float().cpu().numpy()         # [3][B][HQ][D]
+        for s in samples:
+            if s not in act:
+                continue
+            st = state[s]
+            for li in range(len(LAYERS)):
+                for h in range(HKV):
+                    st["K"][li][h].append(kh[i % nvar, li, s, h].astype(np.float64))
+                    st["V"][li][h].append(vh[i % nvar, li, s, h].astype(np.float64))
+                    st["F"][li][h].append(0.0)
+                Kl = np.stack([np.stack(st["K"][li][h]) for h in range(HKV)])
+                Vl = np.stack([np.stack(st["V"][li][h]) for h in range(HKV)])
+                o_ref = Z.decode_attention(qh[i % nvar, li, s], Kl, Vl)[0]
+                for j in range(HQ):
+                    err = np.abs(o_h[li, s, j] - o_ref[j]).max() / np.abs(o_ref[j]).max()
+                    assert err <= 2e-2, (s, i, LAYERS[li], j, err)
+                row = Z.window_row(st["n"], BS, W)
+                if row >= 0:
+                    st["Q"][li][:, :, row] = qh[i % nvar, li, s].reshape(HKV, g, -1)
+            st["n"] += 1
+        eng.wait_compressions()
+        # compression events that were launched in this step
+        while logged < len(eng.log):
+            sids, first, sc, kept = eng.log[logged]
+            logged += 1
+            for s in samples:
+                if s not in sids:
+                    continue
+                pos = sids.index(s)
+                st = state[s]
+                n = st["n"]
+                assert n == NMAX * BS and not first[pos]
+                keep = (NMAX - 1) * BS
+                sc_h = sc[LAYERS, pos].cpu().numpy()
+                kept_h = kept[LAYERS, pos].cpu().numpy()
+                for li, l in enumerate(LAYERS):
+                    for h in range(HKV):
+                        Kt = np.stack(st["K"][li][h])
+                        S, F_new = Z.score_tokens(st["Q"][li][h], Kt, np.asarray(st["F"][li][h]),
+                                                  False, BS, params)
+                        fin = np.isfinite(S)
+                        err = np.abs(sc_h[li, h, :n][fin] - S[fin]).max() / np.abs(S[fin]).max()
+                        assert err <= SCORE_TOL, (s, l, h, err)
+                        ref = Z.topk_keep(S, keep)
+                        got = np.sort(kept_h[li, h])
+                        if not np.array_equal(got, ref):
+                            sk = np.sort(S)[::-1][keep - 1]
+                            delta = max(1e-6 * abs(sk), 2 * SCORE_TOL * np.abs(S[fin]).max())
+                            zone = np.abs(S - sk) <= delta
+                            diff = np.zeros(n, bool)
+                            diff[got] ^= True
+                            diff[ref] ^= True
+                            assert not np.any(diff & ~zone), (s, l, h)
+                            pytest.skip("kept set differs inside the tie zone (allowed)")
+                        st["K"][li][h] = [st["K"][li][h][t] for t in ref]
+                        st["V"][li][h] = [st["V"][li][h][t] for t in ref]
+                        st["F"][li][h] = [float(F_new[t]) for t in ref]
+                st["n"] = keep
+                st["events"] += 1
+                # compacted pages hold exactly the kept rows
+                for li, l in enumerate(LAYERS):
+                    for h in range(HKV):
+                        Kr, Vr = eng.resident_kv(s, l, h)
+                        np.testing.assert_array_equal(Kr.float().cpu().numpy(),
+                                                      np.stack(st["K"][li][h]))
+                        np.testing.assert_array_equal(Vr.float().cpu().numpy(),
+                                                      np.stack(st["V"][li][h]))
+    assert state[samples[0]]["events"] == 1 and state[samples[1]]["events"] == 1
+    assert eng.compressions >= 2
+    del eng, q, k, v, out
+    torch.cuda.empty_cache()
