@@ -18,6 +18,8 @@
 //  B  page_s0: per block again, merges the row statistics into log-sum-exp,
 //     recomputes the logits, forms S0 (group max, window mean) and applies
 //     the global score (reads F, writes the updated history to f_new).
+//  F  (flash redundancy only) score_flash_redundancy: per column block, Alg. 3
+//     over all row blocks, row sums accumulated into the redundancy rows.
 //  C  finalize: per (request, kv-head): pooling, redundancy softmax over the
 //     sequence, S - lambda R, +inf window -> scores.
 // The window QK^T and the Gram are dense contractions (bf16 inputs, fp32
@@ -156,6 +158,88 @@ __device__ __forceinline__ int resolve_page(const ScoreParams& P, int pidx, int 
 }
 
 // ---------------------------------------------------------------------------
+// Cosine block C = Kr Kc^T of two b x D key blocks staged in LDS (row token i
+// of Kr, column token j of Kc): the diagonal is zeroed when `diag` (same
+// block), then in every column whose zero-out tag is clear (every column when
+// tag == nullptr) the entry of the highest row with C > p is zeroed and the
+// tag set, and the rows are summed (Zipage Fig. 11 / Alg. 3 on one pair of
+// blocks; the lightning score is the diagonal pair alone). Returns the row
+// sum of row `threadIdx.x` (valid for threadIdx.x < b). All 256 threads call
+// it; it ends with a barrier, so its LDS scratch may be reused afterwards.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__device__ float cosine_block_rows(const char* Kr, const float* inv_r, const char* Kc,
+                                   const float* inv_c, bool diag, float p, int* tag, int b,
+                                   int* colidx, float* colval, float* rowsum, int* istar,
+                                   float* ival) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q = lane >> 4, cl = lane & 15;
+  const int CT = b / 16;
+  for (int j = lane; j < b; j += 64) colidx[wv * b + j] = -1;
+  for (int rt = wv; rt < CT; rt += 4) {
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) {
+      const floatx4 acc = tile_lds_lds<T, D>(Kr, rt * 16, Kc, ct * 16, lane);
+      const int col = ct * 16 + cl;
+      const float invc = inv_c[col];
+      float c[4];
+      uint64_t above[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = rt * 16 + 4 * q + v;
+        c[v] = acc[v] * inv_r[row] * invc;
+        if (diag && row == col) c[v] = 0.f;
+        rsum[v] += c[v];
+        above[v] = __ballot(c[v] > p);
+      }
+      // Highest row of this tile above p in column `col`: row 4*wq + wv2 of
+      // the tile, held by the lane of group wq; that lane records it. Rows
+      // grow with rt, so a later hit replaces an earlier one.
+      int wq = -1, wv2 = 0;
+#pragma unroll
+      for (int qq = 3; qq >= 0; --qq)
+#pragma unroll
+        for (int v = 3; v >= 0; --v)
+          if (wq < 0 && ((above[v] >> (16 * qq + cl)) & 1ull)) { wq = qq; wv2 = v; }
+      if (wq == q) {
+        colidx[wv * b + col] = rt * 16 + 4 * wq + wv2;
+        colval[wv * b + col] = wv2 == 0 ? c[0] : wv2 == 1 ? c[1] : wv2 == 2 ? c[2] : c[3];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) rsum[v] = group_sum<16>(rsum[v]);
+    if (cl == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rowsum[rt * 16 + 4 * q + v] = rsum[v];
+    }
+  }
+  __syncthreads();
+  if (tid < b) {
+    int best = -1;
+    float bv = 0.f;
+    for (int w2 = 0; w2 < 4; ++w2) {
+      const int c = colidx[w2 * b + tid];
+      if (c > best) { best = c; bv = colval[w2 * b + tid]; }
+    }
+    if (tag) {
+      if (tag[tid]) best = -1;
+      else if (best >= 0) tag[tid] = 1;
+    }
+    istar[tid] = best;
+    ival[tid] = bv;
+  }
+  __syncthreads();
+  float r = 0.f;
+  if (tid < b) {
+    r = rowsum[tid];
+    for (int j = 0; j < b; ++j)
+      if (istar[j] == tid) r -= ival[j];
+  }
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // Phase A: row statistics of the window logits + lightning redundancy rows.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int R>
@@ -255,62 +339,85 @@ __global__ __launch_bounds__(256) void score_page_stats_kernel(ScoreParams P) {
   }
 
   if (!(P.flags & ZP_SCORE_REDUNDANCY)) return;
+  float* rrow = P.rbuf + zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b;
+  if (P.flags & ZP_SCORE_REDUNDANCY_FLASH) {
+    // Whole-sequence (flash) redundancy: score_flash_redundancy_kernel
+    // accumulates into these rows next.
+    if (tid < b) rrow[tid] = 0.f;
+    return;
+  }
+  // Lightning redundancy: similarities inside this block only.
+  const float r = cosine_block_rows<T, D>(Ks, inv_norm, Ks, inv_norm, true, P.p, nullptr, b,
+                                          colidx, colval, rowsum, istar, ival);
+  if (tid < b) rrow[tid] = r / (float)n;
+}
 
-  // Lightning redundancy: Gram of the block's keys, row tiles rt = wv, wv+4, ...
-  // For every column j this wavefront records, in its own LDS slice, the
-  // highest row i != j with cos > p among its rows (and that entry's value).
-  for (int j = lane; j < b; j += 64) colidx[wv * b + j] = -1;
-  for (int rt = wv; rt < CT; rt += 4) {
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ct = 0; ct < CT; ++ct) {
-      const floatx4 acc = tile_lds_lds<T, D>(Ks, rt * 16, Ks, ct * 16, lane);
-      const int col = ct * 16 + (lane & 15);
-      const float invc = inv_norm[col];
-      int best = -1;
-      float bestv = 0.f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = rt * 16 + 4 * (lane >> 4) + v;
-        float c = acc[v] * inv_norm[row] * invc;
-        if (row == col) c = 0.f;
-        rsum[v] += group_sum<16>(c);
-        if (c > P.p) { best = row; bestv = c; }
-      }
-      // Highest candidate row across the four 4-row groups of the tile.
-#pragma unroll
-      for (int m = 16; m < 64; m <<= 1) {
-        const int ob = shfl_xor_i(best, m);
-        const float ov = shfl_xor_f(bestv, m);
-        if (ob > best) { best = ob; bestv = ov; }
-      }
-      // Rows grow with rt, so a later hit replaces an earlier one.
-      if (lane < 16 && best >= 0) {
-        colidx[wv * b + col] = best;
-        colval[wv * b + col] = bestv;
-      }
-    }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) rowsum[rt * 16 + 4 * (lane >> 4) + v] = rsum[v];
-    }
+// ---------------------------------------------------------------------------
+// Flash redundancy (Zipage Alg. 3): one workgroup per column block m. Row
+// blocks i are visited from the last to the first with one zero-out tag per
+// column of m, so each column loses only its highest entry above p over the
+// whole sequence; the row sums of every (i, m) pair are added into the row
+// sums of block i (the accumulator R'[i][m] summed over m).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_flash_redundancy_kernel(ScoreParams P) {
+  using L = LdsTile<T, D>;
+  extern __shared__ __align__(16) char smem[];
+  const int b = P.b;
+  char* Km = smem;                                           // [b][D]
+  char* Ki = Km + b * L::ROWB;                               // [b][D]
+  float* inv_m = reinterpret_cast<float*>(Ki + b * L::ROWB); // [b]
+  float* inv_i = inv_m + b;                                  // [b]
+  int* tag = reinterpret_cast<int*>(inv_i + b);              // [b]
+  int* colidx = tag + b;                                     // [4][b]
+  float* colval = reinterpret_cast<float*>(colidx + 4 * b);  // [4][b]
+  float* rowsum = colval + 4 * b;                            // [b]
+  int* istar = reinterpret_cast<int*>(rowsum + b);           // [b]
+  float* ival = reinterpret_cast<float*>(istar + b);         // [b]
+
+  const int m = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
+  int N, slot;
+  const int page_m = resolve_page(P, m, z, &N, &slot);
+  if (page_m < 0) return;
+  const int r = z % P.nreq;
+  const int layer = P.layer_begin + z / P.nreq;
+  const int tid = threadIdx.x;
+  const int n = N * b;
+  const int64_t zh = (int64_t)z * P.h_kv + h;
+  const T* kbase = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems;
+  const int32_t* tab = P.tables + (int64_t)r * P.table_stride;
+  for (int i = 0; i < N; ++i) {          // all block ids were checked by phase A
+    const int pg = tab[i];
+    if (pg < 0 || pg >= P.num_blocks_total) return;
   }
-  __syncthreads();
-  if (tid < b) {
-    int best = -1;
-    float bv = 0.f;
-    for (int w2 = 0; w2 < 4; ++w2) {
-      const int c = colidx[w2 * b + tid];
-      if (c > best) { best = c; bv = colval[w2 * b + tid]; }
+  auto stage = [&](char* dst, float* inv, int page) {
+    stage_rows<T, D>(dst, kbase + ((int64_t)page * P.h_kv + h) * b * D, b, tid, 256);
+    __syncthreads();
+    if (tid < b) {
+      float ss = 0.f;
+      for (int c = 0; c < L::CH; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dst + L::chunk_pos(tid, c) * 16);
+        float f[Vec16<T>::N];
+        Vec16<T>::unpack(v, f);
+#pragma unroll
+        for (int e = 0; e < Vec16<T>::N; ++e) ss = fmaf(f[e], f[e], ss);
+      }
+      inv[tid] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
     }
-    istar[tid] = best;
-    ival[tid] = bv;
-  }
+  };
+  stage(Km, inv_m, page_m);
+  if (tid < b) tag[tid] = 0;
   __syncthreads();
-  if (tid < b) {
-    float r = rowsum[tid];
-    for (int j = 0; j < b; ++j)
-      if (istar[j] == tid) r -= ival[j];
-    P.rbuf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + tid] = r / (float)n;
+  float* rb = P.rbuf + zh * ((int64_t)P.max_blocks * b);
+  for (int i = N - 1; i >= 0; --i) {
+    const bool same = i == m;
+    if (!same) {
+      stage(Ki, inv_i, tab[i]);
+      __syncthreads();
+    }
+    const float rs = cosine_block_rows<T, D>(same ? Km : Ki, same ? inv_m : inv_i, Km, inv_m, same,
+                                             P.p, tag, b, colidx, colval, rowsum, istar, ival);
+    if (tid < b) atomicAdd(rb + (int64_t)i * b + tid, rs / (float)n);
   }
 }
 
@@ -472,8 +579,20 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
   if (smemA > kMaxLds || smemB > kMaxLds)
     return fail(ZP_EINVAL, "zp_score_tokens: block_size %d with this dtype/head_dim needs %zu "
                 "bytes of LDS (max %zu)", b, smemA, kMaxLds);
+  const bool flash = (P.flags & ZP_SCORE_REDUNDANCY) && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
+  const size_t smemF = 2 * size_t(b) * L::ROWB + sizeof(float) * 2 * b + sizeof(int) * b +
+                       sizeof(int) * 4 * b + sizeof(float) * 4 * b + sizeof(float) * b +
+                       sizeof(int) * b + sizeof(float) * b;
+  if (flash && smemF > kMaxLds)
+    return fail(ZP_EINVAL, "zp_score_tokens: flash redundancy with block_size %d and this "
+                "dtype/head_dim needs %zu bytes of LDS (max %zu)", b, smemF, kMaxLds);
   auto kA = score_page_stats_kernel<T, D, R>;
   auto kB = score_page_s0_kernel<T, D, R>;
+  auto kF = score_flash_redundancy_kernel<T, D>;
+  if (flash && hipFuncSetAttribute(reinterpret_cast<const void*>(kF),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   int(smemF)) != hipSuccess)
+    return fail(ZP_EHIP, "zp_score_tokens: cannot reserve %zu bytes of LDS", smemF);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kA),
                           hipFuncAttributeMaxDynamicSharedMemorySize, int(smemA)) != hipSuccess ||
       hipFuncSetAttribute(reinterpret_cast<const void*>(kB),
@@ -481,6 +600,7 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
     return fail(ZP_EHIP, "zp_score_tokens: cannot reserve %zu bytes of LDS", smemA);
   dim3 gridP(P.max_blocks, P.h_kv, items);
   hipLaunchKernelGGL(kA, gridP, dim3(256), smemA, s, P);
+  if (flash) hipLaunchKernelGGL(kF, gridP, dim3(256), smemF, s, P);
   hipLaunchKernelGGL(kB, gridP, dim3(256), smemB, s, P);
   hipLaunchKernelGGL(score_finalize_kernel, dim3(P.h_kv, items), dim3(256), 0, s, P);
   return ZP_OK;
@@ -556,7 +676,7 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   if ((sp.flags & ZP_SCORE_GLOBAL) && (!cache->gscore || !f_new))
     return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL needs cache->gscore and f_new");
   if (sp.flags & ~uint32_t(ZP_SCORE_GLOBAL | ZP_SCORE_POOL | ZP_SCORE_POOL_FIRST_ONLY |
-                           ZP_SCORE_REDUNDANCY))
+                           ZP_SCORE_REDUNDANCY | ZP_SCORE_REDUNDANCY_FLASH))
     return fail(ZP_EINVAL, "zp_score_tokens: unknown flags 0x%x", sp.flags);
   if ((sp.flags & ZP_SCORE_POOL) && (sp.pool_kernel < 1 || sp.pool_kernel % 2 == 0))
     return fail(ZP_EINVAL, "zp_score_tokens: pool_kernel must be odd and >= 1");

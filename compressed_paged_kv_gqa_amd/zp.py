@@ -21,6 +21,7 @@ ZP_OK, ZP_EINVAL, ZP_ENOBLOCKS, ZP_EHIP, ZP_ESTATE = 0, -1, -2, -3, -4
 ZP_DTYPE_F32, ZP_DTYPE_BF16 = 0, 1
 ZP_DEVERR_BLOCK_ID, ZP_DEVERR_SEQ_LEN, ZP_DEVERR_SLOT, ZP_DEVERR_KEEP = 1, 2, 4, 8
 ZP_SCORE_GLOBAL, ZP_SCORE_POOL, ZP_SCORE_POOL_FIRST_ONLY, ZP_SCORE_REDUNDANCY = 1, 2, 4, 8
+ZP_SCORE_REDUNDANCY_FLASH = 0x10
 ZP_SELECT_NO_COMPACT = 1
 
 
@@ -249,7 +250,9 @@ def zp_paged_decode(cache: PagedKVCache, layer, q, k_new, v_new, block_tables, s
 class ScoreParams:
     """Scoring hyper-parameters (defaults: Zipage App. C.8's recommendation,
     lambda 0.2, tau 0.4, alpha 0.8, pooling at the first compression only,
-    lightning redundancy; p and the pooling width are readings: 0.9 and 7)."""
+    lightning redundancy; p and the pooling width are readings: 0.9 and 7).
+    ``redundancy`` picks the lightning (App. C.7, within each block) or the
+    flash (Alg. 3, over the whole sequence) row sums."""
     alpha: float = 0.8
     lam: float = 0.2
     tau: float = 0.4
@@ -259,12 +262,16 @@ class ScoreParams:
     use_pool: bool = True
     pool_first_only: bool = True
     use_redundancy: bool = True
+    redundancy: str = "lightning"
 
     def c(self):
+        if self.redundancy not in ("lightning", "flash"):
+            raise ValueError(f"redundancy must be 'lightning' or 'flash', not {self.redundancy!r}")
         flags = ((ZP_SCORE_GLOBAL if self.use_global else 0)
                  | (ZP_SCORE_POOL if self.use_pool else 0)
                  | (ZP_SCORE_POOL_FIRST_ONLY if self.pool_first_only else 0)
-                 | (ZP_SCORE_REDUNDANCY if self.use_redundancy else 0))
+                 | (ZP_SCORE_REDUNDANCY if self.use_redundancy else 0)
+                 | (ZP_SCORE_REDUNDANCY_FLASH if self.redundancy == "flash" else 0))
         return ScoreParamsC(self.alpha, self.lam, self.tau, self.p, self.pool_kernel, flags)
 
 

@@ -154,7 +154,13 @@ zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t la
 #define ZP_SCORE_GLOBAL 0x1u          /* decayed global score (Alg. 2)            */
 #define ZP_SCORE_POOL 0x2u            /* max pooling along the sequence (eq. (3)) */
 #define ZP_SCORE_POOL_FIRST_ONLY 0x4u /* pool only at a request's first compression */
-#define ZP_SCORE_REDUNDANCY 0x8u      /* lightning key redundancy, S - lambda R   */
+#define ZP_SCORE_REDUNDANCY 0x8u      /* key redundancy, S - lambda R (lightning) */
+#define ZP_SCORE_REDUNDANCY_FLASH 0x10u /* with ZP_SCORE_REDUNDANCY: similarities over the
+                                           whole sequence (Zipage Alg. 3) instead of within
+                                           each block (App. C.7); ignored without
+                                           ZP_SCORE_REDUNDANCY. Needs 2*b*d*sizeof(elem)
+                                           + 56*b bytes of LDS (<= 160 KiB), which
+                                           holds wherever scoring itself fits        */
 
 typedef struct zp_score_params {
   float alpha;         /* decay of the global score                          */
@@ -183,8 +189,9 @@ size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t
  *        shared between requests are never written;
  *   S2 = max-pooled S1 (when ZP_SCORE_POOL, and first_compression[r] if
  *        ZP_SCORE_POOL_FIRST_ONLY);
- *   S3 = S2 - lambda * softmax_t(r_t / n / tau), r_t the lightning row sums,
- *        when ZP_SCORE_REDUNDANCY;
+ *   S3 = S2 - lambda * softmax_t(r_t / n / tau), r_t the lightning row sums
+ *        (or, with ZP_SCORE_REDUNDANCY_FLASH, the flash row sums over the
+ *        whole sequence), when ZP_SCORE_REDUNDANCY;
  *   scores = S3 with +inf on the last w positions.
  *
  *   block_tables [device] int32 [nreq][table_stride]

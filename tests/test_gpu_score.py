@@ -3,7 +3,8 @@
 Zipage (arXiv 2603.08743): App. C.2 Alg. 1 (window logits, causal last block,
 softmax, GQA max, window mean), App. C.3 Alg. 2 (global score with F updated
 in place), App. C.4 (pooling), App. C.5 eq. (4) / C.7 / C.8 (lightning
-redundancy, tempered softmax), Sec. 4.2 (+inf window).
+redundancy, tempered softmax), App. C.6 Alg. 3 (flash redundancy over the
+whole sequence), Sec. 4.2 (+inf window).
 
 Bar: the GPU accumulates in fp32 from inputs that both sides hold exactly,
 so |S_gpu - S_ref| <= 2e-5 * max|S_ref| over the finite entries, +inf
@@ -30,7 +31,7 @@ def _oracle_params(sp: zp.ScoreParams):
     return Z.ScoreParams(alpha=sp.alpha, lam=sp.lam, tau=sp.tau, p=sp.p,
                          pool_kernel=sp.pool_kernel, use_global=sp.use_global,
                          use_pool=sp.use_pool, pool_first_only=sp.pool_first_only,
-                         use_redundancy=sp.use_redundancy, redundancy="lightning")
+                         use_redundancy=sp.use_redundancy, redundancy=sp.redundancy)
 
 
 def _planted_keys(hc, seed):
@@ -92,8 +93,10 @@ def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, laye
                                                      b, op, return_parts=True)
                 if sp.use_redundancy and planted:
                     # no cosine within 1e-3 of p: the threshold decision is robust
-                    for i in range(nblocks[r]):
-                        C = Z.cosine_matrix(K[i * b:(i + 1) * b], K[i * b:(i + 1) * b])
+                    # (within blocks for lightning, over the sequence for flash)
+                    span = n if sp.redundancy == "flash" else b
+                    for i in range(n // span):
+                        C = Z.cosine_matrix(K[i * span:(i + 1) * span], K[i * span:(i + 1) * span])
                         np.fill_diagonal(C, 0)
                         off = C[C != 0]
                         assert off.size == 0 or np.min(np.abs(off - sp.p)) > 1e-3
@@ -152,3 +155,27 @@ def test_score_other_shapes():
          layer_count=1)
     _run("f32", 128, 16, 2, 64, 2, [3, 4], lambda r: 1, DEFAULT, L=1, layer_begin=0,
          layer_count=1)
+
+
+FLASH = zp.ScoreParams(redundancy="flash")
+
+
+def test_score_flash_redundancy_qwen_shape_bf16():
+    _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, FLASH)
+
+
+def test_score_flash_redundancy_tiny_fp32_and_single_block():
+    _run("f32", 64, 4, 1, 16, 8, [13, 1, 4], lambda r: r != 2, FLASH, L=1, layer_begin=0,
+         layer_count=1)
+    _run("f32", 128, 16, 2, 128, 16, [3, 5], lambda r: 1, FLASH, L=1, layer_begin=0,
+         layer_count=1)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.5])
+def test_score_flash_redundancy_planted_clusters_across_blocks(p):
+    # eight directions spread over all blocks: every column has partners above
+    # p in other blocks, so the zero-out tags carry across row blocks
+    sp = zp.ScoreParams(p=p, use_global=False, use_pool=False, redundancy="flash")
+    _run("bf16", 128, 16, 4, 64, 16, [4, 7], lambda r: 1, sp, planted=True, heavy=False)
+    _run("bf16", 64, 8, 8, 32, 16, [5, 2], lambda r: 0, sp, L=1, layer_begin=0, layer_count=1,
+         planted=True, heavy=False)
