@@ -61,6 +61,10 @@ def parse_args():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--sync-compress", action="store_true",
                     help="run compressions on the decode stream (ablation)")
+    ap.add_argument("--compress-kernels", action="store_true",
+                    help="only the isolated compression-kernel measurement (one JSON line)")
+    ap.add_argument("--no-compress-kernels", action="store_true",
+                    help="skip the isolated compression-kernel measurement")
     return ap.parse_args()
 
 
@@ -174,6 +178,121 @@ def run_gpu(args, phases):
 
 
 # --------------------------------------------------------------------------
+# Compression kernels in isolation (score, select + compact)
+# --------------------------------------------------------------------------
+
+MFMA_PEAK_TFS = 2500.0   # dense bf16 MFMA, MI355X
+
+# Burst of the 4096-token-prompt workload: 64 requests whose prompts fill 16
+# blocks compress at once (first compression: pooling on, no F history).
+BURST_REQ, BURST_BLOCKS = 64, 16
+
+
+def score_unit_cost(n, redundancy, first):
+    """Algorithmic (flops, bytes) of scoring one (layer, kv-head, request)
+    with n = N*b resident tokens: window logits g*w x n x d and the key
+    cosines (within each block for lightning: N*b*b*d; over the sequence for
+    flash: n*n*d) as multiply-adds; K read once, the window queries, F read
+    unless it is the first compression, scores and the updated history
+    written."""
+    g = HQ // HKV
+    gram = (n // BS) * BS * BS if redundancy == "lightning" else n * n
+    flops = 2 * g * W * n * D + 2 * gram * D
+    byts = n * D * ELEM + g * W * D * ELEM + (0 if first else 4 * n) + 8 * n
+    return flops, byts
+
+
+def select_unit_bytes(n, keep):
+    """Algorithmic bytes of selecting and compacting one (layer, kv-head,
+    request): the n scores read once, K and V of the keep kept tokens read
+    and written, their global scores read (updated history) and written."""
+    return 4 * n + 4 * keep * D * ELEM + 8 * keep
+
+
+def _time_calls(fn, iters, stream):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def compress_kernel_bench(iters=20):
+    """HIP-event time per call of zp_score_tokens (lightning and flash) and
+    zp_select_compact at the burst shape, on their own stream with nothing
+    else running, against the MFMA and HBM rooflines."""
+    import torch
+    from compressed_paged_kv_gqa_amd import zp
+    R, NB = BURST_REQ, BURST_BLOCKS
+    n = NB * BS
+    keep = (NMAX - 1) * BS
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=R * NB + 8, block_size=BS,
+                            num_kv_heads=HKV, num_q_heads=HQ, head_dim=D, window=W,
+                            max_slots=R, n_max=NMAX, dtype="bf16")
+    cache = zp.PagedKVCache(geom)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(SEED + 7)
+    cache.k.normal_(generator=g)
+    cache.v.normal_(generator=g)
+    cache.qwin.normal_(generator=g)
+    cache.gscore.uniform_(0.0, 1e-3, generator=g)
+    perm = torch.randperm(R * NB, generator=g, device="cuda").to(torch.int32)
+    tables = perm.view(R, NB).contiguous()
+    dst = tables[:, :NMAX - 1].contiguous()
+    nblk = torch.full((R,), NB, dtype=torch.int32, device="cuda")
+    qslot = torch.arange(R, dtype=torch.int32, device="cuda")
+    first = torch.ones(R, dtype=torch.uint8, device="cuda")
+    scores = torch.empty((1, R, HKV, n), dtype=torch.float32, device="cuda")
+    f_new = torch.empty_like(scores)
+    sws = zp.new_workspace(zp.zp_score_workspace_size(geom, 1, R, NB))
+    cws = zp.new_workspace(zp.zp_select_workspace_size(geom, 1, R))
+    stream = torch.cuda.Stream()
+    units = R * HKV
+    out = {"workload": f"{R} requests x {n} tokens ({NB} full blocks) compressing at once, "
+                       f"1 layer, bf16, first compression, keep {keep}",
+           "units_per_call": units}
+    with torch.cuda.stream(stream):
+        for red in ("lightning", "flash"):
+            sp = zp.ScoreParams(redundancy=red)
+            ms = _time_calls(lambda: zp.zp_score_tokens(cache, sp, 0, 1, tables, nblk, NB, qslot,
+                                                        first, scores, f_new, sws, stream=stream),
+                             iters if red == "lightning" else max(3, iters // 4), stream)
+            fl, by = score_unit_cost(n, red, True)
+            tf = units * fl / (ms * 1e-3) / 1e12
+            gb = units * by / (ms * 1e-3) / 1e9
+            ideal = max(units * fl / (MFMA_PEAK_TFS * 1e12), units * by / (HBM_PEAK_GBS * 1e9))
+            out[f"score_{red}"] = {
+                "ms_per_call": round(ms, 4), "achieved_tflops": round(tf, 1),
+                "mfma_peak_tflops": MFMA_PEAK_TFS, "achieved_gbs": round(gb, 1),
+                "bound": "mfma" if units * fl / MFMA_PEAK_TFS / 1e12 > units * by / HBM_PEAK_GBS / 1e9
+                else "hbm",
+                "frac_of_roofline": round(ideal / (ms * 1e-3), 4),
+                "flops_per_unit": fl, "bytes_per_unit": by}
+        # scores of the lightning variant feed the selection
+        sp = zp.ScoreParams()
+        zp.zp_score_tokens(cache, sp, 0, 1, tables, nblk, NB, qslot, first, scores, f_new, sws,
+                           stream=stream)
+        ms = _time_calls(lambda: zp.zp_select_compact(cache, 0, 1, scores, tables, nblk, NB, dst,
+                                                      keep, None, cws, stream=stream,
+                                                      f_new=f_new), iters, stream)
+        by = select_unit_bytes(n, keep)
+        gb = units * by / (ms * 1e-3) / 1e9
+        out["select_compact"] = {"ms_per_call": round(ms, 4), "achieved_gbs": round(gb, 1),
+                                 "bound": "hbm", "frac_of_roofline": round(gb / HBM_PEAK_GBS, 4),
+                                 "bytes_per_unit": by}
+    stream.synchronize()
+    errs = zp.zp_workspace_errors(sws) | zp.zp_workspace_errors(cws)
+    assert errs == 0, f"device errors {errs}"
+    return out
+
+
+# --------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on a bounded sample of the same workload
 # --------------------------------------------------------------------------
 
@@ -273,6 +392,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.compress_kernels:
+        print(json.dumps(compress_kernel_bench()), flush=True)
+        return
     from compressed_paged_kv_gqa_amd import synth
     phases = synth.rng(SEED, 3, 0, "lengths").integers(0, BS, B)
     cpu = None
@@ -284,6 +406,10 @@ def main():
         log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} cores")
     r = run_gpu(args, phases)
     value = r["tokens"] / r["elapsed"]
+    ck = None
+    if not args.no_compress_kernels:
+        log("compression kernels in isolation")
+        ck = compress_kernel_bench()
     traffic = traffic_from_profiles()
     line = {
         "metric": "decode tok/s at 256 seqs with compression; achieved HBM GB/s vs peak",
@@ -312,6 +438,8 @@ def main():
                      "algorithmic_bytes_per_launch": round(r["bytes_per_launch"])},
         "decode_ms_per_step": round(r["decode_ms_per_step"], 3),
     }
+    if ck is not None:
+        line["compress_kernels"] = ck
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -4,26 +4,32 @@
 // observation window with a causal mask on the last block; softmax over the
 // whole sequence per query head, max over the GQA group, mean over the
 // window), App. C.3 Alg. 2 (decayed max-reduce with the global score cache
-// F), App. C.4 eq. (3) (max pooling after the global score), App. C.5 eq. (4)
-// and C.7 (lightning redundancy: cosine similarity inside each block only,
-// diagonal and each column's last entry above p zeroed, row sums over the
-// sequence length), App. C.8 (tempered softmax of the redundancy), Sec. 4.2
-// (+inf on the observation window).
+// F), App. C.4 eq. (3) (max pooling after the global score), App. C.5 eq. (4),
+// Fig. 11 and Alg. 3 (key redundancy: cosine similarities, diagonal and each
+// column's last entry above p zeroed, row sums over the sequence length),
+// App. C.7 (lightning: similarities inside each block only), App. C.8
+// (tempered softmax of the redundancy), Sec. 4.2 (+inf on the window).
 //
-// Three launches per call, all parallel over (block, kv-head, layer x request):
-//  A  page_stats: one workgroup per block. The block's keys are staged once
-//     in LDS (XOR-swizzled 16-byte chunks, conflict-free MFMA operand reads).
-//     MFMA computes the window logits (g*w x b) -> per-row partial (max, sum
-//     of exp2) and the block's Gram matrix (b x b) -> lightning row sums.
-//  B  page_s0: per block again, merges the row statistics into log-sum-exp,
+// Launches per call, parallel over (block, kv-head, layer x request):
+//  A  score_block: one workgroup per block. The block's keys are staged in
+//     LDS (XOR-swizzled 16-byte chunks, 16 loads in flight per thread), two
+//     workgroups per CU. MFMA forms the window logits (g*w x b, per-row
+//     partial max and sum of exp2) and, for the lightning redundancy, the
+//     block's cosine matrix, whose epilogue only tracks each column's
+//     highest row above p. The row sums themselves need no matrix: the sum
+//     of row i of the cosine matrix is khat_i . (sum_j khat_j), minus the
+//     diagonal and the zeroed entries.
+//  F  (flash redundancy only) score_flash: one workgroup per column block;
+//     the cosine blocks against every row block give each column its highest
+//     row above p over the whole sequence (the row that Alg. 3's zero-out
+//     tags single out, independent of the visiting order).
+//  B  score_s0: per block again, merges the row statistics into log-sum-exp,
 //     recomputes the logits, forms S0 (group max, window mean) and applies
 //     the global score (reads F, writes the updated history to f_new).
-//  F  (flash redundancy only) score_flash_redundancy: per column block, Alg. 3
-//     over all row blocks, row sums accumulated into the redundancy rows.
 //  C  finalize: per (request, kv-head): pooling, redundancy softmax over the
 //     sequence, S - lambda R, +inf window -> scores.
-// The window QK^T and the Gram are dense contractions (bf16 inputs, fp32
-// accumulation on MFMA 16x16x32; fp32 inputs use MFMA 16x16x4 f32).
+// The window QK^T and the cosine matrices are dense contractions (bf16
+// inputs, fp32 accumulation on MFMA 16x16x32; fp32 inputs use 16x16x4 f32).
 #include <cmath>
 
 #include "zp_device.h"
@@ -42,6 +48,7 @@ struct LdsTile {
   static constexpr int CH = D * (int)sizeof(T) / 16;  // chunks per row
   static constexpr int SW = CH < 16 ? CH : 16;
   static constexpr int ROWB = CH * 16;                // bytes per row
+  static constexpr int EPC = 16 / (int)sizeof(T);     // elements per chunk
   __device__ static int chunk_pos(int r, int c) { return r * CH + (c ^ (r % SW)); }
 };
 
@@ -83,27 +90,30 @@ struct Mma<float, D> {
   }
 };
 
-// 16x16 tile C[i][j] = sum_k A[a0 + i][k] * B[b0 + j][k], both operands in LDS.
-// Lane l holds C[4*(l/16) + v][l % 16] in element v.
-template <typename T, int D>
-__device__ floatx4 tile_lds_lds(const char* A, int a0, const char* B, int b0, int lane) {
-  using M = Mma<T, D>;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < M::NKS; ++ks)
-    acc = M::mma(M::lds(A, a0 + (lane & 15), ks, lane), M::lds(B, b0 + (lane & 15), ks, lane), acc);
-  return acc;
-}
+// Column tiles (16 tokens each) per wavefront: a block of b <= 256 tokens has
+// at most 16 tiles, dealt to the 4 wavefronts as ct = wv, wv + 4, ...
+constexpr int kCTW = 4;
 
-// Copies `rows` rows of D elements (contiguous in global memory) to an LDS tile.
+// Copies `rows` rows of D elements (contiguous in global memory) to an LDS
+// tile with up to 16 loads in flight per thread.
 template <typename T, int D>
-__device__ void stage_rows(char* dst, const T* src, int rows, int tid, int nthreads) {
+__device__ void stage_rows(char* dst, const T* src, int rows, int tid) {
   using L = LdsTile<T, D>;
+  constexpr int BATCH = 16;
   const int total = rows * L::CH;
-  for (int i = tid; i < total; i += nthreads) {
-    const int r = i / L::CH, c = i % L::CH;
-    *reinterpret_cast<uint4*>(dst + L::chunk_pos(r, c) * 16) =
-        ld16(reinterpret_cast<const char*>(src) + (int64_t)i * 16);
+  const char* s = reinterpret_cast<const char*>(src);
+  for (int i0 = 0; i0 < total; i0 += 256 * BATCH) {
+    uint4 v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i < total) v[u] = ld16(s + (int64_t)i * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i < total) *reinterpret_cast<uint4*>(dst + L::chunk_pos(i / L::CH, i % L::CH) * 16) = v[u];
+    }
   }
 }
 
@@ -118,8 +128,10 @@ struct ScoreParams {
   float* scores;
   float* f_new;  // updated global score (S1) per token, same layout as scores
   float* stats;  // [items][h_kv][max_blocks][R][2]  (max, sum) in the exp2 domain
-  float* rbuf;   // [items][h_kv][max_blocks * b]     lightning row sums / n
+  float* rbuf;   // [items][h_kv][max_blocks * b]     redundancy row sums / n
   float* s1buf;  // [items][h_kv][max_blocks * b]     S1
+  float* inv;    // [items][h_kv][max_blocks * b]     inverse key norms
+  float* ksum;   // [items][h_kv][max_blocks][D]      sum of the block's unit keys
   uint32_t* err;
   int64_t scores_stride;
   int64_t kv_layer_elems, qwin_layer_elems, f_layer_elems;
@@ -157,106 +169,128 @@ __device__ __forceinline__ int resolve_page(const ScoreParams& P, int pidx, int 
   return page;
 }
 
-// ---------------------------------------------------------------------------
-// Cosine block C = Kr Kc^T of two b x D key blocks staged in LDS (row token i
-// of Kr, column token j of Kc): the diagonal is zeroed when `diag` (same
-// block), then in every column whose zero-out tag is clear (every column when
-// tag == nullptr) the entry of the highest row with C > p is zeroed and the
-// tag set, and the rows are summed (Zipage Fig. 11 / Alg. 3 on one pair of
-// blocks; the lightning score is the diagonal pair alone). Returns the row
-// sum of row `threadIdx.x` (valid for threadIdx.x < b). All 256 threads call
-// it; it ends with a barrier, so its LDS scratch may be reused afterwards.
-// ---------------------------------------------------------------------------
+// Loads the B operands (keys as columns of the product) of this wavefront's
+// column tiles, ct = wv + 4 * cw, from an LDS tile or from global memory.
 template <typename T, int D>
-__device__ float cosine_block_rows(const char* Kr, const float* inv_r, const char* Kc,
-                                   const float* inv_c, bool diag, float p, int* tag, int b,
-                                   int* colidx, float* colval, float* rowsum, int* istar,
-                                   float* ival) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+struct ColOps {
+  using M = Mma<T, D>;
+  typename M::op_t op[kCTW][M::NKS];
+  __device__ void from_lds(const char* Ks, int CT, int wv, int lane) {
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      if (ct < CT) {
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) op[cw][ks] = M::lds(Ks, ct * 16 + (lane & 15), ks, lane);
+      }
+    }
+  }
+  __device__ void from_global(const T* kblk, int CT, int wv, int lane) {
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      if (ct < CT) {
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks)
+          op[cw][ks] = M::glb(kblk + (int64_t)(ct * 16 + (lane & 15)) * D, ks, lane);
+      }
+    }
+  }
+};
+
+// Cosine tiles of row tile rt (keys of the LDS block Ks) against this
+// wavefront's column tiles: for each column, remembers the highest row whose
+// cosine exceeds p (global row index row_base + row) and that cosine. Rows
+// grow with rt and with the register index, so the last hit is the highest.
+// The diagonal of the block against itself is skipped when `self`.
+template <typename T, int D>
+__device__ __forceinline__ void cosine_tile_rows(const char* Ks, const float* inv_r, int rt,
+                                                 const ColOps<T, D>& B, const float* invc, int CT,
+                                                 int wv, int lane, bool self, float p,
+                                                 int row_base, int* brow, float* bval) {
+  using M = Mma<T, D>;
   const int q = lane >> 4, cl = lane & 15;
-  const int CT = b / 16;
-  for (int j = lane; j < b; j += 64) colidx[wv * b + j] = -1;
-  for (int rt = wv; rt < CT; rt += 4) {
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ct = 0; ct < CT; ++ct) {
-      const floatx4 acc = tile_lds_lds<T, D>(Kr, rt * 16, Kc, ct * 16, lane);
-      const int col = ct * 16 + cl;
-      const float invc = inv_c[col];
-      float c[4];
-      uint64_t above[4];
+  typename M::op_t a[M::NKS];
+#pragma unroll
+  for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Ks, rt * 16 + cl, ks, lane);
+  const float4 ir = *reinterpret_cast<const float4*>(inv_r + rt * 16 + 4 * q);
+  const float irv[4] = {ir.x, ir.y, ir.z, ir.w};
+#pragma unroll
+  for (int cw = 0; cw < kCTW; ++cw) {
+    const int ct = wv + 4 * cw;
+    if (ct < CT) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
+      const bool diag = self && ct == rt;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = rt * 16 + 4 * q + v;
-        c[v] = acc[v] * inv_r[row] * invc;
-        if (diag && row == col) c[v] = 0.f;
-        rsum[v] += c[v];
-        above[v] = __ballot(c[v] > p);
-      }
-      // Highest row of this tile above p in column `col`: row 4*wq + wv2 of
-      // the tile, held by the lane of group wq; that lane records it. Rows
-      // grow with rt, so a later hit replaces an earlier one.
-      int wq = -1, wv2 = 0;
-#pragma unroll
-      for (int qq = 3; qq >= 0; --qq)
-#pragma unroll
-        for (int v = 3; v >= 0; --v)
-          if (wq < 0 && ((above[v] >> (16 * qq + cl)) & 1ull)) { wq = qq; wv2 = v; }
-      if (wq == q) {
-        colidx[wv * b + col] = rt * 16 + 4 * wq + wv2;
-        colval[wv * b + col] = wv2 == 0 ? c[0] : wv2 == 1 ? c[1] : wv2 == 2 ? c[2] : c[3];
+        float c = acc[v] * irv[v] * invc[cw];
+        if (diag && 4 * q + v == cl) c = 0.f;
+        if (c > p) {
+          brow[cw] = row_base + rt * 16 + 4 * q + v;
+          bval[cw] = c;
+        }
       }
     }
+  }
+}
+
+// Highest (row, cosine) of each column over the four 4-row lane groups;
+// valid in lanes 0..15 (column ct * 16 + lane).
+__device__ __forceinline__ void best_over_groups(int* brow, float* bval, int CT, int wv) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) rsum[v] = group_sum<16>(rsum[v]);
-    if (cl == 0) {
+  for (int cw = 0; cw < kCTW; ++cw) {
+    const int ct = wv + 4 * cw;
+    if (ct < CT) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) rowsum[rt * 16 + 4 * q + v] = rsum[v];
+      for (int m = 16; m < 64; m <<= 1) {
+        const int o = shfl_xor_i(brow[cw], m);
+        const float ov = shfl_xor_f(bval[cw], m);
+        if (o > brow[cw]) { brow[cw] = o; bval[cw] = ov; }
+      }
     }
   }
-  __syncthreads();
-  if (tid < b) {
-    int best = -1;
-    float bv = 0.f;
-    for (int w2 = 0; w2 < 4; ++w2) {
-      const int c = colidx[w2 * b + tid];
-      if (c > best) { best = c; bv = colval[w2 * b + tid]; }
+}
+
+// Sum of squares of row r of an LDS tile, and its dot product with an fp32
+// vector v[D] (when v != nullptr).
+template <typename T, int D>
+__device__ __forceinline__ void row_norm_dot(const char* Ks, int r, const float* v, float* ss,
+                                             float* dot) {
+  using L = LdsTile<T, D>;
+  float s = 0.f, d = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < L::CH; ++c) {
+    const uint4 x = *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(r, c) * 16);
+    float f[L::EPC];
+    Vec16<T>::unpack(x, f);
+#pragma unroll
+    for (int e = 0; e < L::EPC; ++e) {
+      s = fmaf(f[e], f[e], s);
+      if (v) d = fmaf(f[e], v[c * L::EPC + e], d);
     }
-    if (tag) {
-      if (tag[tid]) best = -1;
-      else if (best >= 0) tag[tid] = 1;
-    }
-    istar[tid] = best;
-    ival[tid] = bv;
   }
-  __syncthreads();
-  float r = 0.f;
-  if (tid < b) {
-    r = rowsum[tid];
-    for (int j = 0; j < b; ++j)
-      if (istar[j] == tid) r -= ival[j];
-  }
-  __syncthreads();
-  return r;
+  *ss = s;
+  *dot = d;
 }
 
 // ---------------------------------------------------------------------------
-// Phase A: row statistics of the window logits + lightning redundancy rows.
+// Phase A: row statistics of the window logits; key norms and unit-key sums;
+// lightning redundancy rows.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int R>
-__global__ __launch_bounds__(256) void score_page_stats_kernel(ScoreParams P) {
+__global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   using L = LdsTile<T, D>;
+  using M = Mma<T, D>;
   constexpr int RT = R / 16;
   extern __shared__ __align__(16) char smem[];
   const int b = P.b;
-  char* Ks = smem;                                   // [b][D]
-  char* Qs = Ks + b * L::ROWB;                       // [R][D]
-  float* inv_norm = reinterpret_cast<float*>(Qs + R * L::ROWB);  // [b]
-  float* wstat = inv_norm + b;                       // [4][R][2]
-  float* rowsum = wstat + 4 * R * 2;                 // [b]
-  int* colidx = reinterpret_cast<int*>(rowsum + b);  // [4][b]
-  float* colval = reinterpret_cast<float*>(colidx + 4 * b);  // [4][b]
-  int* istar = reinterpret_cast<int*>(colval + 4 * b);       // [b]
-  float* ival = reinterpret_cast<float*>(istar + b);         // [b]
+  char* Ks = smem;                                            // [b][D]
+  float* inv_s = reinterpret_cast<float*>(Ks + b * L::ROWB);  // [b]
+  float* ksum_s = inv_s + b;                                  // [D]
+  float* wstat = ksum_s + D;                                  // [4][R][2]
+  float* sub = wstat + 4 * R * 2;                             // [b]
 
   const int pidx = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
   int N, slot;
@@ -264,116 +298,172 @@ __global__ __launch_bounds__(256) void score_page_stats_kernel(ScoreParams P) {
   if (page < 0) return;
   const int layer = P.layer_begin + z / P.nreq;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q = lane >> 4, cl = lane & 15;
   const bool last = pidx == N - 1;
   const int n = N * b;
+  const int CT = b / 16;
+  const int64_t zh = (int64_t)z * P.h_kv + h;
+  const bool redun = (P.flags & ZP_SCORE_REDUNDANCY) != 0;
+  const bool flash = redun && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
 
   const T* kpage = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems +
                    ((int64_t)page * P.h_kv + h) * b * D;
   const T* qrows = reinterpret_cast<const T*>(P.qwin) + layer * P.qwin_layer_elems +
                    ((int64_t)slot * P.h_kv + h) * R * D;
-  stage_rows<T, D>(Ks, kpage, b, tid, 256);
-  stage_rows<T, D>(Qs, qrows, R, tid, 256);
+  stage_rows<T, D>(Ks, kpage, b, tid);
+  if (tid < b) sub[tid] = 0.f;
   __syncthreads();
-  if (tid < b) {
-    float ss = 0.f;
-    for (int c = 0; c < L::CH; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(tid, c) * 16);
-      float f[Vec16<T>::N];
-      Vec16<T>::unpack(v, f);
-#pragma unroll
-      for (int e = 0; e < Vec16<T>::N; ++e) ss = fmaf(f[e], f[e], ss);
+
+  // Key norms, and the sum of the block's unit keys (thread = chunk c of the
+  // row, rows rg, rg + RG, ...; the RG partial sums of a chunk sit in
+  // consecutive lanes).
+  float ss = 0.f, mainr = 0.f;
+  if (redun) {
+    if (tid < b) {
+      float unused;
+      row_norm_dot<T, D>(Ks, tid, nullptr, &ss, &unused);
+      inv_s[tid] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
     }
-    inv_norm[tid] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+    __syncthreads();
+    constexpr int RG = 256 / L::CH;
+    const int c = tid / RG, rg = tid % RG;
+    float acc[L::EPC];
+#pragma unroll
+    for (int e = 0; e < L::EPC; ++e) acc[e] = 0.f;
+    for (int r = rg; r < b; r += RG) {
+      const uint4 x = *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(r, c) * 16);
+      float f[L::EPC];
+      Vec16<T>::unpack(x, f);
+      const float iv = inv_s[r];
+#pragma unroll
+      for (int e = 0; e < L::EPC; ++e) acc[e] = fmaf(f[e], iv, acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < L::EPC; ++e) acc[e] = group_sum<RG>(acc[e]);
+    if (rg == 0) {
+#pragma unroll
+      for (int e = 0; e < L::EPC; ++e) ksum_s[c * L::EPC + e] = acc[e];
+    }
+    __syncthreads();
+    float* ks_out = P.ksum + (zh * P.max_blocks + pidx) * D;
+    for (int e = tid; e < D; e += 256) ks_out[e] = ksum_s[e];
+    if (tid < b) {
+      P.inv[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + tid] = inv_s[tid];
+      // row sum of the block's cosine matrix without its diagonal
+      float ss2, dot;
+      row_norm_dot<T, D>(Ks, tid, ksum_s, &ss2, &dot);
+      const float iv = inv_s[tid];
+      mainr = iv * dot - iv * iv * ss2;
+    }
   }
 
-  // Window logits: this wavefront takes column tiles ct = wv, wv+4, ...
-  const int CT = b / 16;
-  float rm[RT][4], rs[RT][4];
+  // Window logits: B operands = this wavefront's column tiles of the block.
+  ColOps<T, D> B;
+  B.from_lds(Ks, CT, wv, lane);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RT; ++rt) {
+    typename M::op_t a[M::NKS];
+    const T* qr = qrows + (int64_t)(rt * 16 + cl) * D;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) { rm[rt][v] = -INFINITY; rs[rt][v] = 0.f; }
-  for (int ct = wv; ct < CT; ct += 4) {
+    for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::glb(qr, ks, lane);
+    floatx4 acc[kCTW];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const floatx4 acc = tile_lds_lds<T, D>(Qs, rt * 16, Ks, ct * 16, lane);
+    for (int cw = 0; cw < kCTW; ++cw) {
+      acc[cw] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (wv + 4 * cw < CT) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = rt * 16 + 4 * (lane >> 4) + v;
-        const int col = ct * 16 + (lane & 15);
-        const int u = row % P.w;
-        float x = acc[v] * P.qk_scale;
-        if (last && col > b - P.w + u) x = -INFINITY;
-        const float tm = group_max<16>(x);
-        const float mn = fmaxf(rm[rt][v], tm);
-        if (mn != -INFINITY) {
-          const float e = group_sum<16>(exp2f(x - mn));
-          rs[rt][v] = rs[rt][v] * exp2f(rm[rt][v] - mn) + e;
-          rm[rt][v] = mn;
+        for (int ks = 0; ks < M::NKS; ++ks) acc[cw] = M::mma(a[ks], B.op[cw][ks], acc[cw]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = rt * 16 + 4 * q + v;
+      const int u = row % P.w;
+      float x[kCTW];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int cw = 0; cw < kCTW; ++cw) {
+        const int ct = wv + 4 * cw;
+        x[cw] = -INFINITY;
+        if (ct < CT) {
+          const int col = ct * 16 + cl;
+          x[cw] = acc[cw][v] * P.qk_scale;
+          if (last && col > b - P.w + u) x[cw] = -INFINITY;
+          mx = fmaxf(mx, x[cw]);
         }
+      }
+      const float Mx = group_max<16>(mx);
+      float s = 0.f;
+      if (Mx != -INFINITY) {
+#pragma unroll
+        for (int cw = 0; cw < kCTW; ++cw)
+          if (wv + 4 * cw < CT) s += exp2f(x[cw] - Mx);
+      }
+      s = group_sum<16>(s);
+      if (cl == 0) {
+        wstat[(wv * R + row) * 2] = Mx;
+        wstat[(wv * R + row) * 2 + 1] = s;
       }
     }
   }
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = rt * 16 + 4 * (lane >> 4) + v;
-        wstat[(wv * R + row) * 2] = rm[rt][v];
-        wstat[(wv * R + row) * 2 + 1] = rs[rt][v];
-      }
-  }
   __syncthreads();
-  const int64_t zh = (int64_t)z * P.h_kv + h;
   if (tid < R) {
-    float M = -INFINITY;
-    for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, wstat[(w2 * R + tid) * 2]);
+    float Mx = -INFINITY;
+    for (int w2 = 0; w2 < 4; ++w2) Mx = fmaxf(Mx, wstat[(w2 * R + tid) * 2]);
     float S = 0.f;
-    if (M != -INFINITY)
+    if (Mx != -INFINITY)
       for (int w2 = 0; w2 < 4; ++w2)
-        S += wstat[(w2 * R + tid) * 2 + 1] * exp2f(wstat[(w2 * R + tid) * 2] - M);
+        S += wstat[(w2 * R + tid) * 2 + 1] * exp2f(wstat[(w2 * R + tid) * 2] - Mx);
     float* st = P.stats + ((zh * P.max_blocks + pidx) * R + tid) * 2;
-    st[0] = M;
+    st[0] = Mx;
     st[1] = S;
   }
 
-  if (!(P.flags & ZP_SCORE_REDUNDANCY)) return;
+  if (!redun) return;
   float* rrow = P.rbuf + zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b;
-  if (P.flags & ZP_SCORE_REDUNDANCY_FLASH) {
-    // Whole-sequence (flash) redundancy: score_flash_redundancy_kernel
-    // accumulates into these rows next.
+  if (flash) {
+    // score_flash_kernel accumulates into these rows next.
     if (tid < b) rrow[tid] = 0.f;
     return;
   }
-  // Lightning redundancy: similarities inside this block only.
-  const float r = cosine_block_rows<T, D>(Ks, inv_norm, Ks, inv_norm, true, P.p, nullptr, b,
-                                          colidx, colval, rowsum, istar, ival);
-  if (tid < b) rrow[tid] = r / (float)n;
+  // Lightning redundancy: cosines inside this block only.
+  int brow[kCTW];
+  float bval[kCTW], invc[kCTW];
+#pragma unroll
+  for (int cw = 0; cw < kCTW; ++cw) {
+    brow[cw] = -1;
+    bval[cw] = 0.f;
+    const int ct = wv + 4 * cw;
+    invc[cw] = ct < CT ? inv_s[ct * 16 + cl] : 0.f;
+  }
+  for (int rt = 0; rt < CT; ++rt)
+    cosine_tile_rows<T, D>(Ks, inv_s, rt, B, invc, CT, wv, lane, true, P.p, 0, brow, bval);
+  best_over_groups(brow, bval, CT, wv);
+  if (q == 0) {
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw)
+      if (wv + 4 * cw < CT && brow[cw] >= 0) atomicAdd(&sub[brow[cw]], bval[cw]);
+  }
+  __syncthreads();
+  if (tid < b) rrow[tid] = (mainr - sub[tid]) / (float)n;
 }
 
 // ---------------------------------------------------------------------------
-// Flash redundancy (Zipage Alg. 3): one workgroup per column block m. Row
-// blocks i are visited from the last to the first with one zero-out tag per
-// column of m, so each column loses only its highest entry above p over the
-// whole sequence; the row sums of every (i, m) pair are added into the row
-// sums of block i (the accumulator R'[i][m] summed over m).
+// Flash redundancy (Zipage Alg. 3): one workgroup per column block m. Every
+// row block i is staged in turn and its cosines against the columns of m are
+// formed; each column keeps its highest row above p over the whole sequence
+// (the entry Alg. 3 zeroes when it scans the row blocks from the last one
+// with a zero-out tag per column). Row i's sum over the whole sequence is
+// khat_i . (sum of all unit keys) minus its diagonal; the zeroed entries are
+// subtracted from the rows they sit in.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void score_flash_redundancy_kernel(ScoreParams P) {
+__global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
   using L = LdsTile<T, D>;
   extern __shared__ __align__(16) char smem[];
   const int b = P.b;
-  char* Km = smem;                                           // [b][D]
-  char* Ki = Km + b * L::ROWB;                               // [b][D]
-  float* inv_m = reinterpret_cast<float*>(Ki + b * L::ROWB); // [b]
-  float* inv_i = inv_m + b;                                  // [b]
-  int* tag = reinterpret_cast<int*>(inv_i + b);              // [b]
-  int* colidx = tag + b;                                     // [4][b]
-  float* colval = reinterpret_cast<float*>(colidx + 4 * b);  // [4][b]
-  float* rowsum = colval + 4 * b;                            // [b]
-  int* istar = reinterpret_cast<int*>(rowsum + b);           // [b]
-  float* ival = reinterpret_cast<float*>(istar + b);         // [b]
+  char* Ks = smem;                                            // [b][D]
+  float* stot = reinterpret_cast<float*>(Ks + b * L::ROWB);   // [D]
 
   const int m = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
   int N, slot;
@@ -381,58 +471,74 @@ __global__ __launch_bounds__(256) void score_flash_redundancy_kernel(ScoreParams
   if (page_m < 0) return;
   const int r = z % P.nreq;
   const int layer = P.layer_begin + z / P.nreq;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q = lane >> 4, cl = lane & 15;
   const int n = N * b;
+  const int CT = b / 16;
   const int64_t zh = (int64_t)z * P.h_kv + h;
-  const T* kbase = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems;
   const int32_t* tab = P.tables + (int64_t)r * P.table_stride;
   for (int i = 0; i < N; ++i) {          // all block ids were checked by phase A
     const int pg = tab[i];
     if (pg < 0 || pg >= P.num_blocks_total) return;
   }
-  auto stage = [&](char* dst, float* inv, int page) {
-    stage_rows<T, D>(dst, kbase + ((int64_t)page * P.h_kv + h) * b * D, b, tid, 256);
-    __syncthreads();
-    if (tid < b) {
-      float ss = 0.f;
-      for (int c = 0; c < L::CH; ++c) {
-        const uint4 v = *reinterpret_cast<const uint4*>(dst + L::chunk_pos(tid, c) * 16);
-        float f[Vec16<T>::N];
-        Vec16<T>::unpack(v, f);
-#pragma unroll
-        for (int e = 0; e < Vec16<T>::N; ++e) ss = fmaf(f[e], f[e], ss);
-      }
-      inv[tid] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-    }
-  };
-  stage(Km, inv_m, page_m);
-  if (tid < b) tag[tid] = 0;
-  __syncthreads();
-  float* rb = P.rbuf + zh * ((int64_t)P.max_blocks * b);
-  for (int i = N - 1; i >= 0; --i) {
-    const bool same = i == m;
-    if (!same) {
-      stage(Ki, inv_i, tab[i]);
-      __syncthreads();
-    }
-    const float rs = cosine_block_rows<T, D>(same ? Km : Ki, same ? inv_m : inv_i, Km, inv_m, same,
-                                             P.p, tag, b, colidx, colval, rowsum, istar, ival);
-    if (tid < b) atomicAdd(rb + (int64_t)i * b + tid, rs / (float)n);
+  const T* kbase = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems;
+  const float* invz = P.inv + zh * ((int64_t)P.max_blocks * b);
+  const float* ksz = P.ksum + zh * P.max_blocks * D;
+  for (int e = tid; e < D; e += 256) {
+    float s = 0.f;
+    for (int i = 0; i < N; ++i) s += ksz[(int64_t)i * D + e];
+    stot[e] = s;
   }
+  ColOps<T, D> B;
+  B.from_global(kbase + ((int64_t)page_m * P.h_kv + h) * b * D, CT, wv, lane);
+  int brow[kCTW];
+  float bval[kCTW], invc[kCTW];
+#pragma unroll
+  for (int cw = 0; cw < kCTW; ++cw) {
+    brow[cw] = -1;
+    bval[cw] = 0.f;
+    const int ct = wv + 4 * cw;
+    invc[cw] = ct < CT ? invz[(int64_t)m * b + ct * 16 + cl] : 0.f;
+  }
+  float mainr = 0.f;
+  for (int i = 0; i < N; ++i) {          // ascending rows: the last hit is the highest
+    __syncthreads();                     // the previous block is no longer read
+    stage_rows<T, D>(Ks, kbase + ((int64_t)tab[i] * P.h_kv + h) * b * D, b, tid);
+    __syncthreads();
+    if (i == m && tid < b) {
+      float ss, dot;
+      row_norm_dot<T, D>(Ks, tid, stot, &ss, &dot);
+      const float iv = invz[(int64_t)m * b + tid];
+      mainr = iv * dot - iv * iv * ss;
+    }
+    const float* inv_r = invz + (int64_t)i * b;
+    for (int rt = 0; rt < CT; ++rt)
+      cosine_tile_rows<T, D>(Ks, inv_r, rt, B, invc, CT, wv, lane, i == m, P.p, i * b, brow, bval);
+  }
+  best_over_groups(brow, bval, CT, wv);
+  float* rb = P.rbuf + zh * ((int64_t)P.max_blocks * b);
+  const float inv_n = 1.0f / (float)n;
+  if (q == 0) {
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw)
+      if (wv + 4 * cw < CT && brow[cw] >= 0) atomicAdd(rb + brow[cw], -bval[cw] * inv_n);
+  }
+  if (tid < b) atomicAdd(rb + (int64_t)m * b + tid, mainr * inv_n);
 }
 
 // ---------------------------------------------------------------------------
 // Phase B: S0 of one block (App. C.2) and the global score (Alg. 2).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int R>
-__global__ __launch_bounds__(256) void score_page_s0_kernel(ScoreParams P) {
-  using L = LdsTile<T, D>;
+// W16: the window is 16 slots, so row tile rt holds query head rt and its 16
+// rows are the window positions: the group max is a max over row tiles in
+// registers and the window mean a sum over the lane's rows and lane groups.
+template <typename T, int D, int R, bool W16>
+__global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   using M = Mma<T, D>;
   constexpr int RT = R / 16;
   extern __shared__ __align__(16) char smem[];
-  char* Qs = smem;                                           // [R][D]
-  float* lse2 = reinterpret_cast<float*>(Qs + R * L::ROWB);  // [R]
-  float* ptile = lse2 + R;                                   // [4][R][16]
+  float* lse2 = reinterpret_cast<float*>(smem);   // [R]
+  float* ptile = lse2 + R;                        // [4][R][16] (general window only)
 
   const int pidx = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
   int N, slot;
@@ -441,67 +547,118 @@ __global__ __launch_bounds__(256) void score_page_s0_kernel(ScoreParams P) {
   const int r = z % P.nreq;
   const int layer = P.layer_begin + z / P.nreq;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q = lane >> 4, cl = lane & 15;
   const int b = P.b;
+  const int CT = b / 16;
   const bool last = pidx == N - 1;
   const int64_t zh = (int64_t)z * P.h_kv + h;
 
-  const T* qrows = reinterpret_cast<const T*>(P.qwin) + layer * P.qwin_layer_elems +
-                   ((int64_t)slot * P.h_kv + h) * R * D;
-  stage_rows<T, D>(Qs, qrows, R, tid, 256);
+  const T* kpage = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems +
+                   ((int64_t)page * P.h_kv + h) * b * D;
+  ColOps<T, D> B;
+  B.from_global(kpage, CT, wv, lane);
   if (tid < R) {
     const float* st = P.stats + (zh * P.max_blocks) * R * 2 + tid * 2;
     float Mx = -INFINITY;
-    for (int q = 0; q < N; ++q) Mx = fmaxf(Mx, st[(int64_t)q * R * 2]);
+    for (int i = 0; i < N; ++i) Mx = fmaxf(Mx, st[(int64_t)i * R * 2]);
     float S = 0.f;
-    for (int q = 0; q < N; ++q) S += st[(int64_t)q * R * 2 + 1] * exp2f(st[(int64_t)q * R * 2] - Mx);
+    for (int i = 0; i < N; ++i) S += st[(int64_t)i * R * 2 + 1] * exp2f(st[(int64_t)i * R * 2] - Mx);
     lse2[tid] = Mx + log2f(S);
   }
   __syncthreads();
 
-  const T* kpage = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems +
-                   ((int64_t)page * P.h_kv + h) * b * D;
-  const int G = R / P.w;
+  const T* qrows = reinterpret_cast<const T*>(P.qwin) + layer * P.qwin_layer_elems +
+                   ((int64_t)slot * P.h_kv + h) * R * D;
   const bool first = P.first[r] != 0;
-  float* ptw = ptile + wv * R * 16;
-  for (int ct = wv; ct < b / 16; ct += 4) {
-    const T* krow = kpage + (int64_t)(ct * 16 + (lane & 15)) * D;
-    typename M::op_t bop[M::NKS];
+  auto emit = [&](int col, float s0) {
+    float s1 = s0;
+    if (P.flags & ZP_SCORE_GLOBAL) {
+      // F is read only: blocks may be shared by several requests.
+      if (!first && !last)
+        s1 = fmaxf(P.alpha * P.gscore[layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col], s0);
+      P.f_new[zh * P.scores_stride + (int64_t)pidx * b + col] = s1;
+    }
+    P.s1buf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + col] = s1;
+  };
+
+  if constexpr (W16) {
+    float pm[kCTW][4];
 #pragma unroll
-    for (int ks = 0; ks < M::NKS; ++ks) bop[ks] = M::glb(krow, ks, lane);
+    for (int cw = 0; cw < kCTW; ++cw)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pm[cw][v] = 0.f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      typename M::op_t a[M::NKS];
+      const T* qr = qrows + (int64_t)(rt * 16 + cl) * D;
 #pragma unroll
-      for (int ks = 0; ks < M::NKS; ++ks)
-        acc = M::mma(M::lds(Qs, rt * 16 + (lane & 15), ks, lane), bop[ks], acc);
+      for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::glb(qr, ks, lane);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = rt * 16 + 4 * (lane >> 4) + v;
-        const int col = ct * 16 + (lane & 15);
-        const int u = row % P.w;
-        float pv = exp2f(acc[v] * P.qk_scale - lse2[row]);
-        if (last && col > b - P.w + u) pv = 0.f;
-        ptw[row * 16 + (lane & 15)] = pv;
+      for (int cw = 0; cw < kCTW; ++cw) {
+        const int ct = wv + 4 * cw;
+        if (ct < CT) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = rt * 16 + 4 * q + v;
+            const int u = 4 * q + v;
+            const int col = ct * 16 + cl;
+            float pv = exp2f(acc[v] * P.qk_scale - lse2[row]);
+            if (last && col > b - 16 + u) pv = 0.f;
+            pm[cw][v] = fmaxf(pm[cw][v], pv);
+          }
+        }
       }
     }
-    // Within a wavefront LDS writes and reads are ordered; no barrier needed.
-    if (lane < 16) {
-      const int col = ct * 16 + lane;
-      float s0 = 0.f;
-      for (int u = 0; u < P.w; ++u) {
-        float mx = 0.f;
-        for (int gi = 0; gi < G; ++gi) mx = fmaxf(mx, ptw[(gi * P.w + u) * 16 + lane]);
-        s0 += mx;
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      if (ct < CT) {
+        float s = (pm[cw][0] + pm[cw][1]) + (pm[cw][2] + pm[cw][3]);
+        s += shfl_xor_f(s, 16);
+        s += shfl_xor_f(s, 32);
+        if (q == 0) emit(ct * 16 + cl, s * (1.0f / 16.0f));
       }
-      s0 /= (float)P.w;
-      float s1 = s0;
-      if (P.flags & ZP_SCORE_GLOBAL) {
-        // F is read only: blocks may be shared by several requests.
-        if (!first && !last)
-          s1 = fmaxf(P.alpha * P.gscore[layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col], s0);
-        P.f_new[zh * P.scores_stride + (int64_t)pidx * b + col] = s1;
+    }
+  } else {
+    // Any window: the probabilities of one column tile go through LDS.
+    const int G = R / P.w;
+    float* ptw = ptile + wv * R * 16;
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      if (ct >= CT) continue;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        typename M::op_t a[M::NKS];
+        const T* qr = qrows + (int64_t)(rt * 16 + cl) * D;
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::glb(qr, ks, lane);
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = rt * 16 + 4 * q + v;
+          const int col = ct * 16 + cl;
+          const int u = row % P.w;
+          float pv = exp2f(acc[v] * P.qk_scale - lse2[row]);
+          if (last && col > b - P.w + u) pv = 0.f;
+          ptw[row * 16 + cl] = pv;
+        }
       }
-      P.s1buf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + col] = s1;
+      // Within a wavefront LDS writes and reads are ordered; no barrier needed.
+      if (lane < 16) {
+        float s0 = 0.f;
+        for (int u = 0; u < P.w; ++u) {
+          float mx = 0.f;
+          for (int gi = 0; gi < G; ++gi) mx = fmaxf(mx, ptw[(gi * P.w + u) * 16 + lane]);
+          s0 += mx;
+        }
+        emit(ct * 16 + lane, s0 / (float)P.w);
+      }
     }
   }
 }
@@ -572,29 +729,22 @@ template <typename T, int D, int R>
 static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
   using L = LdsTile<T, D>;
   const int b = P.b;
-  const size_t smemA = size_t(b) * L::ROWB + size_t(R) * L::ROWB +
-                       sizeof(float) * (b + 4 * R * 2 + b) + sizeof(int) * 4 * b +
-                       sizeof(float) * 4 * b + sizeof(int) * b + sizeof(float) * b;
-  const size_t smemB = size_t(R) * L::ROWB + sizeof(float) * (R + 4 * R * 16);
-  if (smemA > kMaxLds || smemB > kMaxLds)
+  const size_t smemA = size_t(b) * L::ROWB + sizeof(float) * (b + D + 4 * R * 2 + b);
+  const size_t smemF = size_t(b) * L::ROWB + sizeof(float) * D;
+  const bool w16 = P.w == 16;
+  const size_t smemB = sizeof(float) * (R + (w16 ? 0 : 4 * R * 16));
+  const bool flash = (P.flags & ZP_SCORE_REDUNDANCY) && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
+  if (smemA > kMaxLds || smemB > kMaxLds || (flash && smemF > kMaxLds))
     return fail(ZP_EINVAL, "zp_score_tokens: block_size %d with this dtype/head_dim needs %zu "
                 "bytes of LDS (max %zu)", b, smemA, kMaxLds);
-  const bool flash = (P.flags & ZP_SCORE_REDUNDANCY) && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
-  const size_t smemF = 2 * size_t(b) * L::ROWB + sizeof(float) * 2 * b + sizeof(int) * b +
-                       sizeof(int) * 4 * b + sizeof(float) * 4 * b + sizeof(float) * b +
-                       sizeof(int) * b + sizeof(float) * b;
-  if (flash && smemF > kMaxLds)
-    return fail(ZP_EINVAL, "zp_score_tokens: flash redundancy with block_size %d and this "
-                "dtype/head_dim needs %zu bytes of LDS (max %zu)", b, smemF, kMaxLds);
-  auto kA = score_page_stats_kernel<T, D, R>;
-  auto kB = score_page_s0_kernel<T, D, R>;
-  auto kF = score_flash_redundancy_kernel<T, D>;
-  if (flash && hipFuncSetAttribute(reinterpret_cast<const void*>(kF),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   int(smemF)) != hipSuccess)
-    return fail(ZP_EHIP, "zp_score_tokens: cannot reserve %zu bytes of LDS", smemF);
+  auto kA = score_block_kernel<T, D, R>;
+  auto kF = score_flash_kernel<T, D>;
+  auto kB = w16 ? score_s0_kernel<T, D, R, true> : score_s0_kernel<T, D, R, false>;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kA),
                           hipFuncAttributeMaxDynamicSharedMemorySize, int(smemA)) != hipSuccess ||
+      (flash && hipFuncSetAttribute(reinterpret_cast<const void*>(kF),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    int(smemF)) != hipSuccess) ||
       hipFuncSetAttribute(reinterpret_cast<const void*>(kB),
                           hipFuncAttributeMaxDynamicSharedMemorySize, int(smemB)) != hipSuccess)
     return fail(ZP_EHIP, "zp_score_tokens: cannot reserve %zu bytes of LDS", smemA);
@@ -623,17 +773,21 @@ static zp_status dispatch_rows(int R, const ScoreParams& P, int items, hipStream
 
 static size_t score_ws_layout(const zp_geom* g, int32_t layer_count, int32_t nreq,
                               int32_t max_blocks, size_t* stats_off, size_t* r_off,
-                              size_t* s1_off) {
+                              size_t* s1_off, size_t* inv_off, size_t* ksum_off) {
   const size_t items = size_t(layer_count) * nreq * g->num_kv_heads;
   const size_t R = size_t(group_size(g)) * g->window;
   const size_t per_tok = size_t(max_blocks) * g->block_size;
   const size_t st = kWsHeader;
   const size_t ro = round_up(st + items * max_blocks * R * 2 * sizeof(float), 256);
   const size_t so = round_up(ro + items * per_tok * sizeof(float), 256);
-  const size_t total = round_up(so + items * per_tok * sizeof(float), 256);
+  const size_t io = round_up(so + items * per_tok * sizeof(float), 256);
+  const size_t ko = round_up(io + items * per_tok * sizeof(float), 256);
+  const size_t total = round_up(ko + items * max_blocks * g->head_dim * sizeof(float), 256);
   if (stats_off) *stats_off = st;
   if (r_off) *r_off = ro;
   if (s1_off) *s1_off = so;
+  if (inv_off) *inv_off = io;
+  if (ksum_off) *ksum_off = ko;
   return total;
 }
 
@@ -646,7 +800,8 @@ extern "C" size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_cou
   if (validate_geom(geom, "zp_score_workspace_size") != ZP_OK || layer_count < 0 || nreq < 0 ||
       max_blocks < 0)
     return 0;
-  return score_ws_layout(geom, layer_count, nreq, max_blocks, nullptr, nullptr, nullptr);
+  return score_ws_layout(geom, layer_count, nreq, max_blocks, nullptr, nullptr, nullptr,
+                         nullptr, nullptr);
 }
 
 extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
@@ -685,8 +840,8 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   if ((sp.flags & ZP_SCORE_REDUNDANCY) && !(sp.sim_threshold >= 0.f))
     return fail(ZP_EINVAL, "zp_score_tokens: sim_threshold must be >= 0");
   if (geom->max_slots <= 0) return fail(ZP_EINVAL, "zp_score_tokens: no query slots");
-  size_t so, ro, s1o;
-  const size_t need = score_ws_layout(geom, layer_count, nreq, max_blocks, &so, &ro, &s1o);
+  size_t so, ro, s1o, io, ko;
+  const size_t need = score_ws_layout(geom, layer_count, nreq, max_blocks, &so, &ro, &s1o, &io, &ko);
   if (workspace_bytes < need)
     return fail(ZP_EINVAL, "zp_score_tokens: workspace %zu bytes, need %zu", workspace_bytes, need);
   const int64_t items = int64_t(layer_count) * nreq;
@@ -702,6 +857,8 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   P.stats = reinterpret_cast<float*>(ws + so);
   P.rbuf = reinterpret_cast<float*>(ws + ro);
   P.s1buf = reinterpret_cast<float*>(ws + s1o);
+  P.inv = reinterpret_cast<float*>(ws + io);
+  P.ksum = reinterpret_cast<float*>(ws + ko);
   const int64_t d = geom->head_dim;
   P.kv_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size * d;
   P.qwin_layer_elems = int64_t(geom->max_slots) * geom->num_q_heads * geom->window * d;
