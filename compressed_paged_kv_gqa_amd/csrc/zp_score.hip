@@ -131,6 +131,7 @@ struct ScoreParams {
   float* rbuf;   // [items][h_kv][max_blocks * b]     redundancy row sums / n
   float* s1buf;  // [items][h_kv][max_blocks * b]     S1
   float* inv;    // [items][h_kv][max_blocks * b]     inverse key norms
+  float* nrm;    // [items][h_kv][max_blocks * b]     key norms
   float* ksum;   // [items][h_kv][max_blocks][D]      sum of the block's unit keys
   uint32_t* err;
   int64_t scores_stride;
@@ -169,110 +170,157 @@ __device__ __forceinline__ int resolve_page(const ScoreParams& P, int pidx, int 
   return page;
 }
 
-// Loads the B operands (keys as columns of the product) of this wavefront's
-// column tiles, ct = wv + 4 * cw, from an LDS tile or from global memory.
+// The wavefront index as a scalar (wave-uniform) value, so that conditions on
+// it compile to scalar branches rather than lane masks.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// B operands (keys as columns of the product) of this wavefront's column
+// tiles ct = wv + 4 * cw, from an LDS tile or from global memory. Tiles past
+// the block (b < 256) are clamped to the last one: they are computed but
+// their results are discarded, which keeps the tile loops free of branches so
+// that the MFMA chains of the four tiles interleave.
 template <typename T, int D>
 struct ColOps {
   using M = Mma<T, D>;
   typename M::op_t op[kCTW][M::NKS];
+  __device__ static int tile(int wv, int cw, int CT) { return min(wv + 4 * cw, CT - 1); }
   __device__ void from_lds(const char* Ks, int CT, int wv, int lane) {
 #pragma unroll
     for (int cw = 0; cw < kCTW; ++cw) {
-      const int ct = wv + 4 * cw;
-      if (ct < CT) {
+      const int ct = tile(wv, cw, CT);
 #pragma unroll
-        for (int ks = 0; ks < M::NKS; ++ks) op[cw][ks] = M::lds(Ks, ct * 16 + (lane & 15), ks, lane);
-      }
+      for (int ks = 0; ks < M::NKS; ++ks) op[cw][ks] = M::lds(Ks, ct * 16 + (lane & 15), ks, lane);
     }
   }
   __device__ void from_global(const T* kblk, int CT, int wv, int lane) {
 #pragma unroll
     for (int cw = 0; cw < kCTW; ++cw) {
-      const int ct = wv + 4 * cw;
-      if (ct < CT) {
+      const int ct = tile(wv, cw, CT);
 #pragma unroll
-        for (int ks = 0; ks < M::NKS; ++ks)
-          op[cw][ks] = M::glb(kblk + (int64_t)(ct * 16 + (lane & 15)) * D, ks, lane);
-      }
+      for (int ks = 0; ks < M::NKS; ++ks)
+        op[cw][ks] = M::glb(kblk + (int64_t)(ct * 16 + (lane & 15)) * D, ks, lane);
     }
   }
 };
 
+// acc[cw] = A (one 16-row tile, k-slices a[]) times the column tiles of B,
+// with the k-steps of the four independent products interleaved.
+template <typename T, int D>
+__device__ __forceinline__ void mma_tiles(const typename Mma<T, D>::op_t* a, const ColOps<T, D>& B,
+                                          floatx4* acc) {
+  using M = Mma<T, D>;
+#pragma unroll
+  for (int cw = 0; cw < kCTW; ++cw) acc[cw] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < M::NKS; ++ks)
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw) acc[cw] = M::mma(a[ks], B.op[cw][ks], acc[cw]);
+}
+
 // Cosine tiles of row tile rt (keys of the LDS block Ks) against this
 // wavefront's column tiles: for each column, remembers the highest row whose
-// cosine exceeds p (global row index row_base + row) and that cosine. Rows
-// grow with rt and with the register index, so the last hit is the highest.
-// The diagonal of the block against itself is skipped when `self`.
+// cosine exceeds p (global row index row_base + row). cos(k_i, k_j) > p is
+// tested as k_i . k_j > p |k_i| |k_j| (zero-norm keys never pass, p >= 0);
+// pnc[cw] = p |k_j| of the lane's column (+inf for tiles past the block).
+// Rows grow with rt and with the register index, so the last hit is the
+// highest. The diagonal of the block against itself is excluded when `self`.
+// Branch-free, so that consecutive row tiles overlap in the schedule.
 template <typename T, int D>
-__device__ __forceinline__ void cosine_tile_rows(const char* Ks, const float* inv_r, int rt,
-                                                 const ColOps<T, D>& B, const float* invc, int CT,
-                                                 int wv, int lane, bool self, float p,
-                                                 int row_base, int* brow, float* bval) {
+__device__ __forceinline__ void cosine_tile_rows(const char* Ks, const float* nrm_r, int rt,
+                                                 const ColOps<T, D>& B, const float* pnc,
+                                                 int wv, int lane, bool self, int row_base,
+                                                 int* brow) {
   using M = Mma<T, D>;
   const int q = lane >> 4, cl = lane & 15;
   typename M::op_t a[M::NKS];
 #pragma unroll
   for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Ks, rt * 16 + cl, ks, lane);
-  const float4 ir = *reinterpret_cast<const float4*>(inv_r + rt * 16 + 4 * q);
-  const float irv[4] = {ir.x, ir.y, ir.z, ir.w};
+  const float4 nr = *reinterpret_cast<const float4*>(nrm_r + rt * 16 + 4 * q);
+  const float nrv[4] = {nr.x, nr.y, nr.z, nr.w};
+  floatx4 acc[kCTW];
+  mma_tiles<T, D>(a, B, acc);
+  const int row0 = row_base + rt * 16 + 4 * q;
 #pragma unroll
   for (int cw = 0; cw < kCTW; ++cw) {
-    const int ct = wv + 4 * cw;
-    if (ct < CT) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const bool dg = self && wv + 4 * cw == rt;  // the block's diagonal tile
 #pragma unroll
-      for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
-      const bool diag = self && ct == rt;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float c = acc[v] * irv[v] * invc[cw];
-        if (diag && 4 * q + v == cl) c = 0.f;
-        if (c > p) {
-          brow[cw] = row_base + rt * 16 + 4 * q + v;
-          bval[cw] = c;
-        }
-      }
+    for (int v = 0; v < 4; ++v) {
+      const float thr = dg && 4 * q + v == cl ? INFINITY : nrv[v] * pnc[cw];
+      brow[cw] = acc[cw][v] > thr ? row0 + v : brow[cw];
     }
   }
 }
 
-// Highest (row, cosine) of each column over the four 4-row lane groups;
-// valid in lanes 0..15 (column ct * 16 + lane).
-__device__ __forceinline__ void best_over_groups(int* brow, float* bval, int CT, int wv) {
+// Highest row of each column over the four 4-row lane groups; valid in all
+// lanes (column ct * 16 + lane % 16).
+__device__ __forceinline__ void best_over_groups(int* brow) {
 #pragma unroll
   for (int cw = 0; cw < kCTW; ++cw) {
-    const int ct = wv + 4 * cw;
-    if (ct < CT) {
-#pragma unroll
-      for (int m = 16; m < 64; m <<= 1) {
-        const int o = shfl_xor_i(brow[cw], m);
-        const float ov = shfl_xor_f(bval[cw], m);
-        if (o > brow[cw]) { brow[cw] = o; bval[cw] = ov; }
-      }
-    }
+    brow[cw] = max(brow[cw], shfl_xor_i(brow[cw], 16));
+    brow[cw] = max(brow[cw], shfl_xor_i(brow[cw], 32));
   }
 }
 
-// Sum of squares of row r of an LDS tile, and its dot product with an fp32
-// vector v[D] (when v != nullptr).
+// Dot product of two rows of D elements (fp32 accumulation).
 template <typename T, int D>
-__device__ __forceinline__ void row_norm_dot(const char* Ks, int r, const float* v, float* ss,
-                                             float* dot) {
+__device__ __forceinline__ float row_dot(const T* x, const T* y) {
+  float d = 0.f;
+  if constexpr (sizeof(T) == 2) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll 4
+    for (int c = 0; c < D / 8; ++c) {
+      const uint4 u = ld16(x + c * 8), v = ld16(y + c * 8);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), __builtin_bit_cast(bf2, v.x), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), __builtin_bit_cast(bf2, v.y), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), __builtin_bit_cast(bf2, v.z), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), __builtin_bit_cast(bf2, v.w), d, false);
+    }
+  } else {
+#pragma unroll 4
+    for (int e = 0; e < D; ++e) d = fmaf(x[e], y[e], d);
+  }
+  return d;
+}
+
+// Same for two rows of an LDS tile.
+template <typename T, int D>
+__device__ __forceinline__ float lds_row_dot(const char* Ks, int r1, int r2) {
   using L = LdsTile<T, D>;
-  float s = 0.f, d = 0.f;
+  float d = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < L::CH; ++c) {
+    const uint4 u = *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(r1, c) * 16);
+    const uint4 v = *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(r2, c) * 16);
+    if constexpr (sizeof(T) == 2) {
+      typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), __builtin_bit_cast(bf2, v.x), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), __builtin_bit_cast(bf2, v.y), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), __builtin_bit_cast(bf2, v.z), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), __builtin_bit_cast(bf2, v.w), d, false);
+    } else {
+      d = fmaf(__uint_as_float(u.x), __uint_as_float(v.x), d);
+      d = fmaf(__uint_as_float(u.y), __uint_as_float(v.y), d);
+      d = fmaf(__uint_as_float(u.z), __uint_as_float(v.z), d);
+      d = fmaf(__uint_as_float(u.w), __uint_as_float(v.w), d);
+    }
+  }
+  return d;
+}
+
+// Dot product of row r of an LDS tile with an fp32 vector v[D].
+template <typename T, int D>
+__device__ __forceinline__ float lds_row_dot_f32(const char* Ks, int r, const float* v) {
+  using L = LdsTile<T, D>;
+  float d = 0.f;
 #pragma unroll 4
   for (int c = 0; c < L::CH; ++c) {
     const uint4 x = *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(r, c) * 16);
     float f[L::EPC];
     Vec16<T>::unpack(x, f);
 #pragma unroll
-    for (int e = 0; e < L::EPC; ++e) {
-      s = fmaf(f[e], f[e], s);
-      if (v) d = fmaf(f[e], v[c * L::EPC + e], d);
-    }
+    for (int e = 0; e < L::EPC; ++e) d = fmaf(f[e], v[c * L::EPC + e], d);
   }
-  *ss = s;
-  *dot = d;
+  return d;
 }
 
 // ---------------------------------------------------------------------------
@@ -288,16 +336,18 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   const int b = P.b;
   char* Ks = smem;                                            // [b][D]
   float* inv_s = reinterpret_cast<float*>(Ks + b * L::ROWB);  // [b]
-  float* ksum_s = inv_s + b;                                  // [D]
+  float* nrm_s = inv_s + b;                                   // [b]
+  float* ksum_s = nrm_s + b;                                  // [D]
   float* wstat = ksum_s + D;                                  // [4][R][2]
   float* sub = wstat + 4 * R * 2;                             // [b]
+  int* istar = reinterpret_cast<int*>(sub + b);               // [b]
 
   const int pidx = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
   int N, slot;
   const int page = resolve_page(P, pidx, z, &N, &slot);
   if (page < 0) return;
   const int layer = P.layer_begin + z / P.nreq;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int q = lane >> 4, cl = lane & 15;
   const bool last = pidx == N - 1;
   const int n = N * b;
@@ -312,17 +362,30 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
                    ((int64_t)slot * P.h_kv + h) * R * D;
   stage_rows<T, D>(Ks, kpage, b, tid);
   if (tid < b) sub[tid] = 0.f;
+  // Window-query operands (A) of every row tile, in flight while the key
+  // norms are formed (fp32 operands take 4x the registers: those are loaded
+  // per row tile).
+  constexpr bool PREQ = sizeof(T) == 2;
+  typename M::op_t qa[PREQ ? RT : 1][M::NKS];
+  if constexpr (PREQ) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < M::NKS; ++ks)
+        qa[rt][ks] = M::glb(qrows + (int64_t)(rt * 16 + cl) * D, ks, lane);
+  }
   __syncthreads();
 
   // Key norms, and the sum of the block's unit keys (thread = chunk c of the
   // row, rows rg, rg + RG, ...; the RG partial sums of a chunk sit in
   // consecutive lanes).
-  float ss = 0.f, mainr = 0.f;
+  float mainr = 0.f;
   if (redun) {
+    float ss = 0.f;
     if (tid < b) {
-      float unused;
-      row_norm_dot<T, D>(Ks, tid, nullptr, &ss, &unused);
+      ss = lds_row_dot<T, D>(Ks, tid, tid);
       inv_s[tid] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+      nrm_s[tid] = sqrtf(ss);
     }
     __syncthreads();
     constexpr int RG = 256 / L::CH;
@@ -349,59 +412,57 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
     for (int e = tid; e < D; e += 256) ks_out[e] = ksum_s[e];
     if (tid < b) {
       P.inv[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + tid] = inv_s[tid];
+      P.nrm[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + tid] = nrm_s[tid];
       // row sum of the block's cosine matrix without its diagonal
-      float ss2, dot;
-      row_norm_dot<T, D>(Ks, tid, ksum_s, &ss2, &dot);
-      const float iv = inv_s[tid];
-      mainr = iv * dot - iv * iv * ss2;
+      if (!flash) {
+        const float iv = inv_s[tid];
+        mainr = iv * lds_row_dot_f32<T, D>(Ks, tid, ksum_s) - iv * iv * ss;
+      }
     }
   }
 
   // Window logits: B operands = this wavefront's column tiles of the block.
+  // Row statistics in the exp2 domain of the scaled logits: per row the max
+  // (M * scale) and the sum of exp2((x - M) * scale) over the block.
   ColOps<T, D> B;
   B.from_lds(Ks, CT, wv, lane);
+  const float sc2 = P.qk_scale;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    typename M::op_t a[M::NKS];
-    const T* qr = qrows + (int64_t)(rt * 16 + cl) * D;
+    if constexpr (!PREQ) {
 #pragma unroll
-    for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::glb(qr, ks, lane);
+      for (int ks = 0; ks < M::NKS; ++ks)
+        qa[0][ks] = M::glb(qrows + (int64_t)(rt * 16 + cl) * D, ks, lane);
+    }
     floatx4 acc[kCTW];
+    mma_tiles<T, D>(qa[PREQ ? rt : 0], B, acc);
 #pragma unroll
     for (int cw = 0; cw < kCTW; ++cw) {
-      acc[cw] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (wv + 4 * cw < CT) {
+      const int ct = wv + 4 * cw;
+      if (ct >= CT) {  // scalar
+        acc[cw] = floatx4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      } else if (last) {  // scalar: causal mask of the window rows in the last block
 #pragma unroll
-        for (int ks = 0; ks < M::NKS; ++ks) acc[cw] = M::mma(a[ks], B.op[cw][ks], acc[cw]);
+        for (int v = 0; v < 4; ++v) {
+          const int u = (rt * 16 + 4 * q + v) % P.w;
+          if (ct * 16 + cl > b - P.w + u) acc[cw][v] = -INFINITY;
+        }
       }
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = rt * 16 + 4 * q + v;
-      const int u = row % P.w;
-      float x[kCTW];
-      float mx = -INFINITY;
+      float mx = acc[0][v];
 #pragma unroll
-      for (int cw = 0; cw < kCTW; ++cw) {
-        const int ct = wv + 4 * cw;
-        x[cw] = -INFINITY;
-        if (ct < CT) {
-          const int col = ct * 16 + cl;
-          x[cw] = acc[cw][v] * P.qk_scale;
-          if (last && col > b - P.w + u) x[cw] = -INFINITY;
-          mx = fmaxf(mx, x[cw]);
-        }
-      }
+      for (int cw = 1; cw < kCTW; ++cw) mx = fmaxf(mx, acc[cw][v]);
       const float Mx = group_max<16>(mx);
+      const float ms = Mx == -INFINITY ? 0.f : Mx * sc2;
       float s = 0.f;
-      if (Mx != -INFINITY) {
 #pragma unroll
-        for (int cw = 0; cw < kCTW; ++cw)
-          if (wv + 4 * cw < CT) s += exp2f(x[cw] - Mx);
-      }
+      for (int cw = 0; cw < kCTW; ++cw) s += __builtin_amdgcn_exp2f(fmaf(acc[cw][v], sc2, -ms));
       s = group_sum<16>(s);
       if (cl == 0) {
-        wstat[(wv * R + row) * 2] = Mx;
+        wstat[(wv * R + row) * 2] = Mx == -INFINITY ? -INFINITY : ms;
         wstat[(wv * R + row) * 2 + 1] = s;
       }
     }
@@ -428,21 +489,28 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   }
   // Lightning redundancy: cosines inside this block only.
   int brow[kCTW];
-  float bval[kCTW], invc[kCTW];
+  float pnc[kCTW];
 #pragma unroll
   for (int cw = 0; cw < kCTW; ++cw) {
     brow[cw] = -1;
-    bval[cw] = 0.f;
-    const int ct = wv + 4 * cw;
-    invc[cw] = ct < CT ? inv_s[ct * 16 + cl] : 0.f;
+    pnc[cw] = wv + 4 * cw < CT ? P.p * nrm_s[(wv + 4 * cw) * 16 + cl] : INFINITY;
   }
+#pragma unroll 2
   for (int rt = 0; rt < CT; ++rt)
-    cosine_tile_rows<T, D>(Ks, inv_s, rt, B, invc, CT, wv, lane, true, P.p, 0, brow, bval);
-  best_over_groups(brow, bval, CT, wv);
+    cosine_tile_rows<T, D>(Ks, nrm_s, rt, B, pnc, wv, lane, true, 0, brow);
+  best_over_groups(brow);
   if (q == 0) {
 #pragma unroll
-    for (int cw = 0; cw < kCTW; ++cw)
-      if (wv + 4 * cw < CT && brow[cw] >= 0) atomicAdd(&sub[brow[cw]], bval[cw]);
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      if (ct < CT) istar[ct * 16 + cl] = brow[cw];
+    }
+  }
+  __syncthreads();
+  // The zeroed entry of column j is cos(k_i*, k_j), subtracted from row i*.
+  if (tid < b) {
+    const int is = istar[tid];
+    if (is >= 0) atomicAdd(&sub[is], lds_row_dot<T, D>(Ks, is, tid) * inv_s[is] * inv_s[tid]);
   }
   __syncthreads();
   if (tid < b) rrow[tid] = (mainr - sub[tid]) / (float)n;
@@ -471,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
   if (page_m < 0) return;
   const int r = z % P.nreq;
   const int layer = P.layer_begin + z / P.nreq;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int q = lane >> 4, cl = lane & 15;
   const int n = N * b;
   const int CT = b / 16;
@@ -483,22 +551,22 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
   }
   const T* kbase = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems;
   const float* invz = P.inv + zh * ((int64_t)P.max_blocks * b);
+  const float* nrmz = P.nrm + zh * ((int64_t)P.max_blocks * b);
   const float* ksz = P.ksum + zh * P.max_blocks * D;
   for (int e = tid; e < D; e += 256) {
     float s = 0.f;
     for (int i = 0; i < N; ++i) s += ksz[(int64_t)i * D + e];
     stot[e] = s;
   }
+  const T* kpm = kbase + ((int64_t)page_m * P.h_kv + h) * b * D;
   ColOps<T, D> B;
-  B.from_global(kbase + ((int64_t)page_m * P.h_kv + h) * b * D, CT, wv, lane);
+  B.from_global(kpm, CT, wv, lane);
   int brow[kCTW];
-  float bval[kCTW], invc[kCTW];
+  float pnc[kCTW];
 #pragma unroll
   for (int cw = 0; cw < kCTW; ++cw) {
     brow[cw] = -1;
-    bval[cw] = 0.f;
-    const int ct = wv + 4 * cw;
-    invc[cw] = ct < CT ? invz[(int64_t)m * b + ct * 16 + cl] : 0.f;
+    pnc[cw] = wv + 4 * cw < CT ? P.p * nrmz[(int64_t)m * b + (wv + 4 * cw) * 16 + cl] : INFINITY;
   }
   float mainr = 0.f;
   for (int i = 0; i < N; ++i) {          // ascending rows: the last hit is the highest
@@ -506,22 +574,29 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
     stage_rows<T, D>(Ks, kbase + ((int64_t)tab[i] * P.h_kv + h) * b * D, b, tid);
     __syncthreads();
     if (i == m && tid < b) {
-      float ss, dot;
-      row_norm_dot<T, D>(Ks, tid, stot, &ss, &dot);
       const float iv = invz[(int64_t)m * b + tid];
-      mainr = iv * dot - iv * iv * ss;
+      mainr = iv * lds_row_dot_f32<T, D>(Ks, tid, stot) - iv * iv * lds_row_dot<T, D>(Ks, tid, tid);
     }
-    const float* inv_r = invz + (int64_t)i * b;
+    const float* nrm_r = nrmz + (int64_t)i * b;
+#pragma unroll 2
     for (int rt = 0; rt < CT; ++rt)
-      cosine_tile_rows<T, D>(Ks, inv_r, rt, B, invc, CT, wv, lane, i == m, P.p, i * b, brow, bval);
+      cosine_tile_rows<T, D>(Ks, nrm_r, rt, B, pnc, wv, lane, i == m, i * b, brow);
   }
-  best_over_groups(brow, bval, CT, wv);
+  best_over_groups(brow);
   float* rb = P.rbuf + zh * ((int64_t)P.max_blocks * b);
   const float inv_n = 1.0f / (float)n;
   if (q == 0) {
 #pragma unroll
-    for (int cw = 0; cw < kCTW; ++cw)
-      if (wv + 4 * cw < CT && brow[cw] >= 0) atomicAdd(rb + brow[cw], -bval[cw] * inv_n);
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      const int is = brow[cw];
+      if (ct < CT && is >= 0) {
+        const int j = ct * 16 + cl;
+        const T* ki = kbase + ((int64_t)tab[is / b] * P.h_kv + h) * b * D + (int64_t)(is % b) * D;
+        const float c = row_dot<T, D>(ki, kpm + (int64_t)j * D) * invz[is] * invz[(int64_t)m * b + j];
+        atomicAdd(rb + is, -c * inv_n);
+      }
+    }
   }
   if (tid < b) atomicAdd(rb + (int64_t)m * b + tid, mainr * inv_n);
 }
@@ -534,10 +609,12 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
 // registers and the window mean a sum over the lane's rows and lane groups.
 template <typename T, int D, int R, bool W16>
 __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
+  using L = LdsTile<T, D>;
   using M = Mma<T, D>;
   constexpr int RT = R / 16;
   extern __shared__ __align__(16) char smem[];
-  float* lse2 = reinterpret_cast<float*>(smem);   // [R]
+  char* Qs = smem;                                           // [R][D]
+  float* lse2 = reinterpret_cast<float*>(Qs + R * L::ROWB);  // [R]
   float* ptile = lse2 + R;                        // [4][R][16] (general window only)
 
   const int pidx = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
@@ -546,7 +623,7 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   if (page < 0) return;
   const int r = z % P.nreq;
   const int layer = P.layer_begin + z / P.nreq;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int q = lane >> 4, cl = lane & 15;
   const int b = P.b;
   const int CT = b / 16;
@@ -555,8 +632,11 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
 
   const T* kpage = reinterpret_cast<const T*>(P.kc) + layer * P.kv_layer_elems +
                    ((int64_t)page * P.h_kv + h) * b * D;
+  const T* qrows = reinterpret_cast<const T*>(P.qwin) + layer * P.qwin_layer_elems +
+                   ((int64_t)slot * P.h_kv + h) * R * D;
   ColOps<T, D> B;
   B.from_global(kpage, CT, wv, lane);
+  stage_rows<T, D>(Qs, qrows, R, tid);
   if (tid < R) {
     const float* st = P.stats + (zh * P.max_blocks) * R * 2 + tid * 2;
     float Mx = -INFINITY;
@@ -567,8 +647,6 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   }
   __syncthreads();
 
-  const T* qrows = reinterpret_cast<const T*>(P.qwin) + layer * P.qwin_layer_elems +
-                   ((int64_t)slot * P.h_kv + h) * R * D;
   const bool first = P.first[r] != 0;
   auto emit = [&](int col, float s0) {
     float s1 = s0;
@@ -580,6 +658,7 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
     }
     P.s1buf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + col] = s1;
   };
+  const float sc2 = P.qk_scale;
 
   if constexpr (W16) {
     float pm[kCTW][4];
@@ -590,37 +669,31 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       typename M::op_t a[M::NKS];
-      const T* qr = qrows + (int64_t)(rt * 16 + cl) * D;
 #pragma unroll
-      for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::glb(qr, ks, lane);
+      for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
+      floatx4 acc[kCTW];
+      mma_tiles<T, D>(a, B, acc);
+      const float4 l4 = *reinterpret_cast<const float4*>(lse2 + rt * 16 + 4 * q);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-      for (int cw = 0; cw < kCTW; ++cw) {
-        const int ct = wv + 4 * cw;
-        if (ct < CT) {
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int cw = 0; cw < kCTW; ++cw)
 #pragma unroll
-          for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = rt * 16 + 4 * q + v;
-            const int u = 4 * q + v;
-            const int col = ct * 16 + cl;
-            float pv = exp2f(acc[v] * P.qk_scale - lse2[row]);
-            if (last && col > b - 16 + u) pv = 0.f;
-            pm[cw][v] = fmaxf(pm[cw][v], pv);
-          }
-        }
-      }
+        for (int v = 0; v < 4; ++v)
+          pm[cw][v] = fmaxf(pm[cw][v], __builtin_amdgcn_exp2f(fmaf(acc[cw][v], sc2, -lv[v])));
     }
 #pragma unroll
     for (int cw = 0; cw < kCTW; ++cw) {
       const int ct = wv + 4 * cw;
-      if (ct < CT) {
-        float s = (pm[cw][0] + pm[cw][1]) + (pm[cw][2] + pm[cw][3]);
-        s += shfl_xor_f(s, 16);
-        s += shfl_xor_f(s, 32);
-        if (q == 0) emit(ct * 16 + cl, s * (1.0f / 16.0f));
+      if (ct >= CT) continue;  // scalar
+      if (last) {              // scalar: causal mask, window slot u = 4q + v
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (ct * 16 + cl > b - 16 + 4 * q + v) pm[cw][v] = 0.f;
       }
+      float s = (pm[cw][0] + pm[cw][1]) + (pm[cw][2] + pm[cw][3]);
+      s += shfl_xor_f(s, 16);
+      s += shfl_xor_f(s, 32);
+      if (q == 0) emit(ct * 16 + cl, s * (1.0f / 16.0f));
     }
   } else {
     // Any window: the probabilities of one column tile go through LDS.
@@ -633,9 +706,8 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         typename M::op_t a[M::NKS];
-        const T* qr = qrows + (int64_t)(rt * 16 + cl) * D;
 #pragma unroll
-        for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::glb(qr, ks, lane);
+        for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
@@ -644,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
           const int row = rt * 16 + 4 * q + v;
           const int col = ct * 16 + cl;
           const int u = row % P.w;
-          float pv = exp2f(acc[v] * P.qk_scale - lse2[row]);
+          float pv = exp2f(acc[v] * sc2 - lse2[row]);
           if (last && col > b - P.w + u) pv = 0.f;
           ptw[row * 16 + cl] = pv;
         }
@@ -729,10 +801,10 @@ template <typename T, int D, int R>
 static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
   using L = LdsTile<T, D>;
   const int b = P.b;
-  const size_t smemA = size_t(b) * L::ROWB + sizeof(float) * (b + D + 4 * R * 2 + b);
+  const size_t smemA = size_t(b) * L::ROWB + sizeof(float) * (2 * b + D + 4 * R * 2 + 2 * b);
   const size_t smemF = size_t(b) * L::ROWB + sizeof(float) * D;
   const bool w16 = P.w == 16;
-  const size_t smemB = sizeof(float) * (R + (w16 ? 0 : 4 * R * 16));
+  const size_t smemB = size_t(R) * L::ROWB + sizeof(float) * (R + (w16 ? 0 : 4 * R * 16));
   const bool flash = (P.flags & ZP_SCORE_REDUNDANCY) && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
   if (smemA > kMaxLds || smemB > kMaxLds || (flash && smemF > kMaxLds))
     return fail(ZP_EINVAL, "zp_score_tokens: block_size %d with this dtype/head_dim needs %zu "
@@ -773,7 +845,8 @@ static zp_status dispatch_rows(int R, const ScoreParams& P, int items, hipStream
 
 static size_t score_ws_layout(const zp_geom* g, int32_t layer_count, int32_t nreq,
                               int32_t max_blocks, size_t* stats_off, size_t* r_off,
-                              size_t* s1_off, size_t* inv_off, size_t* ksum_off) {
+                              size_t* s1_off, size_t* inv_off, size_t* nrm_off,
+                              size_t* ksum_off) {
   const size_t items = size_t(layer_count) * nreq * g->num_kv_heads;
   const size_t R = size_t(group_size(g)) * g->window;
   const size_t per_tok = size_t(max_blocks) * g->block_size;
@@ -781,12 +854,14 @@ static size_t score_ws_layout(const zp_geom* g, int32_t layer_count, int32_t nre
   const size_t ro = round_up(st + items * max_blocks * R * 2 * sizeof(float), 256);
   const size_t so = round_up(ro + items * per_tok * sizeof(float), 256);
   const size_t io = round_up(so + items * per_tok * sizeof(float), 256);
-  const size_t ko = round_up(io + items * per_tok * sizeof(float), 256);
+  const size_t no = round_up(io + items * per_tok * sizeof(float), 256);
+  const size_t ko = round_up(no + items * per_tok * sizeof(float), 256);
   const size_t total = round_up(ko + items * max_blocks * g->head_dim * sizeof(float), 256);
   if (stats_off) *stats_off = st;
   if (r_off) *r_off = ro;
   if (s1_off) *s1_off = so;
   if (inv_off) *inv_off = io;
+  if (nrm_off) *nrm_off = no;
   if (ksum_off) *ksum_off = ko;
   return total;
 }
@@ -801,7 +876,7 @@ extern "C" size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_cou
       max_blocks < 0)
     return 0;
   return score_ws_layout(geom, layer_count, nreq, max_blocks, nullptr, nullptr, nullptr,
-                         nullptr, nullptr);
+                         nullptr, nullptr, nullptr);
 }
 
 extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
@@ -840,8 +915,9 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   if ((sp.flags & ZP_SCORE_REDUNDANCY) && !(sp.sim_threshold >= 0.f))
     return fail(ZP_EINVAL, "zp_score_tokens: sim_threshold must be >= 0");
   if (geom->max_slots <= 0) return fail(ZP_EINVAL, "zp_score_tokens: no query slots");
-  size_t so, ro, s1o, io, ko;
-  const size_t need = score_ws_layout(geom, layer_count, nreq, max_blocks, &so, &ro, &s1o, &io, &ko);
+  size_t so, ro, s1o, io, no, ko;
+  const size_t need =
+      score_ws_layout(geom, layer_count, nreq, max_blocks, &so, &ro, &s1o, &io, &no, &ko);
   if (workspace_bytes < need)
     return fail(ZP_EINVAL, "zp_score_tokens: workspace %zu bytes, need %zu", workspace_bytes, need);
   const int64_t items = int64_t(layer_count) * nreq;
@@ -858,6 +934,7 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   P.rbuf = reinterpret_cast<float*>(ws + ro);
   P.s1buf = reinterpret_cast<float*>(ws + s1o);
   P.inv = reinterpret_cast<float*>(ws + io);
+  P.nrm = reinterpret_cast<float*>(ws + no);
   P.ksum = reinterpret_cast<float*>(ws + ko);
   const int64_t d = geom->head_dim;
   P.kv_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size * d;
