@@ -251,7 +251,7 @@ def compress_kernel_bench(iters=20):
     scores = torch.empty((1, R, HKV, n), dtype=torch.float32, device="cuda")
     f_new = torch.empty_like(scores)
     sws = zp.new_workspace(zp.zp_score_workspace_size(geom, 1, R, NB))
-    cws = zp.new_workspace(zp.zp_select_workspace_size(geom, 1, R))
+    cws = zp.new_workspace(zp.zp_select_workspace_size(geom, 1, R, keep))
     stream = torch.cuda.Stream()
     units = R * HKV
     out = {"workload": f"{R} requests x {n} tokens ({NB} full blocks) compressing at once, "

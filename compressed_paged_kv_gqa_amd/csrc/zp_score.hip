@@ -495,7 +495,6 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
     brow[cw] = -1;
     pnc[cw] = wv + 4 * cw < CT ? P.p * nrm_s[(wv + 4 * cw) * 16 + cl] : INFINITY;
   }
-#pragma unroll 2
   for (int rt = 0; rt < CT; ++rt)
     cosine_tile_rows<T, D>(Ks, nrm_s, rt, B, pnc, wv, lane, true, 0, brow);
   best_over_groups(brow);
@@ -578,7 +577,6 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
       mainr = iv * lds_row_dot_f32<T, D>(Ks, tid, stot) - iv * iv * lds_row_dot<T, D>(Ks, tid, tid);
     }
     const float* nrm_r = nrmz + (int64_t)i * b;
-#pragma unroll 2
     for (int rt = 0; rt < CT; ++rt)
       cosine_tile_rows<T, D>(Ks, nrm_r, rt, B, pnc, wv, lane, i == m, i * b, brow);
   }

@@ -7,18 +7,22 @@
 // d), Sec. 4.4 (the packed entries go to target blocks, fresh ones for shared
 // prefix blocks).
 //
-// One workgroup per (kv-head, request, layer):
-//  1. radix select over order-preserving 32-bit keys of the fp32 scores
-//     (4 passes of 8 bits, LDS histogram) finds the k-th largest key;
-//  2. ties at that key go to the highest token indices (a backward block
-//     scan), giving a selection bitmap in LDS;
-//  3. a forward block scan turns the bitmap into the ascending kept list;
-//  4. the kept rows are moved in chunks: every thread loads its rows, the
-//     workgroup waits until all loads of the chunk have completed, then
-//     stores. Destination slot j <= source slot kept[j] and targets are
-//     either the same block or a fresh one, so no chunk reads a slot that an
-//     earlier chunk wrote, and no chunk writes a slot a later chunk still
-//     has to read before that read has completed.
+// Two launches:
+//  1. select_kernel, one workgroup per (kv-head, request, layer): radix
+//     select over order-preserving 32-bit keys of the fp32 scores (4 passes
+//     of 8 bits, LDS histogram) finds the k-th largest key; ties at that key
+//     go to the highest token indices (a backward block scan), giving a
+//     selection bitmap in LDS; a forward block scan turns it into the
+//     ascending kept list, written to the workspace (and to kept_idx).
+//  2. compact_kernel, one workgroup per (128-byte slice of a token row, K or
+//     V, kv-head, request, layer): the kept rows' slices are moved in chunks:
+//     every thread loads its rows, the workgroup waits until all loads of the
+//     chunk have completed, then stores. Destination slot j <= source slot
+//     kept[j] and targets are either the same block or a fresh one, so no
+//     chunk reads a slot that an earlier chunk wrote, and no chunk writes a
+//     slot a later chunk still has to read before that read has completed.
+//     Different workgroups touch disjoint bytes. The global-score entries
+//     move with the first slice of K.
 #include "zp_device.h"
 #include "zp_internal.h"
 
@@ -37,6 +41,8 @@ struct SelectParams {
   const int32_t* num_blocks;
   const int32_t* dst_tables;
   int32_t* kept_out;
+  int32_t* status;   // [layer_count][nreq][h_kv]: 1 = selection done, move it
+  int32_t* kept_ws;  // [layer_count][nreq][h_kv][keep] ascending kept indices
   uint32_t* err;
   int64_t scores_stride;
   int64_t kv_layer_elems, f_layer_elems;
@@ -69,8 +75,7 @@ __device__ int block_inclusive_scan(int v, int* wsum) {
   return v;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
+__global__ __launch_bounds__(256) void select_kernel(SelectParams P) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bitmap[kSelMaxTokens / 32];
   __shared__ int32_t kept[kKeepMax];
@@ -80,9 +85,10 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
 
   const int h = blockIdx.x, r = blockIdx.y, li = blockIdx.z;
   const int z = li * P.nreq + r;
-  const int layer = P.layer_begin + li;
   const int tid = threadIdx.x;
   const int N = P.num_blocks[r];
+  int32_t* status = P.status + (int64_t)z * P.h_kv + h;
+  if (tid == 0) *status = 0;  // nothing to move unless the selection completes
   if (N <= 0) return;
   if (N > P.max_blocks || N > P.src_stride) {
     if (tid == 0) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
@@ -116,7 +122,6 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
   }
 
   const float* sc = P.scores + ((int64_t)z * P.h_kv + h) * P.scores_stride;
-  const float* fnew = P.f_new ? P.f_new + ((int64_t)z * P.h_kv + h) * P.scores_stride : nullptr;
 
   // 1. Radix select of the keep-th largest key.
   uint32_t prefix = 0, pmask = 0, krem = keep;
@@ -183,40 +188,61 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
     __syncthreads();
   }
   __syncthreads();
+  int32_t* kw = P.kept_ws + ((int64_t)z * P.h_kv + h) * keep;
+  for (int j = tid; j < keep; j += 256) kw[j] = kept[j];
   if (P.kept_out) {
     int32_t* ko = P.kept_out + ((int64_t)z * P.h_kv + h) * keep;
     for (int j = tid; j < keep; j += 256) ko[j] = kept[j];
   }
-  if (!compact) return;
+  if (tid == 0 && compact) *status = 1;
+}
 
-  // 4. Ordered move of K, V (and F).
-  constexpr int EPL = Vec16<T>::N;
-  constexpr int LPR = D / EPL;          // lanes per token row
-  constexpr int RPR = 256 / LPR;        // rows per workgroup pass
-  constexpr int PASSES = 4;
-  constexpr int CHUNK = RPR * PASSES;   // rows per chunk
+
+// Moves the kept rows of one (layer, request, kv-head): this workgroup takes
+// byte slice `sl` (128 bytes = 8 lanes x 16 B) of every row of K (kv = 0) or
+// V (kv = 1).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void compact_kernel(SelectParams P) {
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int SLICES = ROWB / 128;
+  constexpr int RPP = 256 / 8;           // rows per pass
+  constexpr int PASSES = 8;
+  constexpr int CHUNK = RPP * PASSES;    // rows per chunk (256)
+  extern __shared__ int32_t kept[];      // [keep]
+
+  const int sl = blockIdx.x % SLICES, kv = blockIdx.x / SLICES;
+  const int h = blockIdx.y, z = blockIdx.z;
+  const int r = z % P.nreq;
+  const int layer = P.layer_begin + z / P.nreq;
+  const int tid = threadIdx.x;
+  if (P.status[(int64_t)z * P.h_kv + h] != 1) return;  // selection flagged an error
+  const int keep = P.keep;
   const int b = P.b;
-  T* kc = reinterpret_cast<T*>(P.kc) + layer * P.kv_layer_elems;
-  T* vc = reinterpret_cast<T*>(P.vc) + layer * P.kv_layer_elems;
-  float* fc = P.gscore ? P.gscore + layer * P.f_layer_elems : nullptr;
-  const int64_t page_elems = (int64_t)P.h_kv * b * D;
-  const int64_t head_off = (int64_t)h * b * D;
-  const int rr = tid / LPR, sub = tid % LPR;
+  const int32_t* kw = P.kept_ws + ((int64_t)z * P.h_kv + h) * keep;
+  for (int j = tid; j < keep; j += 256) kept[j] = kw[j];
+  __syncthreads();
+  const int32_t* stab = P.src_tables + (int64_t)r * P.src_stride;
+  const int32_t* dtab = P.dst_tables + (int64_t)r * P.dst_stride;
+  char* base = reinterpret_cast<char*>(kv ? P.vc : P.kc) + layer * P.kv_layer_elems * (int64_t)sizeof(T);
+  float* fc = (P.gscore && kv == 0 && sl == 0) ? P.gscore + layer * P.f_layer_elems : nullptr;
+  const float* fnew = P.f_new ? P.f_new + ((int64_t)z * P.h_kv + h) * P.scores_stride : nullptr;
+  const int64_t page_bytes = (int64_t)P.h_kv * b * ROWB;
+  const int64_t head_bytes = (int64_t)h * b * ROWB;
+  const int rr = tid / 8;
+  const int lane_off = sl * 128 + (tid % 8) * 16;
   for (int j0 = 0; j0 < keep; j0 += CHUNK) {
-    uint4 kv[PASSES], vv[PASSES];
+    uint4 v[PASSES];
     float fv = 0.f;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      const int j = j0 + ps * RPR + rr;
+      const int j = j0 + ps * RPP + rr;
       if (j < keep) {
         const int t = kept[j];
-        const int64_t off = (int64_t)stab[t / b] * page_elems + head_off + (int64_t)(t % b) * D +
-                            sub * EPL;
-        kv[ps] = ld16(kc + off);
-        vv[ps] = ld16(vc + off);
+        v[ps] = ld16(base + (int64_t)stab[t / b] * page_bytes + head_bytes +
+                     (int64_t)(t % b) * ROWB + lane_off);
       }
     }
-    if (fc && tid < CHUNK && j0 + tid < keep) {
+    if (fc && j0 + tid < keep) {
       const int t = kept[j0 + tid];
       fv = fnew ? fnew[t] : fc[((int64_t)stab[t / b] * P.h_kv + h) * b + (t % b)];
     }
@@ -224,15 +250,12 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
     __syncthreads();
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      const int j = j0 + ps * RPR + rr;
-      if (j < keep) {
-        const int64_t off = (int64_t)dtab[j / b] * page_elems + head_off + (int64_t)(j % b) * D +
-                            sub * EPL;
-        st16(kc + off, kv[ps]);
-        st16(vc + off, vv[ps]);
-      }
+      const int j = j0 + ps * RPP + rr;
+      if (j < keep)
+        st16(base + (int64_t)dtab[j / b] * page_bytes + head_bytes + (int64_t)(j % b) * ROWB +
+                 lane_off, v[ps]);
     }
-    if (fc && tid < CHUNK && j0 + tid < keep) {
+    if (fc && j0 + tid < keep) {
       const int j = j0 + tid;
       fc[((int64_t)dtab[j / b] * P.h_kv + h) * b + (j % b)] = fv;
     }
@@ -241,19 +264,34 @@ __global__ __launch_bounds__(256) void select_compact_kernel(SelectParams P) {
 
 template <typename T, int D>
 static void launch_select(const SelectParams& P, int layer_count, hipStream_t s) {
-  dim3 grid(P.h_kv, P.nreq, layer_count);
-  hipLaunchKernelGGL((select_compact_kernel<T, D>), grid, dim3(256), 0, s, P);
+  hipLaunchKernelGGL(select_kernel, dim3(P.h_kv, P.nreq, layer_count), dim3(256), 0, s, P);
+  if (!(P.flags & ZP_SELECT_NO_COMPACT)) {
+    constexpr int SLICES = D * (int)sizeof(T) / 128;
+    hipLaunchKernelGGL((compact_kernel<T, D>), dim3(2 * SLICES, P.h_kv, P.nreq * layer_count),
+                       dim3(256), sizeof(int32_t) * P.keep, s, P);
+  }
 }
 
 }  // namespace zp
 
 using namespace zp;
 
+static size_t select_ws_layout(const zp_geom* g, int32_t layer_count, int32_t nreq, int32_t keep,
+                               size_t* status_off, size_t* kept_off) {
+  const size_t items = size_t(layer_count) * nreq * g->num_kv_heads;
+  const size_t so = kWsHeader;
+  const size_t ko = round_up(so + items * sizeof(int32_t), 256);
+  if (status_off) *status_off = so;
+  if (kept_off) *kept_off = ko;
+  return round_up(ko + items * size_t(keep) * sizeof(int32_t), 256);
+}
+
 extern "C" size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_count,
-                                           int32_t nreq) {
-  if (validate_geom(geom, "zp_select_workspace_size") != ZP_OK || layer_count < 0 || nreq < 0)
+                                           int32_t nreq, int32_t keep) {
+  if (validate_geom(geom, "zp_select_workspace_size") != ZP_OK || layer_count < 0 || nreq < 0 ||
+      keep < 0)
     return 0;
-  return kWsHeader;
+  return select_ws_layout(geom, layer_count, nreq, keep, nullptr, nullptr);
 }
 
 extern "C" zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cache,
@@ -286,7 +324,10 @@ extern "C" zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cach
     return fail(ZP_EINVAL, "zp_select_compact: NULL buffer");
   if (scores_stride < int64_t(max_blocks) * geom->block_size)
     return fail(ZP_EINVAL, "zp_select_compact: scores_stride < max_blocks*b");
-  if (workspace_bytes < kWsHeader) return fail(ZP_EINVAL, "zp_select_compact: workspace too small");
+  size_t status_off, kept_off;
+  const size_t need = select_ws_layout(geom, layer_count, nreq, keep, &status_off, &kept_off);
+  if (workspace_bytes < need)
+    return fail(ZP_EINVAL, "zp_select_compact: workspace %zu bytes, need %zu", workspace_bytes, need);
   if (nreq > 65535 || layer_count > 65535)
     return fail(ZP_EINVAL, "zp_select_compact: nreq and layer_count must be <= 65535");
 
@@ -298,6 +339,8 @@ extern "C" zp_status zp_select_compact(const zp_geom* geom, const zp_cache* cach
   P.dst_stride = dst_tables ? dst_stride : src_stride;
   P.kept_out = kept_idx;
   P.err = static_cast<uint32_t*>(workspace);
+  P.status = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + status_off);
+  P.kept_ws = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kept_off);
   const int64_t d = geom->head_dim;
   P.kv_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size * d;
   P.f_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size;

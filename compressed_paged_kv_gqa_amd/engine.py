@@ -245,7 +245,7 @@ class DecodeEngine:
             kept = (torch.empty((G.num_layers, nreq, G.num_kv_heads, keep), dtype=torch.int32,
                                 device=self.device) if self.record else None)
             sws = zp.new_workspace(zp.zp_score_workspace_size(G, ls, nreq, maxb), self.device)
-            cws = zp.new_workspace(zp.zp_select_workspace_size(G, ls, nreq), self.device)
+            cws = zp.new_workspace(zp.zp_select_workspace_size(G, ls, nreq, keep), self.device)
             for lb in range(0, G.num_layers, ls):
                 lc = min(ls, G.num_layers - lb)
                 sl = slice(lb, lb + lc) if self.record else slice(0, lc)

@@ -69,7 +69,7 @@ def _declare(lib):
         "zp_score_workspace_size": (sz, [g, i32, i32, i32]),
         "zp_score_tokens": (C.c_int, [g, c, sp, i32, i32, i32, _P, i32, _P, i32, _P, _P, _P,
                                       _P, i64, _P, sz, _P]),
-        "zp_select_workspace_size": (sz, [g, i32, i32]),
+        "zp_select_workspace_size": (sz, [g, i32, i32, i32]),
         "zp_select_compact": (C.c_int, [g, c, i32, i32, i32, _P, _P, i64, _P, i32, _P, i32, _P,
                                         i32, i32, _P, u32, _P, sz, _P]),
         "zp_workspace_errors": (C.c_int, [_P, C.POINTER(C.c_uint32), _P]),
@@ -217,8 +217,8 @@ def zp_score_workspace_size(geom: CacheGeometry, layer_count, nreq, max_blocks):
     return lib().zp_score_workspace_size(C.byref(geom.c()), layer_count, nreq, max_blocks)
 
 
-def zp_select_workspace_size(geom: CacheGeometry, layer_count, nreq):
-    return lib().zp_select_workspace_size(C.byref(geom.c()), layer_count, nreq)
+def zp_select_workspace_size(geom: CacheGeometry, layer_count, nreq, keep):
+    return lib().zp_select_workspace_size(C.byref(geom.c()), layer_count, nreq, int(keep))
 
 
 def new_workspace(nbytes, device="cuda"):

@@ -217,7 +217,10 @@ zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
 
 #define ZP_SELECT_NO_COMPACT 0x1u /* only select; leave K, V, F untouched */
 
-size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t nreq);
+/* Workspace bytes of zp_select_compact for `keep` kept tokens per (layer,
+ * request, kv-head): error bits, per-item status and the kept indices. */
+size_t zp_select_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t nreq,
+                                int32_t keep);
 
 /* For every (layer, request, kv-head): keep the `keep` tokens with the
  * highest score (ties go to the higher token index), and move their K, V and

@@ -47,7 +47,7 @@ def _run(dtype, d, h_kv, b, w, nblocks, keep, fresh_mask, levels, L=2, layer_beg
                 S[li, r, h, :n] = synth.scores_with_ties(seed + 97 * li + 13 * h, r, n, w, levels)
     FN = (synth.rng(seed, 3, 1, "gscore").random(S.shape) * 0.01).astype(np.float32)
     kept = torch.full((layer_count, nreq, h_kv, keep), -1, dtype=torch.int32, device="cuda")
-    ws = zp.new_workspace(zp.zp_select_workspace_size(geom, layer_count, nreq))
+    ws = zp.new_workspace(zp.zp_select_workspace_size(geom, layer_count, nreq, keep))
     zp.zp_select_compact(hc.dev, layer_begin, layer_count, torch.from_numpy(S).cuda(),
                          dev_i32(tab), dev_i32(nblocks), max_blocks, dev_i32(dst), keep, kept, ws,
                          flags=zp.ZP_SELECT_NO_COMPACT if no_compact else 0,
