@@ -86,6 +86,34 @@ def decode_attention(q, K, V, scale=None):
     return o, lse
 
 
+def prefill_attention(Q, K, V, ctx, rows=None, scale=None):
+    """Causal attention of a prompt chunk over a request's resident tokens.
+
+    Q: [T][h_q][d], the queries of the T new tokens, which sit at positions
+    ctx .. ctx+T-1 after the ctx tokens already resident (a shared prefix or
+    an earlier chunk). K, V: [h_kv][ctx+T][d], every resident token including
+    the new ones. Token i attends to positions 0 .. ctx+i: ordinary causal
+    softmax attention, which the paper runs with FlashAttention over the
+    paged cache before any eviction (Zipage Sec. 3 and Sec. 6; the prompt may
+    exceed the N_max-block cap until its first compression, Sec. 4.1). Each
+    row is the decode attention of that token over its causal prefix.
+    ``rows`` restricts the computation to some token indices i. Returns
+    (O [len(rows)][h_q][d], lse [len(rows)][h_q]).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    T = Q.shape[0]
+    rows = range(T) if rows is None else rows
+    O, L = [], []
+    for i in rows:
+        o, lse = decode_attention(Q[i], K[:, :ctx + i + 1], V[:, :ctx + i + 1], scale)
+        O.append(o)
+        L.append(lse)
+    h_q, d = Q.shape[1], Q.shape[2]
+    if not O:
+        return np.zeros((0, h_q, d), _F), np.zeros((0, h_q), _F)
+    return np.stack(O), np.stack(L)
+
+
 # ---------------------------------------------------------------------------
 # Attention score (Zipage App. C.2, Alg. 1)
 # ---------------------------------------------------------------------------

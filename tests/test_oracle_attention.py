@@ -185,3 +185,50 @@ def test_attention_score_group_reduction_is_max_closed_form():
     ea = math.exp(s / math.sqrt(2))
     ref = np.array([ea, ea, 1.0, 1.0]) / (ea + 3)
     np.testing.assert_allclose(Z.attention_score(Qw, K, 4), ref, atol=1e-15)
+
+
+def _sdpa_causal(Q, K, V, ctx):
+    """torch SDPA on the CPU in float64 with the bottom-right causal mask of
+    a chunk of T queries after ctx resident tokens (library routine)."""
+    T, h_q, d = Q.shape
+    h_kv = K.shape[0]
+    g = h_q // h_kv
+    qt = torch.from_numpy(Q).double().permute(1, 0, 2)          # [h_q][T][d]
+    Kt = torch.from_numpy(K).double().repeat_interleave(g, 0)   # [h_q][n][d]
+    Vt = torch.from_numpy(V).double().repeat_interleave(g, 0)
+    n = K.shape[1]
+    mask = torch.arange(n)[None, :] <= (ctx + torch.arange(T))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask)
+    lse = torch.logsumexp(torch.where(mask, qt @ Kt.transpose(1, 2) / math.sqrt(d),
+                                      torch.tensor(-math.inf, dtype=torch.float64)), -1)
+    return o.permute(1, 0, 2).numpy(), lse.T.numpy()
+
+
+@pytest.mark.parametrize("h_q,h_kv,d,ctx,T", [(4, 1, 64, 0, 37), (32, 8, 128, 0, 70),
+                                              (8, 2, 64, 45, 20), (4, 4, 16, 300, 5)])
+def test_prefill_matches_causal_sdpa(h_q, h_kv, d, ctx, T):
+    rng = np.random.default_rng([2, h_q, d, ctx, T])
+    Q = rng.standard_normal((T, h_q, d))
+    K = rng.standard_normal((h_kv, ctx + T, d))
+    V = rng.standard_normal((h_kv, ctx + T, d))
+    O, L = Z.prefill_attention(Q, K, V, ctx)
+    Oref, Lref = _sdpa_causal(Q, K, V, ctx)
+    np.testing.assert_allclose(O, Oref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L, Lref, rtol=1e-12, atol=1e-12)
+    # a subset of rows is the same rows
+    O2, L2 = Z.prefill_attention(Q, K, V, ctx, rows=[T - 1, 0])
+    np.testing.assert_array_equal(O2, O[[T - 1, 0]])
+    np.testing.assert_array_equal(L2, L[[T - 1, 0]])
+
+
+def test_prefill_first_token_without_context_returns_its_own_value():
+    """Position 0 sees only itself: softmax over one key is 1, so o = v_0."""
+    rng = np.random.default_rng(5)
+    Q = rng.standard_normal((3, 4, 8))
+    K = rng.standard_normal((2, 3, 8))
+    V = rng.standard_normal((2, 3, 8))
+    O, L = Z.prefill_attention(Q, K, V, 0, rows=[0])
+    np.testing.assert_allclose(O[0], np.repeat(V[:, 0], 2, axis=0), rtol=0, atol=1e-15)
+    # and the log-sum-exp of one logit is that logit
+    k0 = np.repeat(K[:, 0], 2, axis=0)
+    np.testing.assert_allclose(L[0], np.einsum("hd,hd->h", Q[0], k0) / math.sqrt(8), rtol=1e-14)
