@@ -65,6 +65,8 @@ def parse_args():
                     help="only the isolated compression-kernel measurement (one JSON line)")
     ap.add_argument("--no-compress-kernels", action="store_true",
                     help="skip the isolated compression-kernel measurement")
+    ap.add_argument("--prefill-kernels", action="store_true",
+                    help="only the isolated prefill measurement (one JSON line)")
     return ap.parse_args()
 
 
@@ -292,6 +294,52 @@ def compress_kernel_bench(iters=20):
     return out
 
 
+def prefill_flops(lens):
+    """Algorithmic flops of causal prefill: a query at position p multiplies
+    q.k and p.v over p + 1 keys in every query head (2 flops per
+    multiply-add, two products)."""
+    return sum(4 * HQ * D * t * (t + 1) // 2 for t in lens)
+
+
+def prefill_kernel_bench(iters=5):
+    """HIP-event time per call of zp_paged_prefill for 64 prompts of 4096
+    tokens (one layer, bf16), the prompt pass of the 4096-token workload,
+    against the bf16 MFMA roofline."""
+    import torch
+    from compressed_paged_kv_gqa_amd import zp
+    R, T = BURST_REQ, BURST_BLOCKS * BS
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=R * BURST_BLOCKS + 8, block_size=BS,
+                            num_kv_heads=HKV, num_q_heads=HQ, head_dim=D, window=W, max_slots=R,
+                            n_max=NMAX, dtype="bf16")
+    cache = zp.PagedKVCache(geom, with_global=False, with_window_lse=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(SEED + 9)
+    q = torch.randn((R * T, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((R * T, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((R * T, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lse = torch.empty((R * T, HQ), dtype=torch.float32, device="cuda")
+    tables = torch.randperm(R * BURST_BLOCKS, generator=g, device="cuda").to(torch.int32)
+    tables = tables.view(R, BURST_BLOCKS).contiguous()
+    cu = torch.arange(0, (R + 1) * T, T, dtype=torch.int32, device="cuda")
+    ctx = torch.zeros(R, dtype=torch.int32, device="cuda")
+    qslot = torch.arange(R, dtype=torch.int32, device="cuda")
+    ws = zp.new_workspace(zp.zp_prefill_workspace_size(geom, R))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        ms = _time_calls(lambda: zp.zp_paged_prefill(cache, 0, q, k, v, cu, ctx, T, tables, qslot,
+                                                     out, lse, ws, stream=stream), iters, stream)
+    stream.synchronize()
+    assert zp.zp_workspace_errors(ws) == 0
+    fl = prefill_flops([T] * R)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": f"{R} prompts x {T} tokens, 1 layer, bf16, causal, K/V appended to "
+                        f"block {BS} pages, window queries and LSE captured",
+            "ms_per_call": round(ms, 3), "achieved_tflops": round(tf, 1),
+            "mfma_peak_tflops": MFMA_PEAK_TFS, "bound": "mfma",
+            "frac_of_roofline": round(tf / MFMA_PEAK_TFS, 4), "flops_per_call": fl}
+
+
 # --------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on a bounded sample of the same workload
 # --------------------------------------------------------------------------
@@ -395,6 +443,9 @@ def main():
     if args.compress_kernels:
         print(json.dumps(compress_kernel_bench()), flush=True)
         return
+    if args.prefill_kernels:
+        print(json.dumps(prefill_kernel_bench()), flush=True)
+        return
     from compressed_paged_kv_gqa_amd import synth
     phases = synth.rng(SEED, 3, 0, "lengths").integers(0, BS, B)
     cpu = None
@@ -410,6 +461,8 @@ def main():
     if not args.no_compress_kernels:
         log("compression kernels in isolation")
         ck = compress_kernel_bench()
+        log("prefill in isolation")
+        ck = {"compress": ck, "prefill": prefill_kernel_bench()}
     traffic = traffic_from_profiles()
     line = {
         "metric": "decode tok/s at 256 seqs with compression; achieved HBM GB/s vs peak",
@@ -439,7 +492,8 @@ def main():
         "decode_ms_per_step": round(r["decode_ms_per_step"], 3),
     }
     if ck is not None:
-        line["compress_kernels"] = ck
+        line["compress_kernels"] = ck["compress"]
+        line["prefill_kernels"] = ck["prefill"]
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

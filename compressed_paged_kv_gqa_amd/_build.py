@@ -30,7 +30,7 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
-HIP_SOURCES = ["zp_decode.hip", "zp_score.hip", "zp_select.hip"]
+HIP_SOURCES = ["zp_decode.hip", "zp_prefill.hip", "zp_score.hip", "zp_select.hip"]
 CXX_SOURCES = ["zp_host.cpp"]
 
 

@@ -43,7 +43,7 @@ class Geom(C.Structure):
 
 class Cache(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("qwin", C.c_void_p),
-                ("gscore", C.c_void_p)]
+                ("gscore", C.c_void_p), ("qwin_lse", C.c_void_p)]
 
 
 class ScoreParamsC(C.Structure):
@@ -66,6 +66,9 @@ def _declare(lib):
         "zp_decode_workspace_size": (sz, [g, i32, i32]),
         "zp_paged_decode": (C.c_int, [g, c, i32, i32, _P, _P, _P, _P, i32, _P, i32, _P, _P,
                                       _P, _P, sz, _P]),
+        "zp_prefill_workspace_size": (sz, [g, i32]),
+        "zp_paged_prefill": (C.c_int, [g, c, i32, i32, _P, _P, _P, _P, _P, i32, _P, i32, _P, _P,
+                                       _P, _P, sz, _P]),
         "zp_score_workspace_size": (sz, [g, i32, i32, i32]),
         "zp_score_tokens": (C.c_int, [g, c, sp, i32, i32, i32, _P, i32, _P, i32, _P, _P, _P,
                                       _P, i64, _P, sz, _P]),
@@ -163,7 +166,8 @@ class PagedKVCache:
     """Device buffers of K, V, the window query cache and the global-score
     cache F, in the layouts include/zp.h documents. Allocated with torch."""
 
-    def __init__(self, geom: CacheGeometry, device="cuda", with_global=True, init=None):
+    def __init__(self, geom: CacheGeometry, device="cuda", with_global=True, init=None,
+                 with_window_lse=False):
         import torch
         self.geom = geom
         dt = geom.torch_dtype()
@@ -176,10 +180,14 @@ class PagedKVCache:
                            G.window, G.head_dim), dtype=dt, device=device)
         self.gscore = (alloc((G.num_layers, G.num_blocks, G.num_kv_heads, G.block_size),
                              dtype=torch.float32, device=device) if with_global else None)
+        self.qwin_lse = (torch.zeros((G.num_layers, max(G.max_slots, 1), G.num_kv_heads, G.group,
+                                      G.window), dtype=torch.float32, device=device)
+                         if with_window_lse else None)
 
     def c(self):
         return Cache(self.k.data_ptr(), self.v.data_ptr(), self.qwin.data_ptr(),
-                     self.gscore.data_ptr() if self.gscore is not None else None)
+                     self.gscore.data_ptr() if self.gscore is not None else None,
+                     self.qwin_lse.data_ptr() if self.qwin_lse is not None else None)
 
 
 def _ptr(t):
@@ -244,6 +252,34 @@ def zp_paged_decode(cache: PagedKVCache, layer, q, k_new, v_new, block_tables, s
         v_new.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
         int(max_seq_len), _ptr(qslot), out.data_ptr(), _ptr(lse), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)), "zp_paged_decode")
+
+
+def zp_prefill_workspace_size(geom: CacheGeometry, nreq):
+    return lib().zp_prefill_workspace_size(C.byref(geom.c()), nreq)
+
+
+def zp_paged_prefill(cache: PagedKVCache, layer, q, k_new, v_new, cu_seqlens, ctx_lens,
+                     max_q_len, block_tables, qslot, out, lse, workspace, stream=None):
+    """q/out [T][h_q][d], k_new/v_new [T][h_kv][d]; cu_seqlens [nreq+1],
+    ctx_lens [nreq], block_tables [nreq][stride] int32 device tensors."""
+    import torch
+    geom = cache.geom
+    dt = geom.torch_dtype()
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out")):
+        _need(t, dt, n)
+    for t, n in ((cu_seqlens, "cu_seqlens"), (ctx_lens, "ctx_lens"),
+                 (block_tables, "block_tables"), (qslot, "qslot")):
+        _need(t, torch.int32, n)
+    _need(lse, torch.float32, "lse")
+    nreq = ctx_lens.shape[0]
+    if cu_seqlens.shape[0] != nreq + 1:
+        raise ValueError("cu_seqlens must hold nreq + 1 offsets")
+    _check(lib().zp_paged_prefill(
+        C.byref(geom.c()), C.byref(cache.c()), layer, nreq, q.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), cu_seqlens.data_ptr(), ctx_lens.data_ptr(), int(max_q_len),
+        block_tables.data_ptr(), block_tables.shape[1], _ptr(qslot), out.data_ptr(), _ptr(lse),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "zp_paged_prefill")
 
 
 @dataclass

@@ -40,6 +40,7 @@
  *          g = num_q_heads / num_kv_heads; query head j belongs to kv-head
  *          j / g (contiguous grouping).
  *   F      [num_layers][num_blocks][num_kv_heads][block_size] float32
+ *   Qlse   [num_layers][max_slots][num_kv_heads][g][window] float32
  * These hold the contents Zipage Sec. 3 (K, V), Sec. 4.2 (query cache) and
  * App. C.3 (global score cache F) define; only the axis order differs: one
  * (layer, block, kv-head) slice of K or V is contiguous.
@@ -102,10 +103,14 @@ typedef struct zp_geom {
 
 /* Device buffers of the caches, all [device], caller-owned. */
 typedef struct zp_cache {
-  void* k;       /* K cache                                              */
-  void* v;       /* V cache                                              */
-  void* qwin;    /* query cache of the observation window                */
-  float* gscore; /* global score cache F, or NULL when it is not used    */
+  void* k;         /* K cache                                            */
+  void* v;         /* V cache                                            */
+  void* qwin;      /* query cache of the observation window              */
+  float* gscore;   /* global score cache F, or NULL when it is not used  */
+  float* qwin_lse; /* log-sum-exp of each window query's attention row,
+                      [num_layers][max_slots][num_kv_heads][g][window]
+                      float32 (natural log, scale 1/sqrt(d)), written next
+                      to Qwin by the attention calls; NULL when not kept   */
 } zp_cache;
 
 /* ------------------------------------------------------------------------ */
@@ -145,6 +150,50 @@ zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t la
                           const int32_t* seq_lens, int32_t max_seq_len, const int32_t* qslot,
                           void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill attention (Zipage Sec. 3 block tables; Sec. 4.1 the prompt is     */
+/* written in full and may exceed N_max blocks until its first compression;  */
+/* Sec. 4.2 window queries; Sec. 4.4 a chunk may follow shared prefix        */
+/* blocks; Sec. 6 attention is ordinary causal softmax attention)            */
+/* ------------------------------------------------------------------------ */
+
+size_t zp_prefill_workspace_size(const zp_geom* geom, int32_t nreq);
+
+/* Causal attention of one layer for a ragged batch of `nreq` prompt chunks.
+ *
+ * Chunk r has q_len = cu_seqlens[r+1] - cu_seqlens[r] new tokens (rows
+ * cu_seqlens[r] .. cu_seqlens[r+1]-1 of q, k_new, v_new, out, lse), which sit
+ * at positions ctx_lens[r] .. ctx_lens[r]+q_len-1 of the request: the first
+ * ctx_lens[r] tokens (for example shared prefix blocks) are already in the
+ * cache. For each new token i at position p:
+ *   1. k_new[i], v_new[i] are written to block block_tables[r][p/b], slot p%b;
+ *   2. if qslot != NULL and p lies in the block of the chunk's last token at
+ *      slot p%b >= b-w, q[i] is written to row p%b-(b-w) of query-cache slot
+ *      qslot[r] (Zipage Sec. 4.2), and its log-sum-exp to cache->qwin_lse if
+ *      that is not NULL;
+ *   3. out[i][j] = sum_{t<=p} softmax_t(q[i][j] . k_t / sqrt(d)) v_t over kv-head
+ *      j/g, and lse[i][j] = log sum_{t<=p} exp(.) if lse != NULL.
+ *
+ *   q        [device] [T][h_q][d] dtype,  T = cu_seqlens[nreq]
+ *   k_new    [device] [T][h_kv][d] dtype;  v_new likewise
+ *   cu_seqlens [device] int32 [nreq+1], non-decreasing, cu_seqlens[0] = 0
+ *   ctx_lens   [device] int32 [nreq]
+ *   max_q_len  [host] upper bound of every q_len (sets the launch)
+ *   block_tables [device] int32 [nreq][table_stride], covering ctx + q_len tokens
+ *   qslot      [device] int32 [nreq] or NULL
+ *   out        [device] [T][h_q][d] dtype;  lse [device] float32 [T][h_q] or NULL
+ * Chunks whose geometry does not fit (q_len > max_q_len, ctx + q_len beyond
+ * the table) set ZP_DEVERR_SEQ_LEN and are skipped. bf16 runs on MFMA
+ * (tiles of 128/g tokens, all g heads of a kv-head per workgroup); fp32 runs
+ * one workgroup per token.
+ */
+zp_status zp_paged_prefill(const zp_geom* geom, const zp_cache* cache, int32_t layer,
+                           int32_t nreq, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* cu_seqlens, const int32_t* ctx_lens, int32_t max_q_len,
+                           const int32_t* block_tables, int32_t table_stride,
+                           const int32_t* qslot, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Importance scores (Zipage Sec. 4.2; App. C.2 Alg. 1, C.3 Alg. 2, C.4,     */

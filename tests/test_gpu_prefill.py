@@ -1,0 +1,159 @@
+"""GPU parity of zp_paged_prefill against the float64 oracle.
+
+Zipage (arXiv 2603.08743) Sec. 3 / Sec. 6: attention over a block table is
+ordinary causal softmax attention over the resident tokens; Sec. 4.1: the
+prompt is written in full; Sec. 4.2: the queries of the last w slots of the
+final block go to the query cache; Sec. 4.4: a chunk may follow ctx tokens
+(shared prefix blocks) already in the cache.
+Bar: max |out - ref| <= tol * max |ref| per (token, query head) on sampled
+rows, tol 1e-5 for fp32 and 2e-2 for bf16; lse within 2e-5 (fp32) / 2e-3
+(bf16) absolute; appended K/V, captured window queries bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_paged_kv_gqa_amd import synth, zp
+from oracle import zipage as Z
+
+from gpu_cases import HostCache, announce, dev_i32, device_k, device_v, random_tables, tol_for
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens
+    ("f32", 64, 4, 1, 16, 8, [200, 1, 37], [0, 0, 16]),
+    ("bf16", 128, 32, 8, 256, 16, [4096, 300, 17, 512], [0, 0, 700, 1024]),
+    ("bf16", 64, 8, 8, 32, 16, [130, 64, 1], [0, 33, 5]),
+    ("bf16", 128, 16, 2, 64, 8, [257, 1000], [0, 100]),
+    ("bf16", 128, 8, 8, 16, 16, [95, 16], [0, 32]),
+    ("bf16", 64, 16, 2, 128, 16, [640, 3], [130, 0]),
+    ("f32", 128, 16, 2, 64, 2, [70, 129], [0, 64]),
+]
+
+
+def _sample_rows(rng, qlen, b, w, ctx, k=24):
+    """First and last rows, rows of the final block's window, tile and block
+    edges, and random rows."""
+    rows = {0, qlen - 1}
+    last = ctx + qlen - 1
+    for off in range(b - w, b):
+        p = (last // b) * b + off
+        if ctx <= p <= last:
+            rows.add(p - ctx)
+    for e in (15, 16, 31, 32, 63, 64, 127, 128, 255, 256, 1023, 1024):
+        if e < qlen:
+            rows.add(e)
+    rows.update(rng.integers(0, qlen, min(k, qlen)).tolist())
+    return sorted(rows)
+
+
+def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24):
+    announce(f"prefill dtype={dtype} d={d} hq={h_q} hkv={h_kv} b={b} w={w} q={q_lens} ctx={ctx_lens}")
+    nreq = len(q_lens)
+    g = h_q // h_kv
+    ntok = [c + n for c, n in zip(ctx_lens, q_lens)]
+    nb = [-(-n // b) for n in ntok]
+    stride = max(nb) + 1
+    pool = sum(nb) + 2
+    geom = zp.CacheGeometry(num_layers=2, num_blocks=pool, block_size=b, num_kv_heads=h_kv,
+                            num_q_heads=h_q, head_dim=d, window=w, max_slots=nreq + 1, n_max=2,
+                            dtype=dtype)
+    hc = HostCache(geom, seed, 2)
+    hc.dev.qwin_lse = torch.full((2, nreq + 1, h_kv, g, w), 5.0, dtype=torch.float32,
+                                 device="cuda")
+    tab = random_tables(seed, 2, nb, pool, stride)
+    T = sum(q_lens)
+    gen = synth.rng(seed, 2, layer, "prompt_q")
+    q = synth.cast(gen.standard_normal((T, h_q, d)), dtype)
+    kn = synth.cast(gen.standard_normal((T, h_kv, d)) * np.where(gen.random((T, h_kv)) < 0.02, 4.0, 1.0)[..., None], dtype)
+    vn = synth.cast(gen.standard_normal((T, h_kv, d)), dtype)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    qslot = np.arange(nreq, dtype=np.int32) + 1
+    dt = geom.torch_dtype()
+    tq = torch.from_numpy(q).to(dt).cuda()
+    tk = torch.from_numpy(kn).to(dt).cuda()
+    tv = torch.from_numpy(vn).to(dt).cuda()
+    out = torch.full((T, h_q, d), 7.0, dtype=dt, device="cuda")
+    lse = torch.zeros((T, h_q), dtype=torch.float32, device="cuda")
+    qwin0 = hc.dev.qwin.float().cpu().numpy()
+    ws = zp.new_workspace(zp.zp_prefill_workspace_size(geom, nreq))
+    zp.zp_paged_prefill(hc.dev, layer, tq, tk, tv, dev_i32(cu), dev_i32(np.array(ctx_lens, np.int32)),
+                        max(q_lens), dev_i32(tab), dev_i32(qslot), out, lse, ws)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(ws) == 0
+    out_h = out.float().cpu().numpy()
+    lse_h = lse.cpu().numpy()
+    Kd, Vd = device_k(hc), device_v(hc)
+    qwin = hc.dev.qwin.float().cpu().numpy()
+    qlse = hc.dev.qwin_lse.cpu().numpy()
+    tol = tol_for(dtype)
+    ltol = 2e-5 if dtype == "f32" else 2e-3
+    srng = np.random.default_rng(seed)
+    worst = 0.0
+    for r in range(nreq):
+        c0, n, ctx = cu[r], q_lens[r], ctx_lens[r]
+        # appended rows bit-exact, context rows untouched
+        for h in range(h_kv):
+            Kr = Z.gather_sequence(Kd[layer, :, h], tab[r], ntok[r], b)
+            Vr = Z.gather_sequence(Vd[layer, :, h], tab[r], ntok[r], b)
+            np.testing.assert_array_equal(Kr[ctx:], kn[c0:c0 + n, h])
+            np.testing.assert_array_equal(Vr[ctx:], vn[c0:c0 + n, h])
+            np.testing.assert_array_equal(Kr[:ctx], Z.gather_sequence(hc.K[layer, :, h], tab[r], ctx, b))
+        K = np.stack([Z.gather_sequence(Kd[layer, :, h], tab[r], ntok[r], b) for h in range(h_kv)])
+        V = np.stack([Z.gather_sequence(Vd[layer, :, h], tab[r], ntok[r], b) for h in range(h_kv)])
+        rows = _sample_rows(srng, n, b, w, ctx, sample)
+        O, L = Z.prefill_attention(q[c0:c0 + n], K, V, ctx, rows=rows)
+        for x, i in enumerate(rows):
+            for j in range(h_q):
+                ref = O[x, j]
+                err = np.abs(out_h[c0 + i, j] - ref).max() / np.abs(ref).max()
+                worst = max(worst, err)
+                assert err <= tol, f"req {r} row {i} head {j}: {err}"
+            np.testing.assert_allclose(lse_h[c0 + i], L[x], rtol=0, atol=ltol)
+        # window rows of the final block: query and lse captured, nothing else
+        last = ctx + n - 1
+        slot = qslot[r]
+        for off in range(b - w, b):
+            p = (last // b) * b + off
+            u = off - (b - w)
+            if ctx <= p <= last:
+                i = p - ctx
+                for gi in range(g):
+                    np.testing.assert_array_equal(qwin[layer, slot, :, gi, u],
+                                                  q[c0 + i].reshape(h_kv, g, d)[:, gi])
+                    np.testing.assert_array_equal(qlse[layer, slot, :, gi, u],
+                                                  lse_h[c0 + i].reshape(h_kv, g)[:, gi])
+            else:
+                np.testing.assert_array_equal(qwin[layer, slot, :, :, u], qwin0[layer, slot, :, :, u])
+                assert np.all(qlse[layer, slot, :, :, u] == 5.0)
+    print(f"[prefill] worst relative error {worst:.3g}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2] // c[3]}-b{c[4]}" for c in CASES])
+def test_prefill_parity(case):
+    _run(*case)
+
+
+def test_prefill_reports_bad_block_ids_without_faulting():
+    announce("prefill bad block id")
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=8, block_size=16, num_kv_heads=2,
+                            num_q_heads=8, head_dim=64, window=8, max_slots=1, n_max=2,
+                            dtype="bf16")
+    cache = zp.PagedKVCache(geom)
+    tab = np.array([[0, 1, 99, 3]], np.int32)        # block 99 does not exist
+    T = 60
+    q = torch.randn((T, 8, 64), device="cuda").bfloat16()
+    k = torch.randn((T, 2, 64), device="cuda").bfloat16()
+    out = torch.zeros_like(q)
+    ws = zp.new_workspace(zp.zp_prefill_workspace_size(geom, 1))
+    zp.zp_paged_prefill(cache, 0, q, k, k, dev_i32([0, T]), dev_i32([0]), T, dev_i32(tab), None,
+                        out, None, ws)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(ws) & zp.ZP_DEVERR_BLOCK_ID
+    # a chunk longer than max_q_len is skipped with a length error
+    zp.zp_workspace_clear_errors(ws)
+    zp.zp_paged_prefill(cache, 0, q, k, k, dev_i32([0, T]), dev_i32([0]), T - 1,
+                        dev_i32([[0, 1, 2, 3]]), None, out, None, ws)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(ws) & zp.ZP_DEVERR_SEQ_LEN
