@@ -228,7 +228,10 @@ def _time_calls(fn, iters, stream):
 def compress_kernel_bench(iters=20):
     """HIP-event time per call of zp_score_tokens (lightning and flash) and
     zp_select_compact at the burst shape, on their own stream with nothing
-    else running, against the MFMA and HBM rooflines."""
+    else running, against the MFMA and HBM rooflines. The window rows carry
+    their log-sum-exp (as after zp_paged_prefill), so scoring reads each key
+    once; score_lightning_stats times the path that first gathers the softmax
+    statistics itself."""
     import torch
     from compressed_paged_kv_gqa_amd import zp
     R, NB = BURST_REQ, BURST_BLOCKS
@@ -237,19 +240,21 @@ def compress_kernel_bench(iters=20):
     geom = zp.CacheGeometry(num_layers=1, num_blocks=R * NB + 8, block_size=BS,
                             num_kv_heads=HKV, num_q_heads=HQ, head_dim=D, window=W,
                             max_slots=R, n_max=NMAX, dtype="bf16")
-    cache = zp.PagedKVCache(geom)
+    cache = zp.PagedKVCache(geom, with_window_lse=True)
     g = torch.Generator(device="cuda")
     g.manual_seed(SEED + 7)
     cache.k.normal_(generator=g)
     cache.v.normal_(generator=g)
     cache.qwin.normal_(generator=g)
     cache.gscore.uniform_(0.0, 1e-3, generator=g)
+    cache.qwin_lse.fill_(float(np.log(n)) + 1.0)
     perm = torch.randperm(R * NB, generator=g, device="cuda").to(torch.int32)
     tables = perm.view(R, NB).contiguous()
     dst = tables[:, :NMAX - 1].contiguous()
     nblk = torch.full((R,), NB, dtype=torch.int32, device="cuda")
     qslot = torch.arange(R, dtype=torch.int32, device="cuda")
     first = torch.ones(R, dtype=torch.uint8, device="cuda")
+    lse_ok = torch.ones(R, dtype=torch.uint8, device="cuda")
     scores = torch.empty((1, R, HKV, n), dtype=torch.float32, device="cuda")
     f_new = torch.empty_like(scores)
     sws = zp.new_workspace(zp.zp_score_workspace_size(geom, 1, R, NB))
@@ -260,16 +265,19 @@ def compress_kernel_bench(iters=20):
                        f"1 layer, bf16, first compression, keep {keep}",
            "units_per_call": units}
     with torch.cuda.stream(stream):
-        for red in ("lightning", "flash"):
+        for name, red, lse in (("score_lightning", "lightning", lse_ok),
+                               ("score_lightning_stats", "lightning", None),
+                               ("score_flash", "flash", lse_ok)):
             sp = zp.ScoreParams(redundancy=red)
             ms = _time_calls(lambda: zp.zp_score_tokens(cache, sp, 0, 1, tables, nblk, NB, qslot,
-                                                        first, scores, f_new, sws, stream=stream),
+                                                        first, scores, f_new, sws, stream=stream,
+                                                        window_lse_valid=lse),
                              iters if red == "lightning" else max(3, iters // 4), stream)
             fl, by = score_unit_cost(n, red, True)
             tf = units * fl / (ms * 1e-3) / 1e12
             gb = units * by / (ms * 1e-3) / 1e9
             ideal = max(units * fl / (MFMA_PEAK_TFS * 1e12), units * by / (HBM_PEAK_GBS * 1e9))
-            out[f"score_{red}"] = {
+            out[name] = {
                 "ms_per_call": round(ms, 4), "achieved_tflops": round(tf, 1),
                 "mfma_peak_tflops": MFMA_PEAK_TFS, "achieved_gbs": round(gb, 1),
                 "bound": "mfma" if units * fl / MFMA_PEAK_TFS / 1e12 > units * by / HBM_PEAK_GBS / 1e9
@@ -279,7 +287,7 @@ def compress_kernel_bench(iters=20):
         # scores of the lightning variant feed the selection
         sp = zp.ScoreParams()
         zp.zp_score_tokens(cache, sp, 0, 1, tables, nblk, NB, qslot, first, scores, f_new, sws,
-                           stream=stream)
+                           stream=stream, window_lse_valid=lse_ok)
         ms = _time_calls(lambda: zp.zp_select_compact(cache, 0, 1, scores, tables, nblk, NB, dst,
                                                       keep, None, cws, stream=stream,
                                                       f_new=f_new), iters, stream)

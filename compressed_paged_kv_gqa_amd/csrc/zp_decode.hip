@@ -39,6 +39,7 @@ struct DecodeParams {
   void* kc;
   void* vc;
   void* qwin;
+  float* qwin_lse;
   const int32_t* tables;
   const int32_t* seq_lens;
   const int32_t* qslot;
@@ -48,6 +49,7 @@ struct DecodeParams {
   uint32_t* err;
   int64_t kv_layer_off;    // element offset of the layer in K / V
   int64_t qwin_layer_off;  // element offset of the layer in Qwin
+  int64_t qlse_layer_off;  // element offset of the layer in the Qwin LSE table
   int32_t table_stride, num_blocks, b, h_kv, w, max_slots;
   int32_t split_tokens, max_splits, max_seq_len, log2b;
   float qk_scale;  // log2(e) / sqrt(d)
@@ -116,6 +118,18 @@ constexpr float kLazy = 8.0f;
 // split_tokens <= kMaxSplitPages * block_size).
 constexpr int kMaxSplitPages = 1024;
 constexpr float kNoMax = -1.0e30f;  // finite "nothing seen yet"
+
+// Window row of the token at position n - 1 of sequence `seq` (its slot in
+// the query cache), or -1 when the token is not in the final w slots of its
+// block or no valid query-cache slot is given.
+__device__ __forceinline__ int window_row_of(const DecodeParams& P, int seq, int n, int* slot) {
+  if (!P.qslot) return -1;
+  const int off = (n - 1) % P.b;
+  const int s = P.qslot[seq];
+  if (off < P.b - P.w || s < 0 || s >= P.max_slots) return -1;
+  *slot = s;
+  return off - (P.b - P.w);
+}
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_decode_kernel(
@@ -390,7 +404,14 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
       if (i < PAIRS) {
         const int h = i / D, e = i % D;
         out[(out_row + h) * D + e] = from_f32<T>(Ow[k] / Lw[k]);
-        if (P.lse && e == 0) P.lse[out_row + h] = (Mw[k] + log2f(Lw[k])) * kLn2;
+        if (e == 0) {
+          const float lse_nat = (Mw[k] + log2f(Lw[k])) * kLn2;
+          if (P.lse) P.lse[out_row + h] = lse_nat;
+          int slot;
+          const int u = P.qwin_lse ? window_row_of(P, seq, n, &slot) : -1;
+          if (u >= 0)
+            P.qwin_lse[P.qlse_layer_off + (((int64_t)slot * P.h_kv + kvh) * G + h) * P.w + u] = lse_nat;
+        }
       }
     }
     return;
@@ -438,7 +459,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams P) {
       O += pp[2 + e] * sc;
     }
     out[(out_row + h) * D + e] = from_f32<T>(O / L);
-    if (P.lse && e == 0) P.lse[out_row + h] = (M + log2f(L)) * kLn2;
+    if (e == 0) {
+      const float lse_nat = (M + log2f(L)) * kLn2;
+      if (P.lse) P.lse[out_row + h] = lse_nat;
+      int slot;
+      const int u = P.qwin_lse ? window_row_of(P, seq, n, &slot) : -1;
+      if (u >= 0)
+        P.qwin_lse[P.qlse_layer_off + (((int64_t)slot * P.h_kv + kvh) * G + h) * P.w + u] = lse_nat;
+    }
   }
 }
 
@@ -512,6 +540,7 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
   DecodeParams P{};
   P.q = q; P.k_new = k_new; P.v_new = v_new;
   P.kc = cache->k; P.vc = cache->v; P.qwin = cache->qwin;
+  P.qwin_lse = qslot ? cache->qwin_lse : nullptr;
   P.tables = block_tables; P.seq_lens = seq_lens; P.qslot = qslot;
   P.out = out; P.lse = lse;
   char* ws = static_cast<char*>(workspace);
@@ -520,6 +549,7 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
   const int64_t d = geom->head_dim;
   P.kv_layer_off = int64_t(layer) * geom->num_blocks * geom->num_kv_heads * geom->block_size * d;
   P.qwin_layer_off = int64_t(layer) * geom->max_slots * geom->num_q_heads * geom->window * d;
+  P.qlse_layer_off = int64_t(layer) * geom->max_slots * geom->num_q_heads * geom->window;
   P.table_stride = table_stride; P.num_blocks = geom->num_blocks; P.b = geom->block_size;
   P.h_kv = geom->num_kv_heads; P.w = geom->window; P.max_slots = geom->max_slots;
   P.split_tokens = split_tokens; P.max_splits = max_splits; P.max_seq_len = max_seq_len;

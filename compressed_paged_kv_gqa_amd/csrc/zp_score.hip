@@ -125,6 +125,8 @@ struct ScoreParams {
   const int32_t* num_blocks;
   const int32_t* qslot;
   const uint8_t* first;
+  const uint8_t* lse_ok;  // per request: window rows' log-sum-exp in qwin_lse (or NULL)
+  const float* qwin_lse;  // [L][max_slots][h_kv][g][w] natural-log LSE of window rows
   float* scores;
   float* f_new;  // updated global score (S1) per token, same layout as scores
   float* stats;  // [items][h_kv][max_blocks][R][2]  (max, sum) in the exp2 domain
@@ -135,7 +137,7 @@ struct ScoreParams {
   float* ksum;   // [items][h_kv][max_blocks][D]      sum of the block's unit keys
   uint32_t* err;
   int64_t scores_stride;
-  int64_t kv_layer_elems, qwin_layer_elems, f_layer_elems;
+  int64_t kv_layer_elems, qwin_layer_elems, f_layer_elems, qlse_layer_elems;
   int32_t layer_begin, nreq, table_stride, max_blocks, num_blocks_total;
   int32_t b, h_kv, w, max_slots;
   float qk_scale;  // log2(e) / sqrt(d)
@@ -324,6 +326,117 @@ __device__ __forceinline__ float lds_row_dot_f32(const char* Ks, int r, const fl
 }
 
 // ---------------------------------------------------------------------------
+// S0 of one block (App. C.2) and the global score (Alg. 2), given the
+// log-sum-exp of every window row.
+// ---------------------------------------------------------------------------
+// For this wavefront's column tiles (B) and the window rows' log-sum-exp in
+// the exp2 domain (lse2[R], LDS), forms P = exp2(logit - lse2) with the causal
+// mask of the last block, S0 = window mean of the group max, applies the
+// global score and writes f_new and S1. qop(rt, a) fills the A operands of row
+// tile rt. W16: the window is 16 slots, so row tile rt holds query head rt and
+// its 16 rows are the window positions: the group max is a max over row tiles
+// in registers and the window mean a sum over the lane's rows and lane
+// groups. Otherwise the probabilities of a column tile go through LDS (ptile,
+// [4][R][16] floats).
+template <typename T, int D, int R, bool W16, typename QOp>
+__device__ __forceinline__ void s0_columns(const ScoreParams& P, const ColOps<T, D>& B, QOp qop,
+                                           const float* lse2, float* ptile, int wv, int lane,
+                                           int CT, bool last, bool first, int layer, int page,
+                                           int pidx, int64_t zh, int h) {
+  using M = Mma<T, D>;
+  constexpr int RT = R / 16;
+  const int q = lane >> 4, cl = lane & 15;
+  const int b = P.b;
+  auto emit = [&](int col, float s0) {
+    float s1 = s0;
+    if (P.flags & ZP_SCORE_GLOBAL) {
+      // F is read only: blocks may be shared by several requests.
+      if (!first && !last)
+        s1 = fmaxf(P.alpha * P.gscore[layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col], s0);
+      P.f_new[zh * P.scores_stride + (int64_t)pidx * b + col] = s1;
+    }
+    P.s1buf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + col] = s1;
+  };
+  const float sc2 = P.qk_scale;
+
+  if constexpr (W16) {
+    float pm[kCTW][4];
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pm[cw][v] = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      typename M::op_t a[M::NKS];
+      qop(rt, a);
+      floatx4 acc[kCTW];
+      mma_tiles<T, D>(a, B, acc);
+      const float4 l4 = *reinterpret_cast<const float4*>(lse2 + rt * 16 + 4 * q);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+      for (int cw = 0; cw < kCTW; ++cw)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          pm[cw][v] = fmaxf(pm[cw][v], __builtin_amdgcn_exp2f(fmaf(acc[cw][v], sc2, -lv[v])));
+    }
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      if (ct >= CT) continue;  // scalar
+      if (last) {              // scalar: causal mask, window slot u = 4q + v
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (ct * 16 + cl > b - 16 + 4 * q + v) pm[cw][v] = 0.f;
+      }
+      float s = (pm[cw][0] + pm[cw][1]) + (pm[cw][2] + pm[cw][3]);
+      s += shfl_xor_f(s, 16);
+      s += shfl_xor_f(s, 32);
+      if (q == 0) emit(ct * 16 + cl, s * (1.0f / 16.0f));
+    }
+  } else {
+    const int G = R / P.w;
+    float* ptw = ptile + wv * R * 16;
+#pragma unroll
+    for (int cw = 0; cw < kCTW; ++cw) {
+      const int ct = wv + 4 * cw;
+      if (ct >= CT) continue;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        typename M::op_t a[M::NKS];
+        qop(rt, a);
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = rt * 16 + 4 * q + v;
+          const int col = ct * 16 + cl;
+          const int u = row % P.w;
+          float pv = exp2f(acc[v] * sc2 - lse2[row]);
+          if (last && col > b - P.w + u) pv = 0.f;
+          ptw[row * 16 + cl] = pv;
+        }
+      }
+      // Within a wavefront LDS writes and reads are ordered; no barrier needed.
+      if (lane < 16) {
+        float s0 = 0.f;
+        for (int u = 0; u < P.w; ++u) {
+          float mx = 0.f;
+          for (int gi = 0; gi < G; ++gi) mx = fmaxf(mx, ptw[(gi * P.w + u) * 16 + lane]);
+          s0 += mx;
+        }
+        emit(ct * 16 + lane, s0 / (float)P.w);
+      }
+    }
+  }
+}
+
+// Whether request r's window rows come with their log-sum-exp.
+__device__ __forceinline__ bool lse_given(const ScoreParams& P, int r) {
+  return P.lse_ok && P.qwin_lse && P.lse_ok[r] != 0;
+}
+
+// ---------------------------------------------------------------------------
 // Phase A: row statistics of the window logits; key norms and unit-key sums;
 // lightning redundancy rows.
 // ---------------------------------------------------------------------------
@@ -341,6 +454,8 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   float* wstat = ksum_s + D;                                  // [4][R][2]
   float* sub = wstat + 4 * R * 2;                             // [b]
   int* istar = reinterpret_cast<int*>(sub + b);               // [b]
+  float* lse2 = reinterpret_cast<float*>(istar + b);          // [R]
+  float* ptile = lse2 + R;     // [4][R][16], window LSE given and window != 16 only
 
   const int pidx = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
   int N, slot;
@@ -422,10 +537,34 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   }
 
   // Window logits: B operands = this wavefront's column tiles of the block.
-  // Row statistics in the exp2 domain of the scaled logits: per row the max
-  // (M * scale) and the sum of exp2((x - M) * scale) over the block.
   ColOps<T, D> B;
   B.from_lds(Ks, CT, wv, lane);
+  const int r = z % P.nreq;
+  if (lse_given(P, r)) {
+    // The window rows' log-sum-exp came with the queries (the attention pass
+    // that produced each window token saw exactly its causal row): S0 and the
+    // global score straight from this block, no statistics pass.
+    if (tid < R)
+      lse2[tid] = P.qwin_lse[layer * P.qlse_layer_elems + ((int64_t)slot * P.h_kv + h) * R + tid] * kLog2e;
+    __syncthreads();
+    auto qop = [&](int rt, typename M::op_t* a) {
+      if constexpr (PREQ) {
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) a[ks] = qa[rt][ks];
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::glb(qrows + (int64_t)(rt * 16 + cl) * D, ks, lane);
+      }
+    };
+    if (P.w == 16)
+      s0_columns<T, D, R, true>(P, B, qop, lse2, ptile, wv, lane, CT, last, P.first[r] != 0,
+                                layer, page, pidx, zh, h);
+    else
+      s0_columns<T, D, R, false>(P, B, qop, lse2, ptile, wv, lane, CT, last, P.first[r] != 0,
+                                 layer, page, pidx, zh, h);
+  } else {
+  // Row statistics in the exp2 domain of the scaled logits: per row the max
+  // (M * scale) and the sum of exp2((x - M) * scale) over the block.
   const float sc2 = P.qk_scale;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -478,6 +617,7 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
     float* st = P.stats + ((zh * P.max_blocks + pidx) * R + tid) * 2;
     st[0] = Mx;
     st[1] = S;
+  }
   }
 
   if (!redun) return;
@@ -600,16 +740,13 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase B: S0 of one block (App. C.2) and the global score (Alg. 2).
+// Phase B (requests without window log-sum-exp): merges the per-block row
+// statistics into log-sum-exp, recomputes the logits, S0 and global score.
 // ---------------------------------------------------------------------------
-// W16: the window is 16 slots, so row tile rt holds query head rt and its 16
-// rows are the window positions: the group max is a max over row tiles in
-// registers and the window mean a sum over the lane's rows and lane groups.
 template <typename T, int D, int R, bool W16>
 __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   using L = LdsTile<T, D>;
   using M = Mma<T, D>;
-  constexpr int RT = R / 16;
   extern __shared__ __align__(16) char smem[];
   char* Qs = smem;                                           // [R][D]
   float* lse2 = reinterpret_cast<float*>(Qs + R * L::ROWB);  // [R]
@@ -620,9 +757,10 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   const int page = resolve_page(P, pidx, z, &N, &slot);
   if (page < 0) return;
   const int r = z % P.nreq;
+  if (lse_given(P, r)) return;  // done by phase A
   const int layer = P.layer_begin + z / P.nreq;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
-  const int q = lane >> 4, cl = lane & 15;
+  const int cl = lane & 15;
   const int b = P.b;
   const int CT = b / 16;
   const bool last = pidx == N - 1;
@@ -644,93 +782,12 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
     lse2[tid] = Mx + log2f(S);
   }
   __syncthreads();
-
-  const bool first = P.first[r] != 0;
-  auto emit = [&](int col, float s0) {
-    float s1 = s0;
-    if (P.flags & ZP_SCORE_GLOBAL) {
-      // F is read only: blocks may be shared by several requests.
-      if (!first && !last)
-        s1 = fmaxf(P.alpha * P.gscore[layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col], s0);
-      P.f_new[zh * P.scores_stride + (int64_t)pidx * b + col] = s1;
-    }
-    P.s1buf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + col] = s1;
+  auto qop = [&](int rt, typename M::op_t* a) {
+#pragma unroll
+    for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
   };
-  const float sc2 = P.qk_scale;
-
-  if constexpr (W16) {
-    float pm[kCTW][4];
-#pragma unroll
-    for (int cw = 0; cw < kCTW; ++cw)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) pm[cw][v] = 0.f;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      typename M::op_t a[M::NKS];
-#pragma unroll
-      for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
-      floatx4 acc[kCTW];
-      mma_tiles<T, D>(a, B, acc);
-      const float4 l4 = *reinterpret_cast<const float4*>(lse2 + rt * 16 + 4 * q);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-      for (int cw = 0; cw < kCTW; ++cw)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          pm[cw][v] = fmaxf(pm[cw][v], __builtin_amdgcn_exp2f(fmaf(acc[cw][v], sc2, -lv[v])));
-    }
-#pragma unroll
-    for (int cw = 0; cw < kCTW; ++cw) {
-      const int ct = wv + 4 * cw;
-      if (ct >= CT) continue;  // scalar
-      if (last) {              // scalar: causal mask, window slot u = 4q + v
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (ct * 16 + cl > b - 16 + 4 * q + v) pm[cw][v] = 0.f;
-      }
-      float s = (pm[cw][0] + pm[cw][1]) + (pm[cw][2] + pm[cw][3]);
-      s += shfl_xor_f(s, 16);
-      s += shfl_xor_f(s, 32);
-      if (q == 0) emit(ct * 16 + cl, s * (1.0f / 16.0f));
-    }
-  } else {
-    // Any window: the probabilities of one column tile go through LDS.
-    const int G = R / P.w;
-    float* ptw = ptile + wv * R * 16;
-#pragma unroll
-    for (int cw = 0; cw < kCTW; ++cw) {
-      const int ct = wv + 4 * cw;
-      if (ct >= CT) continue;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        typename M::op_t a[M::NKS];
-#pragma unroll
-        for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], B.op[cw][ks], acc);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = rt * 16 + 4 * q + v;
-          const int col = ct * 16 + cl;
-          const int u = row % P.w;
-          float pv = exp2f(acc[v] * sc2 - lse2[row]);
-          if (last && col > b - P.w + u) pv = 0.f;
-          ptw[row * 16 + cl] = pv;
-        }
-      }
-      // Within a wavefront LDS writes and reads are ordered; no barrier needed.
-      if (lane < 16) {
-        float s0 = 0.f;
-        for (int u = 0; u < P.w; ++u) {
-          float mx = 0.f;
-          for (int gi = 0; gi < G; ++gi) mx = fmaxf(mx, ptw[(gi * P.w + u) * 16 + lane]);
-          s0 += mx;
-        }
-        emit(ct * 16 + lane, s0 / (float)P.w);
-      }
-    }
-  }
+  s0_columns<T, D, R, W16>(P, B, qop, lse2, ptile, wv, lane, CT, last, P.first[r] != 0, layer,
+                           page, pidx, zh, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -799,9 +856,11 @@ template <typename T, int D, int R>
 static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
   using L = LdsTile<T, D>;
   const int b = P.b;
-  const size_t smemA = size_t(b) * L::ROWB + sizeof(float) * (2 * b + D + 4 * R * 2 + 2 * b);
-  const size_t smemF = size_t(b) * L::ROWB + sizeof(float) * D;
   const bool w16 = P.w == 16;
+  const size_t ptileA = (P.lse_ok && !w16) ? size_t(4) * R * 16 : 0;
+  const size_t smemA = size_t(b) * L::ROWB +
+                       sizeof(float) * (2 * b + D + 4 * R * 2 + 2 * b + R + ptileA);
+  const size_t smemF = size_t(b) * L::ROWB + sizeof(float) * D;
   const size_t smemB = size_t(R) * L::ROWB + sizeof(float) * (R + (w16 ? 0 : 4 * R * 16));
   const bool flash = (P.flags & ZP_SCORE_REDUNDANCY) && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
   if (smemA > kMaxLds || smemB > kMaxLds || (flash && smemF > kMaxLds))
@@ -883,7 +942,8 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
                                      const int32_t* block_tables, int32_t table_stride,
                                      const int32_t* num_blocks, int32_t max_blocks,
                                      const int32_t* qslot, const uint8_t* first_compression,
-                                     float* scores, float* f_new, int64_t scores_stride,
+                                     const uint8_t* window_lse_valid, float* scores, float* f_new,
+                                     int64_t scores_stride,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   zp_status st = validate_geom(geom, "zp_score_tokens");
   if (st != ZP_OK) return st;
@@ -901,6 +961,8 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
     return fail(ZP_EINVAL, "zp_score_tokens: scores_stride %lld < max_blocks*b",
                 (long long)scores_stride);
   const zp_score_params& sp = *params;
+  if (window_lse_valid && !cache->qwin_lse)
+    return fail(ZP_EINVAL, "zp_score_tokens: window_lse_valid needs cache->qwin_lse");
   if ((sp.flags & ZP_SCORE_GLOBAL) && (!cache->gscore || !f_new))
     return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL needs cache->gscore and f_new");
   if (sp.flags & ~uint32_t(ZP_SCORE_GLOBAL | ZP_SCORE_POOL | ZP_SCORE_POOL_FIRST_ONLY |
@@ -925,6 +987,7 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   P.kc = cache->k; P.qwin = cache->qwin; P.gscore = cache->gscore;
   P.tables = block_tables; P.num_blocks = num_blocks; P.qslot = qslot;
   P.first = first_compression; P.scores = scores; P.f_new = f_new;
+  P.lse_ok = window_lse_valid; P.qwin_lse = cache->qwin_lse;
   P.scores_stride = scores_stride;
   char* ws = static_cast<char*>(workspace);
   P.err = reinterpret_cast<uint32_t*>(ws);
@@ -937,6 +1000,7 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   const int64_t d = geom->head_dim;
   P.kv_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size * d;
   P.qwin_layer_elems = int64_t(geom->max_slots) * geom->num_q_heads * geom->window * d;
+  P.qlse_layer_elems = int64_t(geom->max_slots) * geom->num_q_heads * geom->window;
   P.f_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size;
   P.layer_begin = layer_begin; P.nreq = nreq; P.table_stride = table_stride;
   P.max_blocks = max_blocks; P.num_blocks_total = geom->num_blocks;

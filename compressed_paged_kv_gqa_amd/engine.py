@@ -32,6 +32,7 @@ class Request:
     first: bool = True          # never compressed so far
     compressing: bool = False
     done: bool = False
+    lse_from: int = 0           # window rows at positions >= lse_from carry their log-sum-exp
 
 
 @dataclass
@@ -47,7 +48,7 @@ class DecodeEngine:
 
     def __init__(self, geom: zp.CacheGeometry, params: zp.ScoreParams, max_seqs, table_cap,
                  layer_stride=8, async_compress=True, with_global=True, device="cuda",
-                 cache_init=None, record=False):
+                 cache_init=None, record=False, window_lse=True):
         self.geom = geom
         self.params = params
         self.B = max_seqs
@@ -55,7 +56,11 @@ class DecodeEngine:
         self.layer_stride = max(1, min(layer_stride, geom.num_layers))
         self.async_compress = async_compress
         self.device = device
-        self.cache = zp.PagedKVCache(geom, device=device, with_global=with_global, init=cache_init)
+        # window_lse: the attention kernels keep each window query's
+        # log-sum-exp, and scoring reuses it instead of a statistics pass
+        self.window_lse = window_lse
+        self.cache = zp.PagedKVCache(geom, device=device, with_global=with_global, init=cache_init,
+                                     with_window_lse=window_lse)
         self.alloc = zp.BlockAllocator(geom.num_blocks)
         self.reqs: dict[int, Request] = {}
         # Host master copies, staged through a ring of pinned buffers: a
@@ -97,8 +102,42 @@ class DecodeEngine:
             table = list(prefix_table)
         table += self.alloc.alloc(nb - len(table))
         assert len(table) <= self.cap
-        self.reqs[sid] = Request(sid, table, n_tokens)
+        # tokens written by the caller come without window log-sum-exp
+        self.reqs[sid] = Request(sid, table, n_tokens, lse_from=n_tokens)
         return table
+
+    def prefill(self, sids, chunk_lens, q, k_new, v_new, out, lse=None):
+        """Prompt chunks of requests `sids` through every layer with
+        zp_paged_prefill (Zipage Sec. 4.1: the prompt is written in full and
+        may exceed N_max blocks until its first compression). Request sids[i]
+        must have been added with the length it has after its chunk of
+        chunk_lens[i] tokens; the tokens before the chunk (a shared prefix,
+        say) are already resident. Chunk i occupies rows cu[i]..cu[i+1]-1
+        (cu = running sum of chunk_lens) of q/out [L][T][h_q][d] and
+        k_new/v_new [L][T][h_kv][d]. Window rows of each chunk's final block
+        get their log-sum-exp. Compressions whose trigger the prompt meets
+        are launched at the end."""
+        G = self.geom
+        lens = [int(x) for x in chunk_lens]
+        assert len(lens) == len(sids) and q.shape[1] == sum(lens)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        ctx = np.array([self.reqs[s].n - n for s, n in zip(sids, lens)], np.int32)
+        assert (ctx >= 0).all()
+        stride = max(len(self.reqs[s].table) for s in sids)
+        tab = np.zeros((len(sids), stride), np.int32)
+        for i, s in enumerate(sids):
+            tab[i, :len(self.reqs[s].table)] = self.reqs[s].table
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+        cu_d, ctx_d, tab_d = dev(cu), dev(ctx), dev(tab)
+        slot_d = dev(np.array(sids, np.int32))
+        ws = zp.new_workspace(zp.zp_prefill_workspace_size(G, len(sids)), self.device)
+        for l in range(G.num_layers):
+            zp.zp_paged_prefill(self.cache, l, q[l], k_new[l], v_new[l], cu_d, ctx_d, max(lens),
+                                tab_d, slot_d, out[l], None if lse is None else lse[l], ws)
+        for s, c in zip(sids, ctx):
+            self.reqs[s].lse_from = int(c)
+        self.prefill_ws = ws      # device error bits of the last prefill
+        self.compress_due_now()
 
     def write_tokens(self, sid, layer, start, k, v):
         """Copies K/V rows [h_kv][t][d] of request `sid` into its pages from
@@ -209,18 +248,21 @@ class DecodeEngine:
         nreq = len(ok)
         maxb = max(len(p[0]) for p in plans)
         nd = n_max - 1
-        # one pinned int32 staging buffer: src tables | dst tables | N | slot | first
-        meta = torch.zeros(nreq * (maxb + nd + 3), dtype=torch.int32).pin_memory()
+        # one pinned int32 staging buffer: src tables | dst tables | N | slot |
+        # first | window log-sum-exp valid
+        meta = torch.zeros(nreq * (maxb + nd + 4), dtype=torch.int32).pin_memory()
         m = meta.numpy()
         src = m[:nreq * maxb].reshape(nreq, maxb)
         dst = m[nreq * maxb:nreq * (maxb + nd)].reshape(nreq, nd)
-        tail = m[nreq * (maxb + nd):].reshape(3, nreq)
+        tail = m[nreq * (maxb + nd):].reshape(4, nreq)
         for i, p in enumerate(plans):
             src[i, :len(p[0])] = p[0]
             dst[i] = p[1]
         tail[0] = [len(p[0]) for p in plans]
         tail[1] = ok
         tail[2] = [1 if self.reqs[s].first else 0 for s in ok]
+        # every window row (the last w positions) carries its log-sum-exp
+        tail[3] = [1 if self.reqs[s].n - G.window >= self.reqs[s].lse_from else 0 for s in ok]
         first = tail[2].astype(np.uint8)
         stream = self.side if self.async_compress else torch.cuda.current_stream()
         ready = torch.cuda.Event()
@@ -236,6 +278,8 @@ class DecodeEngine:
             nblk_d = meta_d[o:o + nreq]
             qslot_d = meta_d[o + nreq:o + 2 * nreq]
             first_d = meta_d[o + 2 * nreq:o + 3 * nreq].to(torch.uint8)
+            lse_d = (meta_d[o + 3 * nreq:o + 4 * nreq].to(torch.uint8) if self.window_lse
+                     else None)
             ls = self.layer_stride
             nl = G.num_layers if self.record else ls     # recording keeps every layer
             scores = torch.empty((nl, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
@@ -251,13 +295,13 @@ class DecodeEngine:
                 sl = slice(lb, lb + lc) if self.record else slice(0, lc)
                 sc, fn = scores[sl], (f_new[sl] if use_f else None)
                 zp.zp_score_tokens(self.cache, self.params, lb, lc, src_d, nblk_d, maxb, qslot_d,
-                                   first_d, sc, fn, sws, stream=stream)
+                                   first_d, sc, fn, sws, stream=stream, window_lse_valid=lse_d)
                 zp.zp_select_compact(self.cache, lb, lc, sc, src_d, nblk_d, maxb, dst_d, keep,
                                      kept[sl] if kept is not None else None, cws,
                                      stream=stream, f_new=fn)
             done = torch.cuda.Event()
             done.record(stream)
-            bufs += [meta_d, first_d, scores, f_new, sws, cws]
+            bufs += [meta_d, first_d, lse_d, scores, f_new, sws, cws]
             if self.record:
                 self.log.append((list(ok), first.copy(), scores, kept))
         self.pending.append(_Pending(ok, plans, done, bufs))
@@ -282,6 +326,7 @@ class DecodeEngine:
                 r.n = keep
                 r.first = False
                 r.compressing = False
+                r.lse_from = keep     # the next window rows come from decode
         self.pending = still
 
     def wait_compressions(self):

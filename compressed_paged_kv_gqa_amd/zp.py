@@ -71,7 +71,7 @@ def _declare(lib):
                                        _P, _P, sz, _P]),
         "zp_score_workspace_size": (sz, [g, i32, i32, i32]),
         "zp_score_tokens": (C.c_int, [g, c, sp, i32, i32, i32, _P, i32, _P, i32, _P, _P, _P,
-                                      _P, i64, _P, sz, _P]),
+                                      _P, _P, i64, _P, sz, _P]),
         "zp_select_workspace_size": (sz, [g, i32, i32, i32]),
         "zp_select_compact": (C.c_int, [g, c, i32, i32, i32, _P, _P, i64, _P, i32, _P, i32, _P,
                                         i32, i32, _P, u32, _P, sz, _P]),
@@ -313,12 +313,13 @@ class ScoreParams:
 
 def zp_score_tokens(cache: PagedKVCache, params: ScoreParams, layer_begin, layer_count,
                     block_tables, num_blocks, max_blocks, qslot, first_compression, scores,
-                    f_new, workspace, stream=None):
+                    f_new, workspace, stream=None, window_lse_valid=None):
     import torch
     _need(block_tables, torch.int32, "block_tables")
     _need(num_blocks, torch.int32, "num_blocks")
     _need(qslot, torch.int32, "qslot")
     _need(first_compression, torch.uint8, "first_compression")
+    _need(window_lse_valid, torch.uint8, "window_lse_valid")
     _need(scores, torch.float32, "scores")
     _need(f_new, torch.float32, "f_new")
     if f_new is not None and f_new.shape != scores.shape:
@@ -328,8 +329,9 @@ def zp_score_tokens(cache: PagedKVCache, params: ScoreParams, layer_begin, layer
         C.byref(cache.geom.c()), C.byref(cache.c()), C.byref(params.c()), layer_begin,
         layer_count, nreq, block_tables.data_ptr(), block_tables.shape[1],
         num_blocks.data_ptr(), int(max_blocks), qslot.data_ptr(), first_compression.data_ptr(),
-        scores.data_ptr(), _ptr(f_new), scores.shape[-1], workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(stream)), "zp_score_tokens")
+        _ptr(window_lse_valid), scores.data_ptr(), _ptr(f_new), scores.shape[-1],
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "zp_score_tokens")
 
 
 def zp_select_compact(cache: PagedKVCache, layer_begin, layer_count, scores, src_tables,

@@ -246,6 +246,13 @@ size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t
  *   block_tables [device] int32 [nreq][table_stride]
  *   num_blocks   [device] int32 [nreq];  qslot [device] int32 [nreq]
  *   first_compression [device] uint8 [nreq]
+ *   window_lse_valid  [device] uint8 [nreq] or NULL: nonzero when every
+ *          window row of request r has its log-sum-exp in cache->qwin_lse
+ *          (zp_paged_decode and zp_paged_prefill write it next to each
+ *          window query they capture; the attention of a window query
+ *          already covered exactly its causal row of Alg. 1). Those
+ *          requests skip the pass that gathers the softmax statistics, and
+ *          their keys are read once. Needs cache->qwin_lse.
  *   scores [device] float32 [layer_count][nreq][h_kv][scores_stride],
  *          scores_stride >= max_blocks*b; entries past n are not written.
  *   f_new  [device] float32, same layout as scores: S1 of every token; may be
@@ -255,9 +262,10 @@ zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
                           const zp_score_params* params, int32_t layer_begin,
                           int32_t layer_count, int32_t nreq, const int32_t* block_tables,
                           int32_t table_stride, const int32_t* num_blocks, int32_t max_blocks,
-                          const int32_t* qslot, const uint8_t* first_compression, float* scores,
-                          float* f_new, int64_t scores_stride, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          const int32_t* qslot, const uint8_t* first_compression,
+                          const uint8_t* window_lse_valid, float* scores, float* f_new,
+                          int64_t scores_stride, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Top-k selection and compaction (Zipage Sec. 4.2, App. C.6 Alg. 4,         */

@@ -56,7 +56,7 @@ def test_short_workspace_and_null_buffers_are_rejected():
     assert st == zp.ZP_EINVAL  # layer out of range
     sp = zp.ScoreParams(tau=0.0).c()
     st = zp.lib().zp_score_tokens(C.byref(g), C.byref(cache), C.byref(sp), 0, 1, 1, 1, 4, 1, 4, 1,
-                                  1, 1, None, 64, 1, 1 << 20, None)
+                                  1, None, 1, None, 64, 1, 1 << 20, None)
     assert st == zp.ZP_EINVAL  # global flag without F, or tau = 0
     st = zp.lib().zp_select_compact(C.byref(g), C.byref(cache), 0, 1, 1, 1, None, 64, 1, 4, 1, 4,
                                     1, 4, 0, None, 0, 1, 256, None)

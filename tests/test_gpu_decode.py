@@ -55,6 +55,8 @@ def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=()):
     out = torch.full((B, h_q, d), 7.0, dtype=dt, device="cuda")
     lse = torch.zeros((B, h_q), dtype=torch.float32, device="cuda")
     max_len = max(lens)
+    g = h_q // h_kv
+    hc.dev.qwin_lse = torch.full((2, B, h_kv, g, w), 9.0, dtype=torch.float32, device="cuda")
     ws = zp.new_workspace(zp.zp_decode_workspace_size(geom, B, max_len))
     zp.zp_paged_decode(hc.dev, layer, tq, tk, tv, dev_i32(tab), dev_i32(seq), max_len,
                        dev_i32(qslot), out, lse, ws)
@@ -66,7 +68,9 @@ def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=()):
     K_after = hc.dev.k.float().cpu().numpy()
     V_after = hc.dev.v.float().cpu().numpy()
     Q_after = hc.dev.qwin.float().cpu().numpy()
+    QL_after = hc.dev.qwin_lse.cpu().numpy()
     expK, expV, expQ = hc.K.copy(), hc.V.copy(), hc.Q.copy()
+    expQL = np.full_like(QL_after, 9.0)
     for r in range(B):
         if seq[r] <= 0:
             assert np.all(out_h[r] == 7.0)
@@ -89,9 +93,11 @@ def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=()):
             expQ[layer, r] = expQ[layer, r]
             for j in range(h_q):
                 expQ[layer, r, j // gq, j % gq, sl - (b - w)] = q[r, j]
+                expQL[layer, r, j // gq, j % gq, sl - (b - w)] = lse_h[r, j]
     np.testing.assert_array_equal(K_after, expK)
     np.testing.assert_array_equal(V_after, expV)
     np.testing.assert_array_equal(Q_after, expQ)
+    np.testing.assert_array_equal(QL_after, expQL)   # window rows' lse next to their query
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2]//c[3]}-b{c[4]}" for c in CASES])

@@ -48,8 +48,15 @@ def _planted_keys(hc, seed):
     hc.K = synth.cast(K, G.dtype)
 
 
+def _window_lse(Qw, K, b):
+    """log-sum-exp of each window row's causal attention row (oracle logits)."""
+    A = Z.window_logits(Qw, K, b)              # [g][w][n], -inf past each query
+    m = A.max(axis=-1, keepdims=True)
+    return (m[..., 0] + np.log(np.exp(A - m).sum(axis=-1)))
+
+
 def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, layer_count=2,
-         seed=11, planted=False, heavy=True):
+         seed=11, planted=False, heavy=True, lse=None):
     announce(f"score dtype={dtype} d={d} g={h_q // h_kv} b={b} w={w} N={nblocks} first={first} "
              f"sp={sp}")
     nreq = len(nblocks)
@@ -71,10 +78,26 @@ def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, laye
     scores = torch.full((layer_count, nreq, h_kv, stride), -7.0, device="cuda")
     f_new = torch.full_like(scores, -5.0) if sp.use_global else None
     F_before = hc.dev.gscore.clone()
+    lse_valid = None
+    if lse is not None:
+        # window log-sum-exp from the oracle for the requests that have it;
+        # a far-off value elsewhere, which must not be used
+        g = h_q // h_kv
+        tbl = np.full((L, nreq + 1, h_kv, g, w), 1.0e3, np.float32)
+        flags = np.array([1 if lse(r) else 0 for r in range(nreq)], np.uint8)
+        for li in range(layer_count):
+            l = layer_begin + li
+            for r in range(nreq):
+                if flags[r]:
+                    for h in range(h_kv):
+                        K = Z.gather_sequence(hc.K[l, :, h], tab[r], nblocks[r] * b, b)
+                        tbl[l, qslot[r], h] = _window_lse(hc.Q[l, qslot[r], h], K, b)
+        hc.dev.qwin_lse = torch.from_numpy(tbl).cuda()
+        lse_valid = torch.from_numpy(flags).cuda()
     ws = zp.new_workspace(zp.zp_score_workspace_size(geom, layer_count, nreq, max_blocks))
     zp.zp_score_tokens(hc.dev, sp, layer_begin, layer_count, dev_i32(tab), dev_i32(nblocks),
                        max_blocks, dev_i32(qslot), torch.from_numpy(firsts).cuda(), scores, f_new,
-                       ws)
+                       ws, window_lse_valid=lse_valid)
     torch.cuda.synchronize()
     assert zp.zp_workspace_errors(ws) == 0
     assert torch.equal(hc.dev.gscore, F_before)        # the cache's F is only read
@@ -179,3 +202,18 @@ def test_score_flash_redundancy_planted_clusters_across_blocks(p):
     _run("bf16", 128, 16, 4, 64, 16, [4, 7], lambda r: 1, sp, planted=True, heavy=False)
     _run("bf16", 64, 8, 8, 32, 16, [5, 2], lambda r: 0, sp, L=1, layer_begin=0, layer_count=1,
          planted=True, heavy=False)
+
+
+@pytest.mark.parametrize("red", ["lightning", "flash"])
+def test_score_with_window_lse_qwen_shape(red):
+    # requests 0 and 2 bring their window rows' log-sum-exp: one pass over K
+    sp = zp.ScoreParams(redundancy=red)
+    _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, sp, lse=lambda r: r != 1)
+
+
+def test_score_with_window_lse_other_windows():
+    # w != 16 takes the general S0 path inside the first pass
+    _run("f32", 64, 4, 1, 16, 8, [13, 4], lambda r: r == 0, DEFAULT, L=1, layer_begin=0,
+         layer_count=1, lse=lambda r: True)
+    _run("bf16", 128, 16, 2, 64, 8, [3, 5], lambda r: 1, DEFAULT, L=1, layer_begin=0,
+         layer_count=1, lse=lambda r: r == 1)
