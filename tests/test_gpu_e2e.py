@@ -50,15 +50,55 @@ def _compare_kept(kept_gpu, S_ref, keep):
     return outside, False
 
 
+def _prefill_and_check(cfg, eng, geom, inputs, prompt_q_full, sample, rows_per_req=12):
+    """Registers every request and runs its whole prompt through the engine's
+    prefill (one ragged batch per layer); checks sampled output rows against
+    the oracle's causal prefill."""
+    L, h_q, h_kv, d = geom.num_layers, geom.num_q_heads, geom.num_kv_heads, geom.head_dim
+    dt = geom.torch_dtype()
+    lens = [x.prompt_k.shape[2] for x in inputs]
+    for r, n0 in enumerate(lens):
+        eng.add_request(r, n0)
+    # [L][T][heads][d], requests concatenated along T
+    q = torch.from_numpy(np.concatenate([qf.transpose(0, 2, 1, 3) for qf in prompt_q_full], 1))
+    k = torch.from_numpy(np.concatenate([x.prompt_k.transpose(0, 2, 1, 3) for x in inputs], 1))
+    v = torch.from_numpy(np.concatenate([x.prompt_v.transpose(0, 2, 1, 3) for x in inputs], 1))
+    q, k, v = (t.to(dt).cuda().contiguous() for t in (q, k, v))
+    out = torch.empty_like(q)
+    eng.prefill(list(range(len(inputs))), lens, q, k, v, out)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(eng.prefill_ws) == 0
+    out_h = out.float().cpu().numpy()
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    tol = tol_for(geom.dtype)
+    rng = np.random.default_rng(7)
+    worst = 0.0
+    for r in sample:
+        x = inputs[r]
+        rows = sorted(set([0, lens[r] - 1] + rng.integers(0, lens[r], rows_per_req).tolist()))
+        for l in range(L):
+            O, _ = Z.prefill_attention(prompt_q_full[r][l].transpose(1, 0, 2), x.prompt_k[l],
+                                       x.prompt_v[l], 0, rows=rows)
+            for a, i in enumerate(rows):
+                for j in range(h_q):
+                    err = np.abs(out_h[l, cu[r] + i, j] - O[a, j]).max() / np.abs(O[a, j]).max()
+                    worst = max(worst, err)
+                    assert err <= tol, (cfg, "prefill", r, l, i, j, err)
+    print(f"{cfg}: worst prefill error {worst:.3e}", flush=True)
+
+
 def _run_requests(cfg, geom, sp, inputs, n_steps, sample, layer_stride=1, async_compress=True,
-                  wait_each_step=True, prefix_len=0, check_prefix=None):
+                  wait_each_step=True, prefix_len=0, check_prefix=None, prompt_q_full=None):
     """Drives all requests on the GPU and compares `sample` of them with the
     oracle simulation. `inputs[r]` is a synth.RequestInputs. Every request
     consumes its own next decode input: with wait_each_step=False a
     compressing request sits out decode steps until its side-stream event has
     fired (Sec. 4.5), so requests drift apart in step count. With
     prefix_len > 0 the first prefix_len prompt tokens of every request are
-    identical and their blocks are shared (Sec. 4.4)."""
+    identical and their blocks are shared (Sec. 4.4). With prompt_q_full
+    (per request [L][h_q][n0][d]) the prompts go through zp_paged_prefill
+    instead of being written directly; their outputs are checked on sampled
+    rows and the window queries are the prompts' last w queries."""
     B = len(inputs)
     L, h_q, h_kv, d = geom.num_layers, geom.num_q_heads, geom.num_kv_heads, geom.head_dim
     b, w = geom.block_size, geom.window
@@ -67,7 +107,9 @@ def _run_requests(cfg, geom, sp, inputs, n_steps, sample, layer_stride=1, async_
     eng = DecodeEngine(geom, sp, B, cap, layer_stride=layer_stride,
                        async_compress=async_compress, record=True)
     prefix_table = None
-    for r, x in enumerate(inputs):
+    if prompt_q_full is not None:
+        _prefill_and_check(cfg, eng, geom, inputs, prompt_q_full, sample)
+    for r, x in enumerate(inputs if prompt_q_full is None else []):
         n0 = x.prompt_k.shape[2]
         share = prefix_table if (prefix_len and r > 0) else None
         table = eng.add_request(r, n0, prefix_table=share)
@@ -268,3 +310,30 @@ def test_ragged_long_context_sampled():
                         wait_each_step=False)
     for r in eng.reqs.values():
         assert len(r.table) <= 8
+
+
+@pytest.mark.timeout(600)
+def test_qwen_shape_real_prefill_then_compress_and_decode_sampled():
+    """The 4096-token prompts of 16 requests go through zp_paged_prefill
+    (bf16 MFMA), which also captures the window queries and their
+    log-sum-exp; the compression that the prompt triggers then scores with
+    that log-sum-exp in one pass over the keys; 64 decode steps follow. Two
+    requests are checked against the oracle in full (prefill rows sampled)."""
+    announce("e2e qwen-shape prefill 16x4096")
+    B, n0, T = 16, 4096, 64
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=B * 16 + 8, block_size=256,
+                            num_kv_heads=8, num_q_heads=32, head_dim=128, window=16,
+                            max_slots=B, n_max=8, dtype="bf16")
+    inputs, qfull = [], []
+    for r in range(B):
+        x = synth.request_inputs(6, 6000 + r, 1, 32, 8, 128, n0, T, dtype="bf16")
+        qf = synth.cast(synth.rng(6, 6000 + r, 0, "prompt_q").standard_normal((1, 32, n0, 128)),
+                        "bf16")
+        x.prompt_q = qf[:, :, n0 - 16:]          # the window: the prompt's last 16 queries
+        inputs.append(x)
+        qfull.append(qf)
+    eng = _run_requests("qwen16-prefill", geom, zp.ScoreParams(), inputs, T, [0, 11],
+                        prompt_q_full=qfull)
+    assert eng.compressions == B
+    for r in eng.reqs.values():
+        assert r.n == 1792 + T and len(r.table) == 8 and not r.first
