@@ -13,8 +13,10 @@ zipage   decode attention, window attention score, global score, pooling,
          compaction, and a whole compression event.
 planner  block-level target rule for shared prefixes and the capacity
          formulas (Zipage paper, Sec. 4.2 eq. (1), Sec. 4.4, App. C.3 eq. (2)).
+scheduler constrained and hybrid scheduling with query slots, preemption and
+         shared prefixes (Sec. 4.3, Fig. 2, Sec. 4.4), as a state machine.
 
 Parity status of each function is stated in its docstring; every function is
 pinned by a ``-m "not gpu"`` test except where it says "parity unpinned".
 """
-from . import zipage, planner  # noqa: F401
+from . import zipage, planner, scheduler  # noqa: F401

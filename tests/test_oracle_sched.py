@@ -1,0 +1,291 @@
+"""Pins of the oracle's constrained / hybrid scheduler (no GPU).
+
+Zipage (arXiv 2603.08743) Sec. 4.3 (constrained scheduling, the four rules of
+hybrid scheduling, Fig. 2), Sec. 4.1 (trigger at N >= N_max full blocks,
+N_max - 1 blocks kept plus the reserved block), Sec. 4.4 (shared prefix
+blocks, targets, preemption of the last uncompressed request).
+
+The step-by-step traces below were worked out by hand from those rules and
+the readings stated in the oracle module; the random-stream tests check
+invariants that hold for any correct scheduler.
+"""
+import numpy as np
+import pytest
+
+from oracle.scheduler import CONSTRAINED, HYBRID, Scheduler
+
+
+def _brief(o):
+    return (o["kind"], [(e["rid"], e["slot"], e["ctx"], e["len"], e["table"]) for e in o["batch"]],
+            [(c["rid"], c["src"], c["dst"], c["new"]) for c in o["comp"]],
+            o["finished"], o["preempted"], o["blocked"])
+
+
+def test_constrained_admits_at_most_m():
+    """M = 2: the third request waits for a slot, gets the freed slot and the
+    lowest free block once the second request finishes."""
+    s = Scheduler(100, 16, 4, 4, 2, 8, 1000, CONSTRAINED)
+    s.add(0, 10, 3)
+    s.add(1, 20, 2)
+    s.add(2, 5, 2)
+    want = [
+        ("prefill", [(0, 0, 0, 10, [0]), (1, 1, 0, 20, [1, 2])], [], [], [], 0),
+        ("decode", [(0, 0, 10, 1, [0]), (1, 1, 20, 1, [1, 2])], [], [1], [], 0),
+        ("prefill", [(2, 1, 0, 5, [1])], [], [], [], 0),
+        ("decode", [(0, 0, 11, 1, [0]), (2, 1, 5, 1, [1])], [], [0, 2], [], 0),
+        ("idle", [], [], [], [], 0),
+    ]
+    for w in want:
+        assert _brief(s.step()) == w
+    assert s.unfinished() == 0 and s.num_free() == 100
+
+
+def test_hybrid_slotless_request_blocks_at_the_window_then_takes_the_slot():
+    """M = 1, N_max = 2, b = 16, w = 4: positions 28..31 need a slot. The
+    second request is admitted without one, stops before position 28, takes
+    slot 0 when the first request finishes, is compressed at n = 32 (targets:
+    its own first block, reserved: its second) and resumes with n = 16."""
+    s = Scheduler(100, 16, 4, 2, 1, 8, 1000, HYBRID)
+    s.add(0, 8, 5)
+    s.add(1, 26, 10)
+    want = [
+        ("prefill", [(0, 0, 0, 8, [0]), (1, None, 0, 26, [1, 2])], [], [], [], 0),
+        ("decode", [(0, 0, 8, 1, [0]), (1, None, 26, 1, [1, 2])], [], [], [], 0),
+        ("decode", [(0, 0, 9, 1, [0]), (1, None, 27, 1, [1, 2])], [], [], [], 0),
+        ("decode", [(0, 0, 10, 1, [0])], [], [], [], 1),
+        ("decode", [(0, 0, 11, 1, [0])], [], [0], [], 1),
+        ("decode", [(1, 0, 28, 1, [1, 2])], [], [], [], 0),
+        ("decode", [(1, 0, 29, 1, [1, 2])], [], [], [], 0),
+        ("decode", [(1, 0, 30, 1, [1, 2])], [], [], [], 0),
+        ("decode", [(1, 0, 31, 1, [1, 2])], [], [], [], 0),
+        ("idle", [], [(1, [1, 2], [1], [1, 2])], [], [], 0),
+        ("decode", [(1, 0, 16, 1, [1, 2])], [], [], [], 0),
+        ("decode", [(1, 0, 17, 1, [1, 2])], [], [], [], 0),
+        ("decode", [(1, 0, 18, 1, [1, 2])], [], [1], [], 0),
+    ]
+    for w in want:
+        o = s.step()
+        assert _brief(o) == w, s.t
+        for c in o["comp"]:
+            s.compress_done(c["rid"])
+    assert s.unfinished() == 0
+
+
+def test_constrained_waits_for_blocks_released_by_compression():
+    """Four blocks = M N_max. A 40-token prompt holds three blocks; the short
+    request finds no free block at n = 16 and waits (no preemption) until the
+    long one is compressed into two blocks and its third block is released."""
+    s = Scheduler(4, 16, 4, 2, 2, 8, 1000, CONSTRAINED)
+    s.add(0, 40, 30)
+    s.add(1, 10, 30)
+    trace = []
+    for _ in range(11):
+        o = s.step()
+        trace.append(_brief(o))
+        for c in o["comp"]:
+            s.compress_done(c["rid"])
+    assert all(t[4] == [] for t in trace)                     # never preempts
+    assert [t[5] for t in trace] == [0] * 7 + [1, 1, 1, 0]
+    assert trace[7][1] == [(0, 0, 46, 1, [0, 1, 2])]
+    assert trace[9] == ("idle", [], [(0, [0, 1, 2], [0], [0, 1])], [], [], 1)
+    assert trace[10][1] == [(0, 0, 16, 1, [0, 1]), (1, 1, 16, 1, [3, 2])]
+
+
+def test_hybrid_preempts_the_last_slotless_request():
+    """M = 1 and four blocks. The slot-less second request needs its third
+    block when none is free; being the last request without a slot it is
+    itself preempted, and re-enters the waiting queue with its outputs."""
+    s = Scheduler(4, 16, 4, 4, 1, 8, 1000, HYBRID)
+    s.add(0, 16, 40)
+    s.add(1, 20, 40)
+    o = s.step()
+    assert _brief(o)[1] == [(0, 0, 0, 16, [0]), (1, None, 0, 20, [1, 2])]
+    o = s.step()
+    assert _brief(o)[1] == [(0, 0, 16, 1, [0, 3]), (1, None, 20, 1, [1, 2])]
+    for t in range(3, 14):
+        o = s.step()
+        assert o["preempted"] == []
+    o = s.step()                                               # step 14
+    assert o["preempted"] == [1] and [e["rid"] for e in o["batch"]] == [0]
+    assert s.reqs[1].gen == 13 and s.reqs[1].table == [] and list(s.waiting) == [s.reqs[1]]
+    assert s.num_free() == 2
+    o = s.step()                                               # 33 tokens need 3 blocks
+    assert o["kind"] == "decode" and [e["rid"] for e in o["batch"]] == [0]
+
+
+def test_prefix_sharing_and_preemption_of_the_last_uncompressed_request():
+    """Shared prefixes (Sec. 4.4), four blocks, M = 2. The second member of
+    the group shares block 0 and prefills only 4 tokens. When the first
+    member is due, its shared position needs a fresh target block and none
+    is free: the last uncompressed request (the second member, which holds
+    a slot) is preempted; block 0 is then private and compressed in place."""
+    s = Scheduler(4, 16, 4, 2, 2, 8, 1000, HYBRID, prefix_sharing=True)
+    s.add(0, 40, 20, 1, 16)
+    assert _brief(s.step())[1] == [(0, 0, 0, 40, [0, 1, 2])]
+    s.add(1, 20, 20, 1, 16)
+    assert _brief(s.step())[1] == [(1, 1, 16, 4, [0, 3])]
+    assert s.refcount == [2, 1, 1, 1]
+    for _ in range(8):
+        assert s.step()["kind"] == "decode"
+    o = s.step()                                               # step 11
+    assert _brief(o) == ("idle", [], [(0, [0, 1, 2], [0], [0, 1])], [], [1], 0)
+    assert s.refcount == [1, 1, 1, 0] and s.groups == {}
+    assert s.step()["kind"] == "idle"                         # 29 tokens need 2 blocks
+    s.compress_done(0)
+    assert s.refcount == [1, 1, 0, 0]
+    o = s.step()
+    assert _brief(o)[1] == [(1, 1, 0, 29, [2, 3])]
+
+
+def test_prefix_members_of_one_step_do_not_share():
+    """Members admitted in the step that writes the prefix prefill it
+    themselves; a member admitted later shares it."""
+    s = Scheduler(16, 16, 4, 2, 4, 8, 1000, HYBRID, prefix_sharing=True)
+    s.add(0, 40, 10, 7, 32)
+    s.add(1, 36, 10, 7, 32)
+    o = s.step()
+    assert _brief(o)[1] == [(0, 0, 0, 40, [0, 1, 2]), (1, 1, 0, 36, [3, 4, 5])]
+    s.add(2, 34, 10, 7, 32)
+    o = s.step()
+    assert _brief(o)[1] == [(2, 2, 32, 2, [0, 1, 6])]
+    assert s.refcount[:7] == [2, 2, 1, 1, 1, 1, 1] and s.groups[7]["holders"] == 2
+
+
+def test_prefix_target_is_a_fresh_block_when_shared():
+    s = Scheduler(16, 16, 4, 2, 4, 8, 1000, HYBRID, prefix_sharing=True)
+    s.add(0, 40, 20, 7, 32)
+    s.step()
+    s.add(2, 34, 20, 7, 32)
+    o = s.step()                                               # shares blocks 0, 1
+    assert _brief(o)[1] == [(2, 1, 32, 2, [0, 1, 3])]
+    for _ in range(8):
+        s.step()                                               # request 0 reaches 48
+    o = s.step()
+    assert [(c["rid"], c["src"], c["dst"], c["new"]) for c in o["comp"]] == [(0, [0, 1, 2], [4], [4, 2])]
+    s.compress_done(0)
+    assert s.refcount[:6] == [1, 1, 1, 1, 1, 0]                # request 0 dropped blocks 0 and 1
+
+
+# ----------------------------------------------------------------- invariants
+def random_stream(seed, n, b, short=False):
+    """Prompts of 1..10 blocks (1..4 when short), outputs of 1..16 blocks
+    (1..3 when short); 60 % of the requests in one of two prefix groups
+    (prefix lengths 2b and b + 1)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for rid in range(n):
+        prompt = int(rng.integers(1, 4 * b if short else 10 * b))
+        new = int(rng.integers(1, 3 * b if short else 16 * b))
+        grp, plen = -1, 0
+        if rng.random() < 0.6:
+            grp = int(rng.integers(0, 2))
+            plen = b + 1 if grp else 2 * b          # one prefix length per group
+            if plen >= prompt:
+                grp, plen = -1, 0
+        out.append((rid, prompt, new, grp, plen))
+    return out
+
+
+def drive(s, stream, seed, max_steps=200000, arrivals=True, check=None):
+    """Adds requests over time, completes compressions after 0-3 steps."""
+    rng = np.random.default_rng(seed + 1000)
+    pend = []
+    pos = 0
+    steps = []
+    for _ in range(max_steps):
+        if pos < len(stream):
+            k = len(stream) - pos if not arrivals else int(rng.integers(0, 4))
+            for rid, p, m, g, pl in stream[pos:pos + k]:
+                s.add(rid, p, m, g, pl)
+            pos = min(pos + k, len(stream))
+        o = s.step()
+        steps.append(o)
+        if check:
+            check(s, o)
+        pend += [[c["rid"], int(rng.integers(0, 4))] for c in o["comp"]]
+        in_flight = bool(pend)
+        keep = []
+        for x in pend:
+            if x[1] == 0:
+                s.compress_done(x[0])
+            else:
+                x[1] -= 1
+                keep.append(x)
+        pend = keep
+        if pos == len(stream) and s.unfinished() == 0 and not pend:
+            return steps
+        if o["kind"] == "idle" and not in_flight and pos == len(stream):
+            raise AssertionError(f"no progress at step {s.t}")
+    raise AssertionError("did not finish")
+
+
+def _invariants(s, o):
+    b, nmax = s.b, s.n_max
+    # every block's count equals the number of tables (and pending plans) that hold it
+    held = [0] * len(s.refcount)
+    for r in s.reqs.values():
+        for p in r.table:
+            held[p] += 1
+        if r.plan:
+            for p in r.plan[2]:
+                if p not in r.plan[0]:
+                    held[p] += 1
+    assert held == s.refcount
+    slots = [r.slot for r in s.running if r.slot is not None]
+    assert len(slots) == len(set(slots)) and all(0 <= x < s.M for x in slots)
+    assert all(r.slot is not None for r in s.running if r.compressed or r.state == "compressing")
+    # R4: slot holders sit among the first M running requests
+    assert all(r.slot is None for r in s.running[s.M:])
+    if s.policy == CONSTRAINED:
+        assert len(s.running) <= s.M
+    rows = [r.row for r in s.running]
+    assert len(rows) == len(set(rows)) and all(0 <= x < s.max_running for x in rows)
+    for e in o["batch"]:
+        r = s.reqs[e["rid"]]
+        if o["kind"] == "decode":
+            assert e["slot"] is not None or not s.needs_slot(e["ctx"])
+            assert e["ctx"] < len(e["table"]) * b
+        else:
+            last = e["ctx"] + e["len"] - 1
+            assert e["slot"] is not None or not s.needs_slot(last)
+            assert len(e["table"]) == -(-(last + 1) // b)
+    for r in s.running:
+        if r.compressed and r.state == "running":
+            assert len(r.table) == nmax and r.n <= nmax * b
+    for c in o["comp"]:
+        assert len(c["dst"]) == nmax - 1 and len(c["new"]) == nmax and c["slot"] is not None
+
+
+@pytest.mark.parametrize("policy", [CONSTRAINED, HYBRID])
+@pytest.mark.parametrize("prefix", [False, True])
+@pytest.mark.parametrize("extra", [0, 6])
+@pytest.mark.parametrize("seed", range(4))
+def test_random_streams_finish_with_invariants(policy, prefix, extra, seed):
+    b, nmax, M = 16, 3, 4
+    stream = random_stream(seed, 40, b, short=seed % 2 == 1)
+    if not prefix:
+        stream = [(r, p, m, -1, 0) for r, p, m, _g, _pl in stream]
+    # the longest prompt (10 blocks) fits; M N_max <= blocks (Sec. 4.2)
+    nb = max(M * nmax, 10) + extra
+    s = Scheduler(nb, b, 4, nmax, M, 8, 256, policy, prefix_sharing=prefix, table_cap=64)
+    drive(s, stream, seed, check=_invariants)
+    out = {r.rid: r.gen for r in s.reqs.values()}
+    assert out == {rid: m for rid, _p, m, _g, _pl in stream}
+    assert s.num_free() == nb
+
+
+def test_constrained_never_preempts_and_hybrid_runs_more_requests():
+    """Short requests (fewer than N_max blocks each): constrained scheduling
+    keeps at most M requests running; hybrid scheduling fills the idle
+    blocks with requests that need no slot (Sec. 4.3)."""
+    b, nmax, M = 16, 4, 2
+    stream = [(r, 20, 20, -1, 0) for r in range(24)]
+    res = {}
+    for pol in (CONSTRAINED, HYBRID):
+        s = Scheduler(M * nmax + 8, b, 4, nmax, M, 16, 10000, pol)
+        steps = drive(s, stream, 0, arrivals=False)
+        dec = [len(o["batch"]) for o in steps if o["kind"] == "decode"]
+        res[pol] = (len(steps), max(dec), sum(len(o["preempted"]) for o in steps))
+    assert res[CONSTRAINED][1] == M and res[CONSTRAINED][2] == 0
+    assert res[HYBRID][1] > M
+    assert res[HYBRID][0] < res[CONSTRAINED][0]
