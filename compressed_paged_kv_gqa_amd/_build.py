@@ -1,5 +1,5 @@
 """Builds libzp.so in-tree: HIP kernels for gfx950 with hipcc, the host-only
-allocator/planner with g++, linked into one shared library next to this file.
+allocator, planner and scheduler with g++, linked into one shared library next to this file.
 
 Usage: ``python -m compressed_paged_kv_gqa_amd._build`` (or ``build()``).
 """
@@ -31,7 +31,7 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 HIP_SOURCES = ["zp_decode.hip", "zp_prefill.hip", "zp_score.hip", "zp_select.hip"]
-CXX_SOURCES = ["zp_host.cpp"]
+CXX_SOURCES = ["zp_host.cpp", "zp_sched.cpp"]
 
 
 def _run(cmd):

@@ -52,6 +52,38 @@ class ScoreParamsC(C.Structure):
                 ("flags", C.c_uint32)]
 
 
+ZP_SCHED_CONSTRAINED, ZP_SCHED_HYBRID = 0, 1
+ZP_STEP_IDLE, ZP_STEP_PREFILL, ZP_STEP_DECODE = 0, 1, 2
+ZP_REQ_WAITING, ZP_REQ_RUNNING, ZP_REQ_COMPRESSING, ZP_REQ_FINISHED, ZP_REQ_UNKNOWN = 0, 1, 2, 3, -1
+
+
+class SchedConfig(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "num_blocks", "block_size", "window", "n_max", "num_slots", "max_running",
+        "max_prefill_tokens", "table_cap", "policy", "prefix_sharing")]
+
+
+_OUT_ARRAYS = ("rid", "slot", "ctx", "len", "tables", "c_rid", "c_slot", "c_first", "c_nblocks",
+               "c_src", "c_dst", "c_new", "finished", "preempted")
+_OUT_COUNTS = ("kind", "n", "n_comp", "n_finished", "n_preempted", "n_blocked")
+
+
+class SchedStepOut(C.Structure):
+    _fields_ = ([(n, C.POINTER(C.c_int32)) for n in _OUT_ARRAYS] +
+                [(n, C.c_int32) for n in _OUT_COUNTS])
+
+
+class SchedStats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in (
+        "steps", "prefill_steps", "decode_steps", "idle_steps", "waiting", "running",
+        "compressing", "finished", "free_blocks", "slots_in_use", "prefill_tokens",
+        "decode_tokens", "compressions", "preemptions", "blocked")]
+
+
+class SchedReqInfo(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("state", "n", "gen", "slot", "compressed", "ntable")]
+
+
 _lib = None
 _P = C.c_void_p
 _I32P = C.POINTER(C.c_int32)
@@ -89,6 +121,15 @@ def _declare(lib):
         "zp_commit_compress": (C.c_int, [_P, _I32P, i32, _I32P, i32]),
         "zp_abort_compress": (C.c_int, [_P, _I32P, i32, _I32P, i32]),
         "zp_capacity": (C.c_int, [i64, i64, i64, i64, i32, C.POINTER(i64), C.POINTER(i64)]),
+        "zp_sched_create": (_P, [C.POINTER(SchedConfig)]),
+        "zp_sched_destroy": (None, [_P]),
+        "zp_sched_add": (C.c_int, [_P, i32, i32, i32, i32, i32]),
+        "zp_sched_step": (C.c_int, [_P, C.POINTER(SchedStepOut)]),
+        "zp_sched_compress_done": (C.c_int, [_P, i32]),
+        "zp_sched_get_stats": (C.c_int, [_P, C.POINTER(SchedStats)]),
+        "zp_sched_request": (C.c_int, [_P, i32, C.POINTER(SchedReqInfo), _P]),
+        "zp_sched_unfinished": (i32, [_P]),
+        "zp_sched_allocator": (_P, [_P]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -447,3 +488,116 @@ def zp_capacity(m_avail, m_kv, m_f, m_q, n_max):
     _check(lib().zp_capacity(m_avail, m_kv, m_f, m_q, n_max, C.byref(M), C.byref(N)),
            "zp_capacity")
     return M.value, N.value
+
+
+# --------------------------------------------------------------------------
+# Scheduler (zp_sched_*)
+# --------------------------------------------------------------------------
+
+class Step:
+    """Output of one zp_sched_step: numpy views of the caller-owned arrays
+    (valid until the next step) and the counts."""
+
+    def __init__(self, bufs, raw, table_cap, n_max):
+        self.kind = raw.kind
+        self.n = raw.n
+        self.n_comp = raw.n_comp
+        self.n_blocked = raw.n_blocked
+        n, nc = raw.n, raw.n_comp
+        self.rid, self.slot = bufs["rid"][:n], bufs["slot"][:n]
+        self.ctx, self.len = bufs["ctx"][:n], bufs["len"][:n]
+        self.tables = bufs["tables"].reshape(-1, table_cap)[:n]
+        self.c_rid, self.c_slot = bufs["c_rid"][:nc], bufs["c_slot"][:nc]
+        self.c_first, self.c_nblocks = bufs["c_first"][:nc], bufs["c_nblocks"][:nc]
+        self.c_src = bufs["c_src"].reshape(-1, table_cap)[:nc]
+        self.c_dst = bufs["c_dst"].reshape(-1, n_max - 1)[:nc]
+        self.c_new = bufs["c_new"].reshape(-1, n_max)[:nc]
+        self.finished = bufs["finished"][:raw.n_finished]
+        self.preempted = bufs["preempted"][:raw.n_preempted]
+
+    def as_dict(self):
+        """Plain-Python form (lists; slot None for no slot)."""
+        kinds = {ZP_STEP_IDLE: "idle", ZP_STEP_PREFILL: "prefill", ZP_STEP_DECODE: "decode"}
+        sl = lambda x: None if x < 0 else int(x)
+        batch = []
+        for i in range(self.n):
+            nt = int((self.tables[i] >= 0).sum())
+            batch.append(dict(rid=int(self.rid[i]), slot=sl(self.slot[i]), ctx=int(self.ctx[i]),
+                              len=int(self.len[i]), table=self.tables[i, :nt].tolist()))
+        comp = []
+        for i in range(self.n_comp):
+            nb = int(self.c_nblocks[i])
+            comp.append(dict(rid=int(self.c_rid[i]), slot=sl(self.c_slot[i]),
+                             first=bool(self.c_first[i]), src=self.c_src[i, :nb].tolist(),
+                             dst=self.c_dst[i].tolist(), new=self.c_new[i].tolist()))
+        return dict(kind=kinds[self.kind], batch=batch, comp=comp,
+                    finished=self.finished.tolist(), preempted=self.preempted.tolist(),
+                    blocked=int(self.n_blocked))
+
+
+class Scheduler:
+    """Binding of zp_sched (constrained / hybrid scheduling, Zipage Sec. 4.3
+    and Sec. 4.4). Arrays of the step output are allocated once, here."""
+
+    def __init__(self, num_blocks, block_size, window, n_max, num_slots, max_running,
+                 max_prefill_tokens, policy="hybrid", prefix_sharing=False, table_cap=64):
+        import numpy as np
+        pol = {"constrained": ZP_SCHED_CONSTRAINED, "hybrid": ZP_SCHED_HYBRID}[policy]
+        self.cfg = SchedConfig(num_blocks, block_size, window, n_max, num_slots, max_running,
+                               max_prefill_tokens, table_cap, pol, 1 if prefix_sharing else 0)
+        self._h = lib().zp_sched_create(C.byref(self.cfg))
+        if not self._h:
+            raise ZpError(ZP_EINVAL, lib().zp_last_error().decode())
+        R, cap = max_running, table_cap
+        sizes = dict(rid=R, slot=R, ctx=R, len=R, tables=R * cap, c_rid=R, c_slot=R, c_first=R,
+                     c_nblocks=R, c_src=R * cap, c_dst=R * (n_max - 1), c_new=R * n_max,
+                     finished=R, preempted=R)
+        self._bufs = {k: np.zeros(v, np.int32) for k, v in sizes.items()}
+        self._out = SchedStepOut()
+        for k, a in self._bufs.items():
+            setattr(self._out, k, a.ctypes.data_as(C.POINTER(C.c_int32)))
+        self.table_cap, self.n_max = table_cap, n_max
+
+    def close(self):
+        if self._h:
+            lib().zp_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0):
+        _check(lib().zp_sched_add(self._h, rid, prompt_len, max_new, prefix_group, prefix_len),
+               "zp_sched_add")
+
+    def step(self) -> Step:
+        _check(lib().zp_sched_step(self._h, C.byref(self._out)), "zp_sched_step")
+        return Step(self._bufs, self._out, self.table_cap, self.n_max)
+
+    def compress_done(self, rid):
+        _check(lib().zp_sched_compress_done(self._h, rid), "zp_sched_compress_done")
+
+    def stats(self):
+        st = SchedStats()
+        _check(lib().zp_sched_get_stats(self._h, C.byref(st)), "zp_sched_get_stats")
+        return {k: getattr(st, k) for k, _ in SchedStats._fields_}
+
+    def request(self, rid):
+        info = SchedReqInfo()
+        tab = (C.c_int32 * self.table_cap)()
+        _check(lib().zp_sched_request(self._h, rid, C.byref(info), tab), "zp_sched_request")
+        d = {k: getattr(info, k) for k, _ in SchedReqInfo._fields_}
+        d["table"] = list(tab[:info.ntable])
+        return d
+
+    def unfinished(self):
+        return lib().zp_sched_unfinished(self._h)
+
+    def refcount(self, block):
+        return lib().zp_block_refcount(lib().zp_sched_allocator(self._h), block)
+
+    def num_free(self):
+        return lib().zp_num_free(lib().zp_sched_allocator(self._h))

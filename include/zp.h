@@ -374,6 +374,153 @@ zp_status zp_abort_compress(zp_alloc* a, const int32_t* old_table, int32_t n_blo
 zp_status zp_capacity(int64_t m_avail, int64_t m_kv, int64_t m_f, int64_t m_q, int32_t n_max,
                       int64_t* max_concurrency, int64_t* num_blocks);
 
+/* ------------------------------------------------------------------------ */
+/* Request scheduler (Zipage Sec. 4.3 constrained and hybrid scheduling,     */
+/* Fig. 2; Sec. 4.4 shared prefixes and their preemption rule). Host-only,   */
+/* deterministic, not thread-safe. It owns a block pool of num_blocks ids    */
+/* and M = num_slots query-cache slots, and decides, step by step, which     */
+/* requests are prefilled or decoded, which are compressed (with their       */
+/* source and target tables) and which are preempted.                        */
+/*                                                                           */
+/* Policy, in the order one zp_sched_step applies it:                        */
+/*  (a) requests that became due in an earlier step (n = N b tokens,         */
+/*      N >= n_max, Sec. 4.1) get their compression planned with             */
+/*      zp_plan_compress's target rule; if fresh targets cannot be allocated */
+/*      (shared prefixes only) victims are preempted per (e), else it waits. */
+/*      Compressions are listed in the step output and must run after the    */
+/*      kernels of earlier steps and before those of this step;             */
+/*  (b) free slots go to the foremost slot-less requests among the first M   */
+/*      of the running queue (hybrid rules 1 and 3);                         */
+/*  (c) admission, first come first served: the head of the waiting queue is */
+/*      prefilled if its prompt (plus outputs, after a preemption) fits the  */
+/*      free blocks; with a slot if fewer than M requests run, else (hybrid  */
+/*      only) without one if its last prompt position needs no slot;         */
+/*      admission stops at the first request that does not fit. If any is   */
+/*      admitted, the step is a prefill step;                                */
+/*  (d) otherwise every running request that is neither compressing nor due  */
+/*      decodes one token, except a slot-less request whose next position    */
+/*      needs a slot (position p needs one iff p / b >= n_max - 1 and        */
+/*      p % b >= b - w: its query belongs to the window of a block whose end */
+/*      can trigger a compression; hybrid rule 2), and a request that needs  */
+/*      a new block while none is free and no victim remains (it waits:      */
+/*      constrained scheduling);                                             */
+/*  (e) victims of a block shortage, one at a time from the back of the      */
+/*      running queue: with prefix_sharing, the last request never           */
+/*      compressed and not being compressed (Sec. 4.4); otherwise, hybrid,   */
+/*      the last request without a slot (hybrid rule 4); constrained, none.  */
+/*      A preempted request frees its blocks and slot and goes to the front  */
+/*      of the waiting queue keeping its outputs (it is prefilled again over */
+/*      prompt + outputs).                                                   */
+/* Token accounting: a prefill produces one output token, each decode step   */
+/* appends the previous output token's K/V and produces one; a request       */
+/* finishes after max_new outputs and its blocks and slot are freed at once. */
+/* Shared prefixes: requests of one prefix group share their first           */
+/* prefix_len / b blocks, written by the first member admitted; members      */
+/* admitted in a later step take a reference and prefill only the rest       */
+/* (ctx > 0). A member stops holding the prefix when its compression is      */
+/* planned, when it finishes or when it is preempted. Block, slot and row    */
+/* ids are always taken lowest first.                                        */
+/* ------------------------------------------------------------------------ */
+
+typedef struct zp_sched zp_sched;
+
+enum { ZP_SCHED_CONSTRAINED = 0, ZP_SCHED_HYBRID = 1 };
+enum { ZP_STEP_IDLE = 0, ZP_STEP_PREFILL = 1, ZP_STEP_DECODE = 2 };
+enum { ZP_REQ_WAITING = 0, ZP_REQ_RUNNING = 1, ZP_REQ_COMPRESSING = 2, ZP_REQ_FINISHED = 3,
+       ZP_REQ_UNKNOWN = -1 };
+
+typedef struct {
+  int32_t num_blocks;          /* block pool size */
+  int32_t block_size;          /* b, a power of two */
+  int32_t window;              /* w, 1..b */
+  int32_t n_max;               /* N_max >= 2 */
+  int32_t num_slots;           /* M, query-cache slots, >= 1 */
+  int32_t max_running;         /* largest running queue (and batch), >= 1 */
+  int32_t max_prefill_tokens;  /* tokens of one prefill step (a longer first request still runs alone) */
+  int32_t table_cap;           /* largest block table, >= n_max */
+  int32_t policy;              /* ZP_SCHED_CONSTRAINED or ZP_SCHED_HYBRID */
+  int32_t prefix_sharing;      /* nonzero: share prefix blocks, preemption rule of Sec. 4.4 */
+} zp_sched_config;
+
+/* Output of one step. The caller provides every array with the capacity
+ * noted (R = max_running, C = table_cap); the step fills the counts.
+ * Batch entries (n of them) are in running-queue order:
+ *   rid, slot (-1 = none), ctx (tokens resident before the entry's tokens),
+ *   len (prefill: tokens to write, decode: 1), tables [R][C] (entry i's
+ *   block table in row i, -1 beyond its length). A prefill entry writes
+ *   positions ctx..ctx+len-1; a decode entry writes position ctx and attends
+ *   over ctx + 1 tokens.
+ * Compressions (n_comp): c_rid, c_slot, c_first (1 = first compression of
+ *   the request), c_nblocks (source table length), c_src [R][C] (-1 padded),
+ *   c_dst [R][n_max-1], c_new [R][n_max].
+ * finished / preempted: request ids (n_finished / n_preempted, <= R each).
+ * n_blocked: requests that could not decode this step (slot or block wait). */
+typedef struct {
+  int32_t* rid;
+  int32_t* slot;
+  int32_t* ctx;
+  int32_t* len;
+  int32_t* tables;
+  int32_t* c_rid;
+  int32_t* c_slot;
+  int32_t* c_first;
+  int32_t* c_nblocks;
+  int32_t* c_src;
+  int32_t* c_dst;
+  int32_t* c_new;
+  int32_t* finished;
+  int32_t* preempted;
+  int32_t kind;       /* ZP_STEP_* */
+  int32_t n;
+  int32_t n_comp;
+  int32_t n_finished;
+  int32_t n_preempted;
+  int32_t n_blocked;
+} zp_sched_step_out;
+
+typedef struct {
+  int64_t steps, prefill_steps, decode_steps, idle_steps;
+  int64_t waiting, running, compressing, finished;
+  int64_t free_blocks, slots_in_use;
+  int64_t prefill_tokens, decode_tokens, compressions, preemptions, blocked;
+} zp_sched_stats;
+
+typedef struct {
+  int32_t state;       /* ZP_REQ_* */
+  int32_t n;           /* resident tokens */
+  int32_t gen;         /* outputs produced */
+  int32_t slot;        /* -1 = none */
+  int32_t compressed;  /* 1 once a compression has committed */
+  int32_t ntable;      /* block table length */
+} zp_sched_req_info;
+
+/* NULL (with zp_last_error) on an invalid configuration. */
+zp_sched* zp_sched_create(const zp_sched_config* cfg);
+void zp_sched_destroy(zp_sched* s);
+/* Queues a request at the back of the waiting queue. prefix_group < 0: no
+ * shared prefix; else 0 <= prefix_len < prompt_len, one prefix_len per group.
+ * ZP_EINVAL for a repeated rid, bad lengths, or a prompt longer than
+ * table_cap blocks. */
+zp_status zp_sched_add(zp_sched* s, int32_t rid, int32_t prompt_len, int32_t max_new,
+                       int32_t prefix_group, int32_t prefix_len);
+/* One scheduling step (policy above). ZP_ESTATE if a table would exceed
+ * table_cap: the scheduler is then unusable and must be destroyed. */
+zp_status zp_sched_step(zp_sched* s, zp_sched_step_out* out);
+/* The compaction of request rid (listed by an earlier step) has completed:
+ * its table becomes c_new, blocks it no longer lists lose its reference, it
+ * holds (n_max - 1) b tokens and decodes again. ZP_ESTATE if rid is not
+ * compressing. */
+zp_status zp_sched_compress_done(zp_sched* s, int32_t rid);
+zp_status zp_sched_get_stats(const zp_sched* s, zp_sched_stats* out);
+/* State of request rid; table [host] (capacity table_cap) may be NULL. An
+ * unknown rid gives state ZP_REQ_UNKNOWN. */
+zp_status zp_sched_request(const zp_sched* s, int32_t rid, zp_sched_req_info* info,
+                           int32_t* table);
+/* Requests not finished yet. */
+int32_t zp_sched_unfinished(const zp_sched* s);
+/* The scheduler's block pool (read-only use: refcounts, free count). */
+const zp_alloc* zp_sched_allocator(const zp_sched* s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,7 +52,7 @@ Readings where the pages leave a step open (the product follows the same):
       prefilling them. A member stops holding the group's blocks when its
       compression is planned, when it finishes or when it is preempted; a
       group whose last holder stopped is forgotten.
-  R8  Ids (blocks, slots, batch rows) are taken lowest first.
+  R8  Ids (blocks, slots) are taken lowest first.
 """
 from __future__ import annotations
 
@@ -75,7 +75,6 @@ class Req:
         self.n = 0                   # tokens resident in the cache
         self.table = []
         self.slot = None
-        self.row = None
         self.state = WAITING
         self.compressed = False      # at least one compression committed
         self.due = False
@@ -129,9 +128,6 @@ class Scheduler:
     def _free_slot(self):
         return self._lowest_free({r.slot for r in self.running if r.slot is not None}, self.M)
 
-    def _free_row(self):
-        return self._lowest_free({r.row for r in self.running}, self.max_running)
-
     # ---------------------------------------------------------------- rules
     def needs_slot(self, p):
         """R3: writing position p needs a query-cache slot."""
@@ -154,7 +150,7 @@ class Scheduler:
     def _release(self, r):
         self._decref(r.table)
         self._leave_group(r)
-        r.table, r.slot, r.row, r.n, r.due = [], None, None, 0, False
+        r.table, r.slot, r.n, r.due = [], None, 0, False
         self.running.remove(r)
 
     def _preempt(self, v, out):
@@ -263,7 +259,7 @@ class Scheduler:
         r.plan = (list(r.table), dst, new)
         r.state = COMPRESSING
         r.due = False
-        out["comp"].append(dict(rid=r.rid, row=r.row, slot=r.slot, first=not r.compressed,
+        out["comp"].append(dict(rid=r.rid, slot=r.slot, first=not r.compressed,
                                 src=list(r.table), dst=dst, new=new))
 
     def _admit(self, out):
@@ -300,11 +296,10 @@ class Scheduler:
                 self.groups[r.group] = dict(blocks=table[:k], holders=1, step=self.t)
                 r.holds_prefix = True
             r.table = table
-            r.row = self._free_row()
             r.slot = self._free_slot() if with_slot else None
             r.state = RUNNING
             self.running.append(r)
-            out["batch"].append(dict(rid=r.rid, row=r.row, slot=r.slot, ctx=nshare * self.b,
+            out["batch"].append(dict(rid=r.rid, slot=r.slot, ctx=nshare * self.b,
                                      len=chunk, table=list(table)))
             tokens += chunk
         return bool(out["batch"])
@@ -339,5 +334,5 @@ class Scheduler:
                 r.table.append(self._alloc(1)[0])
             sched.append(r)
         for r in sched:
-            out["batch"].append(dict(rid=r.rid, row=r.row, slot=r.slot, ctx=r.n, len=1,
+            out["batch"].append(dict(rid=r.rid, slot=r.slot, ctx=r.n, len=1,
                                      table=list(r.table)))
