@@ -67,6 +67,13 @@ def parse_args():
                     help="skip the isolated compression-kernel measurement")
     ap.add_argument("--prefill-kernels", action="store_true",
                     help="only the isolated prefill measurement (one JSON line)")
+    ap.add_argument("--serve", action="store_true",
+                    help="only the scheduled serving run of a synthetic request stream "
+                         "(one JSON line)")
+    ap.add_argument("--serve-requests", type=int, default=256)
+    ap.add_argument("--serve-mem-gib", type=float, default=24.0,
+                    help="HBM given to K/V, F and the query cache (sets M and N_total)")
+    ap.add_argument("--serve-policies", default="hybrid,constrained")
     return ap.parse_args()
 
 
@@ -352,6 +359,93 @@ def prefill_kernel_bench(iters=5):
 # CPU baseline: the float64 oracle on a bounded sample of the same workload
 # --------------------------------------------------------------------------
 
+def serve_stream(n_req, seed):
+    """Synthetic offline request stream standing in for a reasoning benchmark:
+    short prompts (uniform 64..1024 tokens) and long, skewed outputs
+    (log-uniform 256..4096 tokens), all submitted at once."""
+    from compressed_paged_kv_gqa_amd import synth
+    g = synth.rng(seed, 9, 0, "serve_stream")
+    prompts = g.integers(64, 1025, n_req)
+    outs = np.exp(g.uniform(np.log(256), np.log(4096), n_req)).astype(np.int64)
+    return [(i, int(p), int(m)) for i, (p, m) in enumerate(zip(prompts, outs))]
+
+
+def serve_bench(n_req, mem_gib, policies):
+    """Every request of the stream through ServingEngine (zp_sched driving
+    prefill, decode and asynchronous compression) to completion, once per
+    policy. TPS = output tokens / wall time of the whole run."""
+    import torch
+    from compressed_paged_kv_gqa_amd import engine as E
+    from compressed_paged_kv_gqa_amd import zp
+    blk = L * 2 * HKV * BS * D * ELEM                 # K and V of one block, all layers
+    m_f = L * HKV * BS * 4                            # global score F of one block
+    m_q = L * HQ * W * (D * ELEM + 4)                 # query cache + its LSE per slot
+    M, NT = zp.zp_capacity(int(mem_gib * (1 << 30)), blk, m_f, m_q, NMAX)
+    stream = serve_stream(n_req, SEED)
+    cap = 16
+    maxpf = 16384
+    res = {"workload": f"{n_req} requests (prompts U[64,1024], outputs log-U[256,4096]) "
+                       f"through {L} Qwen3-8B-shaped attention layers, bf16, b={BS}, "
+                       f"N_max={NMAX}, w={W}",
+           "mem_gib": mem_gib, "M": M, "num_blocks": NT,
+           "output_tokens": sum(m for _i, _p, m in stream), "policies": {}}
+    for pol in policies:
+        geom = zp.CacheGeometry(num_layers=L, num_blocks=NT, block_size=BS, num_kv_heads=HKV,
+                                num_q_heads=HQ, head_dim=D, window=W, max_slots=M, n_max=NMAX,
+                                dtype="bf16")
+        eng = E.ServingEngine(geom, zp.ScoreParams(), max_running=min(n_req, 1024),
+                              table_cap=cap, max_prefill_tokens=maxpf, policy=pol,
+                              layer_stride=8, async_compress=True)
+        rows = max(maxpf, cap * BS)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(SEED)
+        pool = [torch.randn((2 * rows, h, D), generator=gen, device="cuda").to(torch.bfloat16)
+                for h in (HQ, HKV, HKV)]
+        state = {"t": 0, "T": 0}
+
+        def inputs(kind, st, layer):
+            if layer == 0:
+                state["T"] = int(st.len.sum()) if kind == zp.ZP_STEP_PREFILL else st.n
+                state["t"] += 1
+            o = (state["t"] * 7919 + layer * 131) % rows
+            T = state["T"]
+            return pool[0][o:o + T], pool[1][o:o + T], pool[2][o:o + T]
+
+        for i, p, m in stream:
+            eng.add(i, p, m)
+        log(f"serve {pol}: M={M} blocks={NT} requests={n_req}")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        kinds = {zp.ZP_STEP_IDLE: 0, zp.ZP_STEP_PREFILL: 0, zp.ZP_STEP_DECODE: 0}
+        max_run = 0
+        steps = 0
+        while eng.unfinished() > 0:
+            st = eng.step(inputs)
+            kinds[st.kind] += 1
+            steps += 1
+            if st.kind == zp.ZP_STEP_DECODE:
+                max_run = max(max_run, st.n)
+            if steps % 500 == 0:
+                log(f"  step {steps}: {eng.unfinished()} unfinished")
+        eng.poll(wait=True)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        assert eng.device_errors() == 0
+        stt = eng.sched.stats()
+        res["policies"][pol] = {
+            "tps": round(eng.generated / el, 1), "seconds": round(el, 2), "steps": steps,
+            "prefill_steps": kinds[zp.ZP_STEP_PREFILL], "decode_steps": kinds[zp.ZP_STEP_DECODE],
+            "idle_steps": kinds[zp.ZP_STEP_IDLE],
+            "avg_decode_batch": round(stt["decode_tokens"] / max(1, stt["decode_steps"]), 1),
+            "max_decode_batch": max_run, "compressions": stt["compressions"],
+            "preemptions": stt["preemptions"], "blocked": stt["blocked"],
+            "prefill_tokens": stt["prefill_tokens"]}
+        log(f"serve {pol}: {res['policies'][pol]}")
+        del eng, pool
+        torch.cuda.empty_cache()
+    return res
+
+
 def _oracle_worker(job):
     import threadpoolctl
     with threadpoolctl.threadpool_limits(1):
@@ -453,6 +547,10 @@ def main():
         return
     if args.prefill_kernels:
         print(json.dumps(prefill_kernel_bench()), flush=True)
+        return
+    if args.serve:
+        print(json.dumps(serve_bench(args.serve_requests, args.serve_mem_gib,
+                                     args.serve_policies.split(","))), flush=True)
         return
     from compressed_paged_kv_gqa_amd import synth
     phases = synth.rng(SEED, 3, 0, "lengths").integers(0, BS, B)

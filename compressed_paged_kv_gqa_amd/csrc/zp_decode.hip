@@ -236,11 +236,15 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h][u] = group_sum<LPR>(q.dot(h, kr[u]));
     if (base + CHUNK > t1 || off < 0) {
+      // Masked rows: slots past the sequence (never written, may hold
+      // anything, NaN included) or a bad block. Their weight is exactly 0
+      // and their V is zeroed, so 0 * garbage never enters the sum.
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const bool valid = off >= 0 && base + u * RPW + row < t1;
 #pragma unroll
         for (int h = 0; h < G; ++h) s[h][u] = valid ? s[h][u] : -INFINITY;
+        if (!valid) vr[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
     const float sc2 = P.qk_scale;

@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillParams P) {
   const int last = ctx + qlen - 1;
   int slot = -1;
   if (P.qslot) {
-    slot = P.qslot[r];
-    if (slot < 0 || slot >= P.max_slots) {
+    slot = P.qslot[r];  // negative: no query slot, nothing captured
+    if (slot >= P.max_slots) {
       if (tid == 0) flag_error(P.err, ZP_DEVERR_SLOT);
       slot = -1;
     }

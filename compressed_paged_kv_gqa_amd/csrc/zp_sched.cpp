@@ -177,12 +177,14 @@ zp_status try_compress(zp_sched* s, Req* r, zp_sched_step_out* out) {
   return ZP_OK;
 }
 
-void emit_entry(zp_sched* s, zp_sched_step_out* out, const Req* r, int32_t ctx, int32_t len) {
+void emit_entry(zp_sched* s, zp_sched_step_out* out, const Req* r, int32_t ctx, int32_t pos,
+                int32_t len) {
   const int32_t i = out->n++;
   const int32_t cap = s->cfg.table_cap;
   out->rid[i] = r->rid;
   out->slot[i] = r->slot;
   out->ctx[i] = ctx;
+  out->pos[i] = pos;
   out->len[i] = len;
   int32_t* row = out->tables + static_cast<int64_t>(i) * cap;
   const int32_t nt = static_cast<int32_t>(r->table.size());
@@ -235,7 +237,7 @@ zp_status admit(zp_sched* s, zp_sched_step_out* out, int32_t* admitted,
     r->slot = with_slot ? take_slot(s) : -1;
     r->state = ZP_REQ_RUNNING;
     s->running.push_back(r);
-    emit_entry(s, out, r, nshare * b, chunk);
+    emit_entry(s, out, r, nshare * b, nshare * b, chunk);
     batch->push_back(r);
     tokens += chunk;
     ++*admitted;
@@ -281,7 +283,7 @@ zp_status decode(zp_sched* s, zp_sched_step_out* out, std::vector<Req*>* sched) 
     }
     sched->push_back(r);
   }
-  for (Req* r : *sched) emit_entry(s, out, r, r->n, 1);
+  for (Req* r : *sched) emit_entry(s, out, r, r->n, r->prompt + r->gen - 1, 1);
   return ZP_OK;
 }
 
@@ -348,7 +350,8 @@ extern "C" zp_status zp_sched_add(zp_sched* s, int32_t rid, int32_t prompt_len, 
 }
 
 extern "C" zp_status zp_sched_step(zp_sched* s, zp_sched_step_out* out) {
-  if (!s || !out || !out->rid || !out->slot || !out->ctx || !out->len || !out->tables ||
+  if (!s || !out || !out->rid || !out->slot || !out->ctx || !out->pos || !out->len ||
+      !out->tables ||
       !out->c_rid || !out->c_slot || !out->c_first || !out->c_nblocks || !out->c_src ||
       !out->c_dst || !out->c_new || !out->finished || !out->preempted)
     return fail(ZP_EINVAL, "zp_sched_step: NULL argument");

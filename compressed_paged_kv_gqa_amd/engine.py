@@ -1,18 +1,20 @@
 """Host runtime around libzp: per-step decode of a batch of requests, the
-compression trigger, target planning, and asynchronous compression on a side
-HIP stream.
+compression trigger, target planning, asynchronous compression on a side HIP
+stream, and a serving loop driven by the library's scheduler.
 
 Zipage (arXiv 2603.08743): Sec. 4.1 (cap of N_max blocks, trigger after a
 step that leaves N >= N_max full blocks, reserved N_max-th block), Sec. 4.2
-(query-cache slot per request), Sec. 4.4 (shared prefix blocks and their
-target blocks), Sec. 4.5 (decoding requests do not wait for compression; a
-compressing request rejoins decode once its compression has finished),
-App. C.1 (compression runs layer_stride layers per launch).
+(query-cache slot per request), Sec. 4.3 and Fig. 2 (constrained / hybrid
+scheduling), Sec. 4.4 (shared prefix blocks and their target blocks),
+Sec. 4.5 (decoding requests do not wait for compression; a compressing
+request rejoins decode once its compression has finished), App. C.1
+(compression runs layer_stride layers per launch).
 
 Every numeric step runs in the library's kernels; this module only keeps
 block tables and per-request state and enqueues work (torch supplies device
-memory and streams). Scheduling policies (admission, preemption, hybrid query
-slots) are out of scope: requests are added explicitly.
+memory and streams). DecodeEngine takes requests added explicitly with their
+tokens; ServingEngine takes a request stream and lets zp_sched decide
+admission, query slots, preemption and compression.
 """
 from __future__ import annotations
 
@@ -41,6 +43,82 @@ class _Pending:
     plans: list                 # (old_table, dst, new_table)
     event: torch.cuda.Event
     buffers: list = field(default_factory=list)   # keep tensors alive until the event
+
+
+class Compressor:
+    """Enqueues compressions (Zipage Sec. 4.2 scoring, then top-k and
+    compaction, App. C.6) of a batch of requests, layer_stride layers per
+    launch (App. C.1), on a side stream that first waits for the work already
+    enqueued on the current stream (Sec. 4.5)."""
+
+    def __init__(self, cache: zp.PagedKVCache, params: zp.ScoreParams, layer_stride,
+                 stream=None, device="cuda"):
+        self.cache = cache
+        self.geom = cache.geom
+        self.params = params
+        self.layer_stride = max(1, min(layer_stride, cache.geom.num_layers))
+        self.stream = stream
+        self.device = device
+
+    def launch(self, src, dst, nblocks, slots, first, lse_ok, record=False):
+        """src [nreq][maxb] / dst [nreq][N_max-1] block tables, nblocks, query
+        slots, first-compression and window-LSE flags per request (host
+        values). Returns (done event, buffers to keep alive until it, scores,
+        kept indices); scores and kept cover every layer only when record."""
+        G = self.geom
+        b, keep = G.block_size, G.keep
+        nreq, maxb = src.shape
+        nd = G.n_max - 1
+        # one pinned int32 staging buffer: src tables | dst tables | N | slot |
+        # first | window log-sum-exp valid
+        meta = torch.zeros(nreq * (maxb + nd + 4), dtype=torch.int32).pin_memory()
+        m = meta.numpy()
+        m[:nreq * maxb] = np.asarray(src, np.int32).reshape(-1)
+        m[nreq * maxb:nreq * (maxb + nd)] = np.asarray(dst, np.int32).reshape(-1)
+        tail = m[nreq * (maxb + nd):].reshape(4, nreq)
+        tail[0] = nblocks
+        tail[1] = slots
+        tail[2] = [1 if f else 0 for f in first]
+        tail[3] = [1 if f else 0 for f in lse_ok]
+        stream = self.stream or torch.cuda.current_stream()
+        ready = torch.cuda.Event()
+        ready.record()
+        bufs = [meta]
+        with torch.cuda.stream(stream):
+            stream.wait_event(ready)
+            meta_d = meta.to(self.device, non_blocking=True)
+            o = nreq * maxb
+            src_d = meta_d[:o].view(nreq, maxb)
+            dst_d = meta_d[o:o + nreq * nd].view(nreq, nd)
+            o += nreq * nd
+            nblk_d = meta_d[o:o + nreq]
+            qslot_d = meta_d[o + nreq:o + 2 * nreq]
+            first_d = meta_d[o + 2 * nreq:o + 3 * nreq].to(torch.uint8)
+            lse_d = (meta_d[o + 3 * nreq:o + 4 * nreq].to(torch.uint8)
+                     if self.cache.qwin_lse is not None else None)
+            ls = self.layer_stride
+            nl = G.num_layers if record else ls     # recording keeps every layer
+            scores = torch.empty((nl, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
+                                 device=self.device)
+            use_f = self.params.use_global and self.cache.gscore is not None
+            f_new = torch.empty_like(scores) if use_f else None
+            kept = (torch.empty((G.num_layers, nreq, G.num_kv_heads, keep), dtype=torch.int32,
+                                device=self.device) if record else None)
+            sws = zp.new_workspace(zp.zp_score_workspace_size(G, ls, nreq, maxb), self.device)
+            cws = zp.new_workspace(zp.zp_select_workspace_size(G, ls, nreq, keep), self.device)
+            for lb in range(0, G.num_layers, ls):
+                lc = min(ls, G.num_layers - lb)
+                sl = slice(lb, lb + lc) if record else slice(0, lc)
+                sc, fn = scores[sl], (f_new[sl] if use_f else None)
+                zp.zp_score_tokens(self.cache, self.params, lb, lc, src_d, nblk_d, maxb, qslot_d,
+                                   first_d, sc, fn, sws, stream=stream, window_lse_valid=lse_d)
+                zp.zp_select_compact(self.cache, lb, lc, sc, src_d, nblk_d, maxb, dst_d, keep,
+                                     kept[sl] if kept is not None else None, cws,
+                                     stream=stream, f_new=fn)
+            done = torch.cuda.Event()
+            done.record(stream)
+            bufs += [meta_d, first_d, lse_d, scores, f_new, sws, cws]
+        return done, bufs, scores, kept
 
 
 class DecodeEngine:
@@ -78,6 +156,8 @@ class DecodeEngine:
         self.dec_ws = zp.new_workspace(zp.zp_decode_workspace_size(geom, max_seqs,
                                                                     self.max_seq_len), device)
         self.side = torch.cuda.Stream(device=device)
+        self.compressor = Compressor(self.cache, params, self.layer_stride,
+                                     self.side if async_compress else None, device)
         self.pending: list[_Pending] = []
         self.compressions = 0
         self.decoded_tokens = 0
@@ -231,13 +311,11 @@ class DecodeEngine:
 
     def compress(self, sids):
         G = self.geom
-        b, n_max = G.block_size, G.n_max
-        keep = G.keep
         plans, ok = [], []
         for s in sids:
             r = self.reqs[s]
             try:
-                dst, new, _ = self.alloc.plan_compress(r.table, n_max)
+                dst, new, _ = self.alloc.plan_compress(r.table, G.n_max)
             except zp.NoBlocks:
                 continue          # stays uncompressed; a scheduler would preempt
             plans.append((list(r.table), dst, new))
@@ -247,63 +325,17 @@ class DecodeEngine:
             return
         nreq = len(ok)
         maxb = max(len(p[0]) for p in plans)
-        nd = n_max - 1
-        # one pinned int32 staging buffer: src tables | dst tables | N | slot |
-        # first | window log-sum-exp valid
-        meta = torch.zeros(nreq * (maxb + nd + 4), dtype=torch.int32).pin_memory()
-        m = meta.numpy()
-        src = m[:nreq * maxb].reshape(nreq, maxb)
-        dst = m[nreq * maxb:nreq * (maxb + nd)].reshape(nreq, nd)
-        tail = m[nreq * (maxb + nd):].reshape(4, nreq)
+        src = np.zeros((nreq, maxb), np.int32)
         for i, p in enumerate(plans):
             src[i, :len(p[0])] = p[0]
-            dst[i] = p[1]
-        tail[0] = [len(p[0]) for p in plans]
-        tail[1] = ok
-        tail[2] = [1 if self.reqs[s].first else 0 for s in ok]
         # every window row (the last w positions) carries its log-sum-exp
-        tail[3] = [1 if self.reqs[s].n - G.window >= self.reqs[s].lse_from else 0 for s in ok]
-        first = tail[2].astype(np.uint8)
-        stream = self.side if self.async_compress else torch.cuda.current_stream()
-        ready = torch.cuda.Event()
-        ready.record()
-        bufs = [meta]
-        with torch.cuda.stream(stream):
-            stream.wait_event(ready)
-            meta_d = meta.to(self.device, non_blocking=True)
-            o = nreq * maxb
-            src_d = meta_d[:o].view(nreq, maxb)
-            dst_d = meta_d[o:o + nreq * nd].view(nreq, nd)
-            o += nreq * nd
-            nblk_d = meta_d[o:o + nreq]
-            qslot_d = meta_d[o + nreq:o + 2 * nreq]
-            first_d = meta_d[o + 2 * nreq:o + 3 * nreq].to(torch.uint8)
-            lse_d = (meta_d[o + 3 * nreq:o + 4 * nreq].to(torch.uint8) if self.window_lse
-                     else None)
-            ls = self.layer_stride
-            nl = G.num_layers if self.record else ls     # recording keeps every layer
-            scores = torch.empty((nl, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
-                                 device=self.device)
-            use_f = self.params.use_global and self.cache.gscore is not None
-            f_new = torch.empty_like(scores) if use_f else None
-            kept = (torch.empty((G.num_layers, nreq, G.num_kv_heads, keep), dtype=torch.int32,
-                                device=self.device) if self.record else None)
-            sws = zp.new_workspace(zp.zp_score_workspace_size(G, ls, nreq, maxb), self.device)
-            cws = zp.new_workspace(zp.zp_select_workspace_size(G, ls, nreq, keep), self.device)
-            for lb in range(0, G.num_layers, ls):
-                lc = min(ls, G.num_layers - lb)
-                sl = slice(lb, lb + lc) if self.record else slice(0, lc)
-                sc, fn = scores[sl], (f_new[sl] if use_f else None)
-                zp.zp_score_tokens(self.cache, self.params, lb, lc, src_d, nblk_d, maxb, qslot_d,
-                                   first_d, sc, fn, sws, stream=stream, window_lse_valid=lse_d)
-                zp.zp_select_compact(self.cache, lb, lc, sc, src_d, nblk_d, maxb, dst_d, keep,
-                                     kept[sl] if kept is not None else None, cws,
-                                     stream=stream, f_new=fn)
-            done = torch.cuda.Event()
-            done.record(stream)
-            bufs += [meta_d, first_d, lse_d, scores, f_new, sws, cws]
-            if self.record:
-                self.log.append((list(ok), first.copy(), scores, kept))
+        lse_ok = [self.reqs[s].n - G.window >= self.reqs[s].lse_from for s in ok]
+        first = [self.reqs[s].first for s in ok]
+        done, bufs, scores, kept = self.compressor.launch(
+            src, np.array([p[1] for p in plans], np.int32), [len(p[0]) for p in plans], ok,
+            first, lse_ok, record=self.record)
+        if self.record:
+            self.log.append((list(ok), np.array(first, np.uint8), scores, kept))
         self.pending.append(_Pending(ok, plans, done, bufs))
         self.compressions += nreq
         if not self.async_compress:
@@ -341,3 +373,170 @@ class DecodeEngine:
         K = self.cache.k[layer, idx, head].reshape(-1, self.geom.head_dim)[:r.n]
         V = self.cache.v[layer, idx, head].reshape(-1, self.geom.head_dim)[:r.n]
         return K, V
+
+
+class ServingEngine:
+    """Requests driven by the library's scheduler (zp_sched: constrained or
+    hybrid scheduling with query slots, preemption and shared prefixes,
+    Zipage Sec. 4.3 / Fig. 2 / Sec. 4.4) through the prefill, decode and
+    compression kernels.
+
+    One call of step() asks the scheduler for a step and enqueues its work:
+    first the compressions it planned (on the side stream, after the kernels
+    of earlier steps, Sec. 4.5), then either one prefill of the admitted
+    prompt chunks or one decode token of every scheduled request, layer by
+    layer. Compressions whose event has completed are committed at the start
+    of the next step. There are no weights: `inputs` supplies each layer's
+    q / k / v rows for a step (see step()), and attention outputs go to
+    buffers owned here (`out_prefill`, `out_decode`, the last step's values).
+    """
+
+    def __init__(self, geom: zp.CacheGeometry, params: zp.ScoreParams, max_running, table_cap,
+                 max_prefill_tokens, policy="hybrid", prefix_sharing=False, layer_stride=8,
+                 async_compress=True, with_global=True, device="cuda", keep_layer_outputs=False):
+        G = geom
+        self.geom = G
+        self.device = device
+        self.R, self.cap = max_running, table_cap
+        self.max_seq_len = table_cap * G.block_size
+        self.max_prefill = max_prefill_tokens
+        self.cache = zp.PagedKVCache(G, device=device, with_global=with_global,
+                                     with_window_lse=True)
+        self.sched = zp.Scheduler(G.num_blocks, G.block_size, G.window, G.n_max, G.max_slots,
+                                  max_running, max_prefill_tokens, policy,
+                                  prefix_sharing=prefix_sharing, table_cap=table_cap)
+        self.async_compress = async_compress
+        self.side = torch.cuda.Stream(device=device)
+        self.compressor = Compressor(self.cache, params, layer_stride,
+                                     self.side if async_compress else None, device)
+        # the decode batch varies step by step and smaller batches split the
+        # sequences further: size the workspace for the largest need
+        ws = max(zp.zp_decode_workspace_size(G, nb, self.max_seq_len)
+                 for nb in range(1, max_running + 1))
+        self.dec_ws = zp.new_workspace(ws, device)
+        self.pf_ws = zp.new_workspace(zp.zp_prefill_workspace_size(G, max_running), device)
+        # pinned staging ring for step metadata: tables [R][cap] | a [R] | slot [R] | cu [R+1]
+        n_meta = max_running * (table_cap + 3) + 1
+        self._ring = [(torch.zeros(n_meta, dtype=torch.int32).pin_memory(), torch.cuda.Event())
+                      for _ in range(4)]
+        self._ring_i = 0
+        self.meta_d = torch.zeros(n_meta, dtype=torch.int32, device=device)
+        dt = G.torch_dtype()
+        nl = G.num_layers if keep_layer_outputs else 1
+        # a request longer than max_prefill_tokens is prefilled alone
+        self.max_chunk = max(max_prefill_tokens, self.max_seq_len)
+        self.out_prefill = torch.empty((nl, self.max_chunk, G.num_q_heads, G.head_dim),
+                                       dtype=dt, device=device)
+        self.out_decode = torch.empty((nl, max_running, G.num_q_heads, G.head_dim), dtype=dt,
+                                      device=device)
+        self.pending = []           # (rids, event, buffers)
+        self.generated = 0          # output tokens produced
+        self.steps = 0
+
+    # ---------------------------------------------------------------- intake
+    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0):
+        self.sched.add(rid, prompt_len, max_new, prefix_group, prefix_len)
+
+    def unfinished(self):
+        return self.sched.unfinished()
+
+    # ------------------------------------------------------------------ step
+    def _stage(self, st, first_col):
+        """Uploads the step's tables, per-entry values and slots; returns the
+        device views (tables [n][cap], a [n], slot [n], cu [n+1])."""
+        n, cap = st.n, self.cap
+        buf, ev = self._ring[self._ring_i]
+        self._ring_i = (self._ring_i + 1) % len(self._ring)
+        ev.synchronize()
+        m = buf.numpy()
+        m[:n * cap] = st.tables.reshape(-1)
+        m[n * cap:n * cap + n] = first_col
+        m[n * cap + n:n * cap + 2 * n] = st.slot
+        cu = m[n * cap + 2 * n:n * cap + 3 * n + 1]
+        cu[0] = 0
+        np.cumsum(st.len, out=cu[1:])
+        tot = n * (cap + 3) + 1
+        self.meta_d[:tot].copy_(buf[:tot], non_blocking=True)
+        ev.record()
+        d = self.meta_d
+        return (d[:n * cap].view(n, cap), d[n * cap:n * cap + n],
+                d[n * cap + n:n * cap + 2 * n], d[n * cap + 2 * n:n * cap + 3 * n + 1])
+
+    def _compress(self, st):
+        nc = st.n_comp
+        maxb = int(st.c_nblocks.max())
+        src = np.ascontiguousarray(st.c_src[:, :maxb])
+        # every window row is written by a kernel that holds the request's
+        # slot, so the window log-sum-exp is always valid here
+        done, bufs, _s, _k = self.compressor.launch(
+            src, st.c_dst.copy(), st.c_nblocks.copy(), st.c_slot.copy(),
+            st.c_first.astype(bool), [True] * nc)
+        self.pending.append((st.c_rid.tolist(), done, bufs))
+        if not self.async_compress:
+            self.poll(wait=True)
+
+    def poll(self, wait=False):
+        """Commits compressions whose kernels have finished (all if wait)."""
+        still = []
+        for rids, ev, bufs in self.pending:
+            if wait:
+                ev.synchronize()
+            elif not ev.query():
+                still.append((rids, ev, bufs))
+                continue
+            for r in rids:
+                self.sched.compress_done(r)
+        self.pending = still
+
+    def step(self, inputs):
+        """One scheduler step. inputs(kind, st, layer) returns (q, k, v) for
+        the step's tokens in batch-entry order: [T][h_q][d], [T][h_kv][d],
+        [T][h_kv][d] with T = sum(st.len) (prefill) or st.n (decode).
+        Returns the scheduler's Step."""
+        self.poll()
+        st = self.sched.step()
+        self.steps += 1
+        if st.n_comp:
+            self._compress(st)
+        G = self.geom
+        if st.kind == zp.ZP_STEP_PREFILL:
+            tab, ctx, slot, cu = self._stage(st, st.ctx)
+            T = int(st.len.sum())
+            mq = int(st.len.max())
+            if T > self.max_chunk:
+                raise RuntimeError(f"prefill of {T} tokens exceeds {self.max_chunk}")
+            for l in range(G.num_layers):
+                q, k, v = inputs(st.kind, st, l)
+                o = self.out_prefill[l if self.out_prefill.shape[0] > 1 else 0, :T]
+                zp.zp_paged_prefill(self.cache, l, q, k, v, cu, ctx, mq, tab, slot, o, None,
+                                    self.pf_ws)
+            self.generated += st.n
+        elif st.kind == zp.ZP_STEP_DECODE:
+            tab, lens, slot, _cu = self._stage(st, st.ctx + 1)
+            for l in range(G.num_layers):
+                q, k, v = inputs(st.kind, st, l)
+                o = self.out_decode[l if self.out_decode.shape[0] > 1 else 0, :st.n]
+                zp.zp_paged_decode(self.cache, l, q, k, v, tab, lens, self.max_seq_len, slot, o,
+                                   None, self.dec_ws)
+            self.generated += st.n
+        elif self.pending:
+            # nothing to run until a compression commits
+            self.pending[0][1].synchronize()
+        elif st.n_comp == 0 and self.sched.unfinished() > 0:
+            raise RuntimeError("scheduler made no progress: every request waits")
+        return st
+
+    def run(self, inputs, max_steps=1 << 30):
+        """Steps until every request has finished; returns the step count."""
+        n = 0
+        while (self.sched.unfinished() > 0 or self.pending) and n < max_steps:
+            if self.sched.unfinished() == 0:
+                self.poll(wait=True)
+                break
+            self.step(inputs)
+            n += 1
+        return n
+
+    def device_errors(self):
+        """Device error bits of the decode and prefill workspaces."""
+        return zp.zp_workspace_errors(self.dec_ws) | zp.zp_workspace_errors(self.pf_ws)

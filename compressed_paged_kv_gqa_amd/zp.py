@@ -63,7 +63,7 @@ class SchedConfig(C.Structure):
         "max_prefill_tokens", "table_cap", "policy", "prefix_sharing")]
 
 
-_OUT_ARRAYS = ("rid", "slot", "ctx", "len", "tables", "c_rid", "c_slot", "c_first", "c_nblocks",
+_OUT_ARRAYS = ("rid", "slot", "ctx", "pos", "len", "tables", "c_rid", "c_slot", "c_first", "c_nblocks",
                "c_src", "c_dst", "c_new", "finished", "preempted")
 _OUT_COUNTS = ("kind", "n", "n_comp", "n_finished", "n_preempted", "n_blocked")
 
@@ -287,7 +287,15 @@ def zp_paged_decode(cache: PagedKVCache, layer, q, k_new, v_new, block_tables, s
     _need(seq_lens, torch.int32, "seq_lens")
     _need(qslot, torch.int32, "qslot")
     _need(lse, torch.float32, "lse")
-    batch = q.shape[0]
+    batch, hq, hkv, d = q.shape[0], geom.num_q_heads, geom.num_kv_heads, geom.head_dim
+    for t, n, h in ((q, "q", hq), (out, "out", hq), (k_new, "k_new", hkv), (v_new, "v_new", hkv)):
+        if tuple(t.shape) != (batch, h, d) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous [{batch}][{h}][{d}] tensor, got {tuple(t.shape)}")
+    if block_tables.shape[0] < batch or seq_lens.shape[0] < batch or (
+            qslot is not None and qslot.shape[0] < batch):
+        raise ValueError("block_tables, seq_lens and qslot need a row per batch entry")
+    if lse is not None and (tuple(lse.shape) != (batch, hq) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous [{batch}][{hq}] tensor")
     _check(lib().zp_paged_decode(
         C.byref(geom.c()), C.byref(cache.c()), layer, batch, q.data_ptr(), k_new.data_ptr(),
         v_new.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
@@ -315,6 +323,13 @@ def zp_paged_prefill(cache: PagedKVCache, layer, q, k_new, v_new, cu_seqlens, ct
     nreq = ctx_lens.shape[0]
     if cu_seqlens.shape[0] != nreq + 1:
         raise ValueError("cu_seqlens must hold nreq + 1 offsets")
+    T, hq, hkv, d = q.shape[0], geom.num_q_heads, geom.num_kv_heads, geom.head_dim
+    # the kernels take cu_seqlens[nreq] == T on trust: the buffers must agree
+    for t, n, h in ((q, "q", hq), (out, "out", hq), (k_new, "k_new", hkv), (v_new, "v_new", hkv)):
+        if tuple(t.shape) != (T, h, d) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous [{T}][{h}][{d}] tensor, got {tuple(t.shape)}")
+    if lse is not None and (tuple(lse.shape) != (T, hq) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous [{T}][{hq}] tensor")
     _check(lib().zp_paged_prefill(
         C.byref(geom.c()), C.byref(cache.c()), layer, nreq, q.data_ptr(), k_new.data_ptr(),
         v_new.data_ptr(), cu_seqlens.data_ptr(), ctx_lens.data_ptr(), int(max_q_len),
@@ -506,6 +521,7 @@ class Step:
         n, nc = raw.n, raw.n_comp
         self.rid, self.slot = bufs["rid"][:n], bufs["slot"][:n]
         self.ctx, self.len = bufs["ctx"][:n], bufs["len"][:n]
+        self.pos = bufs["pos"][:n]
         self.tables = bufs["tables"].reshape(-1, table_cap)[:n]
         self.c_rid, self.c_slot = bufs["c_rid"][:nc], bufs["c_slot"][:nc]
         self.c_first, self.c_nblocks = bufs["c_first"][:nc], bufs["c_nblocks"][:nc]
@@ -523,7 +539,8 @@ class Step:
         for i in range(self.n):
             nt = int((self.tables[i] >= 0).sum())
             batch.append(dict(rid=int(self.rid[i]), slot=sl(self.slot[i]), ctx=int(self.ctx[i]),
-                              len=int(self.len[i]), table=self.tables[i, :nt].tolist()))
+                              pos=int(self.pos[i]), len=int(self.len[i]),
+                              table=self.tables[i, :nt].tolist()))
         comp = []
         for i in range(self.n_comp):
             nb = int(self.c_nblocks[i])
@@ -549,7 +566,7 @@ class Scheduler:
         if not self._h:
             raise ZpError(ZP_EINVAL, lib().zp_last_error().decode())
         R, cap = max_running, table_cap
-        sizes = dict(rid=R, slot=R, ctx=R, len=R, tables=R * cap, c_rid=R, c_slot=R, c_first=R,
+        sizes = dict(rid=R, slot=R, ctx=R, pos=R, len=R, tables=R * cap, c_rid=R, c_slot=R, c_first=R,
                      c_nblocks=R, c_src=R * cap, c_dst=R * (n_max - 1), c_new=R * n_max,
                      finished=R, preempted=R)
         self._bufs = {k: np.zeros(v, np.int32) for k, v in sizes.items()}

@@ -168,10 +168,11 @@ size_t zp_prefill_workspace_size(const zp_geom* geom, int32_t nreq);
  * ctx_lens[r] tokens (for example shared prefix blocks) are already in the
  * cache. For each new token i at position p:
  *   1. k_new[i], v_new[i] are written to block block_tables[r][p/b], slot p%b;
- *   2. if qslot != NULL and p lies in the block of the chunk's last token at
- *      slot p%b >= b-w, q[i] is written to row p%b-(b-w) of query-cache slot
- *      qslot[r] (Zipage Sec. 4.2), and its log-sum-exp to cache->qwin_lse if
- *      that is not NULL;
+ *   2. if qslot != NULL, qslot[r] >= 0 and p lies in the block of the
+ *      chunk's last token at slot p%b >= b-w, q[i] is written to row
+ *      p%b-(b-w) of query-cache slot qslot[r] (Zipage Sec. 4.2), and its
+ *      log-sum-exp to cache->qwin_lse if that is not NULL (a negative slot:
+ *      a request scheduled without a query slot, nothing is captured);
  *   3. out[i][j] = sum_{t<=p} softmax_t(q[i][j] . k_t / sqrt(d)) v_t over kv-head
  *      j/g, and lse[i][j] = log sum_{t<=p} exp(.) if lse != NULL.
  *
@@ -446,10 +447,12 @@ typedef struct {
  * noted (R = max_running, C = table_cap); the step fills the counts.
  * Batch entries (n of them) are in running-queue order:
  *   rid, slot (-1 = none), ctx (tokens resident before the entry's tokens),
+ *   pos (index of the entry's first token in the request's token sequence,
+ *   e.g. for position encodings; equal to ctx until the first compression),
  *   len (prefill: tokens to write, decode: 1), tables [R][C] (entry i's
  *   block table in row i, -1 beyond its length). A prefill entry writes
- *   positions ctx..ctx+len-1; a decode entry writes position ctx and attends
- *   over ctx + 1 tokens.
+ *   cache positions ctx..ctx+len-1; a decode entry writes cache position
+ *   ctx and attends over ctx + 1 tokens.
  * Compressions (n_comp): c_rid, c_slot, c_first (1 = first compression of
  *   the request), c_nblocks (source table length), c_src [R][C] (-1 padded),
  *   c_dst [R][n_max-1], c_new [R][n_max].
@@ -459,6 +462,7 @@ typedef struct {
   int32_t* rid;
   int32_t* slot;
   int32_t* ctx;
+  int32_t* pos;
   int32_t* len;
   int32_t* tables;
   int32_t* c_rid;

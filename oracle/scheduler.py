@@ -26,6 +26,9 @@ Readings where the pages leave a step open (the product follows the same):
       the next one. A request finishes when it has produced max_new tokens.
       A preempted request keeps its outputs and is prefilled again over
       prompt + outputs (recomputation), at the front of the waiting queue.
+      A batch entry carries ctx (tokens resident before it: its cache
+      position) and pos (its first token's index in the request's token
+      sequence); they differ once the request has been compressed.
   R3  "Needs a query slot": writing the token at position p (0-based) needs
       a slot iff p lies in block N_max - 1 or later and in the last w slots
       of its block (its query is a window query of a block whose end can
@@ -300,7 +303,7 @@ class Scheduler:
             r.state = RUNNING
             self.running.append(r)
             out["batch"].append(dict(rid=r.rid, slot=r.slot, ctx=nshare * self.b,
-                                     len=chunk, table=list(table)))
+                                     pos=nshare * self.b, len=chunk, table=list(table)))
             tokens += chunk
         return bool(out["batch"])
 
@@ -334,5 +337,5 @@ class Scheduler:
                 r.table.append(self._alloc(1)[0])
             sched.append(r)
         for r in sched:
-            out["batch"].append(dict(rid=r.rid, slot=r.slot, ctx=r.n, len=1,
-                                     table=list(r.table)))
+            out["batch"].append(dict(rid=r.rid, slot=r.slot, ctx=r.n, pos=r.prompt + r.gen - 1,
+                                     len=1, table=list(r.table)))

@@ -29,8 +29,8 @@ CASES = [
 ]
 
 
-def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=()):
-    announce(f"decode dtype={dtype} d={d} hq={h_q} hkv={h_kv} b={b} lens={lens}")
+def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=(), poison_tail=False):
+    announce(f"decode dtype={dtype} d={d} hq={h_q} hkv={h_kv} b={b} lens={lens} poison={poison_tail}")
     B = len(lens)
     nb = [-(-n // b) for n in lens]
     stride = max(nb) + 1
@@ -40,6 +40,14 @@ def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=()):
                             dtype=dtype)
     hc = HostCache(geom, seed, 1)
     tab = random_tables(seed, 1, nb, pool, stride)
+    if poison_tail:
+        # slots at and after the new token's, in its block, were never
+        # written: NaN there must not reach the output
+        for r, n in enumerate(lens):
+            pg = tab[r][(n - 1) // b]
+            hc.K[:, pg, :, (n - 1) % b:] = np.nan
+            hc.V[:, pg, :, (n - 1) % b:] = np.nan
+        hc.upload()
     g = synth.rng(seed, 1, layer, "step_q")
     q = synth.cast(g.standard_normal((B, h_q, d)), dtype)
     kn = synth.cast(g.standard_normal((B, h_kv, d)), dtype)
@@ -98,6 +106,14 @@ def _run_case(dtype, d, h_q, h_kv, b, w, lens, seed=3, layer=1, skip_rows=()):
     np.testing.assert_array_equal(V_after, expV)
     np.testing.assert_array_equal(Q_after, expQ)
     np.testing.assert_array_equal(QL_after, expQL)   # window rows' lse next to their query
+
+
+def test_decode_ignores_unwritten_slots():
+    """Slots of the last block past the sequence hold whatever was there
+    before (here NaN): masked tokens contribute nothing, not even NaN."""
+    _run_case("bf16", 64, 4, 2, 16, 8, [13, 16, 17, 200, 1], poison_tail=True)
+    _run_case("f32", 64, 4, 1, 16, 8, [1, 17, 30, 16, 300], poison_tail=True)
+    _run_case("bf16", 128, 32, 8, 256, 16, [1, 300, 2047, 4000], poison_tail=True)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2]//c[3]}-b{c[4]}" for c in CASES])

@@ -48,7 +48,7 @@ def _sample_rows(rng, qlen, b, w, ctx, k=24):
     return sorted(rows)
 
 
-def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24):
+def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24, noslot=None):
     announce(f"prefill dtype={dtype} d={d} hq={h_q} hkv={h_kv} b={b} w={w} q={q_lens} ctx={ctx_lens}")
     nreq = len(q_lens)
     g = h_q // h_kv
@@ -70,6 +70,8 @@ def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24
     vn = synth.cast(gen.standard_normal((T, h_kv, d)), dtype)
     cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     qslot = np.arange(nreq, dtype=np.int32) + 1
+    if noslot is not None:
+        qslot[noslot] = -1          # scheduled without a query slot
     dt = geom.torch_dtype()
     tq = torch.from_numpy(q).to(dt).cuda()
     tk = torch.from_numpy(kn).to(dt).cuda()
@@ -114,6 +116,10 @@ def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24
         # window rows of the final block: query and lse captured, nothing else
         last = ctx + n - 1
         slot = qslot[r]
+        if slot < 0:
+            np.testing.assert_array_equal(qwin[layer, r + 1], qwin0[layer, r + 1])
+            assert np.all(qlse[layer, r + 1] == 5.0)
+            continue
         for off in range(b - w, b):
             p = (last // b) * b + off
             u = off - (b - w)
@@ -133,6 +139,11 @@ def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2] // c[3]}-b{c[4]}" for c in CASES])
 def test_prefill_parity(case):
     _run(*case)
+
+
+def test_prefill_without_query_slot_captures_nothing():
+    _run("bf16", 128, 16, 2, 64, 8, [130, 100, 70], [0, 0, 64], noslot=1)
+    _run("f32", 64, 4, 1, 16, 8, [40, 37], [0, 16], noslot=0)
 
 
 def test_prefill_reports_bad_block_ids_without_faulting():

@@ -63,12 +63,17 @@ def test_hybrid_slotless_request_blocks_at_the_window_then_takes_the_slot():
         ("decode", [(1, 0, 17, 1, [1, 2])], [], [], [], 0),
         ("decode", [(1, 0, 18, 1, [1, 2])], [], [1], [], 0),
     ]
+    pos = []
     for w in want:
         o = s.step()
         assert _brief(o) == w, s.t
+        pos += [(e["rid"], e["pos"]) for e in o["batch"]]
         for c in o["comp"]:
             s.compress_done(c["rid"])
     assert s.unfinished() == 0
+    # token indices run on across the compression (cache position 16 holds
+    # token 32), and the prefill of request 1 starts at token 0
+    assert [p for r, p in pos if r == 1] == [0, 26, 27] + list(range(28, 35))
 
 
 def test_constrained_waits_for_blocks_released_by_compression():
@@ -241,7 +246,10 @@ def _invariants(s, o):
     assert len(s.running) <= s.max_running
     for e in o["batch"]:
         r = s.reqs[e["rid"]]
+        if not r.compressed:
+            assert e["pos"] == e["ctx"]
         if o["kind"] == "decode":
+            assert e["pos"] == r.prompt + r.gen - 2          # gen counts this step's output
             assert e["slot"] is not None or not s.needs_slot(e["ctx"])
             assert e["ctx"] < len(e["table"]) * b
         else:
