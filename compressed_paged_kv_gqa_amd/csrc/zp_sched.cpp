@@ -26,6 +26,7 @@ namespace {
 
 struct Req {
   int32_t rid = 0, prompt = 0, max_new = 0, group = -1, prefix_len = 0;
+  int32_t n_max = 0;  // this request's cap (blocks kept + the reserved one)
   int32_t gen = 0;  // outputs produced
   int32_t n = 0;    // resident tokens
   int32_t slot = -1;
@@ -52,6 +53,8 @@ struct zp_sched {
   std::map<int32_t, Group> groups;
   std::map<int32_t, int32_t> group_len;
   std::vector<uint8_t> slot_used;
+  int64_t slot_caps = 0;  // sum of n_max over the slot holders
+  int32_t slot_count = 0;
   int64_t t = 0;
   int32_t unfinished = 0;
   zp_sched_stats st{};
@@ -65,28 +68,37 @@ namespace {
 
 int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
-bool needs_slot(const zp_sched* s, int32_t p) {
+bool needs_slot(const zp_sched* s, const Req* r, int32_t p) {
   const int32_t b = s->cfg.block_size;
-  return p / b >= s->cfg.n_max - 1 && p % b >= b - s->cfg.window;
+  return p / b >= r->n_max - 1 && p % b >= b - s->cfg.window;
 }
 
 bool is_due(const zp_sched* s, const Req* r) {
   const int32_t b = s->cfg.block_size;
-  return r->n > 0 && r->n % b == 0 && r->n / b >= s->cfg.n_max;
+  return r->n > 0 && r->n % b == 0 && r->n / b >= r->n_max;
+}
+
+// A slot is free and the holders' caps, r's included, fit the pool: the
+// per-request form of M <= N_total / N_max.
+bool slot_fits(const zp_sched* s, const Req* r) {
+  return s->slot_count < s->cfg.num_slots && s->slot_caps + r->n_max <= s->cfg.num_blocks;
 }
 
 int32_t share_count(const zp_sched* s, const Req* r) {
   return (s->cfg.prefix_sharing && r->group >= 0) ? r->prefix_len / s->cfg.block_size : 0;
 }
 
-int32_t take_slot(zp_sched* s) {
+// Gives r the lowest free slot (the caller checked slot_fits).
+void take_slot(zp_sched* s, Req* r) {
   for (int32_t i = 0; i < s->cfg.num_slots; ++i) {
     if (!s->slot_used[i]) {
       s->slot_used[i] = 1;
-      return i;
+      r->slot = i;
+      ++s->slot_count;
+      s->slot_caps += r->n_max;
+      return;
     }
   }
-  return -1;  // unreachable: holders sit among the first M running requests
 }
 
 void leave_group(zp_sched* s, Req* r) {
@@ -100,7 +112,11 @@ void release(zp_sched* s, Req* r) {
   if (!r->table.empty())
     zp_block_free(s->pool, r->table.data(), static_cast<int32_t>(r->table.size()));
   leave_group(s, r);
-  if (r->slot >= 0) s->slot_used[r->slot] = 0;
+  if (r->slot >= 0) {
+    s->slot_used[r->slot] = 0;
+    --s->slot_count;
+    s->slot_caps -= r->n_max;
+  }
   r->table.clear();
   r->slot = -1;
   r->n = 0;
@@ -145,7 +161,7 @@ void advance(zp_sched* s, Req* r, zp_sched_step_out* out) {
 
 // Rule (a): plans the compression of a due request; may preempt.
 zp_status try_compress(zp_sched* s, Req* r, zp_sched_step_out* out) {
-  const int32_t nmax = s->cfg.n_max, cap = s->cfg.table_cap;
+  const int32_t nmax = r->n_max, cap = s->cfg.table_cap, cmax = s->cfg.n_max;
   const int32_t nb = static_cast<int32_t>(r->table.size());
   std::vector<int32_t> dst(nmax - 1), nw(nmax), rel(nb);
   int32_t nrel = 0;
@@ -169,10 +185,13 @@ zp_status try_compress(zp_sched* s, Req* r, zp_sched_step_out* out) {
   out->c_slot[i] = r->slot;
   out->c_first[i] = r->compressed ? 0 : 1;
   out->c_nblocks[i] = nb;
+  out->c_nmax[i] = nmax;
   int32_t* src = out->c_src + static_cast<int64_t>(i) * cap;
   for (int32_t j = 0; j < cap; ++j) src[j] = j < nb ? r->table[j] : -1;
-  std::copy(dst.begin(), dst.end(), out->c_dst + static_cast<int64_t>(i) * (nmax - 1));
-  std::copy(nw.begin(), nw.end(), out->c_new + static_cast<int64_t>(i) * nmax);
+  int32_t* d = out->c_dst + static_cast<int64_t>(i) * (cmax - 1);
+  for (int32_t j = 0; j < cmax - 1; ++j) d[j] = j < nmax - 1 ? dst[j] : -1;
+  int32_t* w = out->c_new + static_cast<int64_t>(i) * cmax;
+  for (int32_t j = 0; j < cmax; ++j) w[j] = j < nmax ? nw[j] : -1;
   ++s->st.compressions;
   return ZP_OK;
 }
@@ -213,8 +232,9 @@ zp_status admit(zp_sched* s, zp_sched_step_out* out, int32_t* admitted,
       return fail(ZP_ESTATE, "zp_sched_step: request %d needs %d blocks > table_cap %d", r->rid,
                   nshare + need, s->cfg.table_cap);
     if (zp_num_free(s->pool) < need) break;
-    const bool with_slot = static_cast<int32_t>(s->running.size()) < s->cfg.num_slots;
-    if (!with_slot && (s->cfg.policy == ZP_SCHED_CONSTRAINED || needs_slot(s, L - 1))) break;
+    const bool with_slot =
+        static_cast<int32_t>(s->running.size()) < s->cfg.num_slots && slot_fits(s, r);
+    if (!with_slot && (s->cfg.policy == ZP_SCHED_CONSTRAINED || needs_slot(s, r, L - 1))) break;
     s->waiting.pop_front();
     r->table.clear();
     if (g) {
@@ -234,7 +254,8 @@ zp_status admit(zp_sched* s, zp_sched_step_out* out, int32_t* admitted,
       ng.step = s->t;
       r->holds_prefix = true;
     }
-    r->slot = with_slot ? take_slot(s) : -1;
+    r->slot = -1;
+    if (with_slot) take_slot(s, r);
     r->state = ZP_REQ_RUNNING;
     s->running.push_back(r);
     emit_entry(s, out, r, nshare * b, nshare * b, chunk);
@@ -252,7 +273,7 @@ zp_status decode(zp_sched* s, zp_sched_step_out* out, std::vector<Req*>* sched) 
   for (Req* r : order) {
     // a request preempted earlier in this scan is WAITING now
     if (r->state != ZP_REQ_RUNNING || r->due) continue;
-    if (r->slot < 0 && needs_slot(s, r->n)) {
+    if (r->slot < 0 && needs_slot(s, r, r->n)) {
       ++out->n_blocked;
       continue;
     }
@@ -320,11 +341,14 @@ extern "C" zp_sched* zp_sched_create(const zp_sched_config* cfg) {
 extern "C" void zp_sched_destroy(zp_sched* s) { delete s; }
 
 extern "C" zp_status zp_sched_add(zp_sched* s, int32_t rid, int32_t prompt_len, int32_t max_new,
-                                  int32_t prefix_group, int32_t prefix_len) {
+                                  int32_t prefix_group, int32_t prefix_len, int32_t n_max) {
   if (!s) return fail(ZP_EINVAL, "zp_sched_add: NULL scheduler");
   if (s->reqs.count(rid)) return fail(ZP_EINVAL, "zp_sched_add: request %d exists", rid);
   if (prompt_len < 1 || max_new < 1)
     return fail(ZP_EINVAL, "zp_sched_add: prompt_len and max_new must be >= 1");
+  if (n_max == 0) n_max = s->cfg.n_max;
+  if (n_max < 2 || n_max > s->cfg.n_max)
+    return fail(ZP_EINVAL, "zp_sched_add: n_max %d outside [2, %d]", n_max, s->cfg.n_max);
   if (cdiv(prompt_len, s->cfg.block_size) > s->cfg.table_cap)
     return fail(ZP_EINVAL, "zp_sched_add: prompt of %d tokens exceeds table_cap blocks",
                 prompt_len);
@@ -343,6 +367,7 @@ extern "C" zp_status zp_sched_add(zp_sched* s, int32_t rid, int32_t prompt_len, 
   r->max_new = max_new;
   r->group = prefix_group >= 0 ? prefix_group : -1;
   r->prefix_len = prefix_group >= 0 ? prefix_len : 0;
+  r->n_max = n_max;
   s->waiting.push_back(r.get());
   s->reqs.emplace(rid, std::move(r));
   ++s->unfinished;
@@ -353,7 +378,7 @@ extern "C" zp_status zp_sched_step(zp_sched* s, zp_sched_step_out* out) {
   if (!s || !out || !out->rid || !out->slot || !out->ctx || !out->pos || !out->len ||
       !out->tables ||
       !out->c_rid || !out->c_slot || !out->c_first || !out->c_nblocks || !out->c_src ||
-      !out->c_dst || !out->c_new || !out->finished || !out->preempted)
+      !out->c_dst || !out->c_new || !out->c_nmax || !out->finished || !out->preempted)
     return fail(ZP_EINVAL, "zp_sched_step: NULL argument");
   ++s->t;
   ++s->st.steps;
@@ -369,10 +394,15 @@ extern "C" zp_status zp_sched_step(zp_sched* s, zp_sched_step_out* out) {
       if (st != ZP_OK) return st;
     }
   }
-  // (b) slots to the foremost slot-less requests among the first M
+  // (b) slots to the foremost slot-less requests among the first M, in
+  // order (no overtaking when the caps do not fit)
   const int32_t m = std::min<int32_t>(s->cfg.num_slots, static_cast<int32_t>(s->running.size()));
-  for (int32_t i = 0; i < m; ++i)
-    if (s->running[i]->slot < 0) s->running[i]->slot = take_slot(s);
+  for (int32_t i = 0; i < m; ++i) {
+    Req* r = s->running[i];
+    if (r->slot >= 0) continue;
+    if (!slot_fits(s, r)) break;
+    take_slot(s, r);
+  }
 
   // (c) admission, else (d) decode
   std::vector<Req*> batch;
@@ -421,7 +451,7 @@ extern "C" zp_status zp_sched_compress_done(zp_sched* s, int32_t rid) {
   r->table = r->plan_new;
   r->plan_old.clear();
   r->plan_new.clear();
-  r->n = (s->cfg.n_max - 1) * s->cfg.block_size;
+  r->n = (r->n_max - 1) * s->cfg.block_size;
   r->compressed = true;
   r->state = ZP_REQ_RUNNING;
   return ZP_OK;

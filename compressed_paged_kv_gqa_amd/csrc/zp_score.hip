@@ -351,8 +351,10 @@ __device__ __forceinline__ void s0_columns(const ScoreParams& P, const ColOps<T,
     float s1 = s0;
     if (P.flags & ZP_SCORE_GLOBAL) {
       // F is read only: blocks may be shared by several requests.
-      if (!first && !last)
-        s1 = fmaxf(P.alpha * P.gscore[layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col], s0);
+      if (!first && !last) {
+        const float f = P.alpha * P.gscore[layer * P.f_layer_elems + ((int64_t)page * P.h_kv + h) * b + col];
+        s1 = (P.flags & ZP_SCORE_GLOBAL_SUM) ? f + s0 : fmaxf(f, s0);
+      }
       P.f_new[zh * P.scores_stride + (int64_t)pidx * b + col] = s1;
     }
     P.s1buf[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + col] = s1;
@@ -966,8 +968,10 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   if ((sp.flags & ZP_SCORE_GLOBAL) && (!cache->gscore || !f_new))
     return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL needs cache->gscore and f_new");
   if (sp.flags & ~uint32_t(ZP_SCORE_GLOBAL | ZP_SCORE_POOL | ZP_SCORE_POOL_FIRST_ONLY |
-                           ZP_SCORE_REDUNDANCY | ZP_SCORE_REDUNDANCY_FLASH))
+                           ZP_SCORE_REDUNDANCY | ZP_SCORE_REDUNDANCY_FLASH | ZP_SCORE_GLOBAL_SUM))
     return fail(ZP_EINVAL, "zp_score_tokens: unknown flags 0x%x", sp.flags);
+  if ((sp.flags & ZP_SCORE_GLOBAL_SUM) && !(sp.flags & ZP_SCORE_GLOBAL))
+    return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL_SUM needs ZP_SCORE_GLOBAL");
   if ((sp.flags & ZP_SCORE_POOL) && (sp.pool_kernel < 1 || sp.pool_kernel % 2 == 0))
     return fail(ZP_EINVAL, "zp_score_tokens: pool_kernel must be odd and >= 1");
   if ((sp.flags & ZP_SCORE_REDUNDANCY) && !(sp.tau > 0.f))

@@ -60,15 +60,19 @@ class Compressor:
         self.stream = stream
         self.device = device
 
-    def launch(self, src, dst, nblocks, slots, first, lse_ok, record=False):
-        """src [nreq][maxb] / dst [nreq][N_max-1] block tables, nblocks, query
+    def launch(self, src, dst, nblocks, slots, first, lse_ok, record=False, n_max=None):
+        """src [nreq][maxb] / dst [nreq][n_max-1] block tables, nblocks, query
         slots, first-compression and window-LSE flags per request (host
-        values). Returns (done event, buffers to keep alive until it, scores,
-        kept indices); scores and kept cover every layer only when record."""
+        values); every request of the call keeps (n_max - 1) b tokens
+        (n_max defaults to the geometry's). Returns (done event, buffers to
+        keep alive until it, scores, kept indices); scores and kept cover
+        every layer only when record."""
         G = self.geom
-        b, keep = G.block_size, G.keep
+        n_max = G.n_max if n_max is None else n_max
+        b, keep = G.block_size, (n_max - 1) * G.block_size
         nreq, maxb = src.shape
-        nd = G.n_max - 1
+        nd = n_max - 1
+        assert np.shape(dst) == (nreq, nd)
         # one pinned int32 staging buffer: src tables | dst tables | N | slot |
         # first | window log-sum-exp valid
         meta = torch.zeros(nreq * (maxb + nd + 4), dtype=torch.int32).pin_memory()
@@ -434,8 +438,10 @@ class ServingEngine:
         self.steps = 0
 
     # ---------------------------------------------------------------- intake
-    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0):
-        self.sched.add(rid, prompt_len, max_new, prefix_group, prefix_len)
+    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0, n_max=0):
+        """Queues a request; n_max = its own N_max (0: the geometry's, which
+        is also the largest allowed)."""
+        self.sched.add(rid, prompt_len, max_new, prefix_group, prefix_len, n_max)
 
     def unfinished(self):
         return self.sched.unfinished()
@@ -463,15 +469,18 @@ class ServingEngine:
                 d[n * cap + n:n * cap + 2 * n], d[n * cap + 2 * n:n * cap + 3 * n + 1])
 
     def _compress(self, st):
-        nc = st.n_comp
-        maxb = int(st.c_nblocks.max())
-        src = np.ascontiguousarray(st.c_src[:, :maxb])
-        # every window row is written by a kernel that holds the request's
-        # slot, so the window log-sum-exp is always valid here
-        done, bufs, _s, _k = self.compressor.launch(
-            src, st.c_dst.copy(), st.c_nblocks.copy(), st.c_slot.copy(),
-            st.c_first.astype(bool), [True] * nc)
-        self.pending.append((st.c_rid.tolist(), done, bufs))
+        # one launch per distinct N_max (requests may carry their own)
+        for nm in sorted(set(st.c_nmax.tolist())):
+            sel = np.nonzero(st.c_nmax == nm)[0]
+            maxb = int(st.c_nblocks[sel].max())
+            src = np.ascontiguousarray(st.c_src[sel, :maxb])
+            dst = np.ascontiguousarray(st.c_dst[sel, :nm - 1])
+            # every window row is written by a kernel that holds the
+            # request's slot, so the window log-sum-exp is always valid here
+            done, bufs, _s, _k = self.compressor.launch(
+                src, dst, st.c_nblocks[sel].copy(), st.c_slot[sel].copy(),
+                st.c_first[sel].astype(bool), [True] * len(sel), n_max=nm)
+            self.pending.append((st.c_rid[sel].tolist(), done, bufs))
         if not self.async_compress:
             self.poll(wait=True)
 

@@ -22,6 +22,7 @@ ZP_DTYPE_F32, ZP_DTYPE_BF16 = 0, 1
 ZP_DEVERR_BLOCK_ID, ZP_DEVERR_SEQ_LEN, ZP_DEVERR_SLOT, ZP_DEVERR_KEEP = 1, 2, 4, 8
 ZP_SCORE_GLOBAL, ZP_SCORE_POOL, ZP_SCORE_POOL_FIRST_ONLY, ZP_SCORE_REDUNDANCY = 1, 2, 4, 8
 ZP_SCORE_REDUNDANCY_FLASH = 0x10
+ZP_SCORE_GLOBAL_SUM = 0x20
 ZP_SELECT_NO_COMPACT = 1
 
 
@@ -63,8 +64,8 @@ class SchedConfig(C.Structure):
         "max_prefill_tokens", "table_cap", "policy", "prefix_sharing")]
 
 
-_OUT_ARRAYS = ("rid", "slot", "ctx", "pos", "len", "tables", "c_rid", "c_slot", "c_first", "c_nblocks",
-               "c_src", "c_dst", "c_new", "finished", "preempted")
+_OUT_ARRAYS = ("rid", "slot", "ctx", "pos", "len", "tables", "c_rid", "c_slot", "c_first",
+               "c_nblocks", "c_nmax", "c_src", "c_dst", "c_new", "finished", "preempted")
 _OUT_COUNTS = ("kind", "n", "n_comp", "n_finished", "n_preempted", "n_blocked")
 
 
@@ -123,7 +124,7 @@ def _declare(lib):
         "zp_capacity": (C.c_int, [i64, i64, i64, i64, i32, C.POINTER(i64), C.POINTER(i64)]),
         "zp_sched_create": (_P, [C.POINTER(SchedConfig)]),
         "zp_sched_destroy": (None, [_P]),
-        "zp_sched_add": (C.c_int, [_P, i32, i32, i32, i32, i32]),
+        "zp_sched_add": (C.c_int, [_P, i32, i32, i32, i32, i32, i32]),
         "zp_sched_step": (C.c_int, [_P, C.POINTER(SchedStepOut)]),
         "zp_sched_compress_done": (C.c_int, [_P, i32]),
         "zp_sched_get_stats": (C.c_int, [_P, C.POINTER(SchedStats)]),
@@ -344,13 +345,15 @@ class ScoreParams:
     lambda 0.2, tau 0.4, alpha 0.8, pooling at the first compression only,
     lightning redundancy; p and the pooling width are readings: 0.9 and 7).
     ``redundancy`` picks the lightning (App. C.7, within each block) or the
-    flash (Alg. 3, over the whole sequence) row sums."""
+    flash (Alg. 3, over the whole sequence) row sums; ``global_reduce`` the
+    max-reduce of Alg. 2 or App. C.3's decayed sum-reduce."""
     alpha: float = 0.8
     lam: float = 0.2
     tau: float = 0.4
     p: float = 0.9
     pool_kernel: int = 7
     use_global: bool = True
+    global_reduce: str = "max"
     use_pool: bool = True
     pool_first_only: bool = True
     use_redundancy: bool = True
@@ -359,7 +362,10 @@ class ScoreParams:
     def c(self):
         if self.redundancy not in ("lightning", "flash"):
             raise ValueError(f"redundancy must be 'lightning' or 'flash', not {self.redundancy!r}")
+        if self.global_reduce not in ("max", "sum"):
+            raise ValueError(f"global_reduce must be 'max' or 'sum', not {self.global_reduce!r}")
         flags = ((ZP_SCORE_GLOBAL if self.use_global else 0)
+                 | (ZP_SCORE_GLOBAL_SUM if self.use_global and self.global_reduce == "sum" else 0)
                  | (ZP_SCORE_POOL if self.use_pool else 0)
                  | (ZP_SCORE_POOL_FIRST_ONLY if self.pool_first_only else 0)
                  | (ZP_SCORE_REDUNDANCY if self.use_redundancy else 0)
@@ -525,6 +531,7 @@ class Step:
         self.tables = bufs["tables"].reshape(-1, table_cap)[:n]
         self.c_rid, self.c_slot = bufs["c_rid"][:nc], bufs["c_slot"][:nc]
         self.c_first, self.c_nblocks = bufs["c_first"][:nc], bufs["c_nblocks"][:nc]
+        self.c_nmax = bufs["c_nmax"][:nc]
         self.c_src = bufs["c_src"].reshape(-1, table_cap)[:nc]
         self.c_dst = bufs["c_dst"].reshape(-1, n_max - 1)[:nc]
         self.c_new = bufs["c_new"].reshape(-1, n_max)[:nc]
@@ -543,10 +550,11 @@ class Step:
                               table=self.tables[i, :nt].tolist()))
         comp = []
         for i in range(self.n_comp):
-            nb = int(self.c_nblocks[i])
+            nb, nm = int(self.c_nblocks[i]), int(self.c_nmax[i])
             comp.append(dict(rid=int(self.c_rid[i]), slot=sl(self.c_slot[i]),
-                             first=bool(self.c_first[i]), src=self.c_src[i, :nb].tolist(),
-                             dst=self.c_dst[i].tolist(), new=self.c_new[i].tolist()))
+                             first=bool(self.c_first[i]), n_max=nm,
+                             src=self.c_src[i, :nb].tolist(), dst=self.c_dst[i, :nm - 1].tolist(),
+                             new=self.c_new[i, :nm].tolist()))
         return dict(kind=kinds[self.kind], batch=batch, comp=comp,
                     finished=self.finished.tolist(), preempted=self.preempted.tolist(),
                     blocked=int(self.n_blocked))
@@ -567,7 +575,7 @@ class Scheduler:
             raise ZpError(ZP_EINVAL, lib().zp_last_error().decode())
         R, cap = max_running, table_cap
         sizes = dict(rid=R, slot=R, ctx=R, pos=R, len=R, tables=R * cap, c_rid=R, c_slot=R, c_first=R,
-                     c_nblocks=R, c_src=R * cap, c_dst=R * (n_max - 1), c_new=R * n_max,
+                     c_nblocks=R, c_nmax=R, c_src=R * cap, c_dst=R * (n_max - 1), c_new=R * n_max,
                      finished=R, preempted=R)
         self._bufs = {k: np.zeros(v, np.int32) for k, v in sizes.items()}
         self._out = SchedStepOut()
@@ -586,9 +594,9 @@ class Scheduler:
         except Exception:
             pass
 
-    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0):
-        _check(lib().zp_sched_add(self._h, rid, prompt_len, max_new, prefix_group, prefix_len),
-               "zp_sched_add")
+    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0, n_max=0):
+        _check(lib().zp_sched_add(self._h, rid, prompt_len, max_new, prefix_group, prefix_len,
+                                  n_max), "zp_sched_add")
 
     def step(self) -> Step:
         _check(lib().zp_sched_step(self._h, C.byref(self._out)), "zp_sched_step")

@@ -211,6 +211,10 @@ zp_status zp_paged_prefill(const zp_geom* geom, const zp_cache* cache, int32_t l
                                            ZP_SCORE_REDUNDANCY. Needs 2*b*d*sizeof(elem)
                                            + 56*b bytes of LDS (<= 160 KiB), which
                                            holds wherever scoring itself fits        */
+#define ZP_SCORE_GLOBAL_SUM 0x20u     /* with ZP_SCORE_GLOBAL: decayed sum-reduce,
+                                         alpha*F + S, instead of Alg. 2's
+                                         max(alpha*F, S) (App. C.3 names both);
+                                         invalid without ZP_SCORE_GLOBAL             */
 
 typedef struct zp_score_params {
   float alpha;         /* decay of the global score                          */
@@ -233,7 +237,9 @@ size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_count, int32_t
  *   S0 = mean over the window of the max over the g query heads of
  *        softmax_t(q.k_t/sqrt(d)), the last block causally masked;
  *   S1 = global score (when ZP_SCORE_GLOBAL; first_compression[r] != 0
- *        means the request was never compressed); the cache's F is only read,
+ *        means the request was never compressed): on every block but the
+ *        last, max(alpha*F, S0), or alpha*F + S0 with ZP_SCORE_GLOBAL_SUM;
+ *        the cache's F is only read,
  *        the updated history (Alg. 2's new F, which equals S1) goes to f_new,
  *        and zp_select_compact moves it into the target blocks, so blocks
  *        shared between requests are never written;
@@ -434,7 +440,7 @@ typedef struct {
   int32_t num_blocks;          /* block pool size */
   int32_t block_size;          /* b, a power of two */
   int32_t window;              /* w, 1..b */
-  int32_t n_max;               /* N_max >= 2 */
+  int32_t n_max;               /* N_max >= 2: the default and largest per-request cap */
   int32_t num_slots;           /* M, query-cache slots, >= 1 */
   int32_t max_running;         /* largest running queue (and batch), >= 1 */
   int32_t max_prefill_tokens;  /* tokens of one prefill step (a longer first request still runs alone) */
@@ -454,8 +460,10 @@ typedef struct {
  *   cache positions ctx..ctx+len-1; a decode entry writes cache position
  *   ctx and attends over ctx + 1 tokens.
  * Compressions (n_comp): c_rid, c_slot, c_first (1 = first compression of
- *   the request), c_nblocks (source table length), c_src [R][C] (-1 padded),
- *   c_dst [R][n_max-1], c_new [R][n_max].
+ *   the request), c_nblocks (source table length), c_nmax (the request's
+ *   N_max: keep (c_nmax - 1) * b tokens), c_src [R][C] (-1 padded),
+ *   c_dst [R][n_max-1] and c_new [R][n_max] (c_nmax - 1 and c_nmax entries,
+ *   -1 padded).
  * finished / preempted: request ids (n_finished / n_preempted, <= R each).
  * n_blocked: requests that could not decode this step (slot or block wait). */
 typedef struct {
@@ -469,6 +477,7 @@ typedef struct {
   int32_t* c_slot;
   int32_t* c_first;
   int32_t* c_nblocks;
+  int32_t* c_nmax;
   int32_t* c_src;
   int32_t* c_dst;
   int32_t* c_new;
@@ -503,10 +512,17 @@ zp_sched* zp_sched_create(const zp_sched_config* cfg);
 void zp_sched_destroy(zp_sched* s);
 /* Queues a request at the back of the waiting queue. prefix_group < 0: no
  * shared prefix; else 0 <= prefix_len < prompt_len, one prefix_len per group.
- * ZP_EINVAL for a repeated rid, bad lengths, or a prompt longer than
- * table_cap blocks. */
+ * n_max: this request's N_max in [2, cfg.n_max], 0 for cfg.n_max (Zipage
+ * names a per-request N_max, set from the request's expected length, as a
+ * way to trade concurrency for quality; the choice is the caller's). Every
+ * rule above uses the request's own N_max, and a slot is given only while
+ * the N_max of all slot holders sums to at most num_blocks (the
+ * per-request form of M <= N_total / N_max, Sec. 4.2; with one N_max and a
+ * pool sized by that rule it never binds).
+ * ZP_EINVAL for a repeated rid, bad lengths or n_max, or a prompt longer
+ * than table_cap blocks. */
 zp_status zp_sched_add(zp_sched* s, int32_t rid, int32_t prompt_len, int32_t max_new,
-                       int32_t prefix_group, int32_t prefix_len);
+                       int32_t prefix_group, int32_t prefix_len, int32_t n_max);
 /* One scheduling step (policy above). ZP_ESTATE if a table would exceed
  * table_cap: the scheduler is then unusable and must be destroyed. */
 zp_status zp_sched_step(zp_sched* s, zp_sched_step_out* out);

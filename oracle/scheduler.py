@@ -56,6 +56,15 @@ Readings where the pages leave a step open (the product follows the same):
       compression is planned, when it finishes or when it is preempted; a
       group whose last holder stopped is forgotten.
   R8  Ids (blocks, slots) are taken lowest first.
+  R9  Per-request N_max (the pages name it as a per-request attribute and
+      leave the choice open): each request may carry its own N_max, at most
+      the configured one, which every rule above then uses for it (slot
+      need, trigger, targets, kept tokens). Slots are also reserved
+      blockwise: a slot goes to a request only while the N_max of all slot
+      holders, its own included, sums to at most the pool size, the
+      per-request form of M <= N_total / N_max (Sec. 4.2), so the slot
+      holders can always reach their caps. With one N_max for all and a pool
+      sized by that rule the reservation never binds.
 """
 from __future__ import annotations
 
@@ -68,8 +77,9 @@ CONSTRAINED, HYBRID = "constrained", "hybrid"
 
 
 class Req:
-    def __init__(self, rid, prompt, max_new, group, prefix_len):
+    def __init__(self, rid, prompt, max_new, group, prefix_len, n_max):
         self.rid = rid
+        self.n_max = n_max
         self.prompt = prompt
         self.max_new = max_new
         self.group = group
@@ -98,6 +108,7 @@ class Scheduler:
         self.policy = policy
         self.prefix = prefix_sharing
         self.table_cap = table_cap
+        self.num_blocks = num_blocks
         self.refcount = [0] * num_blocks
         self.reqs = {}
         self.waiting = deque()
@@ -131,13 +142,20 @@ class Scheduler:
     def _free_slot(self):
         return self._lowest_free({r.slot for r in self.running if r.slot is not None}, self.M)
 
+    def _slot_fits(self, r):
+        """R9: a free slot exists and the holders' N_max still fit the pool."""
+        holders = [x for x in self.running if x.slot is not None]
+        return (len(holders) < self.M and
+                sum(x.n_max for x in holders) + r.n_max <= self.num_blocks)
+
     # ---------------------------------------------------------------- rules
-    def needs_slot(self, p):
+    def needs_slot(self, p, n_max=None):
         """R3: writing position p needs a query-cache slot."""
-        return p // self.b >= self.n_max - 1 and p % self.b >= self.b - self.w
+        n_max = self.n_max if n_max is None else n_max
+        return p // self.b >= n_max - 1 and p % self.b >= self.b - self.w
 
     def _is_due(self, r):
-        return r.n > 0 and r.n % self.b == 0 and r.n // self.b >= self.n_max
+        return r.n > 0 and r.n % self.b == 0 and r.n // self.b >= r.n_max
 
     def _share_count(self, r):
         return r.prefix_len // self.b if (self.prefix and r.group >= 0) else 0
@@ -179,12 +197,15 @@ class Scheduler:
         out["finished"].append(r.rid)
 
     # ------------------------------------------------------------------ api
-    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0):
+    def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0, n_max=0):
         assert rid not in self.reqs and prompt_len >= 1 and max_new >= 1
+        n_max = n_max or self.n_max
+        assert 2 <= n_max <= self.n_max
         if prefix_group >= 0:
             assert 0 <= prefix_len < prompt_len
             assert self.group_len.setdefault(prefix_group, prefix_len) == prefix_len
-        r = Req(rid, prompt_len, max_new, prefix_group, prefix_len if prefix_group >= 0 else 0)
+        r = Req(rid, prompt_len, max_new, prefix_group, prefix_len if prefix_group >= 0 else 0,
+                n_max)
         self.reqs[rid] = r
         self.waiting.append(r)
 
@@ -196,7 +217,7 @@ class Scheduler:
         old, _dst, new = r.plan
         self._decref([p for p in old if p not in new])
         r.table = list(new)
-        r.n = (self.n_max - 1) * self.b
+        r.n = (r.n_max - 1) * self.b
         r.compressed = True
         r.state = RUNNING
         r.plan = None
@@ -214,6 +235,8 @@ class Scheduler:
         # (b) Sec. 4.3: free slots go to the foremost of the first M
         for r in self.running[:self.M]:
             if r.slot is None:
+                if not self._slot_fits(r):
+                    break                    # first come first served: no overtaking
                 r.slot = self._free_slot()
         # (c) R1: admission
         if self._admit(out):
@@ -244,7 +267,7 @@ class Scheduler:
     def _try_compress(self, r, out):
         while True:
             shared = {p for p in r.table if self.refcount[p] > 1}
-            plan = plan_targets(r.table, {p: self.refcount[p] for p in r.table}, self.n_max)
+            plan = plan_targets(r.table, {p: self.refcount[p] for p in r.table}, r.n_max)
             if plan["n_new"] <= self.num_free():
                 break
             v = self._victim()
@@ -262,7 +285,7 @@ class Scheduler:
         r.plan = (list(r.table), dst, new)
         r.state = COMPRESSING
         r.due = False
-        out["comp"].append(dict(rid=r.rid, slot=r.slot, first=not r.compressed,
+        out["comp"].append(dict(rid=r.rid, slot=r.slot, first=not r.compressed, n_max=r.n_max,
                                 src=list(r.table), dst=dst, new=new))
 
     def _admit(self, out):
@@ -282,8 +305,8 @@ class Scheduler:
                 assert nshare + need <= self.table_cap, "table_cap exceeded"
             if self.num_free() < need:
                 break
-            with_slot = len(self.running) < self.M
-            if not with_slot and (self.policy == CONSTRAINED or self.needs_slot(L - 1)):
+            with_slot = len(self.running) < self.M and self._slot_fits(r)
+            if not with_slot and (self.policy == CONSTRAINED or self.needs_slot(L - 1, r.n_max)):
                 break
             self.waiting.popleft()
             table = []
@@ -312,7 +335,7 @@ class Scheduler:
         for r in list(self.running):
             if r not in self.running or r.state != RUNNING or r.due:
                 continue
-            if r.slot is None and self.needs_slot(r.n):
+            if r.slot is None and self.needs_slot(r.n, r.n_max):
                 out["blocked"] += 1
                 continue
             if r.n == len(r.table) * self.b:

@@ -173,14 +173,20 @@ def attention_score(Qw, K, b, scale=None, return_probs=False):
 # Global score (Zipage App. C.3, Alg. 2)
 # ---------------------------------------------------------------------------
 
-def global_score(S0, F_old, first_compression, alpha, b):
-    """Decayed max-reduce with the stored history, block by block.
+def global_score(S0, F_old, first_compression, alpha, b, reduce="max"):
+    """Decayed reduction with the stored history, block by block (App. C.3,
+    Alg. 2).
 
     A request that was never compressed stores its scores in F unchanged.
-    Otherwise every block but the last takes max(alpha * F_old, S) and the
-    result both replaces S and is stored in F; the last block (new tokens,
-    no history) stores S as is. Returns (S1, F_new), both [n].
+    Otherwise every block but the last combines the decayed history with the
+    new score, max(alpha * F_old, S) (Alg. 2's max-reduce) or, with
+    reduce="sum", alpha * F_old + S (the decayed sum-reduce the appendix
+    names beside it), and the result both replaces S and is stored in F; the
+    last block (new tokens, no history) stores S as is. Returns (S1, F_new),
+    both [n].
     """
+    if reduce not in ("max", "sum"):
+        raise ValueError(reduce)
     S = _f64(S0).copy()
     n = S.shape[0]
     N = n // b
@@ -193,7 +199,10 @@ def global_score(S0, F_old, first_compression, alpha, b):
         blk = slice(i * b, (i + 1) * b)
         s = S[blk]
         if i != N - 1:
-            s = np.maximum(alpha * F_old[blk], s)
+            if reduce == "max":
+                s = np.maximum(alpha * F_old[blk], s)
+            else:
+                s = alpha * F_old[blk] + s
             S[blk] = s
         F_new[blk] = s
     return S, F_new
@@ -338,6 +347,7 @@ class ScoreParams:
     p: float = 0.9
     pool_kernel: int = 7
     use_global: bool = True
+    global_reduce: str = "max"      # or "sum" (App. C.3's decayed sum-reduce)
     use_pool: bool = True
     pool_first_only: bool = True
     use_redundancy: bool = True
@@ -371,7 +381,8 @@ def score_tokens(Qw, K, F_old, first_compression, b, params: ScoreParams,
     S0 = attention_score(Qw, K, b, scale)
     F_new = None
     if params.use_global:
-        S1, F_new = global_score(S0, F_old, first_compression, params.alpha, b)
+        S1, F_new = global_score(S0, F_old, first_compression, params.alpha, b,
+                                 params.global_reduce)
     else:
         S1 = S0.copy()
     if params.use_pool and (first_compression or not params.pool_first_only):

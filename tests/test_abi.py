@@ -70,6 +70,24 @@ def test_score_redundancy_variant_is_validated():
         zp.ScoreParams(redundancy="original").c()
 
 
+def test_score_global_reduce_is_validated():
+    assert zp.ScoreParams(global_reduce="sum").c().flags & zp.ZP_SCORE_GLOBAL_SUM
+    assert not zp.ScoreParams().c().flags & zp.ZP_SCORE_GLOBAL_SUM
+    # no history, no reduce: the sum flag is only set with the global score
+    assert not zp.ScoreParams(global_reduce="sum", use_global=False).c().flags & zp.ZP_SCORE_GLOBAL_SUM
+    with pytest.raises(ValueError):
+        zp.ScoreParams(global_reduce="mean").c()
+    # the C ABI refuses the sum flag without the global score (host-side,
+    # before anything is enqueued)
+    g = _geom().c()
+    cache = zp.Cache(1, 1, 1, None)
+    sp = zp.ScoreParams(use_global=False).c()
+    sp.flags |= zp.ZP_SCORE_GLOBAL_SUM
+    st = zp.lib().zp_score_tokens(C.byref(g), C.byref(cache), C.byref(sp), 0, 1, 1, 1, 4, 1, 4, 1,
+                                  1, None, 1, None, 64, 1, 1 << 20, None)
+    assert st == zp.ZP_EINVAL and "GLOBAL_SUM" in zp.lib().zp_last_error().decode()
+
+
 # --- allocator ------------------------------------------------------------
 
 def test_alloc_all_or_nothing_and_conservation():

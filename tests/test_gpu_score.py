@@ -30,6 +30,7 @@ SCORE_TOL = 2e-5
 def _oracle_params(sp: zp.ScoreParams):
     return Z.ScoreParams(alpha=sp.alpha, lam=sp.lam, tau=sp.tau, p=sp.p,
                          pool_kernel=sp.pool_kernel, use_global=sp.use_global,
+                         global_reduce=sp.global_reduce,
                          use_pool=sp.use_pool, pool_first_only=sp.pool_first_only,
                          use_redundancy=sp.use_redundancy, redundancy=sp.redundancy)
 
@@ -160,6 +161,8 @@ def test_score_qwen_shape_bf16_mixed_first():
     dict(use_pool=False),
     dict(use_redundancy=False),
     dict(use_global=False, pool_kernel=3),
+    dict(global_reduce="sum"),
+    dict(global_reduce="sum", use_pool=False, use_redundancy=False),
 ])
 def test_score_flag_combinations(flags):
     sp = zp.ScoreParams(**flags)
@@ -208,6 +211,14 @@ def test_score_flash_redundancy_planted_clusters_across_blocks(p):
 def test_score_with_window_lse_qwen_shape(red):
     # requests 0 and 2 bring their window rows' log-sum-exp: one pass over K
     sp = zp.ScoreParams(redundancy=red)
+    _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, sp, lse=lambda r: r != 1)
+
+
+def test_score_global_sum_reduce_every_path():
+    """App. C.3's decayed sum-reduce on the one-pass (window LSE given) and
+    the statistics paths, fp32 and bf16, mixed first / later compressions."""
+    sp = zp.ScoreParams(global_reduce="sum", pool_first_only=False)
+    _run("f32", 64, 4, 1, 16, 8, [4, 6, 5], lambda r: r == 1, sp)
     _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, sp, lse=lambda r: r != 1)
 
 

@@ -38,10 +38,11 @@ class TableModel:
     def __init__(self, geom, stream, seed):
         G = self.G = geom
         self.nreq = len(stream)
-        self.P = max(p + m for _r, p, m, _g, _pl in stream) + 1
-        groups = sorted({g for *_x, g, _pl in stream if g >= 0})
+        self.P = max(p + m for _r, p, m, _g, _pl, _nm in stream) + 1
+        groups = sorted({g for _r, _p, _m, g, _pl, _nm in stream if g >= 0})
         self.src_of_group = {g: self.nreq + i for i, g in enumerate(groups)}
-        self.meta = {r: (g, pl) for r, _p, _m, g, pl in stream}
+        self.meta = {r: (g, pl) for r, _p, _m, g, pl, _nm in stream}
+        self.n_max = {r: nm or geom.n_max for r, _p, _m, _g, _pl, nm in stream}
         S = self.nreq + len(groups)
         gen = synth.rng(seed, 7, 0, "serve")
         L, P = G.num_layers, self.P
@@ -142,14 +143,14 @@ def _check_resident(eng, model):
                     # kept rows in token order; the window of the last
                     # compression and every token since are consecutive
                     assert np.all(np.diff(pos) > 0)
-                    tail = pos[(G.n_max - 1) * b - G.window:]
+                    tail = pos[(model.n_max[r] - 1) * b - G.window:]
                     np.testing.assert_array_equal(tail, np.arange(tail[0], tail[0] + len(tail)))
                 np.testing.assert_array_equal(V, model.V[l, idx[pos], h])
         checked += 1
     return checked
 
 
-def _stream(seed, n, b, prefix):
+def _stream(seed, n, b, prefix, nmax_choices=None):
     rng = np.random.default_rng(seed)
     out = []
     for r in range(n):
@@ -158,31 +159,37 @@ def _stream(seed, n, b, prefix):
         g, pl = -1, 0
         if prefix and rng.random() < 0.6 and p > 20:
             g, pl = 0, 20
-        out.append((r, p, m, g, pl))
+        nm = int(rng.choice(nmax_choices)) if nmax_choices else 0
+        out.append((r, p, m, g, pl, nm))
     return out
 
 
 CASES = [
-    # dtype, policy, prefix, blocks, async; a request arrives every third step
-    ("f32", "hybrid", True, 14, True),
-    ("f32", "hybrid", True, 11, False),
-    ("f32", "hybrid", False, 11, True),
-    ("f32", "constrained", True, 12, True),
-    ("f32", "constrained", False, 9, False),
-    ("bf16", "hybrid", True, 14, True),
+    # dtype, policy, prefix, blocks, async, per-request N_max choices (0 = the
+    # geometry's 3); a request arrives every third step
+    ("f32", "hybrid", True, 14, True, None),
+    ("f32", "hybrid", True, 11, False, None),
+    ("f32", "hybrid", False, 11, True, None),
+    ("f32", "constrained", True, 12, True, None),
+    ("f32", "constrained", False, 9, False, None),
+    ("bf16", "hybrid", True, 14, True, None),
+    ("f32", "hybrid", True, 12, True, [2, 0]),
+    ("bf16", "constrained", False, 8, True, [2, 0]),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-{'prefix' if c[2] else 'noprefix'}-nb{c[3]}"
-                                             for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[
+    f"{c[0]}-{c[1]}-{'prefix' if c[2] else 'noprefix'}-nb{c[3]}{'-nmax' if c[5] else ''}"
+    for c in CASES])
 def test_serving_loop(case):
-    dtype, policy, prefix, nblocks, async_c = case
+    dtype, policy, prefix, nblocks, async_c, nmax_choices = case
     b, nmax, M = 16, 3, 3
-    announce(f"serve dtype={dtype} policy={policy} prefix={prefix} blocks={nblocks} async={async_c}")
+    announce(f"serve dtype={dtype} policy={policy} prefix={prefix} blocks={nblocks} "
+             f"async={async_c} nmax={nmax_choices}")
     geom = zp.CacheGeometry(num_layers=2, num_blocks=nblocks, block_size=b, num_kv_heads=2,
                             num_q_heads=4, head_dim=64, window=8, max_slots=M, n_max=nmax,
                             dtype=dtype)
-    stream = _stream(11, 14, b, prefix)
+    stream = _stream(11, 14, b, prefix, nmax_choices)
     model = TableModel(geom, stream, 3)
     eng = E.ServingEngine(geom, zp.ScoreParams(), max_running=8, table_cap=24,
                           max_prefill_tokens=128, policy=policy, prefix_sharing=prefix,
@@ -214,7 +221,7 @@ def test_serving_loop(case):
     assert eng.device_errors() == 0
     stats = eng.sched.stats()
     assert stats["finished"] == len(stream)
-    assert eng.generated == sum(m for _r, _p, m, _g, _pl in stream)
+    assert eng.generated == sum(x[2] for x in stream)
     assert stats["compressions"] > 0
     if policy == "constrained" and not prefix:
         assert stats["preemptions"] == 0

@@ -172,11 +172,13 @@ def test_prefix_target_is_a_fresh_block_when_shared():
 
 
 # ----------------------------------------------------------------- invariants
-def random_stream(seed, n, b, short=False):
+def random_stream(seed, n, b, short=False, nmax_choices=None):
     """Prompts of 1..10 blocks (1..4 when short), outputs of 1..16 blocks
     (1..3 when short); 60 % of the requests in one of two prefix groups
-    (prefix lengths 2b and b + 1)."""
+    (prefix lengths 2b and b + 1). With nmax_choices, each request also draws
+    its own N_max from them (0 = the configured one)."""
     rng = np.random.default_rng(seed)
+    nm = np.random.default_rng(seed + 77)
     out = []
     for rid in range(n):
         prompt = int(rng.integers(1, 4 * b if short else 10 * b))
@@ -187,7 +189,8 @@ def random_stream(seed, n, b, short=False):
             plen = b + 1 if grp else 2 * b          # one prefix length per group
             if plen >= prompt:
                 grp, plen = -1, 0
-        out.append((rid, prompt, new, grp, plen))
+        out.append((rid, prompt, new, grp, plen,
+                    int(nm.choice(nmax_choices)) if nmax_choices else 0))
     return out
 
 
@@ -200,8 +203,8 @@ def drive(s, stream, seed, max_steps=200000, arrivals=True, check=None):
     for _ in range(max_steps):
         if pos < len(stream):
             k = len(stream) - pos if not arrivals else int(rng.integers(0, 4))
-            for rid, p, m, g, pl in stream[pos:pos + k]:
-                s.add(rid, p, m, g, pl)
+            for rid, p, m, g, pl, nm in stream[pos:pos + k]:
+                s.add(rid, p, m, g, pl, nm)
             pos = min(pos + k, len(stream))
         o = s.step()
         steps.append(o)
@@ -225,7 +228,7 @@ def drive(s, stream, seed, max_steps=200000, arrivals=True, check=None):
 
 
 def _invariants(s, o):
-    b, nmax = s.b, s.n_max
+    b = s.b
     # every block's count equals the number of tables (and pending plans) that hold it
     held = [0] * len(s.refcount)
     for r in s.reqs.values():
@@ -241,6 +244,8 @@ def _invariants(s, o):
     assert all(r.slot is not None for r in s.running if r.compressed or r.state == "compressing")
     # R4: slot holders sit among the first M running requests
     assert all(r.slot is None for r in s.running[s.M:])
+    # per-request form of M <= N_total / N_max
+    assert sum(r.n_max for r in s.running if r.slot is not None) <= len(s.refcount)
     if s.policy == CONSTRAINED:
         assert len(s.running) <= s.M
     assert len(s.running) <= s.max_running
@@ -250,17 +255,18 @@ def _invariants(s, o):
             assert e["pos"] == e["ctx"]
         if o["kind"] == "decode":
             assert e["pos"] == r.prompt + r.gen - 2          # gen counts this step's output
-            assert e["slot"] is not None or not s.needs_slot(e["ctx"])
+            assert e["slot"] is not None or not s.needs_slot(e["ctx"], r.n_max)
             assert e["ctx"] < len(e["table"]) * b
         else:
             last = e["ctx"] + e["len"] - 1
-            assert e["slot"] is not None or not s.needs_slot(last)
+            assert e["slot"] is not None or not s.needs_slot(last, r.n_max)
             assert len(e["table"]) == -(-(last + 1) // b)
     for r in s.running:
         if r.compressed and r.state == "running":
-            assert len(r.table) == nmax and r.n <= nmax * b
+            assert len(r.table) == r.n_max and r.n <= r.n_max * b
     for c in o["comp"]:
-        assert len(c["dst"]) == nmax - 1 and len(c["new"]) == nmax and c["slot"] is not None
+        nm = c["n_max"]
+        assert len(c["dst"]) == nm - 1 and len(c["new"]) == nm and c["slot"] is not None
 
 
 @pytest.mark.parametrize("policy", [CONSTRAINED, HYBRID])
@@ -271,14 +277,69 @@ def test_random_streams_finish_with_invariants(policy, prefix, extra, seed):
     b, nmax, M = 16, 3, 4
     stream = random_stream(seed, 40, b, short=seed % 2 == 1)
     if not prefix:
-        stream = [(r, p, m, -1, 0) for r, p, m, _g, _pl in stream]
+        stream = [(r, p, m, -1, 0, nm) for r, p, m, _g, _pl, nm in stream]
     # the longest prompt (10 blocks) fits; M N_max <= blocks (Sec. 4.2)
     nb = max(M * nmax, 10) + extra
     s = Scheduler(nb, b, 4, nmax, M, 8, 256, policy, prefix_sharing=prefix, table_cap=64)
     drive(s, stream, seed, check=_invariants)
     out = {r.rid: r.gen for r in s.reqs.values()}
-    assert out == {rid: m for rid, _p, m, _g, _pl in stream}
+    assert out == {x[0]: x[2] for x in stream}
     assert s.num_free() == nb
+
+
+@pytest.mark.parametrize("policy", [CONSTRAINED, HYBRID])
+@pytest.mark.parametrize("prefix", [False, True])
+@pytest.mark.parametrize("seed", range(3))
+def test_per_request_n_max_streams_finish_with_invariants(policy, prefix, seed):
+    """Requests with their own N_max (2, 3 or the configured 4) on a pool
+    smaller than M times the largest N_max: the slot reservation keeps the
+    holders within the pool and every request finishes."""
+    b, nmax, M = 16, 4, 4
+    stream = random_stream(seed, 40, b, short=seed % 2 == 1, nmax_choices=[2, 3, 0])
+    if not prefix:
+        stream = [(r, p, m, -1, 0, nm) for r, p, m, _g, _pl, nm in stream]
+    nb = 12
+    s = Scheduler(nb, b, 4, nmax, M, 8, 256, policy, prefix_sharing=prefix, table_cap=64)
+    steps = drive(s, stream, seed, check=_invariants)
+    assert {r.rid: r.gen for r in s.reqs.values()} == {x[0]: x[2] for x in stream}
+    assert s.num_free() == nb
+    kept = {c["n_max"] for o in steps for c in o["comp"]}
+    assert kept >= {2, 3}
+
+
+def test_per_request_n_max_compresses_to_its_own_cap():
+    """N_max = 2 for one request, 3 for the other (b = 16): the first is due
+    at 32 tokens and keeps 16, the second at 48 and keeps 32."""
+    s = Scheduler(100, 16, 4, 3, 2, 8, 1000, HYBRID)
+    s.add(0, 30, 20, n_max=2)
+    s.add(1, 46, 20)
+    comps = []
+    for _ in range(6):
+        o = s.step()
+        comps += [(c["rid"], c["n_max"], c["src"], c["dst"], c["new"]) for c in o["comp"]]
+        for c in o["comp"]:
+            s.compress_done(c["rid"])
+    assert comps == [(0, 2, [0, 1], [0], [0, 1]), (1, 3, [2, 3, 4], [2, 3], [2, 3, 4])]
+    # both were due after step 3, compressed in step 4, decoded in steps 5, 6
+    assert (s.reqs[0].n, s.reqs[1].n) == (16 + 2, 32 + 2)
+
+
+def test_slot_reservation_holds_back_a_large_n_max():
+    """Pool of 6 blocks, M = 2: a request with N_max 4 holds a slot, a second
+    with N_max 4 would push the reserved caps to 8 > 6 and is admitted
+    without a slot (hybrid) or not at all (constrained); one with N_max 2
+    fits beside the first."""
+    for pol, want in ((HYBRID, [0, None]), (CONSTRAINED, [0])):
+        s = Scheduler(6, 16, 4, 4, 2, 8, 1000, pol)
+        s.add(0, 10, 5)
+        s.add(1, 10, 5)
+        o = s.step()
+        assert [e["slot"] for e in o["batch"]] == want
+    s = Scheduler(6, 16, 4, 4, 2, 8, 1000, CONSTRAINED)
+    s.add(0, 10, 5)
+    s.add(1, 10, 5, n_max=2)
+    o = s.step()
+    assert [e["slot"] for e in o["batch"]] == [0, 1]
 
 
 def test_constrained_never_preempts_and_hybrid_runs_more_requests():
@@ -286,7 +347,7 @@ def test_constrained_never_preempts_and_hybrid_runs_more_requests():
     keeps at most M requests running; hybrid scheduling fills the idle
     blocks with requests that need no slot (Sec. 4.3)."""
     b, nmax, M = 16, 4, 2
-    stream = [(r, 20, 20, -1, 0) for r in range(24)]
+    stream = [(r, 20, 20, -1, 0, 0) for r in range(24)]
     res = {}
     for pol in (CONSTRAINED, HYBRID):
         s = Scheduler(M * nmax + 8, b, 4, nmax, M, 16, 10000, pol)

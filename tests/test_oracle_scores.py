@@ -48,6 +48,46 @@ def test_global_alpha_zero_is_identity_and_alpha_one_never_decreases_history():
     np.testing.assert_array_equal(F[8:], S0[8:])
 
 
+def test_global_sum_worked_example():
+    """Decayed sum-reduce (App. C.3's second form), same inputs as the max
+    example: S1 = 0.5 F_old + S0 on blocks 0 and 1, the last block as is.
+      aF + S0:  0.7  0.35 0.7  0.15 | 0.2  0.1
+    """
+    F_old = np.array([0.8, 0.1, 0.6, 0.2, 7.0, 7.0])
+    S0 = np.array([0.3, 0.3, 0.4, 0.05, 0.2, 0.1])
+    S1, F = Z.global_score(S0, F_old, False, 0.5, 2, reduce="sum")
+    np.testing.assert_allclose(S1, [0.7, 0.35, 0.7, 0.15, 0.2, 0.1], atol=1e-15)
+    np.testing.assert_allclose(F, S1, atol=1e-15)
+    S1, F = Z.global_score(S0, F_old, True, 0.5, 2, reduce="sum")
+    np.testing.assert_array_equal(S1, S0)                # no history yet
+
+
+def test_global_sum_of_a_constant_score_is_a_geometric_series():
+    """A token that scores s at every compression carries, after its k-th
+    compression with history, s (1 + a + ... + a^k) = s (1 - a^(k+1)) / (1 - a);
+    the max-reduce keeps s (a < 1)."""
+    s, a, b = 0.3, 0.8, 4
+    S0 = np.full(3 * b, s)
+    F = None
+    Fm = None
+    for k in range(6):
+        _, F = Z.global_score(S0, F, k == 0, a, b, reduce="sum")
+        _, Fm = Z.global_score(S0, Fm, k == 0, a, b, reduce="max")
+        np.testing.assert_allclose(F[:2 * b], s * (1 - a ** (k + 1)) / (1 - a), rtol=1e-14)
+        np.testing.assert_array_equal(F[2 * b:], s)      # the last block has no history
+        np.testing.assert_allclose(Fm, s, rtol=0)
+
+
+def test_global_sum_bounds_the_max_for_nonnegative_scores():
+    rng = np.random.default_rng(4)
+    S0, F_old = rng.random(16), rng.random(16)
+    Ss, _ = Z.global_score(S0, F_old, False, 0.7, 4, reduce="sum")
+    Sm, _ = Z.global_score(S0, F_old, False, 0.7, 4, reduce="max")
+    assert np.all(Ss >= Sm) and np.all(Ss <= 2 * Sm + 1e-15)
+    with pytest.raises(ValueError):
+        Z.global_score(S0, F_old, False, 0.7, 4, reduce="mean")
+
+
 # --- pooling ------------------------------------------------------------------
 
 @pytest.mark.parametrize("kernel", [1, 3, 5, 7])

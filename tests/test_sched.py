@@ -46,9 +46,9 @@ def lockstep(o, c, stream, seed, arrivals=True, max_steps=100000, state_every=1)
     while steps < max_steps:
         if pos < len(stream):
             k = len(stream) - pos if not arrivals else int(rng.integers(0, 4))
-            for rid, p, m, g, pl in stream[pos:pos + k]:
-                o.add(rid, p, m, g, pl)
-                c.add(rid, p, m, g, pl)
+            for rid, p, m, g, pl, nm in stream[pos:pos + k]:
+                o.add(rid, p, m, g, pl, nm)
+                c.add(rid, p, m, g, pl, nm)
             pos = min(pos + k, len(stream))
         a = o.step()
         got = c.step().as_dict()
@@ -91,8 +91,22 @@ def test_random_streams_match_the_oracle(policy, prefix, extra, seed):
     b, nmax, M = 16, 3, 4
     stream = random_stream(seed, 40, b, short=seed % 2 == 1)
     if not prefix:
-        stream = [(r, p, m, -1, 0) for r, p, m, _g, _pl in stream]
+        stream = [(r, p, m, -1, 0, nm) for r, p, m, _g, _pl, nm in stream]
     o, c = _pair(max(M * nmax, 10) + extra, b, 4, nmax, M, 8, 256, policy, prefix)
+    lockstep(o, c, stream, seed)
+
+
+@pytest.mark.parametrize("policy", ["constrained", "hybrid"])
+@pytest.mark.parametrize("prefix", [False, True])
+@pytest.mark.parametrize("seed", range(3))
+def test_per_request_n_max_matches_the_oracle(policy, prefix, seed):
+    """Requests with their own N_max (2, 3, or the configured 4) on a pool
+    where the slot reservation binds."""
+    b, nmax, M = 16, 4, 4
+    stream = random_stream(seed, 40, b, short=seed % 2 == 1, nmax_choices=[2, 3, 0])
+    if not prefix:
+        stream = [(r, p, m, -1, 0, nm) for r, p, m, _g, _pl, nm in stream]
+    o, c = _pair(12, b, 4, nmax, M, 8, 256, policy, prefix)
     lockstep(o, c, stream, seed)
 
 
@@ -115,7 +129,7 @@ def test_larger_geometry_matches_the_oracle(seed):
     (the shape of the decode workload, scaled down)."""
     b = 256
     rng = np.random.default_rng(seed)
-    stream = [(r, int(rng.integers(64, 3000)), int(rng.integers(1, 3000)), -1, 0)
+    stream = [(r, int(rng.integers(64, 3000)), int(rng.integers(1, 3000)), -1, 0, 0)
               for r in range(64)]
     o, c = _pair(8 * 8 + 24, b, 16, 8, 8, 32, 16384, "hybrid")
     lockstep(o, c, stream, seed, arrivals=False, state_every=16)
@@ -124,7 +138,7 @@ def test_larger_geometry_matches_the_oracle(seed):
 
 def test_hand_scenario_matches():
     o, c = _pair(100, 16, 4, 2, 1, 8, 1000, "hybrid")
-    lockstep(o, c, [(0, 8, 5, -1, 0), (1, 26, 10, -1, 0)], 0, arrivals=False)
+    lockstep(o, c, [(0, 8, 5, -1, 0, 0), (1, 26, 10, -1, 0, 0)], 0, arrivals=False)
 
 
 # ------------------------------------------------------------------- errors
@@ -146,6 +160,10 @@ def test_bad_configuration_and_arguments():
     c.add(5, 30, 5, 3, 16)
     with pytest.raises(zp.ZpError):
         c.add(6, 40, 5, 3, 17)                           # one prefix length per group
+    with pytest.raises(zp.ZpError):
+        c.add(7, 10, 5, n_max=3)                         # above the configured N_max
+    with pytest.raises(zp.ZpError):
+        c.add(8, 10, 5, n_max=1)
     with pytest.raises(zp.ZpError) as e:
         c.compress_done(0)                               # not compressing
     assert e.value.status == zp.ZP_ESTATE
