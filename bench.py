@@ -16,9 +16,14 @@ One step = one decode token for every active sequence through all 36 layers
 
 Prints one JSON line (metric, value = decode tokens/s, roofline of the decode
 kernel measured with HIP events around every launch, cpu_baseline = the float64
-oracle on the host cores on a bounded sample of the same workload).
+oracle on the host cores on a bounded sample of the same workload). The line
+also carries the compression and prefill kernels timed in isolation, and
+`serve`: a synthetic request stream served to completion by the library's
+scheduler (hybrid and constrained), output tokens per second.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                  [--no-compress-kernels] [--no-serve]
+  python bench.py --serve | --compress-kernels | --prefill-kernels   # one part only
   python bench.py --copy-calibration     # plain device copy of known size
 """
 from __future__ import annotations
@@ -74,6 +79,8 @@ def parse_args():
     ap.add_argument("--serve-mem-gib", type=float, default=24.0,
                     help="HBM given to K/V, F and the query cache (sets M and N_total)")
     ap.add_argument("--serve-policies", default="hybrid,constrained")
+    ap.add_argument("--no-serve", action="store_true",
+                    help="skip the scheduled serving run in the default line")
     return ap.parse_args()
 
 
@@ -569,6 +576,11 @@ def main():
         ck = compress_kernel_bench()
         log("prefill in isolation")
         ck = {"compress": ck, "prefill": prefill_kernel_bench()}
+    serve = None
+    if not args.no_serve:
+        log("scheduled serving of the synthetic request stream")
+        serve = serve_bench(args.serve_requests, args.serve_mem_gib,
+                            args.serve_policies.split(","))
     traffic = traffic_from_profiles()
     line = {
         "metric": "decode tok/s at 256 seqs with compression; achieved HBM GB/s vs peak",
@@ -600,6 +612,8 @@ def main():
     if ck is not None:
         line["compress_kernels"] = ck["compress"]
         line["prefill_kernels"] = ck["prefill"]
+    if serve is not None:
+        line["serve"] = serve
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
