@@ -51,7 +51,7 @@ struct DecodeParams {
   int64_t qwin_layer_off;  // element offset of the layer in Qwin
   int64_t qlse_layer_off;  // element offset of the layer in the Qwin LSE table
   int32_t table_stride, num_blocks, b, h_kv, w, max_slots;
-  int32_t split_tokens, max_splits, max_seq_len, log2b;
+  int32_t split_tokens, max_splits, max_seq_len, log2b, waves;
   float qk_scale;  // log2(e) / sqrt(d)
 };
 
@@ -62,9 +62,8 @@ struct DecodeCfg {
   static constexpr int RPW = 64 / LPR;     // token rows per wavefront load
   static constexpr int CHUNK = 16;         // tokens per wavefront chunk (never crosses a block)
   static constexpr int U = CHUNK / RPW;    // row loads per lane per chunk (K and V each)
-  static constexpr int WAVES = 4;
   // waves per SIMD the register budget is sized for (no spills)
-  static constexpr int MIN_WAVES = (sizeof(T) == 2 && G <= 4) || (D == 64 && G <= 4) ? 3 : 2;
+  static constexpr int MIN_WAVES = decode_waves_per_simd(sizeof(T), D, G);
 };
 
 // Query registers of one lane: its EPL dims of the g query heads.
@@ -114,7 +113,7 @@ struct QRegs<float, G> {
 // lazy: a chunk rescales only when its maximum exceeds the running one by
 // more than kLazy (log2 units), so p = exp2(s - m) stays below 2^kLazy.
 constexpr float kLazy = 8.0f;
-// Upper bound on the blocks one split covers (decode_split_tokens keeps
+// Upper bound on the blocks one split covers (decode_launch_shape keeps
 // split_tokens <= kMaxSplitPages * block_size).
 constexpr int kMaxSplitPages = 1024;
 constexpr float kNoMax = -1.0e30f;  // finite "nothing seen yet"
@@ -131,12 +130,15 @@ __device__ __forceinline__ int window_row_of(const DecodeParams& P, int seq, int
   return off - (P.b - P.w);
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_decode_kernel(
+// WAVES wavefronts per workgroup (one workgroup per (split, kv-head,
+// sequence)); they take the chunks of the split in turn and are merged in
+// LDS at the end.
+template <typename T, int D, int G, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_decode_kernel(
     DecodeParams P) {
   using C = DecodeCfg<T, D, G>;
   constexpr int EPL = C::EPL, LPR = C::LPR, RPW = C::RPW, U = C::U, CHUNK = C::CHUNK;
-  constexpr int WAVES = C::WAVES;
+  constexpr int NT = 64 * WAVES;  // threads
 
   __shared__ float sm_m[WAVES][G];
   __shared__ float sm_l[WAVES][G];
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
     if (split == 0) {
       if (tid == 0) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
       T* out = reinterpret_cast<T*>(P.out);
-      for (int i = tid; i < G * D; i += 256) out[out_row * D + i] = from_f32<T>(NAN);
+      for (int i = tid; i < G * D; i += NT) out[out_row * D + i] = from_f32<T>(NAN);
       if (P.lse && tid < G) P.lse[out_row + tid] = NAN;
     }
     return;
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
   // Block ids of this split (at most kMaxSplitPages by construction).
   const int pg0 = t0 >> P.log2b;
   const int npg = ((t1 - 1) >> P.log2b) - pg0 + 1;
-  for (int i = tid; i < npg; i += 256) sm_pages[i] = tab[pg0 + i];
+  for (int i = tid; i < npg; i += NT) sm_pages[i] = tab[pg0 + i];
   __syncthreads();
 
   float m[G], l[G], o[G][EPL];
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
         const T* qp = reinterpret_cast<const T*>(P.q) + out_row * D;
         T* dst = reinterpret_cast<T*>(P.qwin) + P.qwin_layer_off +
                  (((int64_t)slot * P.h_kv + kvh) * G) * P.w * D + (int64_t)(off - (P.b - P.w)) * D;
-        for (int i = tid; i < G * D; i += 256) {
+        for (int i = tid; i < G * D; i += NT) {
           const int h = i / D, e = i % D;
           dst[(int64_t)h * P.w * D + e] = qp[i];
         }
@@ -377,12 +379,13 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
     }
   }
 
-  // Combine the 4 wavefronts: each thread owns (head, dim) pairs.
+  // Combine the wavefronts: each thread owns (head, dim) pairs.
   constexpr int PAIRS = G * D;
-  float Mw[(PAIRS + 255) / 256], Lw[(PAIRS + 255) / 256], Ow[(PAIRS + 255) / 256];
+  constexpr int PPT = (PAIRS + NT - 1) / NT;  // pairs per thread
+  float Mw[PPT], Lw[PPT], Ow[PPT];
 #pragma unroll
-  for (int k = 0; k < (PAIRS + 255) / 256; ++k) {
-    const int i = tid + k * 256;
+  for (int k = 0; k < PPT; ++k) {
+    const int i = tid + k * NT;
     Mw[k] = kNoMax; Lw[k] = 0.f; Ow[k] = 0.f;
     if (i < PAIRS) {
       const int h = i / D, e = i % D;
@@ -403,8 +406,8 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
   T* out = reinterpret_cast<T*>(P.out);
   if (nsplit == 1) {
 #pragma unroll
-    for (int k = 0; k < (PAIRS + 255) / 256; ++k) {
-      const int i = tid + k * 256;
+    for (int k = 0; k < PPT; ++k) {
+      const int i = tid + k * NT;
       if (i < PAIRS) {
         const int h = i / D, e = i % D;
         out[(out_row + h) * D + e] = from_f32<T>(Ow[k] / Lw[k]);
@@ -426,8 +429,8 @@ __global__ __launch_bounds__(256, (DecodeCfg<T, D, G>::MIN_WAVES)) void paged_de
   const int64_t item = (int64_t)seq * P.h_kv + kvh;
   float* mypart = P.part + (item * P.max_splits + split) * G * (D + 2);
 #pragma unroll
-  for (int k = 0; k < (PAIRS + 255) / 256; ++k) {
-    const int i = tid + k * 256;
+  for (int k = 0; k < PPT; ++k) {
+    const int i = tid + k * NT;
     if (i < PAIRS) {
       const int h = i / D, e = i % D;
       mypart[h * (D + 2) + 2 + e] = Ow[k];
@@ -477,7 +480,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams P) {
 template <typename T, int D, int G>
 static void launch_decode(const DecodeParams& P, int batch, hipStream_t stream) {
   dim3 grid(P.max_splits, P.h_kv, batch);
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, G>), grid, dim3(256), 0, stream, P);
+  constexpr int MW = DecodeCfg<T, D, G>::MIN_WAVES;
+  // the workgroup sizes decode_launch_shape picks from: 4 wavefronts, or a
+  // whole CU's resident waves (small batches)
+  if (P.waves == 4 * MW)
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, 4 * MW>), grid, dim3(256 * MW), 0, stream, P);
+  else
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, 4>), grid, dim3(256), 0, stream, P);
   if (P.max_splits > 1)
     hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(P.h_kv, batch), dim3(256), 0, stream,
                        P);
@@ -494,8 +503,11 @@ static void dispatch_group(int g, const DecodeParams& P, int batch, hipStream_t 
 }
 
 static size_t decode_ws_layout(const zp_geom* g, int32_t batch, int32_t max_seq_len,
-                               size_t* part_off, int32_t* split_tokens, int32_t* max_splits) {
-  const int32_t st = decode_split_tokens(g, batch, max_seq_len);
+                               size_t* part_off, int32_t* split_tokens, int32_t* max_splits,
+                               int32_t* waves) {
+  int32_t wv = 4;
+  const int32_t st = decode_launch_shape(g, batch, max_seq_len, &wv);
+  if (waves) *waves = wv;
   const int32_t ms = std::max<int32_t>(1, (std::max<int32_t>(max_seq_len, 1) + st - 1) / st);
   const size_t items = size_t(batch) * g->num_kv_heads;
   const size_t p_off = kWsHeader;
@@ -514,7 +526,7 @@ extern "C" size_t zp_decode_workspace_size(const zp_geom* geom, int32_t batch,
                                            int32_t max_seq_len) {
   if (validate_geom(geom, "zp_decode_workspace_size") != ZP_OK || batch < 0 || max_seq_len < 0)
     return 0;
-  return decode_ws_layout(geom, batch, max_seq_len, nullptr, nullptr, nullptr);
+  return decode_ws_layout(geom, batch, max_seq_len, nullptr, nullptr, nullptr, nullptr);
 }
 
 extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t layer,
@@ -536,8 +548,9 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
     return fail(ZP_EINVAL, "zp_paged_decode: NULL buffer");
   if (qslot && !cache->qwin) return fail(ZP_EINVAL, "zp_paged_decode: qslot given but qwin NULL");
   size_t p_off;
-  int32_t split_tokens, max_splits;
-  const size_t need = decode_ws_layout(geom, batch, max_seq_len, &p_off, &split_tokens, &max_splits);
+  int32_t split_tokens, max_splits, waves;
+  const size_t need = decode_ws_layout(geom, batch, max_seq_len, &p_off, &split_tokens, &max_splits,
+                                       &waves);
   if (workspace_bytes < need)
     return fail(ZP_EINVAL, "zp_paged_decode: workspace %zu bytes, need %zu", workspace_bytes, need);
 
@@ -557,6 +570,7 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
   P.table_stride = table_stride; P.num_blocks = geom->num_blocks; P.b = geom->block_size;
   P.h_kv = geom->num_kv_heads; P.w = geom->window; P.max_slots = geom->max_slots;
   P.split_tokens = split_tokens; P.max_splits = max_splits; P.max_seq_len = max_seq_len;
+  P.waves = waves;
   P.qk_scale = kLog2e / std::sqrt(float(d));
   P.log2b = __builtin_ctz(unsigned(geom->block_size));
 

@@ -280,19 +280,39 @@ zp_status zp::validate_geom(const zp_geom* g, const char* who) {
   return ZP_OK;
 }
 
-int32_t zp::decode_split_tokens(const zp_geom* g, int32_t batch, int32_t max_seq_len) {
-  // One workgroup per (sequence, kv-head) when those items fill the GPU
-  // (>= 1536 of them: two rounds of 3 resident workgroups on 256 CUs);
-  // otherwise split so that about 2048 workgroups run, with at least 512
-  // tokens each. A split covers at most ~1000 blocks (kMaxSplitPages = 1024).
+int32_t zp::decode_launch_shape(const zp_geom* g, int32_t batch, int32_t max_seq_len,
+                                int32_t* waves) {
+  // Items are (sequence, kv-head) pairs. The GPU holds `slots` resident
+  // wavefronts (256 CUs x 4 SIMDs x the kernel's waves per SIMD). Measured
+  // on MI355X at the Qwen3-8B decode shape (1793..2048 resident tokens):
+  //  - 4 wavefronts per item fill the GPU at least once from 96 sequences
+  //    on; one workgroup per item is best there, except when a second round
+  //    is started but would be mostly empty (between 1 and 1.5 rounds):
+  //    then each item is split in two, which evens the rounds out (5.5 vs
+  //    5.1 TB/s at 112 sequences);
+  //  - below one round, but above a quarter of one, more splits only add
+  //    merge work: one 4-wave workgroup per item (64 sequences: 5.86 TB/s
+  //    vs 5.24 with 4-way splits);
+  //  - at most a quarter of a round (<= 32 sequences of 8 kv-heads): one
+  //    workgroup with a whole CU's waves per item, split only as far as
+  //    needed to reach one round (32 sequences: 5.30 vs 4.34 TB/s).
+  // A split covers at least 256 tokens and at most ~1000 blocks
+  // (kMaxSplitPages = 1024).
+  const int64_t mw = decode_waves_per_simd(static_cast<int>(elem_size(g)), g->head_dim,
+                                           group_size(g));
+  const int64_t slots = int64_t(256) * 4 * mw;
   const int64_t items = std::max<int64_t>(1, int64_t(batch) * g->num_kv_heads);
   const int64_t len = std::max<int32_t>(max_seq_len, 1);
-  int64_t s = len;
-  if (items < 1536) {
-    const int64_t want = (2048 + items - 1) / items;
-    s = std::max<int64_t>(512, (len + want - 1) / want);
+  int64_t w = 4, splits = 1;
+  if (4 * items >= slots) {
+    if (4 * items > slots && 2 * 4 * items < 3 * slots) splits = 2;
+  } else if (4 * mw * items <= slots) {
+    w = 4 * mw;
+    splits = std::max<int64_t>(1, slots / (w * items));
   }
+  int64_t s = std::max<int64_t>(256, (len + splits - 1) / splits);
   s = std::min<int64_t>(s, int64_t(1000) * g->block_size);
   s = (s + 63) / 64 * 64;
+  *waves = static_cast<int32_t>(w);
   return static_cast<int32_t>(s);
 }
