@@ -604,7 +604,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_decode_kernel<bf16,128,4>",
+                     "kernel": "paged_decode_kernel<bf16,128,4,4>",
                      "avg_launch_ms": round(r["launch_ms"], 4),
                      "algorithmic_bytes_per_launch": round(r["bytes_per_launch"])},
         "decode_ms_per_step": round(r["decode_ms_per_step"], 3),

@@ -270,11 +270,12 @@ class DecodeEngine:
         self.tables_d.copy_(tab_h, non_blocking=True)
         self.lens_d.copy_(len_h, non_blocking=True)
         ev.record()
+        self._calls = zp.LayerCalls(self.cache, "decode", self.tables_d, self.lens_d, self.dec_ws,
+                                    qslot=self.qslot_d, max_seq_len=self.max_seq_len)
         return act
 
     def decode_layer(self, layer, q, k_new, v_new, out, lse=None):
-        zp.zp_paged_decode(self.cache, layer, q, k_new, v_new, self.tables_d, self.lens_d,
-                           self.max_seq_len, self.qslot_d, out, lse, self.dec_ws)
+        self._calls(layer, q, k_new, v_new, out, lse)
 
     def finish_step(self, act):
         """Advances lengths and launches compressions that became due."""
@@ -514,19 +515,19 @@ class ServingEngine:
             mq = int(st.len.max())
             if T > self.max_chunk:
                 raise RuntimeError(f"prefill of {T} tokens exceeds {self.max_chunk}")
+            call = zp.LayerCalls(self.cache, "prefill", tab, ctx, self.pf_ws, qslot=slot,
+                                 cu_seqlens=cu, max_q_len=mq)
             for l in range(G.num_layers):
                 q, k, v = inputs(st.kind, st, l)
-                o = self.out_prefill[l if self.out_prefill.shape[0] > 1 else 0, :T]
-                zp.zp_paged_prefill(self.cache, l, q, k, v, cu, ctx, mq, tab, slot, o, None,
-                                    self.pf_ws)
+                call(l, q, k, v, self.out_prefill[l if self.out_prefill.shape[0] > 1 else 0, :T])
             self.generated += st.n
         elif st.kind == zp.ZP_STEP_DECODE:
             tab, lens, slot, _cu = self._stage(st, st.ctx + 1)
+            call = zp.LayerCalls(self.cache, "decode", tab, lens, self.dec_ws, qslot=slot,
+                                 max_seq_len=self.max_seq_len)
             for l in range(G.num_layers):
                 q, k, v = inputs(st.kind, st, l)
-                o = self.out_decode[l if self.out_decode.shape[0] > 1 else 0, :st.n]
-                zp.zp_paged_decode(self.cache, l, q, k, v, tab, lens, self.max_seq_len, slot, o,
-                                   None, self.dec_ws)
+                call(l, q, k, v, self.out_decode[l if self.out_decode.shape[0] > 1 else 0, :st.n])
             self.generated += st.n
         elif self.pending:
             # nothing to run until a compression commits

@@ -304,6 +304,86 @@ def zp_paged_decode(cache: PagedKVCache, layer, q, k_new, v_new, block_tables, s
         workspace.numel() * workspace.element_size(), _stream(stream)), "zp_paged_decode")
 
 
+class LayerCalls:
+    """zp_paged_decode / zp_paged_prefill for every layer of one step, with
+    the per-step arguments (tables, lengths, slots, workspace, stream)
+    validated and converted once. Each layer then passes only its q / k / v /
+    out tensors, checked for shape and dtype against the first layer's.
+    Argument marshalling only, as the functions above."""
+
+    def __init__(self, cache: PagedKVCache, kind, block_tables, lens, workspace, qslot=None,
+                 max_seq_len=None, cu_seqlens=None, max_q_len=None, stream=None):
+        import torch
+        geom = cache.geom
+        self._g = geom.c()
+        self._c = cache.c()
+        self._gp, self._cp = C.byref(self._g), C.byref(self._c)
+        self._dt = geom.torch_dtype()
+        self._hq, self._hkv, self._d = geom.num_q_heads, geom.num_kv_heads, geom.head_dim
+        for t, n in ((block_tables, "block_tables"), (lens, "lens"), (qslot, "qslot"),
+                     (cu_seqlens, "cu_seqlens")):
+            _need(t, torch.int32, n)
+        _need(workspace, torch.uint8, "workspace")
+        self._ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self._st = _stream(stream)
+        self._tab, self._stride = block_tables.data_ptr(), block_tables.shape[1]
+        self._lens, self._slot = lens.data_ptr(), _ptr(qslot)
+        if kind == "decode":
+            self._n = block_tables.shape[0]
+            if lens.shape[0] < self._n or (qslot is not None and qslot.shape[0] < self._n):
+                raise ValueError("lens and qslot need a row per batch entry")
+            self._max = int(max_seq_len)
+            self._fn = lib().zp_paged_decode
+        elif kind == "prefill":
+            self._n = lens.shape[0]
+            if cu_seqlens is None or cu_seqlens.shape[0] != self._n + 1:
+                raise ValueError("cu_seqlens must hold nreq + 1 offsets")
+            if block_tables.shape[0] != self._n:
+                raise ValueError("block_tables needs a row per chunk")
+            self._cu, self._mq = cu_seqlens.data_ptr(), int(max_q_len)
+            self._fn = lib().zp_paged_prefill
+        else:
+            raise ValueError(kind)
+        self.kind = kind
+        self._T = None
+        self._f32 = torch.float32
+
+    def _check_rows(self, q, k, v, out, lse):
+        T = q.shape[0]
+        if self._T is None:
+            for t, n, h in ((q, "q", self._hq), (out, "out", self._hq), (k, "k_new", self._hkv),
+                            (v, "v_new", self._hkv)):
+                if (tuple(t.shape) != (T, h, self._d) or not t.is_contiguous()
+                        or t.dtype != self._dt or t.device.type != "cuda"):
+                    raise ValueError(f"{n} must be a contiguous [{T}][{h}][{self._d}] "
+                                     f"{self._dt} device tensor")
+            if self.kind == "decode" and T != self._n:
+                raise ValueError("q must hold one row per batch entry")
+            self._T = T
+            self._shapes = (q.shape, k.shape, out.shape)
+        elif (q.shape, k.shape, out.shape) != self._shapes or v.shape != k.shape or \
+                q.dtype != self._dt or k.dtype != self._dt or v.dtype != self._dt or \
+                out.dtype != self._dt or not (q.is_contiguous() and k.is_contiguous() and
+                                              v.is_contiguous() and out.is_contiguous()):
+            raise ValueError("every layer's tensors must match the first layer's")
+        if lse is not None and (tuple(lse.shape) != (T, self._hq) or lse.dtype != self._f32
+                                or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous [T][h_q] float32 tensor")
+
+    def __call__(self, layer, q, k, v, out, lse=None):
+        self._check_rows(q, k, v, out, lse)
+        if self.kind == "decode":
+            st = self._fn(self._gp, self._cp, layer, self._n, q.data_ptr(), k.data_ptr(),
+                          v.data_ptr(), self._tab, self._stride, self._lens, self._max, self._slot,
+                          out.data_ptr(), _ptr(lse), self._ws[0], self._ws[1], self._st)
+        else:
+            st = self._fn(self._gp, self._cp, layer, self._n, q.data_ptr(), k.data_ptr(),
+                          v.data_ptr(), self._cu, self._lens, self._mq, self._tab, self._stride,
+                          self._slot, out.data_ptr(), _ptr(lse), self._ws[0], self._ws[1],
+                          self._st)
+        _check(st, "zp_paged_" + self.kind)
+
+
 def zp_prefill_workspace_size(geom: CacheGeometry, nreq):
     return lib().zp_prefill_workspace_size(C.byref(geom.c()), nreq)
 
