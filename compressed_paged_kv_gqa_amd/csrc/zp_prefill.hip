@@ -278,20 +278,25 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     if (t + 1 < ntiles) load_tile(t + 1);  // in flight while this tile is used
     const bool diag = t * kPKT + kPKT - 1 > ctx + q0;  // some key may follow some query
     bf16x8_t pop[2][2];
+    // Logits of both row tiles: each K operand read from LDS feeds two MFMAs.
+    floatx4 sk[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) sk[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int c = ks * 4 + q;
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(ct * 16 + cl, c) * 16));
+        sk[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[0][ks], sk[0][ct], 0, 0, 0);
+        sk[1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[1][ks], sk[1][ct], 0, 0, 0);
+      }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      floatx4 s[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) s[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const int c = ks * 4 + q;
-          const bf16x8_t kop = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(Ks + L::chunk_pos(ct * 16 + cl, c) * 16));
-          s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[k][ks], s[ct], 0, 0, 0);
-        }
+      floatx4 (&s)[4] = sk[k];
       // s[ct][v] = raw logit of key t*64 + ct*16 + 4q + v for this lane's
       // query; softmax in the exp2 domain with the scale folded into an FMA.
       // m is the running max of the scaled logits; it is raised (and O, l
