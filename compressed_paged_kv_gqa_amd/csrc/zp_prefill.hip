@@ -215,32 +215,53 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       qop[k][ks] = __builtin_bit_cast(bf16x8_t, ld16(qr + ks * 32 + q * 8));
   }
 
-  // K/V tile staging: thread -> (key pair kp, 16-byte chunk cc).
+  // K/V tile staging: thread -> (key pair kp, 16-byte chunk cc). The block
+  // ids of a tile are looked up one tile ahead of its K/V loads, and every
+  // load is issued unconditionally (keys past n_keys or on a bad block read
+  // the cache's first row and are zeroed when staged), so no wait on the
+  // lookups or on an earlier tile stalls the loads in flight.
   uint4 kr[L::PAIRS][2], vr[L::PAIRS][2];
+  int pg[L::PAIRS][2];
+  uint32_t live = 0;  // bit 2j+e: key (j, e) of the loaded tile is resident
+  bool bad = false;   // a needed key sits on an out-of-range block id
+  auto lookup = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < L::PAIRS; ++j) {
+      const int kp = (tid + 256 * j) / L::CH;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) pg[j][e] = tab[min(t * kPKT + 2 * kp + e, n_keys - 1) >> P.log2b];
+    }
+  };
   auto load_tile = [&](int t) {
+    live = 0;
 #pragma unroll
     for (int j = 0; j < L::PAIRS; ++j) {
       const int idx = tid + 256 * j;
       const int kp = idx / L::CH, cc = idx % L::CH;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int pos = t * kPKT + 2 * kp + e;
-        kr[j][e] = make_uint4(0, 0, 0, 0);
-        vr[j][e] = make_uint4(0, 0, 0, 0);
-        if (pos < n_keys) {
-          const int page = tab[pos >> P.log2b];
-          if (page >= 0 && page < P.num_blocks) {
-            const int64_t off = (((int64_t)page * P.h_kv + h) * P.b + (pos & (P.b - 1))) * D + cc * 8;
-            kr[j][e] = ld16(kcache + off);
-            vr[j][e] = ld16(vcache + off);
-          } else if (cc == 0) {
-            flag_error(P.err, ZP_DEVERR_BLOCK_ID);
-          }
-        }
+        const int pos = t * kPKT + 2 * kp + e, page = pg[j][e];
+        const bool ok = page >= 0 && page < P.num_blocks;
+        bad |= pos < n_keys && !ok;
+        const bool use = pos < n_keys && ok;
+        live |= uint32_t(use) << (2 * j + e);
+        const int64_t off = use ? (((int64_t)page * P.h_kv + h) * P.b + (pos & (P.b - 1))) * D + cc * 8 : 0;
+        kr[j][e] = ld16(kcache + off);
+        vr[j][e] = ld16(vcache + off);
       }
     }
   };
   auto store_tile = [&]() {
+    if (live != (1u << (2 * L::PAIRS)) - 1u) {  // tail tile or bad block: stage zeros
+#pragma unroll
+      for (int j = 0; j < L::PAIRS; ++j)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (!((live >> (2 * j + e)) & 1u)) {
+            kr[j][e].x = kr[j][e].y = kr[j][e].z = kr[j][e].w = 0u;
+            vr[j][e].x = vr[j][e].y = vr[j][e].z = vr[j][e].w = 0u;
+          }
+    }
 #pragma unroll
     for (int j = 0; j < L::PAIRS; ++j) {
       const int idx = tid + 256 * j;
@@ -271,11 +292,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) qpos[k] = ctx + q0 + ti0_of[k] + cl;  // this lane's query position
 
+  lookup(0);
   load_tile(0);
+  lookup(min(1, ntiles - 1));
   store_tile();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) load_tile(t + 1);  // in flight while this tile is used
+    lookup(min(t + 2, ntiles - 1));
     const bool diag = t * kPKT + kPKT - 1 > ctx + q0;  // some key may follow some query
     bf16x8_t pop[2][2];
     // Logits of both row tiles: each K operand read from LDS feeds two MFMAs.
@@ -366,6 +390,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
     }
   }
 
+  if (bad) flag_error(P.err, ZP_DEVERR_BLOCK_ID);
   // Finish: the four lane groups hold partial sums of each query's weights.
   const int last = ctx + qlen - 1;
   bf16_t* out = reinterpret_cast<bf16_t*>(P.out);
