@@ -89,6 +89,28 @@ __device__ __forceinline__ float dpp_f(float v) {
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Max / sum over lane pairs (l, l ^ 16) and (l, l ^ 32) with gfx950's row
+// swaps: a swap of (v, v) returns, in every lane, the two values of its pair
+// (v_permlane16_swap exchanges odd and even 16-lane rows, v_permlane32_swap
+// the wavefront halves), so a symmetric op of the two outputs is the pair's
+// result in both lanes. One VALU op each, no LDS round trip.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum / max over aligned groups of LANES lanes (LANES in 1..64), result in
 // every lane of the group. Groups of up to 16 lanes use DPP within a row.
 template <int LANES>

@@ -245,7 +245,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
         bad |= pos < n_keys && !ok;
         const bool use = pos < n_keys && ok;
         live |= uint32_t(use) << (2 * j + e);
-        const int64_t off = use ? (((int64_t)page * P.h_kv + h) * P.b + (pos & (P.b - 1))) * D + cc * 8 : 0;
+        // cache row (block, head, slot): fits 32 bits, as a layer's rows times
+        // 2D bytes is far below 2^31 * 256 bytes
+        const uint32_t row = use ? ((uint32_t)page * P.h_kv + h) * P.b + (pos & (P.b - 1)) : 0u;
+        const int64_t off = (int64_t)row * D + cc * 8;
         kr[j][e] = ld16(kcache + off);
         vr[j][e] = ld16(vcache + off);
       }
@@ -326,16 +329,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       // m is the running max of the scaled logits; it is raised (and O, l
       // rescaled) only when a tile's max exceeds it by more than kLazy, so
       // the weights exp2(x - m) stay below 2^kLazy.
+      if (diag) {  // one branch, taken on the last tile or two only
+        const int lim = qpos[k] - t * kPKT - 4 * q;  // last visible key offset
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (ct * 16 + v > lim) s[ct][v] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (diag && t * kPKT + ct * 16 + 4 * q + v > qpos[k]) s[ct][v] = -INFINITY;
-          mx = fmaxf(mx, s[ct][v]);
-        }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[ct][v]);
+      mx = xor32_max(xor16_max(mx));
       mx *= P.qk_scale;
       if (__builtin_amdgcn_read_exec() & __ballot(mx > m[k] + kPLazy)) {  // any lane: rescale
         const float mn = fmaxf(m[k], mx);
@@ -396,8 +403,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   bf16_t* out = reinterpret_cast<bf16_t*>(P.out);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    float lt = l[k] + shfl_xor_f(l[k], 16);
-    lt += shfl_xor_f(lt, 32);
+    const float lt = xor32_sum(xor16_sum(l[k]));
     const int i = q0 + ti0_of[k] + cl;
     if (i >= qlen) continue;
     const float inv = 1.0f / lt;
