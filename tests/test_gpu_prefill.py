@@ -146,14 +146,15 @@ def test_prefill_without_query_slot_captures_nothing():
     _run("f32", 64, 4, 1, 16, 8, [40, 37], [0, 16], noslot=0)
 
 
-def test_prefill_reports_bad_block_ids_without_faulting():
-    announce("prefill bad block id")
-    geom = zp.CacheGeometry(num_layers=1, num_blocks=8, block_size=16, num_kv_heads=2,
+@pytest.mark.parametrize("b", [16, 64])   # per-key lookups; one lookup per 64-key tile
+def test_prefill_reports_bad_block_ids_without_faulting(b):
+    announce(f"prefill bad block id b={b}")
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=8, block_size=b, num_kv_heads=2,
                             num_q_heads=8, head_dim=64, window=8, max_slots=1, n_max=2,
                             dtype="bf16")
     cache = zp.PagedKVCache(geom)
     tab = np.array([[0, 1, 99, 3]], np.int32)        # block 99 does not exist
-    T = 60
+    T = 3 * b + b // 2
     q = torch.randn((T, 8, 64), device="cuda").bfloat16()
     k = torch.randn((T, 2, 64), device="cuda").bfloat16()
     out = torch.zeros_like(q)
