@@ -151,6 +151,7 @@ __device__ __forceinline__ void emit_lse(const PrefillParams& P, int r, int c0, 
 constexpr int kPKT = 64;                 // keys per tile
 constexpr float kPLazy = 8.0f;           // lazy rescale threshold (log2 units)
 constexpr int kPRows = 128;              // query rows (token, head) per workgroup
+constexpr int kPfTabLds = 2048;          // block ids staged in LDS (tables up to this wide)
 constexpr int kVtStride = kPKT + 4;      // bf16 per row of the transposed V tile
 // Key slot of key `key` in row d of the transposed V tile: XOR with a
 // multiple of 4 keyed by d / 8, so the dword writes of lanes that hold
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   constexpr int NKS = D / 32;      // k-steps of the logits
   __shared__ __align__(16) char Ks[kPKT * L::ROWB];
   __shared__ __align__(16) bf16_t Vt[D * kVtStride];
+  __shared__ int32_t s_tab[BIG ? kPfTabLds : 1];  // the request's block ids (BIG)
 
   const int r = blockIdx.z, h = blockIdx.y;
   int c0, qlen, ctx;
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   bool bad = false;   // a needed key sits on an out-of-range block id
   auto lookup = [&](int t) {
     if constexpr (BIG) {
-      pg[0][0] = tab[(t * kPKT) >> P.log2b];
+      pg[0][0] = s_tab[(t * kPKT) >> P.log2b];
     } else {
 #pragma unroll
       for (int j = 0; j < L::PAIRS; ++j) {
@@ -323,6 +325,11 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) qpos[k] = ctx + q0 + ti0_of[k] + cl;  // this lane's query position
 
+  if constexpr (BIG) {  // stage the block ids once; the host caps table_stride
+    const int npg = (n_keys + P.b - 1) >> P.log2b;
+    for (int i = tid; i < npg; i += 256) s_tab[i] = tab[i];
+    __syncthreads();
+  }
   lookup(0);
   load_tile(0);
   lookup(min(1, ntiles - 1));
@@ -536,7 +543,7 @@ static void launch_prefill(const PrefillParams& P, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     constexpr int QT = kPRows / G;
     dim3 g((P.max_q_len + QT - 1) / QT, P.h_kv, P.nreq);
-    if (P.b >= kPKT)
+    if (P.b >= kPKT && P.table_stride <= kPfTabLds)
       hipLaunchKernelGGL((prefill_attn_kernel<D, G, true>), g, dim3(256), 0, s, P);
     else
       hipLaunchKernelGGL((prefill_attn_kernel<D, G, false>), g, dim3(256), 0, s, P);
