@@ -455,6 +455,276 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// 2a'. bf16 attention with K/V tiles copied straight into LDS (blocks of at
+// least 64 tokens, block table staged in LDS).
+//
+// The loads of a tile go from HBM to LDS without registers
+// (global_load_lds): K as 16-byte chunks, XOR-swizzled like the register
+// path; V one 4-byte word per lane, one key row per instruction, into rows
+// padded to 2D + 32 bytes. The Vᵀ operand of the PV product is then read
+// with the transposing LDS load (ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane l receives element l % 4 of the 8-byte pieces addressed by
+// lanes l / 4, l / 4 + 4, l / 4 + 8, l / 4 + 12. Lane (cl, q) addresses row
+// 4q + cl / 4 (plus the tile's key offset), columns d = 16dt + 4(cl % 4) ..
+// +3, and so receives V[4 consecutive keys][16dt + cl]: the A operand of Oᵀ
+// += Vᵀ·Pᵀ in the key order of the P registers. With the 32-byte pad the 16
+// rows one read touches fall in 8 distinct bank windows.
+//
+// Two LDS buffers alternate: tile t + 1 is in flight while tile t is used,
+// and one barrier per tile both retires the copies (the barrier waits for
+// them) and frees the buffer the next copy overwrites.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* gbl_void_ptr;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
+
+template <int D>
+struct PfDma {
+  static constexpr int CH = D * 2 / 16;          // 16-byte chunks per key row
+  static constexpr int KB = kPKT * D * 2;        // bytes of a K tile
+  static constexpr int KI = KB / 1024 / 4;       // 1 KiB K copies per wavefront per tile
+  static constexpr int VS = D * 2 + 32;          // bytes per padded V row
+  static constexpr int VB = kPKT * VS;           // bytes of a V tile
+  static constexpr int VL = D / 2;               // lanes that copy a V row (4 bytes each)
+  __device__ static int chunk_pos(int r, int c) { return r * CH + (c ^ (r % CH)); }
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams P) {
+  using L = PfDma<D>;
+  constexpr int QT = kPRows / G;   // query tokens per workgroup
+  constexpr int NDT = D / 16;      // output column tiles (head dims)
+  constexpr int NKS = D / 32;      // k-steps of the logits
+  __shared__ __align__(16) char Ks0[L::KB];
+  __shared__ __align__(16) char Ks1[L::KB];
+  __shared__ __align__(16) char Vs0[L::VB];
+  __shared__ __align__(16) char Vs1[L::VB];
+  __shared__ int32_t s_tab[kPfTabLds];
+
+  const int r = blockIdx.z, h = blockIdx.y;
+  int c0, qlen, ctx;
+  if (!chunk_of(P, r, &c0, &qlen, &ctx)) return;
+  const int ntq = (P.max_q_len + QT - 1) / QT;
+  const int qt = ntq - 1 - blockIdx.x;            // heavy (late) tiles first
+  const int q0 = qt * QT;
+  if (q0 >= qlen) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, cl = lane & 15;
+  const int q_last = min(qlen, q0 + QT) - 1;
+  const int n_keys = ctx + q_last + 1;             // keys any row of the tile may see
+  const int ntiles = (n_keys + kPKT - 1) / kPKT;
+  const int32_t* tab = P.tables + (int64_t)r * P.table_stride;
+  const bf16_t* kcache = reinterpret_cast<const bf16_t*>(P.kc) + P.kv_layer_off;
+  const bf16_t* vcache = reinterpret_cast<const bf16_t*>(P.vc) + P.kv_layer_off;
+  const int h_q = P.h_kv * G;
+
+  int gi_of[2], ti0_of[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int row0 = (2 * wv + k) * 16;
+    gi_of[k] = row0 / QT;
+    ti0_of[k] = row0 % QT;
+  }
+  bf16x8_t qop[2][NKS];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = min(q0 + ti0_of[k] + cl, qlen - 1);  // rows past the chunk are discarded
+    const bf16_t* qr = reinterpret_cast<const bf16_t*>(P.q) +
+                       ((int64_t)(c0 + i) * h_q + h * G + gi_of[k]) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qop[k][ks] = __builtin_bit_cast(bf16x8_t, ld16(qr + ks * 32 + q * 8));
+  }
+
+  {  // block ids of the keys this workgroup reads (chunk_of bounds them by table_stride)
+    const int npg = (n_keys + P.b - 1) >> P.log2b;
+    for (int i = tid; i < npg; i += 256) s_tab[i] = tab[i];
+  }
+  __syncthreads();
+
+  bool bad = false;  // a needed tile sits on an out-of-range block id
+  // Byte offset, inside a tile of K rows, of the 16-byte chunk this lane
+  // copies in each of its KI copies (LDS chunk p holds row p / CH, chunk
+  // (p % CH) ^ (row % CH)).
+  int koff[L::KI];
+#pragma unroll
+  for (int i = 0; i < L::KI; ++i) {
+    const int pidx = (wv * L::KI + i) * 64 + lane;
+    const int kr = pidx / L::CH, pc = pidx % L::CH;
+    koff[i] = (kr * D + (pc ^ (kr % L::CH)) * 8) * 2;
+  }
+  // Copy tile t into (Kb, Vb): K rows whole, V rows of existing keys; a bad
+  // block or keys past n_keys are written as zeros instead. Wavefront wv
+  // copies V rows 16wv .. 16wv + 15.
+  auto issue = [&](int t, char* Kb, char* Vb) __attribute__((always_inline)) {
+    const int page = s_tab[(t * kPKT) >> P.log2b];
+    const bool ok = page >= 0 && page < P.num_blocks;
+    bad |= !ok;
+    const int row0 = ((page * P.h_kv + h) * P.b) + ((t * kPKT) & (P.b - 1));
+    const int vrow0 = wv * (kPKT / 4);
+    if (ok) {
+      const char* kt = reinterpret_cast<const char*>(kcache + (int64_t)row0 * D);
+#pragma unroll
+      for (int i = 0; i < L::KI; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_void_ptr)(kt + koff[i]),
+                                         (lds_void_ptr)(Kb + (wv * L::KI + i) * 1024), 16, 0, 0);
+      const char* vt = reinterpret_cast<const char*>(vcache + (int64_t)(row0 + vrow0) * D) + 4 * lane;
+      if (t * kPKT + vrow0 + kPKT / 4 <= n_keys) {  // all 16 rows exist
+#pragma unroll
+        for (int i = 0; i < kPKT / 4; ++i)
+          if (lane < L::VL)
+            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(vt + i * D * 2),
+                                             (lds_void_ptr)(Vb + (vrow0 + i) * L::VS), 4, 0, 0);
+      } else {
+        for (int i = 0; i < kPKT / 4; ++i) {
+          if (lane < L::VL) {
+            if (t * kPKT + vrow0 + i < n_keys)
+              __builtin_amdgcn_global_load_lds((gbl_void_ptr)(vt + i * D * 2),
+                                               (lds_void_ptr)(Vb + (vrow0 + i) * L::VS), 4, 0, 0);
+            else
+              *reinterpret_cast<uint32_t*>(Vb + (vrow0 + i) * L::VS + 4 * lane) = 0u;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::KI; ++i)
+        *reinterpret_cast<uint4*>(Kb + ((wv * L::KI + i) * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < kPKT / 4; ++i)
+        if (lane < L::VL) *reinterpret_cast<uint32_t*>(Vb + (vrow0 + i) * L::VS + 4 * lane) = 0u;
+    }
+  };
+
+  floatx4 o[2][NDT];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[k][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-1.0e30f, -1.0e30f}, l[2] = {0.f, 0.f};
+  int qpos[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) qpos[k] = ctx + q0 + ti0_of[k] + cl;  // this lane's query position
+  const int vbase = (4 * q + (cl >> 2)) * L::VS + 8 * (cl & 3);       // Vᵀ read, key row 4q + cl/4
+
+  auto tile = [&](int t, const char* Kb, const char* Vb, char* Kn, char* Vn) __attribute__((always_inline)) {
+    if (t + 1 < ntiles) issue(t + 1, Kn, Vn);  // in flight while this tile is used
+    const bool diag = t * kPKT + kPKT - 1 > ctx + q0;  // some key may follow some query
+    bf16x8_t pop[2][2];
+    floatx4 sk[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) sk[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(Kb + L::chunk_pos(ct * 16 + cl, ks * 4 + q) * 16));
+        sk[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[0][ks], sk[0][ct], 0, 0, 0);
+        sk[1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[1][ks], sk[1][ct], 0, 0, 0);
+      }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      floatx4 (&s)[4] = sk[k];
+      if (diag) {  // one branch, taken on the last tile or two only
+        const int lim = qpos[k] - t * kPKT - 4 * q;  // last visible key offset
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (ct * 16 + v > lim) s[ct][v] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[ct][v]);
+      mx = xor32_max(xor16_max(mx));
+      mx *= P.qk_scale;
+      if (__builtin_amdgcn_read_exec() & __ballot(mx > m[k] + kPLazy)) {  // any lane: rescale
+        const float mn = fmaxf(m[k], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
+        m[k] = mn;
+        l[k] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[k][dt] *= alpha;
+      }
+      float ps = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
+          ps += p[ct][v];
+        }
+      l[k] += ps;
+      // P operands: k-step st holds keys {32st + 4q + v} and {32st + 16 + 4q + v}
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        b2 x0 = __builtin_convertvector(f2{p[2 * st][0], p[2 * st][1]}, b2);
+        b2 x1 = __builtin_convertvector(f2{p[2 * st][2], p[2 * st][3]}, b2);
+        b2 x2 = __builtin_convertvector(f2{p[2 * st + 1][0], p[2 * st + 1][1]}, b2);
+        b2 x3 = __builtin_convertvector(f2{p[2 * st + 1][2], p[2 * st + 1][3]}, b2);
+        const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1),
+                                   __builtin_bit_cast(uint32_t, x2), __builtin_bit_cast(uint32_t, x3));
+        pop[k][st] = __builtin_bit_cast(bf16x8_t, u);
+      }
+    }
+    // Oᵀ += Vᵀ Pᵀ: A = Vᵀ rows d = 16dt + cl from two transposing reads
+    // (keys 32st + 4q + 0..3 and 32st + 16 + 4q + 0..3).
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const char* va = Vb + vbase + 32 * st * L::VS + 32 * dt;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(va));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(va + 16 * L::VS));
+        typedef short v8i16_t __attribute__((ext_vector_type(8)));
+        const v8i16_t lh = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, lh);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          o[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[k][st], o[k][dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // tile t + 1 has landed; every wavefront is done with this one
+  };
+
+  issue(0, Ks0, Vs0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, Ks0, Vs0, Ks1, Vs1);
+    if (t + 1 < ntiles) tile(t + 1, Ks1, Vs1, Ks0, Vs0);
+  }
+
+  if (bad) flag_error(P.err, ZP_DEVERR_BLOCK_ID);
+  // Finish: the four lane groups hold partial sums of each query's weights.
+  const int last = ctx + qlen - 1;
+  bf16_t* out = reinterpret_cast<bf16_t*>(P.out);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float lt = xor32_sum(xor16_sum(l[k]));
+    const int i = q0 + ti0_of[k] + cl;
+    if (i >= qlen) continue;
+    const float inv = 1.0f / lt;
+    bf16_t* orow = out + ((int64_t)(c0 + i) * h_q + h * G + gi_of[k]) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint32_t w0 = uint32_t(f32_to_bf16(o[k][dt][0] * inv)) | (uint32_t(f32_to_bf16(o[k][dt][1] * inv)) << 16);
+      const uint32_t w1 = uint32_t(f32_to_bf16(o[k][dt][2] * inv)) | (uint32_t(f32_to_bf16(o[k][dt][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * q) = make_uint2(w0, w1);
+    }
+    if (q == 0) emit_lse(P, r, c0, i, ctx + i, last, h, G, gi_of[k], (m[k] + log2f(lt)) * kLn2);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 2b. Any dtype: one workgroup per (token, kv-head, request), decode-style.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G>
@@ -544,7 +814,7 @@ static void launch_prefill(const PrefillParams& P, hipStream_t s) {
     constexpr int QT = kPRows / G;
     dim3 g((P.max_q_len + QT - 1) / QT, P.h_kv, P.nreq);
     if (P.b >= kPKT && P.table_stride <= kPfTabLds)
-      hipLaunchKernelGGL((prefill_attn_kernel<D, G, true>), g, dim3(256), 0, s, P);
+      hipLaunchKernelGGL((prefill_attn_dma_kernel<D, G>), g, dim3(256), 0, s, P);
     else
       hipLaunchKernelGGL((prefill_attn_kernel<D, G, false>), g, dim3(256), 0, s, P);
   } else {
