@@ -169,7 +169,7 @@ struct PfTile {
   static constexpr int PAIRS = kPKT / 2 * CH / 256;
 };
 
-template <int D, int G, bool BIG>
+template <int D, int G>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   using L = PfTile<D>;
   constexpr int QT = kPRows / G;   // query tokens per workgroup
@@ -177,7 +177,6 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   constexpr int NKS = D / 32;      // k-steps of the logits
   __shared__ __align__(16) char Ks[kPKT * L::ROWB];
   __shared__ __align__(16) bf16_t Vt[D * kVtStride];
-  __shared__ int32_t s_tab[BIG ? kPfTabLds : 1];  // the request's block ids (BIG)
 
   const int r = blockIdx.z, h = blockIdx.y;
   int c0, qlen, ctx;
@@ -221,66 +220,38 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
   // ids of a tile are looked up one tile ahead of its K/V loads, and every
   // load is issued unconditionally (keys past n_keys or on a bad block read
   // a row that exists and are zeroed when staged), so no wait on the lookups
-  // or on an earlier tile stalls the loads in flight. With blocks of at
-  // least 64 tokens (BIG) a tile lies in one block: one wave-uniform lookup,
-  // and each lane's offset inside the tile never changes.
+  // or on an earlier tile stalls the loads in flight.
   uint4 kr[L::PAIRS][2], vr[L::PAIRS][2];
-  int pg[BIG ? 1 : L::PAIRS][2];
+  int pg[L::PAIRS][2];
   uint32_t live = 0;  // bit 2j+e: key (j, e) of the loaded tile is resident
   bool bad = false;   // a needed key sits on an out-of-range block id
   auto lookup = [&](int t) {
-    if constexpr (BIG) {
-      pg[0][0] = s_tab[(t * kPKT) >> P.log2b];
-    } else {
 #pragma unroll
-      for (int j = 0; j < L::PAIRS; ++j) {
-        const int kp = (tid + 256 * j) / L::CH;
+    for (int j = 0; j < L::PAIRS; ++j) {
+      const int kp = (tid + 256 * j) / L::CH;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) pg[j][e] = tab[min(t * kPKT + 2 * kp + e, n_keys - 1) >> P.log2b];
-      }
+      for (int e = 0; e < 2; ++e) pg[j][e] = tab[min(t * kPKT + 2 * kp + e, n_keys - 1) >> P.log2b];
     }
   };
   auto load_tile = [&](int t) {
     live = 0;
-    if constexpr (BIG) {
-      const int page = pg[0][0];
-      const bool ok = page >= 0 && page < P.num_blocks;
-      bad |= !ok;
-      // first row of the tile: (block, head, slot of key t * 64)
-      const uint32_t row0 = ok ? ((uint32_t)page * P.h_kv + h) * P.b + ((t * kPKT) & (P.b - 1)) : 0u;
-      const bf16_t* kt = kcache + (int64_t)row0 * D;
-      const bf16_t* vt = vcache + (int64_t)row0 * D;
 #pragma unroll
-      for (int j = 0; j < L::PAIRS; ++j) {
-        const int idx = tid + 256 * j;
-        const int kp = idx / L::CH, cc = idx % L::CH;
+    for (int j = 0; j < L::PAIRS; ++j) {
+      const int idx = tid + 256 * j;
+      const int kp = idx / L::CH, cc = idx % L::CH;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int off = (2 * kp + e) * D + cc * 8;
-          live |= uint32_t(ok && t * kPKT + 2 * kp + e < n_keys) << (2 * j + e);
-          kr[j][e] = ld16(kt + off);
-          vr[j][e] = ld16(vt + off);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < L::PAIRS; ++j) {
-        const int idx = tid + 256 * j;
-        const int kp = idx / L::CH, cc = idx % L::CH;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int pos = t * kPKT + 2 * kp + e, page = pg[j][e];
-          const bool ok = page >= 0 && page < P.num_blocks;
-          bad |= pos < n_keys && !ok;
-          const bool use = pos < n_keys && ok;
-          live |= uint32_t(use) << (2 * j + e);
-          // cache row (block, head, slot): fits 32 bits, as a layer's rows
-          // times 2D bytes is far below 2^31 * 256 bytes
-          const uint32_t row = use ? ((uint32_t)page * P.h_kv + h) * P.b + (pos & (P.b - 1)) : 0u;
-          const int64_t off = (int64_t)row * D + cc * 8;
-          kr[j][e] = ld16(kcache + off);
-          vr[j][e] = ld16(vcache + off);
-        }
+      for (int e = 0; e < 2; ++e) {
+        const int pos = t * kPKT + 2 * kp + e, page = pg[j][e];
+        const bool ok = page >= 0 && page < P.num_blocks;
+        bad |= pos < n_keys && !ok;
+        const bool use = pos < n_keys && ok;
+        live |= uint32_t(use) << (2 * j + e);
+        // cache row (block, head, slot): fits 32 bits, as a layer's rows
+        // times 2D bytes is far below 2^31 * 256 bytes
+        const uint32_t row = use ? ((uint32_t)page * P.h_kv + h) * P.b + (pos & (P.b - 1)) : 0u;
+        const int64_t off = (int64_t)row * D + cc * 8;
+        kr[j][e] = ld16(kcache + off);
+        vr[j][e] = ld16(vcache + off);
       }
     }
   };
@@ -325,11 +296,6 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) qpos[k] = ctx + q0 + ti0_of[k] + cl;  // this lane's query position
 
-  if constexpr (BIG) {  // stage the block ids once; the host caps table_stride
-    const int npg = (n_keys + P.b - 1) >> P.log2b;
-    for (int i = tid; i < npg; i += 256) s_tab[i] = tab[i];
-    __syncthreads();
-  }
   lookup(0);
   load_tile(0);
   lookup(min(1, ntiles - 1));
@@ -816,7 +782,7 @@ static void launch_prefill(const PrefillParams& P, hipStream_t s) {
     if (P.b >= kPKT && P.table_stride <= kPfTabLds)
       hipLaunchKernelGGL((prefill_attn_dma_kernel<D, G>), g, dim3(256), 0, s, P);
     else
-      hipLaunchKernelGGL((prefill_attn_kernel<D, G, false>), g, dim3(256), 0, s, P);
+      hipLaunchKernelGGL((prefill_attn_kernel<D, G>), g, dim3(256), 0, s, P);
   } else {
     dim3 g(P.max_q_len, P.h_kv, P.nreq);
     hipLaunchKernelGGL((prefill_simple_kernel<T, D, G>), g, dim3(256), 0, s, P);

@@ -48,13 +48,14 @@ def _sample_rows(rng, qlen, b, w, ctx, k=24):
     return sorted(rows)
 
 
-def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24, noslot=None):
+def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24, noslot=None,
+         min_stride=0):
     announce(f"prefill dtype={dtype} d={d} hq={h_q} hkv={h_kv} b={b} w={w} q={q_lens} ctx={ctx_lens}")
     nreq = len(q_lens)
     g = h_q // h_kv
     ntok = [c + n for c, n in zip(ctx_lens, q_lens)]
     nb = [-(-n // b) for n in ntok]
-    stride = max(nb) + 1
+    stride = max(max(nb) + 1, min_stride)
     pool = sum(nb) + 2
     geom = zp.CacheGeometry(num_layers=2, num_blocks=pool, block_size=b, num_kv_heads=h_kv,
                             num_q_heads=h_q, head_dim=d, window=w, max_slots=nreq + 1, n_max=2,
@@ -139,6 +140,12 @@ def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2] // c[3]}-b{c[4]}" for c in CASES])
 def test_prefill_parity(case):
     _run(*case)
+
+
+def test_prefill_wide_table_big_blocks():
+    """Blocks of >= 64 tokens normally take the kernel that stages the block
+    table in LDS; a table wider than that stage takes the general kernel."""
+    _run("bf16", 128, 16, 2, 64, 8, [300, 70], [0, 130], min_stride=3000)
 
 
 def test_prefill_without_query_slot_captures_nothing():
