@@ -290,14 +290,9 @@ int32_t zp::decode_launch_shape(const zp_geom* g, int32_t batch, int32_t max_seq
   //    is started but would be mostly empty (between 1 and 1.5 rounds):
   //    then each item is split in two, which evens the rounds out (5.5 vs
   //    5.1 TB/s at 112 sequences);
-  //  - below one round, but above a quarter of one, one 4-wave workgroup
-  //    per item (64 sequences: 5.86 TB/s vs 5.24 with 4-way splits), except
-  //    when the workgroups per CU, f = items / 256, sit just above 1 or 2:
-  //    then a few CUs run one workgroup more than the rest and set the
-  //    time, and splitting each item in two evens the CUs out (f = 2.06 ..
-  //    2.38, 66..76 sequences: +2..11%; f = 1.06..1.31, 34..42 sequences:
-  //    +1..4%; f = 1.03 and 2.44: -1..2%). 6 or 8 wavefronts per workgroup
-  //    measured slower than 4 at 24..88 sequences;
+  //  - below one round, but above a quarter of one, more splits only add
+  //    merge work: one 4-wave workgroup per item (64 sequences: 5.86 TB/s
+  //    vs 5.24 with 4-way splits);
   //  - at most a quarter of a round (<= 32 sequences of 8 kv-heads): one
   //    workgroup with a whole CU's waves per item, split only as far as
   //    needed to reach one round (32 sequences: 5.30 vs 4.34 TB/s).
@@ -314,10 +309,6 @@ int32_t zp::decode_launch_shape(const zp_geom* g, int32_t batch, int32_t max_seq
   } else if (4 * mw * items <= slots) {
     w = 4 * mw;
     splits = std::max<int64_t>(1, slots / (w * items));
-  } else {
-    const int64_t cus = slots / (4 * mw);
-    const int64_t whole = items / cus, frac100 = (items % cus) * 100 / cus;
-    if ((whole == 1 || whole == 2) && frac100 >= 6 && frac100 <= 38) splits = 2;
   }
   int64_t s = std::max<int64_t>(256, (len + splits - 1) / splits);
   s = std::min<int64_t>(s, int64_t(1000) * g->block_size);
