@@ -292,7 +292,11 @@ int32_t zp::decode_launch_shape(const zp_geom* g, int32_t batch, int32_t max_seq
   //    5.1 TB/s at 112 sequences);
   //  - below one round, but above a quarter of one, more splits only add
   //    merge work: one 4-wave workgroup per item (64 sequences: 5.86 TB/s
-  //    vs 5.24 with 4-way splits);
+  //    vs 5.24 with 4-way splits). Splitting in two where the workgroups
+  //    per CU sit just above 1 or 2 gained 2..11% on uniform 1793..2048
+  //    lengths (66..76 sequences) but cost 3% of the serving run's tokens/s
+  //    (ragged lengths), and 6 or 8 wavefronts per workgroup measured
+  //    slower than 4 at 24..88 sequences;
   //  - at most a quarter of a round (<= 32 sequences of 8 kv-heads): one
   //    workgroup with a whole CU's waves per item, split only as far as
   //    needed to reach one round (32 sequences: 5.30 vs 4.34 TB/s).
