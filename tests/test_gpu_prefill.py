@@ -96,6 +96,8 @@ def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24
     worst = 0.0
     for r in range(nreq):
         c0, n, ctx = cu[r], q_lens[r], ctx_lens[r]
+        if n == 0:       # an empty chunk: nothing appended, attended or captured
+            continue
         # appended rows bit-exact, context rows untouched
         for h in range(h_kv):
             Kr = Z.gather_sequence(Kd[layer, :, h], tab[r], ntok[r], b)
@@ -140,6 +142,11 @@ def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2] // c[3]}-b{c[4]}" for c in CASES])
 def test_prefill_parity(case):
     _run(*case)
+
+
+@pytest.mark.parametrize("b", [16, 256])   # register-staged and LDS-copy kernels
+def test_prefill_empty_chunks_in_a_batch(b):
+    _run("bf16", 128, 16, 2, b, 8, [70, 0, 300, 0], [0, 0, 40, 0])
 
 
 def test_prefill_wide_table_big_blocks():
