@@ -29,6 +29,8 @@ CASES = [
     ("bf16", 128, 8, 8, 16, 16, [95, 16], [0, 32]),
     ("bf16", 64, 16, 2, 128, 16, [640, 3], [130, 0]),
     ("f32", 128, 16, 2, 64, 2, [70, 129], [0, 64]),
+    ("bf16", 128, 8, 4, 64, 8, [200, 65], [0, 70]),     # g = 2 on the LDS-copy kernel
+    ("bf16", 64, 4, 4, 128, 16, [300, 1], [10, 0]),     # g = 1 on the LDS-copy kernel
 ]
 
 
