@@ -81,6 +81,11 @@ def parse_args():
     ap.add_argument("--serve-policies", default="hybrid,constrained")
     ap.add_argument("--no-serve", action="store_true",
                     help="skip the scheduled serving run in the default line")
+    ap.add_argument("--whole-run", action="store_true",
+                    help="only the whole run from the prompts (one JSON line)")
+    ap.add_argument("--whole-run-steps", type=int, default=2048)
+    ap.add_argument("--no-whole-run", action="store_true",
+                    help="skip the whole run in the default line")
     return ap.parse_args()
 
 
@@ -191,6 +196,63 @@ def run_gpu(args, phases):
     return dict(elapsed=elapsed, tokens=tokens, steps=K, launch_ms=launch_ms,
                 bytes_per_launch=bytes_per_launch, achieved_gbs=achieved,
                 compressions=eng.compressions - comp0, decode_ms_per_step=float(durs.sum(1).mean()))
+
+
+# --------------------------------------------------------------------------
+# Whole run of the 256-sequence workload from its prompts
+# --------------------------------------------------------------------------
+
+def whole_run_bench(steps, seed=SEED):
+    """The 36-layer, 256-sequence workload from the start: seeded prompt
+    lengths U[64, 512), every prompt through zp_paged_prefill (one output
+    token each), then `steps` decode steps in which each sequence compresses
+    when a block fill leaves it at N_max blocks (asynchronously, layer stride
+    8). tokens/s = output tokens / wall time from the first prefill to the
+    last decode step (Zipage's TPS, one GPU). Prompt and step q/k/v are
+    seeded device tensors; one set of prompt rows serves every layer."""
+    import torch
+    from compressed_paged_kv_gqa_amd import synth, zp
+    from compressed_paged_kv_gqa_amd.engine import DecodeEngine
+    plen = synth.rng(seed, 3, 0, "prompt_lengths").integers(64, 512, B)
+    geom = zp.CacheGeometry(num_layers=L, num_blocks=B * (NMAX + 1) + 16, block_size=BS,
+                            num_kv_heads=HKV, num_q_heads=HQ, head_dim=D, window=W,
+                            max_slots=B, n_max=NMAX, dtype="bf16")
+    eng = DecodeEngine(geom, zp.ScoreParams(), B, NMAX, layer_stride=8)
+    for s in range(B):
+        eng.add_request(s, int(plen[s]))
+    T = int(plen.sum())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 11)
+    pq = torch.randn((T, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    pk = torch.randn((T, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    pv = torch.randn((T, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    pout = torch.empty((T, HQ, D), dtype=torch.bfloat16, device="cuda")
+    lay = lambda x: x.unsqueeze(0).expand(L, *x.shape)   # same rows for every layer
+    nvar = 4
+    q = torch.randn((nvar, L, B, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((nvar, L, B, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((nvar, L, B, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((L, B, HQ, D), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"whole run: {B} prompts ({T} tokens), then {steps} decode steps")
+    t0 = time.perf_counter()
+    eng.prefill(list(range(B)), plen, lay(pq), lay(pk), lay(pv), lay(pout))
+    for i in range(steps):
+        eng.step(q[i % nvar], k[i % nvar], v[i % nvar], out)
+        if (i + 1) % 512 == 0:
+            log(f"whole run: {i + 1} steps, {eng.compressions} compressions")
+    torch.cuda.synchronize()
+    eng.side.synchronize()
+    elapsed = time.perf_counter() - t0
+    errs = zp.zp_workspace_errors(eng.dec_ws) | zp.zp_workspace_errors(eng.prefill_ws)
+    assert errs == 0, f"device errors {errs}"
+    tokens = B + eng.decoded_tokens
+    return {"workload": f"{B} sequences x {L} layers from prompts U[64,512) through prefill, "
+                        f"then {steps} decode steps with compression at N_max={NMAX}",
+            "tokens_per_s": round(tokens / elapsed, 1), "seconds": round(elapsed, 2),
+            "output_tokens": tokens, "prompt_tokens": T, "compressions": eng.compressions,
+            "final_resident_tokens": [int(min(r.n for r in eng.reqs.values())),
+                                      int(max(r.n for r in eng.reqs.values()))]}
 
 
 # --------------------------------------------------------------------------
@@ -559,6 +621,9 @@ def main():
         print(json.dumps(serve_bench(args.serve_requests, args.serve_mem_gib,
                                      args.serve_policies.split(","))), flush=True)
         return
+    if args.whole_run:
+        print(json.dumps(whole_run_bench(args.whole_run_steps)), flush=True)
+        return
     from compressed_paged_kv_gqa_amd import synth
     phases = synth.rng(SEED, 3, 0, "lengths").integers(0, BS, B)
     cpu = None
@@ -576,6 +641,12 @@ def main():
         ck = compress_kernel_bench()
         log("prefill in isolation")
         ck = {"compress": ck, "prefill": prefill_kernel_bench()}
+    whole = None
+    if not args.no_whole_run:
+        import torch
+        torch.cuda.empty_cache()
+        log("whole run from the prompts")
+        whole = whole_run_bench(args.whole_run_steps)
     serve = None
     if not args.no_serve:
         log("scheduled serving of the synthetic request stream")
@@ -612,6 +683,8 @@ def main():
     if ck is not None:
         line["compress_kernels"] = ck["compress"]
         line["prefill_kernels"] = ck["prefill"]
+    if whole is not None:
+        line["whole_run"] = whole
     if serve is not None:
         line["serve"] = serve
     if cpu is not None:

@@ -17,7 +17,7 @@ import numpy as np
 
 PURPOSE = {"prompt_k": 1, "prompt_v": 2, "prompt_q": 3, "step_q": 4, "step_k": 5,
            "step_v": 6, "heavy": 7, "gscore": 8, "scores": 9, "lengths": 10, "misc": 11,
-           "serve": 12, "serve_stream": 13}
+           "serve": 12, "serve_stream": 13, "prompt_lengths": 14}
 
 
 def rng(seed, config, layer, purpose):
