@@ -17,13 +17,15 @@ One step = one decode token for every active sequence through all 36 layers
 Prints one JSON line (metric, value = decode tokens/s, roofline of the decode
 kernel measured with HIP events around every launch, cpu_baseline = the float64
 oracle on the host cores on a bounded sample of the same workload). The line
-also carries the compression and prefill kernels timed in isolation, and
-`serve`: a synthetic request stream served to completion by the library's
+also carries the compression and prefill kernels timed in isolation,
+`whole_run`: the same workload from seeded prompts through prefill, decode and
+the compressions as they fall due (output tokens per second of the whole run),
+and `serve`: a synthetic request stream served to completion by the library's
 scheduler (hybrid and constrained), output tokens per second.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                  [--no-compress-kernels] [--no-serve]
-  python bench.py --serve | --compress-kernels | --prefill-kernels   # one part only
+                  [--no-compress-kernels] [--no-whole-run] [--no-serve]
+  python bench.py --serve | --whole-run | --compress-kernels | --prefill-kernels   # one part
   python bench.py --copy-calibration     # plain device copy of known size
 """
 from __future__ import annotations
