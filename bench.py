@@ -586,15 +586,23 @@ def cpu_baseline(phases, steps):
 
 # --------------------------------------------------------------------------
 
+def decode_source_sha():
+    """First 16 hex digits of the SHA-256 of the decode kernel's sources (the
+    kernel file and the device headers it includes, in that order)."""
+    h = hashlib.sha256()
+    for name in ("zp_decode.hip", "zp_device.h", "zp_internal.h"):
+        with open(os.path.join(ROOT, "compressed_paged_kv_gqa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def traffic_from_profiles():
     """HBM bytes per decode launch from the committed rocprofv3 PMC summary,
     if it was taken with the current decode kernel source."""
     path = os.path.join(ROOT, "profiles", f"paged_decode_pmc_{WORKLOAD}.md")
-    src = os.path.join(ROOT, "compressed_paged_kv_gqa_amd", "csrc", "zp_decode.hip")
     if not os.path.exists(path):
         return None
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    sha = decode_source_sha()
     text = open(path).read()
     m_sha = re.search(r"decode_source_sha256_16:\s*([0-9a-f]+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)

@@ -194,6 +194,12 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
   }
+  // bf16 rows of 16 lanes carrying g * U = 16 (head, row) dot products per
+  // chunk take the transposing reduction (see process); lane sub then owns
+  // (head sub / U, row sub % U): its running max mj = m[sub / U] and its
+  // weight sum lacc.
+  constexpr bool kTR = sizeof(T) == 2 && LPR == 16 && G * U == 16;
+  float lacc = 0.f, mj = kNoMax;
 
   const int nchunks = (t1 - t0 + CHUNK - 1) / CHUNK;
 
@@ -233,6 +239,50 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
     }
     // Raw q.k (unscaled); the 1/sqrt(d) * log2(e) factor enters the exp.
     float s[G][U];
+    const float sc2 = P.qk_scale;
+    if constexpr (kTR) {
+      // The row group's 16 (head, row) dot products: one transposing sum
+      // leaves (head sub / U, row sub % U) in lane sub; the chunk maximum of
+      // a head is a max over its 4 lanes (one quad), the weight is one
+      // exp2 per lane, and the 16 weights are broadcast back to every lane
+      // of the row group for o += p v. l accumulates the lane's own weights
+      // (lacc) and is summed over each quad after the last chunk.
+      float part[G * U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[h * U + u] = q.dot(h, kr[u]);
+      float sj = row_transpose_sum16(part, sub);
+      if (base + CHUNK > t1 || off < 0) {
+        // Masked rows (see below): weight exactly 0, V zeroed.
+        if (!(off >= 0 && base + (sub % U) * RPW + row < t1)) sj = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (!(off >= 0 && base + u * RPW + row < t1)) vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      float cq = max_raw(sj, dpp_z<DPP_QUAD_XOR1>(sj));
+      cq = max_raw(cq, dpp_z<DPP_QUAD_XOR2>(cq));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float cm = bcast_row_lane(cq, 4 * h) * sc2;  // head h's chunk max
+        if (cm > m[h] + kLazy) {
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - cm);
+          if (sub / U == h) {
+            lacc *= alpha;
+            mj = cm;
+          }
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+          m[h] = cm;
+        }
+      }
+      const float pj = __builtin_amdgcn_exp2f(fmaf(sj, sc2, -mj));
+      lacc += pj;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[h][u] = bcast_row_lane(pj, h * U + u);
+    } else {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -249,7 +299,6 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
         if (!valid) vr[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    const float sc2 = P.qk_scale;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float cm = s[h][0];
@@ -266,6 +315,7 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
 #pragma unroll
       for (int u = 0; u < U; ++u) s[h][u] = __builtin_amdgcn_exp2f(fmaf(s[h][u], sc2, -m[h]));  // p
     }
+    }
     if constexpr (sizeof(T) == 2) {
       // o += p v over token pairs (u, u+1) with packed-bf16 dot products:
       // the weights enter the numerator rounded to bf16 (the normaliser l
@@ -273,10 +323,12 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
       // dimension with v_perm.
       typedef float f2 __attribute__((ext_vector_type(2)));
       typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      if constexpr (!kTR) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int u = 0; u < U; ++u) l[h] += s[h][u];
+          for (int u = 0; u < U; ++u) l[h] += s[h][u];
+      }
 #pragma unroll
       for (int u = 0; u < U; u += 2) {
         b2 pp[G];
@@ -333,6 +385,12 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
     }
   }
 
+  if constexpr (kTR) {  // l of every head from its quad of lanes
+    float lq = lacc + dpp_z<DPP_QUAD_XOR1>(lacc);
+    lq += dpp_z<DPP_QUAD_XOR2>(lq);
+#pragma unroll
+    for (int h = 0; h < G; ++h) l[h] = bcast_row_lane(lq, 4 * h);
+  }
   // Merge the token-row groups of the wavefront.
 #pragma unroll
   for (int h = 0; h < G; ++h) {

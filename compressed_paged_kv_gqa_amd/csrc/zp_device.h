@@ -80,10 +80,24 @@ constexpr int DPP_QUAD_XOR1 = 0xB1;     // [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;     // [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_MIRROR = 0x140;
+// Within each 16-lane row: lane i reads lane i + 4 (row_shl:4), lane i - 4
+// (row_shr:4), lane (i + 8) mod 16 (row_ror:8, i.e. i ^ 8), and lane n of the
+// row (row_newbcast:n, gfx90a and later). Sources outside the row give the
+// `old` operand (0 in dpp_f) or 0 (dpp_z).
+constexpr int DPP_ROW_SHL4 = 0x104;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_ROR8 = 0x128;
+constexpr int DPP_ROW_NEWBCAST0 = 0x150;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Same move with bound_ctrl set: lanes whose source is outside the row read
+// 0 without a prior write of the destination.
+template <int CTRL>
+__device__ __forceinline__ float dpp_z(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
@@ -116,6 +130,58 @@ __device__ __forceinline__ float xor16_sum(float v) {
 __device__ __forceinline__ float xor32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lane n (0..15) of each 16-lane row, in every lane of the row; n must fold
+// to a constant (unrolled loops), each case being one DPP move.
+__device__ __forceinline__ float bcast_row_lane(float v, int n) {
+  switch (n & 15) {
+    case 0: return dpp_z<DPP_ROW_NEWBCAST0 + 0>(v);
+    case 1: return dpp_z<DPP_ROW_NEWBCAST0 + 1>(v);
+    case 2: return dpp_z<DPP_ROW_NEWBCAST0 + 2>(v);
+    case 3: return dpp_z<DPP_ROW_NEWBCAST0 + 3>(v);
+    case 4: return dpp_z<DPP_ROW_NEWBCAST0 + 4>(v);
+    case 5: return dpp_z<DPP_ROW_NEWBCAST0 + 5>(v);
+    case 6: return dpp_z<DPP_ROW_NEWBCAST0 + 6>(v);
+    case 7: return dpp_z<DPP_ROW_NEWBCAST0 + 7>(v);
+    case 8: return dpp_z<DPP_ROW_NEWBCAST0 + 8>(v);
+    case 9: return dpp_z<DPP_ROW_NEWBCAST0 + 9>(v);
+    case 10: return dpp_z<DPP_ROW_NEWBCAST0 + 10>(v);
+    case 11: return dpp_z<DPP_ROW_NEWBCAST0 + 11>(v);
+    case 12: return dpp_z<DPP_ROW_NEWBCAST0 + 12>(v);
+    case 13: return dpp_z<DPP_ROW_NEWBCAST0 + 13>(v);
+    case 14: return dpp_z<DPP_ROW_NEWBCAST0 + 14>(v);
+    default: return dpp_z<DPP_ROW_NEWBCAST0 + 15>(v);
+  }
+}
+
+// Transposing sum over each 16-lane row: x[i] (i = 0..15) are per-lane
+// partial values; lane j of the row returns the row's total of x[j]. Each
+// step halves the values a lane carries: at the step on lane bit k, a lane
+// keeps the half whose index bit k equals its own bit k and sends the other
+// half to its partner lane (bit k flipped), which keeps that half. 15 adds
+// and ~36 selects/moves, against 64 adds for 16 separate all-reduces.
+__device__ __forceinline__ float row_transpose_sum16(const float (&x)[16], int j) {
+  const bool b0 = j & 1, b1 = j & 2, b2 = j & 4, b3 = j & 8;
+  float w1[8], w2[4], w3[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float keep = b0 ? x[2 * k + 1] : x[2 * k], send = b0 ? x[2 * k] : x[2 * k + 1];
+    w1[k] = keep + dpp_z<DPP_QUAD_XOR1>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = b1 ? w1[2 * k + 1] : w1[2 * k], send = b1 ? w1[2 * k] : w1[2 * k + 1];
+    w2[k] = keep + dpp_z<DPP_QUAD_XOR2>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = b2 ? w2[2 * k + 1] : w2[2 * k], send = b2 ? w2[2 * k] : w2[2 * k + 1];
+    const float up = dpp_z<DPP_ROW_SHL4>(send), dn = dpp_z<DPP_ROW_SHR4>(send);
+    w3[k] = keep + (b2 ? dn : up);
+  }
+  const float keep = b3 ? w3[1] : w3[0], send = b3 ? w3[0] : w3[1];
+  return keep + dpp_z<DPP_ROW_ROR8>(send);
 }
 
 // Sum / max over aligned groups of LANES lanes (LANES in 1..64), result in
