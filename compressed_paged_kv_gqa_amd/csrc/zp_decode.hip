@@ -22,9 +22,12 @@
 //    that extra launch on this chip (measured);
 //  * the block ids a workgroup needs are staged in LDS first, so no K/V load
 //    waits behind a block-table load;
-//  * the token being decoded is taken from k_new / v_new directly by the
-//    split that covers it, which also writes it to its page: no other
-//    workgroup reads that slot, so append and attention need no extra launch.
+//  * K/V chunks come through buffer loads; a chunk past the end gets an
+//    empty range (zeros, no memory read), so the next chunk's loads are
+//    issued unconditionally and the waits cover only the chunk in use;
+//  * the token being decoded is written to its slot, before the chunk loop,
+//    by the one wavefront that reads that chunk: no other workgroup reads
+//    that slot, so append and attention need no extra launch.
 #include <cmath>
 
 #include "zp_device.h"
@@ -148,7 +151,8 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
   const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int n = P.seq_lens[seq];
   if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, made scalar
   const int h_q = P.h_kv * G;
   const int64_t out_row = (int64_t)seq * h_q + (int64_t)kvh * G;  // first head of the group
 
@@ -202,6 +206,9 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
   float lacc = 0.f, mj = kNoMax;
 
   const int nchunks = (t1 - t0 + CHUNK - 1) / CHUNK;
+  // The first 64 block ids also sit one per lane: a chunk takes its id with
+  // one lane read (no LDS access, no address register) in the loop.
+  const int pv = lane < npg ? sm_pages[lane] : -1;
 
   // Element offset of this lane's row 0 in chunk c, or -1 for a bad block id.
   auto chunk_offset = [&](int c) -> int64_t {
@@ -210,33 +217,40 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
     if (page < 0 || page >= P.num_blocks) return -1;
     return (int64_t)page * page_elems + lane_off + (int64_t)(base & (b - 1)) * D;
   };
-  auto load_chunk = [&](int c, uint4 (&kr)[U], uint4 (&vr)[U]) -> int64_t {
-    const int64_t off = chunk_offset(c);
-    const int64_t safe = off < 0 ? lane_off : off;  // a valid address; the chunk is masked
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      kr[u] = ld16_nt(kc + safe + (int64_t)u * RPW * D);
-      vr[u] = ld16_nt(vc + safe + (int64_t)u * RPW * D);
-    }
-    return off;
-  };
-  auto process = [&](int c, uint4 (&kr)[U], uint4 (&vr)[U], int64_t off) {
-    const int base = t0 + c * CHUNK;
-    if (off < 0 && lane == 0) flag_error(P.err, ZP_DEVERR_BLOCK_ID);
-    if (base <= n - 1 && n - 1 < base + CHUNK) {
-      // The token being decoded: take it from k_new / v_new and append it.
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (base + u * RPW + row == n - 1) {
-          kr[u] = ld16(knew);
-          vr[u] = ld16(vnew);
-          if (off >= 0) {
-            st16(kc + off + (int64_t)u * RPW * D, kr[u]);
-            st16(vc + off + (int64_t)u * RPW * D, vr[u]);
-          }
-        }
+  // Chunk c through buffer loads whose range is the chunk's CHUNK token rows
+  // in its (block, kv-head) slice of K (or V). A chunk past the end, or on a
+  // bad block id, gets an empty range: its loads return zeros and read no
+  // memory. So the next chunk's loads are issued unconditionally, and the
+  // compiler's waits in the loop cover only the chunk in use. Returns 0, or
+  // -1 for a bad block id (the chunk is then masked).
+  const uint32_t lane_bytes = (uint32_t)((row * D + sub * EPL) * sizeof(T));
+  auto load_chunk = [&](int c, uint4 (&kr)[U], uint4 (&vr)[U]) __attribute__((always_inline)) -> int64_t {
+    int64_t first = 0;  // element offset of the chunk's first row
+    int bytes = 0, bad = 0;
+    if (c < nchunks) {
+      const int base = t0 + c * CHUNK;
+      const int bi = (base >> P.log2b) - pg0;
+      const int page = bi < 64 ? __builtin_amdgcn_readlane(pv, bi)
+                                : __builtin_amdgcn_readfirstlane(sm_pages[bi]);
+      if (page >= 0 && page < P.num_blocks) {
+        first = (int64_t)page * page_elems + (int64_t)kvh * b * D + (int64_t)(base & (b - 1)) * D;
+        bytes = CHUNK * D * (int)sizeof(T);
+      } else {
+        bad = -1;
       }
     }
+    const BufRsrc rk = make_rsrc(kc + first, bytes);
+    const BufRsrc rv = make_rsrc(vc + first, bytes);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kr[u] = ldbuf16_nt(rk, lane_bytes + (uint32_t)(u * RPW * D * sizeof(T)));
+      vr[u] = ldbuf16_nt(rv, lane_bytes + (uint32_t)(u * RPW * D * sizeof(T)));
+    }
+    return bad;
+  };
+  auto process = [&](int c, uint4 (&kr)[U], uint4 (&vr)[U], int64_t off) __attribute__((always_inline)) {
+    const int base = t0 + c * CHUNK;
+    if (off < 0 && lane == 0) flag_error(P.err, ZP_DEVERR_BLOCK_ID);
     // Raw q.k (unscaled); the 1/sqrt(d) * log2(e) factor enters the exp.
     float s[G][U];
     const float sc2 = P.qk_scale;
@@ -365,23 +379,35 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
     }
   };
 
+  // The token being decoded goes to its slot first, written by the wavefront
+  // whose chunk holds it; that wavefront reads it back with the rest of the
+  // chunk, so the chunk loop carries no special case. The wait retires the
+  // two stores before any load of the loop is issued.
+  if (t0 <= n - 1 && n - 1 < t1 && ((n - 1 - t0) / CHUNK) % WAVES == wv) {
+    const int r = (n - 1 - t0) % CHUNK;  // u * RPW + row of the token in its chunk
+    const int64_t off = chunk_offset((n - 1 - t0) / CHUNK);
+    if (off >= 0 && r % RPW == row) {
+      const int64_t at = off + (int64_t)(r / RPW) * RPW * D;
+      st16(kc + at, ld16(knew));
+      st16(vc + at, ld16(vnew));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
   // Chunks c = wv, wv + 4, ...; the next chunk's loads are issued before the
   // current chunk is processed (two register buffers).
   {
     uint4 ka[U], va[U], kb[U], vb[U];
     int c = wv;
-    int64_t offa = 0, offb = 0;
-    if (c < nchunks) offa = load_chunk(c, ka, va);
+    int64_t offa = load_chunk(c, ka, va), offb;
     while (c < nchunks) {
-      int cn = c + WAVES;
-      if (cn < nchunks) offb = load_chunk(cn, kb, vb);
+      offb = load_chunk(c + WAVES, kb, vb);
       process(c, ka, va, offa);
-      c = cn;
+      c += WAVES;
       if (c >= nchunks) break;
-      cn = c + WAVES;
-      if (cn < nchunks) offa = load_chunk(cn, ka, va);
+      offa = load_chunk(c + WAVES, ka, va);
       process(c, kb, vb, offb);
-      c = cn;
+      c += WAVES;
     }
   }
 

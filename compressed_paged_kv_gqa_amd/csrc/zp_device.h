@@ -74,6 +74,23 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Raw buffer loads. A resource covers [base, base + bytes); a load whose
+// offset falls outside it returns zeros and reads no memory, so an empty
+// resource (bytes = 0) turns a load into a no-op that still counts as an
+// outstanding load. Flags word: 32-bit data, no swizzle (the value CDNA
+// buffer resources take).
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes at byte offset `off` of the resource, non-temporal (cache-policy
+// bit 1).
+__device__ __forceinline__ uint4 ldbuf16_nt(BufRsrc r, uint32_t off) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const u4v t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // ---- cross-lane moves ------------------------------------------------------
 // DPP controls (GCN/CDNA encoding): quad_perm selectors, row mirrors.
 constexpr int DPP_QUAD_XOR1 = 0xB1;     // [1,0,3,2]

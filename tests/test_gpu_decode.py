@@ -121,6 +121,19 @@ def test_decode_parity(case):
     _run_case(*case)
 
 
+def test_decode_split_over_many_small_blocks():
+    """A split that spans more than 64 block ids. With 256 (sequence,
+    kv-head) items at this shape the launch covers each sequence with one
+    split (one workgroup of a CU's wavefronts per item), so a 1300-token
+    sequence of 16-token blocks walks 82 block ids: the first 64 come from
+    a lane of a register, the rest from LDS."""
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(1, 300, 128)]
+    for r, n in zip((3, 40, 77, 127), (1025, 1040, 1299, 1300)):
+        lens[r] = n
+    _run_case("bf16", 128, 8, 2, 16, 16, lens)
+
+
 def test_decode_skips_rows_with_zero_length():
     _run_case("bf16", 128, 32, 8, 256, 16, [300, 1000, 2000], skip_rows=(1,))
 
