@@ -287,9 +287,11 @@ int32_t zp::decode_launch_shape(const zp_geom* g, int32_t batch, int32_t max_seq
   // on MI355X at the Qwen3-8B decode shape (1793..2048 resident tokens):
   //  - 4 wavefronts per item fill the GPU at least once from 96 sequences
   //    on; one workgroup per item is best there, except when a second round
-  //    is started but would be mostly empty (between 1 and 1.5 rounds):
-  //    then each item is split in two, which evens the rounds out (5.5 vs
-  //    5.1 TB/s at 112 sequences);
+  //    is started but would be almost empty (between 1 and 1.125 rounds):
+  //    then each item is split in two, which evens the rounds out (97 and
+  //    104 sequences: +2.6% and +3.2%). From 112 sequences on the unsplit
+  //    launch is faster (+2.0..3.7% at 112..144; 256 and 512 sequences:
+  //    +4.4% and +4.9%);
   //  - below one round, but above a quarter of one, more splits only add
   //    merge work: one 4-wave workgroup per item (64 sequences: 5.86 TB/s
   //    vs 5.24 with 4-way splits). Splitting in two where the workgroups
@@ -309,7 +311,7 @@ int32_t zp::decode_launch_shape(const zp_geom* g, int32_t batch, int32_t max_seq
   const int64_t len = std::max<int32_t>(max_seq_len, 1);
   int64_t w = 4, splits = 1;
   if (4 * items >= slots) {
-    if (4 * items > slots && 2 * 4 * items < 3 * slots) splits = 2;
+    if (4 * items > slots && 8 * 4 * items < 9 * slots) splits = 2;
   } else if (4 * mw * items <= slots) {
     w = 4 * mw;
     splits = std::max<int64_t>(1, slots / (w * items));

@@ -43,6 +43,20 @@ def test_bad_geometry_is_rejected_on_the_host(bad):
     assert zp.lib().zp_decode_workspace_size(C.byref(g), 1, 16) == 0
 
 
+@pytest.mark.parametrize("batch,split", [(64, False), (96, False), (97, True), (107, True),
+                                         (108, False), (128, False), (256, False)])
+def test_decode_launch_splits_only_just_past_one_round(batch, split):
+    """At the Qwen3-8B decode shape (3 resident 4-wavefront workgroups per
+    CU, 768 in all) a batch whose (sequence, kv-head) items fill more than
+    one round but at most 1.125 rounds is split in two (the split partials
+    then need workspace); below one round and from 108 sequences on it is
+    not."""
+    g = _geom(num_layers=36, num_blocks=4096, block_size=256, num_kv_heads=8, num_q_heads=32,
+              head_dim=128, window=16, max_slots=batch, n_max=8, dtype="bf16").c()
+    need = zp.lib().zp_decode_workspace_size(C.byref(g), batch, 2048)
+    assert (need > 256) == split
+
+
 def test_short_workspace_and_null_buffers_are_rejected():
     g = _geom().c()
     cache = zp.Cache(1, 1, 1, None)
