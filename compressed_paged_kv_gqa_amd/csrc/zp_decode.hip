@@ -149,9 +149,22 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
   __shared__ int sm_pages[kMaxSplitPages];
 
   const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
-  const int n = P.seq_lens[seq];
-  if (n <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t* tab = P.tables + (int64_t)seq * P.table_stride;
+  // Block ids of this split, requested before the sequence length is read:
+  // from the split's first block as many as a split can span (within the
+  // table row), so the table load does not wait for the length.
+  const int t0 = split * P.split_tokens;
+  const int pg0 = t0 >> P.log2b;
+  const int span = min(min(P.table_stride - pg0, ((P.split_tokens - 1) >> P.log2b) + 2), kMaxSplitPages);
+  const int n = P.seq_lens[seq];
+  const int pg_first = tid < span ? tab[pg0 + tid] : 0;  // in flight with the length
+  // This lane's 16 bytes of the decoded token's k and v (one of the
+  // wavefronts appends them below).
+  const int64_t new_off = ((int64_t)seq * P.h_kv + kvh) * D + (lane % (D / Vec16<T>::N)) * Vec16<T>::N;
+  const uint4 k_tok = ld16(reinterpret_cast<const T*>(P.k_new) + new_off);
+  const uint4 v_tok = ld16(reinterpret_cast<const T*>(P.v_new) + new_off);
+  if (n <= 0) return;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, made scalar
   const int h_q = P.h_kv * G;
   const int64_t out_row = (int64_t)seq * h_q + (int64_t)kvh * G;  // first head of the group
@@ -168,26 +181,21 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
   }
   const int nsplit = (n + P.split_tokens - 1) / P.split_tokens;
   if (split >= nsplit) return;
-  const int t0 = split * P.split_tokens;
   const int t1 = min(n, t0 + P.split_tokens);
   const int row = lane / LPR;
   const int sub = lane % LPR;
   const int b = P.b;
-  const int32_t* tab = P.tables + (int64_t)seq * P.table_stride;
   T* kc = reinterpret_cast<T*>(P.kc) + P.kv_layer_off;
   T* vc = reinterpret_cast<T*>(P.vc) + P.kv_layer_off;
-  const T* knew = reinterpret_cast<const T*>(P.k_new) + ((int64_t)seq * P.h_kv + kvh) * D + sub * EPL;
-  const T* vnew = reinterpret_cast<const T*>(P.v_new) + ((int64_t)seq * P.h_kv + kvh) * D + sub * EPL;
   const int64_t lane_off = (int64_t)kvh * b * D + (int64_t)row * D + sub * EPL;  // within a page
   const int64_t page_elems = (int64_t)P.h_kv * b * D;
 
   QRegs<T, G> q;
   q.load(reinterpret_cast<const T*>(P.q) + out_row * D + sub * EPL, D);
 
-  // Block ids of this split (at most kMaxSplitPages by construction).
-  const int pg0 = t0 >> P.log2b;
-  const int npg = ((t1 - 1) >> P.log2b) - pg0 + 1;
-  for (int i = tid; i < npg; i += NT) sm_pages[i] = tab[pg0 + i];
+  const int npg = ((t1 - 1) >> P.log2b) - pg0 + 1;  // block ids the split uses (<= span)
+  if (tid < span) sm_pages[tid] = pg_first;
+  for (int i = tid + NT; i < npg; i += NT) sm_pages[i] = tab[pg0 + i];
   __syncthreads();
 
   float m[G], l[G], o[G][EPL];
@@ -388,8 +396,8 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
     const int64_t off = chunk_offset((n - 1 - t0) / CHUNK);
     if (off >= 0 && r % RPW == row) {
       const int64_t at = off + (int64_t)(r / RPW) * RPW * D;
-      st16(kc + at, ld16(knew));
-      st16(vc + at, ld16(vnew));
+      st16(kc + at, k_tok);
+      st16(vc + at, v_tok);
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
