@@ -209,8 +209,8 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (LANES >= 4) v += dpp_f<DPP_QUAD_XOR2>(v);
   if constexpr (LANES >= 8) v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
   if constexpr (LANES >= 16) v += dpp_f<DPP_ROW_MIRROR>(v);
-  if constexpr (LANES >= 32) v += shfl_xor_f(v, 16);
-  if constexpr (LANES >= 64) v += shfl_xor_f(v, 32);
+  if constexpr (LANES >= 32) v = xor16_sum(v);
+  if constexpr (LANES >= 64) v = xor32_sum(v);
   return v;
 }
 
@@ -220,23 +220,29 @@ __device__ __forceinline__ float group_max(float v) {
   if constexpr (LANES >= 4) v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
   if constexpr (LANES >= 8) v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
   if constexpr (LANES >= 16) v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
-  if constexpr (LANES >= 32) v = fmaxf(v, shfl_xor_f(v, 16));
-  if constexpr (LANES >= 64) v = fmaxf(v, shfl_xor_f(v, 32));
+  if constexpr (LANES >= 32) v = xor16_max(v);
+  if constexpr (LANES >= 64) v = xor32_max(v);
   return v;
 }
 
 // Sum / max across lanes whose ids differ only in bits >= log2(FROM), i.e.
 // over the 64/FROM groups of FROM lanes, for FROM in {1,..,64}.
+// The steps across 16-lane rows (lane ^ 16, lane ^ 32) take the row swaps
+// above; the sums equal those of a shuffle bit for bit (a + b = b + a).
 template <int FROM>
 __device__ __forceinline__ float across_groups_sum(float v) {
 #pragma unroll
-  for (int m = FROM; m < 64; m <<= 1) v += shfl_xor_f(v, m);
+  for (int m = FROM; m < 16; m <<= 1) v += shfl_xor_f(v, m);
+  if constexpr (FROM <= 16) v = xor16_sum(v);
+  if constexpr (FROM <= 32) v = xor32_sum(v);
   return v;
 }
 template <int FROM>
 __device__ __forceinline__ float across_groups_max(float v) {
 #pragma unroll
-  for (int m = FROM; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  for (int m = FROM; m < 16; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  if constexpr (FROM <= 16) v = xor16_max(v);
+  if constexpr (FROM <= 32) v = xor32_max(v);
   return v;
 }
 
