@@ -11,9 +11,11 @@
 //  1. select_kernel, one workgroup per (kv-head, request, layer): radix
 //     select over order-preserving 32-bit keys of the fp32 scores (4 passes
 //     of 8 bits, LDS histogram) finds the k-th largest key; ties at that key
-//     go to the highest token indices (a backward block scan), giving a
-//     selection bitmap in LDS; a forward block scan turns it into the
-//     ascending kept list, written to the workspace (and to kept_idx).
+//     go to the highest token indices (a backward block scan, 4 keys per
+//     thread), giving a selection bitmap in LDS; a forward block scan turns
+//     it into the ascending kept list, written to the workspace (and to
+//     kept_idx). The bin holding the k-th key is found with a block scan
+//     over the 256 bins.
 //  2. compact_kernel, one workgroup per (128-byte slice of a token row, K or
 //     V, kv-head, request, layer): the kept rows' slices are moved in chunks:
 //     every thread loads its rows, the workgroup waits until all loads of the
@@ -134,15 +136,19 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams P) {
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t cum = 0;
-      int sel = 0;
-      for (int v = 255; v >= 0; --v) {
-        if (cum + hist[v] >= krem) { sel = v; break; }
-        cum += hist[v];
+    // The bin holding the krem-th largest key: thread tid takes bin 255 - tid,
+    // and a block scan gives the count of keys in higher bins (`above`). The
+    // selected bin is the one with above < krem <= above + its count (the
+    // first bin from the top when krem = 0).
+    {
+      const int v = 255 - tid;
+      const int hv = (int)hist[v];
+      const int incl = block_inclusive_scan(hv, wsum);
+      const uint32_t above = (uint32_t)(incl - hv);
+      if (krem == 0 ? tid == 0 : (above < krem && krem <= (uint32_t)incl)) {
+        sh_prefix = prefix | (uint32_t(v) << shift);
+        sh_krem = krem - above;
       }
-      sh_prefix = prefix | (uint32_t(sel) << shift);
-      sh_krem = krem - cum;
     }
     __syncthreads();
     prefix = sh_prefix;
@@ -153,37 +159,73 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams P) {
   const uint32_t thr = prefix;  // key of the keep-th largest score
   // krem = how many of the keys equal to thr are kept (the highest indices).
 
-  // 2. Selection bitmap; equal keys counted from the end.
-  const int nchunks = (n + 255) / 256;
+  // 2. Selection bitmap; equal keys counted from the end. Chunks of 1024
+  // keys, 4 consecutive ones per thread, from the last chunk to the first;
+  // within a chunk thread tid takes group 255 - tid, so an inclusive scan
+  // over the threads counts the equal keys at higher indices. Each chunk's
+  // scores are loaded one chunk ahead, so their latency overlaps the scan
+  // of the chunk before.
+  constexpr int GRP = 4, CH = 256 * GRP;
+  const int nchunks = (n + CH - 1) / CH;
   int carry = 0;  // equal keys already seen in later chunks
+  float s_next[GRP];
+  auto load_group = [&](int c, float (&s)[GRP]) __attribute__((always_inline)) {
+    const int t0 = c * CH + GRP * (255 - tid);
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) s[g] = t0 + g < n ? sc[t0 + g] : 0.f;
+  };
+  load_group(nchunks - 1, s_next);
   for (int c = nchunks - 1; c >= 0; --c) {
-    // Reverse the order inside the chunk so an inclusive scan counts later keys.
-    const int t = c * 256 + (255 - tid);
-    uint32_t k = 0;
-    int eq = 0;
-    if (t < n) {
-      k = order_key(sc[t]);
-      eq = k == thr;
+    const int t0 = c * CH + GRP * (255 - tid);
+    float s_cur[GRP];
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) s_cur[g] = s_next[g];
+    if (c > 0) load_group(c - 1, s_next);
+    uint32_t k[GRP];
+    uint32_t eqm = 0;
+    int cnt = 0;
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) {
+      const bool valid = t0 + g < n;
+      k[g] = valid ? order_key(s_cur[g]) : 0u;
+      const bool e = valid && k[g] == thr;
+      eqm |= uint32_t(e) << g;
+      cnt += e;
     }
-    const int incl = block_inclusive_scan(eq, wsum);
-    const int later = carry + incl - eq;  // equal keys with a higher index
-    const bool selected = t < n && (k > thr || (eq && later < (int)krem));
-    if (t < n) {
-      if (selected) atomicOr(&bitmap[t >> 5], 1u << (t & 31));
-      else atomicAnd(&bitmap[t >> 5], ~(1u << (t & 31)));
+    const int incl = block_inclusive_scan(cnt, wsum);
+    int later = carry + incl - cnt;  // equal keys above this group
+    uint32_t selm = 0;
+#pragma unroll
+    for (int g = GRP - 1; g >= 0; --g) {  // highest index of the group first
+      const bool e = (eqm >> g) & 1u;
+      if (t0 + g < n && (k[g] > thr || (e && later < (int)krem))) selm |= 1u << g;
+      later += e;
+    }
+    if (t0 < n) {
+      const int w = t0 >> 5, sh = t0 & 31;
+      atomicAnd(&bitmap[w], ~(((1u << GRP) - 1u) << sh));
+      atomicOr(&bitmap[w], selm << sh);
     }
     __syncthreads();
     carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
 
-  // 3. Ascending kept list.
+  // 3. Ascending kept list, 4 consecutive indices per thread.
   int base = 0;
   for (int c = 0; c < nchunks; ++c) {
-    const int t = c * 256 + tid;
-    const int sel = t < n ? (bitmap[t >> 5] >> (t & 31)) & 1 : 0;
-    const int incl = block_inclusive_scan(sel, wsum);
-    if (sel && base + incl - 1 < keep) kept[base + incl - 1] = t;
+    const int t0 = c * CH + GRP * tid;
+    const uint32_t selm = t0 < n ? (bitmap[t0 >> 5] >> (t0 & 31)) & ((1u << GRP) - 1u) : 0u;
+    const int cnt = __popc(selm);
+    const int incl = block_inclusive_scan(cnt, wsum);
+    int pos = base + incl - cnt;
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) {
+      if ((selm >> g) & 1u) {
+        if (pos < keep) kept[pos] = t0 + g;
+        ++pos;
+      }
+    }
     base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
