@@ -159,6 +159,7 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
   const int span = min(min(P.table_stride - pg0, ((P.split_tokens - 1) >> P.log2b) + 2), kMaxSplitPages);
   const int n = P.seq_lens[seq];
   const int pg_first = tid < span ? tab[pg0 + tid] : 0;  // in flight with the length
+  const int pg_lane = lane < span ? tab[pg0 + lane] : 0;  // the first 64, in every wavefront
   // This lane's 16 bytes of the decoded token's k and v (one of the
   // wavefronts appends them below).
   const int64_t new_off = ((int64_t)seq * P.h_kv + kvh) * D + (lane % (D / Vec16<T>::N)) * Vec16<T>::N;
@@ -196,7 +197,8 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
   const int npg = ((t1 - 1) >> P.log2b) - pg0 + 1;  // block ids the split uses (<= span)
   if (tid < span) sm_pages[tid] = pg_first;
   for (int i = tid + NT; i < npg; i += NT) sm_pages[i] = tab[pg0 + i];
-  __syncthreads();
+  // (LDS copy visible after the barrier below, which follows the first
+  // chunk's loads; until then ids come from pv.)
 
   float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -215,13 +217,17 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
 
   const int nchunks = (t1 - t0 + CHUNK - 1) / CHUNK;
   // The first 64 block ids also sit one per lane: a chunk takes its id with
-  // one lane read (no LDS access, no address register) in the loop.
-  const int pv = lane < npg ? sm_pages[lane] : -1;
+  // one lane read (no LDS access, no address register); later ones come from
+  // the LDS copy.
+  const int pv = lane < npg ? pg_lane : -1;
+  auto page_of = [&](int bi) __attribute__((always_inline)) -> int {
+    return bi < 64 ? __builtin_amdgcn_readlane(pv, bi) : __builtin_amdgcn_readfirstlane(sm_pages[bi]);
+  };
 
   // Element offset of this lane's row 0 in chunk c, or -1 for a bad block id.
   auto chunk_offset = [&](int c) -> int64_t {
     const int base = t0 + c * CHUNK;
-    const int page = sm_pages[(base >> P.log2b) - pg0];
+    const int page = page_of((base >> P.log2b) - pg0);
     if (page < 0 || page >= P.num_blocks) return -1;
     return (int64_t)page * page_elems + lane_off + (int64_t)(base & (b - 1)) * D;
   };
@@ -237,9 +243,7 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
     int bytes = 0, bad = 0;
     if (c < nchunks) {
       const int base = t0 + c * CHUNK;
-      const int bi = (base >> P.log2b) - pg0;
-      const int page = bi < 64 ? __builtin_amdgcn_readlane(pv, bi)
-                                : __builtin_amdgcn_readfirstlane(sm_pages[bi]);
+      const int page = page_of((base >> P.log2b) - pg0);
       if (page >= 0 && page < P.num_blocks) {
         first = (int64_t)page * page_elems + (int64_t)kvh * b * D + (int64_t)(base & (b - 1)) * D;
         bytes = CHUNK * D * (int)sizeof(T);
@@ -390,8 +394,12 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
   // The token being decoded goes to its slot first, written by the wavefront
   // whose chunk holds it; that wavefront reads it back with the rest of the
   // chunk, so the chunk loop carries no special case. The wait retires the
-  // two stores before any load of the loop is issued.
-  if (t0 <= n - 1 && n - 1 < t1 && ((n - 1 - t0) / CHUNK) % WAVES == wv) {
+  // two stores before that chunk's loads are issued: ahead of the first
+  // chunk's loads when the token's block id is among the first 64 (always
+  // so when its chunk is a wavefront's first), else after the barrier.
+  const bool tok_here = t0 <= n - 1 && n - 1 < t1 && ((n - 1 - t0) / CHUNK) % WAVES == wv;
+  const bool tok_early = ((n - 1) >> P.log2b) - pg0 < 64;
+  auto append_token = [&]() __attribute__((always_inline)) {
     const int r = (n - 1 - t0) % CHUNK;  // u * RPW + row of the token in its chunk
     const int64_t off = chunk_offset((n - 1 - t0) / CHUNK);
     if (off >= 0 && r % RPW == row) {
@@ -400,14 +408,18 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
       st16(vc + at, v_tok);
     }
     __builtin_amdgcn_s_waitcnt(0);
-  }
+  };
+  if (tok_here && tok_early) append_token();
 
   // Chunks c = wv, wv + 4, ...; the next chunk's loads are issued before the
-  // current chunk is processed (two register buffers).
+  // current chunk is processed (two register buffers). The first chunk's
+  // loads go out before the barrier that publishes the LDS block ids.
   {
     uint4 ka[U], va[U], kb[U], vb[U];
     int c = wv;
     int64_t offa = load_chunk(c, ka, va), offb;
+    __syncthreads();
+    if (tok_here && !tok_early) append_token();
     while (c < nchunks) {
       offb = load_chunk(c + WAVES, kb, vb);
       process(c, ka, va, offa);
