@@ -13,15 +13,18 @@
 //  * a token row of d elements is read by d*sizeof(T)/16 lanes with 16-byte
 //    loads, so one wavefront load instruction covers 1 KiB of contiguous
 //    K (or V) and the head-major page layout keeps the stream sequential;
-//  * q.k partial dot products are all-reduced inside each row group with DPP
-//    (no LDS), softmax is online in exp2 form per chunk of tokens;
+//  * q.k partial dot products are reduced inside each row group with DPP
+//    (no LDS; for bf16, d = 128, g = 4 one transposing reduction of the 16
+//    (head, row) products), softmax is online in exp2 form per chunk;
 //  * a sequence is split over several workgroups only when the (sequence,
 //    kv-head) items alone cannot fill the GPU; then a second small kernel
 //    merges the split partials (max, sum, unnormalised output). A device-wide
 //    fence per workgroup (to merge in the same launch) costs far more than
 //    that extra launch on this chip (measured);
-//  * the block ids a workgroup needs are staged in LDS first, so no K/V load
-//    waits behind a block-table load;
+//  * the block ids of a split are requested together with the sequence
+//    length; the first 64 sit one per lane in every wavefront (the first
+//    chunk's loads go out before any barrier), the rest are staged in LDS, so
+//    no K/V load in the loop waits behind a block-table load;
 //  * K/V chunks come through buffer loads; a chunk past the end gets an
 //    empty range (zeros, no memory read), so the next chunk's loads are
 //    issued unconditionally and the waits cover only the chunk in use;
