@@ -234,10 +234,11 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
     if (page < 0 || page >= P.num_blocks) return -1;
     return (int64_t)page * page_elems + lane_off + (int64_t)(base & (b - 1)) * D;
   };
-  // Chunk c through buffer loads whose range is the chunk's CHUNK token rows
-  // in its (block, kv-head) slice of K (or V). A chunk past the end, or on a
-  // bad block id, gets an empty range: its loads return zeros and read no
-  // memory. So the next chunk's loads are issued unconditionally, and the
+  // Chunk c through buffer loads whose range is the chunk's token rows in
+  // its (block, kv-head) slice of K (or V), up to the end of the split: the
+  // slots after the sequence return zeros and are not read. A chunk past the
+  // end, or on a bad block id, gets an empty range: its loads return zeros
+  // and read no memory. So the next chunk's loads are issued unconditionally, and the
   // compiler's waits in the loop cover only the chunk in use. Returns 0, or
   // -1 for a bad block id (the chunk is then masked).
   const uint32_t lane_bytes = (uint32_t)((row * D + sub * EPL) * sizeof(T));
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
       const int page = page_of((base >> P.log2b) - pg0);
       if (page >= 0 && page < P.num_blocks) {
         first = (int64_t)page * page_elems + (int64_t)kvh * b * D + (int64_t)(base & (b - 1)) * D;
-        bytes = CHUNK * D * (int)sizeof(T);
+        bytes = min(t1 - base, CHUNK) * D * (int)sizeof(T);
       } else {
         bad = -1;
       }

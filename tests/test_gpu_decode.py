@@ -134,6 +134,34 @@ def test_decode_split_over_many_small_blocks():
     _run_case("bf16", 128, 8, 2, 16, 16, lens)
 
 
+# Lengths whose chunk counts (16 tokens each) leave every remainder mod 4,
+# including sequences shorter than one round of the four wavefronts.
+_TAIL_LENS = [1, 2, 15, 16, 17, 33, 48, 49, 64, 65, 100, 130, 200, 257, 300, 513, 1809, 1825, 2048]
+
+
+def _tail_lens(count, long_ok, seed):
+    rng = np.random.default_rng(seed)
+    base = [n for n in _TAIL_LENS if long_ok or n <= 600]
+    extra = [int(x) for x in rng.integers(1, 600, count - len(base))]
+    return base + extra
+
+
+@pytest.mark.parametrize("dtype,d,h_q,h_kv,b,count,poison", [
+    ("bf16", 128, 32, 8, 256, 40, True),
+    ("bf16", 64, 32, 8, 64, 40, False),
+    ("f32", 128, 16, 2, 128, 130, False),
+])
+def test_decode_four_wave_workgroups_all_rows(dtype, d, h_q, h_kv, b, count, poison):
+    """Batches with more (sequence, kv-head) items than a quarter of the GPU's
+    resident wavefronts take 4-wavefront workgroups, one per item. Every row
+    is checked against the oracle, with every count of 16-token chunks modulo
+    the 4 wavefronts (sequences shorter than one round included), 8-row loads
+    (bf16, d = 64), fp32, and (poison) unwritten NaN slots after the token,
+    which the last chunk's load range leaves unread."""
+    lens = _tail_lens(count, long_ok=(b == 256), seed=5)
+    _run_case(dtype, d, h_q, h_kv, b, 16, lens, poison_tail=poison)
+
+
 def test_decode_skips_rows_with_zero_length():
     _run_case("bf16", 128, 32, 8, 256, 16, [300, 1000, 2000], skip_rows=(1,))
 
