@@ -94,6 +94,19 @@ struct Mma<float, D> {
 // at most 16 tiles, dealt to the 4 wavefronts as ct = wv, wv + 4, ...
 constexpr int kCTW = 4;
 
+// Sums of the zeroed cosines are accumulated by atomics whose order varies
+// from run to run. They are kept in 64-bit fixed point (2^-40 units), where
+// addition is exact and commutative, so every run gives the same bits. A
+// cosine lies in [-1, 1] and a row collects at most one entry per column, so
+// a sum stays below n * 2^40 < 2^63 for any n < 2^23.
+constexpr double kFixScale = 1099511627776.0;  // 2^40
+__device__ __forceinline__ unsigned long long to_fix(float c) {
+  return static_cast<unsigned long long>(__double2ll_rn(static_cast<double>(c) * kFixScale));
+}
+__device__ __forceinline__ float from_fix(unsigned long long v) {
+  return static_cast<float>(static_cast<double>(static_cast<long long>(v)) * (1.0 / kFixScale));
+}
+
 // Copies `rows` rows of D elements (contiguous in global memory) to an LDS
 // tile with up to 16 loads in flight per thread.
 template <typename T, int D>
@@ -131,6 +144,7 @@ struct ScoreParams {
   float* f_new;  // updated global score (S1) per token, same layout as scores
   float* stats;  // [items][h_kv][max_blocks][R][2]  (max, sum) in the exp2 domain
   float* rbuf;   // [items][h_kv][max_blocks * b]     redundancy row sums / n
+  unsigned long long* rsub;  // [items][h_kv][max_blocks * b] flash: zeroed entries, fixed point
   float* s1buf;  // [items][h_kv][max_blocks * b]     S1
   float* inv;    // [items][h_kv][max_blocks * b]     inverse key norms
   float* nrm;    // [items][h_kv][max_blocks * b]     key norms
@@ -454,7 +468,9 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   float* nrm_s = inv_s + b;                                   // [b]
   float* ksum_s = nrm_s + b;                                  // [D]
   float* wstat = ksum_s + D;                                  // [4][R][2]
-  float* sub = wstat + 4 * R * 2;                             // [b]
+  // [b] fixed-point sums (8-byte aligned: every array above has an even
+  // number of 4-byte entries and Ks is a multiple of 16 bytes)
+  unsigned long long* sub = reinterpret_cast<unsigned long long*>(wstat + 4 * R * 2);
   int* istar = reinterpret_cast<int*>(sub + b);               // [b]
   float* lse2 = reinterpret_cast<float*>(istar + b);          // [R]
   float* ptile = lse2 + R;     // [4][R][16], window LSE given and window != 16 only
@@ -478,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   const T* qrows = reinterpret_cast<const T*>(P.qwin) + layer * P.qwin_layer_elems +
                    ((int64_t)slot * P.h_kv + h) * R * D;
   stage_rows<T, D>(Ks, kpage, b, tid);
-  if (tid < b) sub[tid] = 0.f;
+  if (tid < b) sub[tid] = 0ull;
   // Window-query operands (A) of every row tile, in flight while the key
   // norms are formed (fp32 operands take 4x the registers: those are loaded
   // per row tile).
@@ -625,8 +641,8 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   if (!redun) return;
   float* rrow = P.rbuf + zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b;
   if (flash) {
-    // score_flash_kernel accumulates into these rows next.
-    if (tid < b) rrow[tid] = 0.f;
+    // score_flash_kernel accumulates the zeroed entries into these rows next.
+    if (tid < b) P.rsub[zh * ((int64_t)P.max_blocks * b) + (int64_t)pidx * b + tid] = 0ull;
     return;
   }
   // Lightning redundancy: cosines inside this block only.
@@ -651,10 +667,10 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
   // The zeroed entry of column j is cos(k_i*, k_j), subtracted from row i*.
   if (tid < b) {
     const int is = istar[tid];
-    if (is >= 0) atomicAdd(&sub[is], lds_row_dot<T, D>(Ks, is, tid) * inv_s[is] * inv_s[tid]);
+    if (is >= 0) atomicAdd(&sub[is], to_fix(lds_row_dot<T, D>(Ks, is, tid) * inv_s[is] * inv_s[tid]));
   }
   __syncthreads();
-  if (tid < b) rrow[tid] = (mainr - sub[tid]) / (float)n;
+  if (tid < b) rrow[tid] = (mainr - from_fix(sub[tid])) / (float)n;
 }
 
 // ---------------------------------------------------------------------------
@@ -682,7 +698,6 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
   const int layer = P.layer_begin + z / P.nreq;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int q = lane >> 4, cl = lane & 15;
-  const int n = N * b;
   const int CT = b / 16;
   const int64_t zh = (int64_t)z * P.h_kv + h;
   const int32_t* tab = P.tables + (int64_t)r * P.table_stride;
@@ -723,8 +738,7 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
       cosine_tile_rows<T, D>(Ks, nrm_r, rt, B, pnc, wv, lane, i == m, i * b, brow);
   }
   best_over_groups(brow);
-  float* rb = P.rbuf + zh * ((int64_t)P.max_blocks * b);
-  const float inv_n = 1.0f / (float)n;
+  unsigned long long* rs = P.rsub + zh * ((int64_t)P.max_blocks * b);
   if (q == 0) {
 #pragma unroll
     for (int cw = 0; cw < kCTW; ++cw) {
@@ -734,11 +748,13 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
         const int j = ct * 16 + cl;
         const T* ki = kbase + ((int64_t)tab[is / b] * P.h_kv + h) * b * D + (int64_t)(is % b) * D;
         const float c = row_dot<T, D>(ki, kpm + (int64_t)j * D) * invz[is] * invz[(int64_t)m * b + j];
-        atomicAdd(rb + is, -c * inv_n);
+        atomicAdd(rs + is, to_fix(c));
       }
     }
   }
-  if (tid < b) atomicAdd(rb + (int64_t)m * b + tid, mainr * inv_n);
+  // Rows of block m belong to this workgroup alone; finalize subtracts the
+  // zeroed entries (rsub) once every column block has added its own.
+  if (tid < b) P.rbuf[zh * ((int64_t)P.max_blocks * b) + (int64_t)m * b + tid] = mainr;
 }
 
 // ---------------------------------------------------------------------------
@@ -822,7 +838,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(ScoreParams P) {
   const int n = N * P.b;
   const int64_t zh = (int64_t)z * P.h_kv + h;
   const float* s1 = P.s1buf + zh * ((int64_t)P.max_blocks * P.b);
-  const float* rr = P.rbuf + zh * ((int64_t)P.max_blocks * P.b);
+  float* rr = P.rbuf + zh * ((int64_t)P.max_blocks * P.b);
   float* out = P.scores + zh * P.scores_stride;
   const bool first = P.first[r] != 0;
   const bool pool = (P.flags & ZP_SCORE_POOL) && (first || !(P.flags & ZP_SCORE_POOL_FIRST_ONLY));
@@ -831,6 +847,12 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(ScoreParams P) {
   const float c2 = P.inv_tau * kLog2e;  // softmax(r / tau) in the exp2 domain
 
   float mx = -INFINITY, sum = 0.f;
+  if (redun && (P.flags & ZP_SCORE_REDUNDANCY_FLASH)) {
+    // flash: row sum over the whole sequence minus its zeroed entries, / n
+    // (each thread keeps the same tokens t in every pass below)
+    const unsigned long long* rs = P.rsub + zh * ((int64_t)P.max_blocks * P.b);
+    for (int t = tid; t < n; t += 256) rr[t] = (rr[t] - from_fix(rs[t])) / (float)n;
+  }
   if (redun) {
     float m = -INFINITY;
     for (int t = tid; t < n; t += 256) m = fmaxf(m, rr[t] * c2);
@@ -861,7 +883,7 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
   const bool w16 = P.w == 16;
   const size_t ptileA = (P.lse_ok && !w16) ? size_t(4) * R * 16 : 0;
   const size_t smemA = size_t(b) * L::ROWB +
-                       sizeof(float) * (2 * b + D + 4 * R * 2 + 2 * b + R + ptileA);
+                       sizeof(float) * (2 * b + D + 4 * R * 2 + 3 * b + R + ptileA);
   const size_t smemF = size_t(b) * L::ROWB + sizeof(float) * D;
   const size_t smemB = size_t(R) * L::ROWB + sizeof(float) * (R + (w16 ? 0 : 4 * R * 16));
   const bool flash = (P.flags & ZP_SCORE_REDUNDANCY) && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
@@ -905,7 +927,7 @@ static zp_status dispatch_rows(int R, const ScoreParams& P, int items, hipStream
 static size_t score_ws_layout(const zp_geom* g, int32_t layer_count, int32_t nreq,
                               int32_t max_blocks, size_t* stats_off, size_t* r_off,
                               size_t* s1_off, size_t* inv_off, size_t* nrm_off,
-                              size_t* ksum_off) {
+                              size_t* ksum_off, size_t* rsub_off) {
   const size_t items = size_t(layer_count) * nreq * g->num_kv_heads;
   const size_t R = size_t(group_size(g)) * g->window;
   const size_t per_tok = size_t(max_blocks) * g->block_size;
@@ -915,13 +937,15 @@ static size_t score_ws_layout(const zp_geom* g, int32_t layer_count, int32_t nre
   const size_t io = round_up(so + items * per_tok * sizeof(float), 256);
   const size_t no = round_up(io + items * per_tok * sizeof(float), 256);
   const size_t ko = round_up(no + items * per_tok * sizeof(float), 256);
-  const size_t total = round_up(ko + items * max_blocks * g->head_dim * sizeof(float), 256);
+  const size_t xo = round_up(ko + items * max_blocks * g->head_dim * sizeof(float), 256);
+  const size_t total = round_up(xo + items * per_tok * sizeof(unsigned long long), 256);
   if (stats_off) *stats_off = st;
   if (r_off) *r_off = ro;
   if (s1_off) *s1_off = so;
   if (inv_off) *inv_off = io;
   if (nrm_off) *nrm_off = no;
   if (ksum_off) *ksum_off = ko;
+  if (rsub_off) *rsub_off = xo;
   return total;
 }
 
@@ -935,7 +959,7 @@ extern "C" size_t zp_score_workspace_size(const zp_geom* geom, int32_t layer_cou
       max_blocks < 0)
     return 0;
   return score_ws_layout(geom, layer_count, nreq, max_blocks, nullptr, nullptr, nullptr,
-                         nullptr, nullptr, nullptr);
+                         nullptr, nullptr, nullptr, nullptr);
 }
 
 extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
@@ -979,9 +1003,9 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   if ((sp.flags & ZP_SCORE_REDUNDANCY) && !(sp.sim_threshold >= 0.f))
     return fail(ZP_EINVAL, "zp_score_tokens: sim_threshold must be >= 0");
   if (geom->max_slots <= 0) return fail(ZP_EINVAL, "zp_score_tokens: no query slots");
-  size_t so, ro, s1o, io, no, ko;
+  size_t so, ro, s1o, io, no, ko, xo;
   const size_t need =
-      score_ws_layout(geom, layer_count, nreq, max_blocks, &so, &ro, &s1o, &io, &no, &ko);
+      score_ws_layout(geom, layer_count, nreq, max_blocks, &so, &ro, &s1o, &io, &no, &ko, &xo);
   if (workspace_bytes < need)
     return fail(ZP_EINVAL, "zp_score_tokens: workspace %zu bytes, need %zu", workspace_bytes, need);
   const int64_t items = int64_t(layer_count) * nreq;
@@ -1001,6 +1025,7 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   P.inv = reinterpret_cast<float*>(ws + io);
   P.nrm = reinterpret_cast<float*>(ws + no);
   P.ksum = reinterpret_cast<float*>(ws + ko);
+  P.rsub = reinterpret_cast<unsigned long long*>(ws + xo);
   const int64_t d = geom->head_dim;
   P.kv_layer_elems = int64_t(geom->num_blocks) * geom->num_kv_heads * geom->block_size * d;
   P.qwin_layer_elems = int64_t(geom->max_slots) * geom->num_q_heads * geom->window * d;

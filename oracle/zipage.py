@@ -478,7 +478,7 @@ def window_row(pos, b, w):
 # ---------------------------------------------------------------------------
 
 def simulate_request(prompt_K, prompt_V, prompt_Q_tail, steps_q, steps_k, steps_v,
-                     b, w, n_max, params: ScoreParams, scale=None):
+                     b, w, n_max, params: ScoreParams, scale=None, choose=None):
     """Run one request through prompt, decode steps and compressions.
 
     prompt_K/V: [L][h_kv][n0][d]; prompt_Q_tail: [L][h_q][m][d] with the
@@ -490,6 +490,13 @@ def simulate_request(prompt_K, prompt_V, prompt_Q_tail, steps_q, steps_k, steps_
     blocks the request is compressed to k = (N_max - 1) b tokens per
     (layer, kv-head) (Sec. 4.1). The prompt itself is checked for the trigger
     too (reading: the trigger follows any step that appends KV).
+
+    ``choose(event, layer, head, S, k)``, if given, returns the kept indices
+    of that (event, layer, kv-head) from its scores S instead of
+    ``topk_keep``. It exists for ties: where several tokens share the k-th
+    score within the tie tolerance, several kept sets are equally correct,
+    and the caller may continue the simulation from another one of them
+    (the caller is responsible for checking that its choice is one).
 
     Returns dict(outputs [T][L][h_q][d], events: list of per-event dicts with
     the kept indices [L][h_kv][k] and scores [L][h_kv][n], and the final
@@ -532,7 +539,8 @@ def simulate_request(prompt_K, prompt_V, prompt_Q_tail, steps_q, steps_k, steps_
             for h in range(h_kv):
                 S, F_new = score_tokens(qwin[l, h], K[l, h, :n], F[l, h, :n], first, b,
                                         params, scale)
-                kept = topk_keep(S, keep)
+                kept = (topk_keep(S, keep) if choose is None
+                        else np.asarray(choose(len(events), l, h, S, keep), np.int64))
                 ev["kept"][l, h] = kept
                 ev["scores"][l, h] = S
                 K[l, h, :keep] = K[l, h, kept]

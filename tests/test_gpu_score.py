@@ -57,7 +57,7 @@ def _window_lse(Qw, K, b):
 
 
 def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, layer_count=2,
-         seed=11, planted=False, heavy=True, lse=None):
+         seed=11, planted=False, heavy=True, lse=None, repeat=1):
     announce(f"score dtype={dtype} d={d} g={h_q // h_kv} b={b} w={w} N={nblocks} first={first} "
              f"sp={sp}")
     nreq = len(nblocks)
@@ -102,6 +102,19 @@ def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, laye
     torch.cuda.synchronize()
     assert zp.zp_workspace_errors(ws) == 0
     assert torch.equal(hc.dev.gscore, F_before)        # the cache's F is only read
+    for _ in range(repeat - 1):
+        # the same call again, into fresh outputs and a fresh workspace: every
+        # score and history value must come out with the same bits
+        sc2 = torch.full_like(scores, -7.0)
+        fn2 = torch.full_like(f_new, -5.0) if f_new is not None else None
+        ws2 = zp.new_workspace(ws.numel())
+        zp.zp_score_tokens(hc.dev, sp, layer_begin, layer_count, dev_i32(tab), dev_i32(nblocks),
+                           max_blocks, dev_i32(qslot), torch.from_numpy(firsts).cuda(), sc2, fn2,
+                           ws2, window_lse_valid=lse_valid)
+        torch.cuda.synchronize()
+        assert torch.equal(sc2.view(torch.int32), scores.view(torch.int32))
+        if f_new is not None:
+            assert torch.equal(fn2.view(torch.int32), f_new.view(torch.int32))
     S_gpu = scores.cpu().numpy()
     Fn_gpu = f_new.cpu().numpy() if f_new is not None else None
     op = _oracle_params(sp)
@@ -228,3 +241,14 @@ def test_score_with_window_lse_other_windows():
          layer_count=1, lse=lambda r: True)
     _run("bf16", 128, 16, 2, 64, 8, [3, 5], lambda r: 1, DEFAULT, L=1, layer_begin=0,
          layer_count=1, lse=lambda r: r == 1)
+
+
+@pytest.mark.parametrize("redundancy", ["lightning", "flash"])
+def test_score_bit_reproducible(redundancy):
+    """Scores are the same bits on every run. Threshold 0 makes nearly every
+    column of every cosine matrix zero one entry (the most order-dependent
+    sums), and planted clusters stack many zeroed entries on one row."""
+    sp = zp.ScoreParams(p=0.0, redundancy=redundancy, pool_first_only=False)
+    _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, sp, repeat=4)
+    sp = zp.ScoreParams(p=0.5, redundancy=redundancy, use_global=False)
+    _run("bf16", 128, 16, 4, 64, 16, [6, 3], lambda r: 1, sp, planted=True, heavy=False, repeat=4)
