@@ -27,6 +27,7 @@ namespace {
 struct Req {
   int32_t rid = 0, prompt = 0, max_new = 0, group = -1, prefix_len = 0;
   int32_t n_max = 0;  // this request's cap (blocks kept + the reserved one)
+  int32_t base_n_max = 0;  // the cap it was added with (adaptive N_max grows from it)
   int32_t gen = 0;  // outputs produced
   int32_t n = 0;    // resident tokens
   int32_t slot = -1;
@@ -152,11 +153,29 @@ void finish(zp_sched* s, Req* r, zp_sched_step_out* out) {
   out->finished[out->n_finished++] = r->rid;
 }
 
+// Adaptive N_max: the cap follows the request's actual sequence length L =
+// prompt + outputs, min(cfg n_max, base + L / nmax_growth), never falling; a
+// slot holder's raise is cut so the holders' caps still fit the pool.
+void grow(zp_sched* s, Req* r) {
+  if (s->cfg.nmax_growth <= 0) return;
+  const int64_t len = int64_t(r->prompt) + r->gen;
+  int64_t want = std::min<int64_t>(s->cfg.n_max, r->base_n_max + len / s->cfg.nmax_growth);
+  if (want <= r->n_max) return;
+  if (r->slot >= 0) {
+    want = std::min<int64_t>(want, r->n_max + int64_t(s->cfg.num_blocks) - s->slot_caps);
+    if (want <= r->n_max) return;
+    s->slot_caps += want - r->n_max;
+  }
+  r->n_max = static_cast<int32_t>(want);
+}
+
 void advance(zp_sched* s, Req* r, zp_sched_step_out* out) {
-  if (r->gen >= r->max_new)
+  if (r->gen >= r->max_new) {
     finish(s, r, out);
-  else if (is_due(s, r))
-    r->due = true;
+    return;
+  }
+  grow(s, r);
+  if (is_due(s, r)) r->due = true;
 }
 
 // Rule (a): plans the compression of a due request; may preempt.
@@ -319,6 +338,7 @@ extern "C" zp_sched* zp_sched_create(const zp_sched_config* cfg) {
   if (c.num_blocks <= 0 || c.block_size <= 0 || (c.block_size & (c.block_size - 1)) != 0 ||
       c.window < 1 || c.window > c.block_size || c.n_max < 2 || c.num_slots < 1 ||
       c.max_running < 1 || c.max_prefill_tokens < 1 || c.table_cap < c.n_max ||
+      c.nmax_growth < 0 ||
       (c.policy != ZP_SCHED_CONSTRAINED && c.policy != ZP_SCHED_HYBRID)) {
     fail(ZP_EINVAL, "zp_sched_create: invalid configuration");
     return nullptr;
@@ -368,6 +388,7 @@ extern "C" zp_status zp_sched_add(zp_sched* s, int32_t rid, int32_t prompt_len, 
   r->group = prefix_group >= 0 ? prefix_group : -1;
   r->prefix_len = prefix_group >= 0 ? prefix_len : 0;
   r->n_max = n_max;
+  r->base_n_max = n_max;
   s->waiting.push_back(r.get());
   s->reqs.emplace(rid, std::move(r));
   ++s->unfinished;
@@ -478,7 +499,7 @@ extern "C" zp_status zp_sched_request(const zp_sched* s, int32_t rid, zp_sched_r
   if (!s || !info) return fail(ZP_EINVAL, "zp_sched_request: NULL argument");
   auto it = s->reqs.find(rid);
   if (it == s->reqs.end()) {
-    *info = zp_sched_req_info{ZP_REQ_UNKNOWN, 0, 0, -1, 0, 0};
+    *info = zp_sched_req_info{ZP_REQ_UNKNOWN, 0, 0, -1, 0, 0, 0};
     return ZP_OK;
   }
   const Req* r = it->second.get();
@@ -488,6 +509,7 @@ extern "C" zp_status zp_sched_request(const zp_sched* s, int32_t rid, zp_sched_r
   info->slot = r->slot;
   info->compressed = r->compressed ? 1 : 0;
   info->ntable = static_cast<int32_t>(r->table.size());
+  info->n_max = r->n_max;
   if (table) std::copy(r->table.begin(), r->table.end(), table);
   return ZP_OK;
 }

@@ -61,7 +61,7 @@ ZP_REQ_WAITING, ZP_REQ_RUNNING, ZP_REQ_COMPRESSING, ZP_REQ_FINISHED, ZP_REQ_UNKN
 class SchedConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "num_blocks", "block_size", "window", "n_max", "num_slots", "max_running",
-        "max_prefill_tokens", "table_cap", "policy", "prefix_sharing")]
+        "max_prefill_tokens", "table_cap", "policy", "prefix_sharing", "nmax_growth")]
 
 
 _OUT_ARRAYS = ("rid", "slot", "ctx", "pos", "len", "tables", "c_rid", "c_slot", "c_first",
@@ -82,7 +82,8 @@ class SchedStats(C.Structure):
 
 
 class SchedReqInfo(C.Structure):
-    _fields_ = [(n, C.c_int32) for n in ("state", "n", "gen", "slot", "compressed", "ntable")]
+    _fields_ = [(n, C.c_int32) for n in ("state", "n", "gen", "slot", "compressed", "ntable",
+                                         "n_max")]
 
 
 _lib = None
@@ -645,11 +646,13 @@ class Scheduler:
     and Sec. 4.4). Arrays of the step output are allocated once, here."""
 
     def __init__(self, num_blocks, block_size, window, n_max, num_slots, max_running,
-                 max_prefill_tokens, policy="hybrid", prefix_sharing=False, table_cap=64):
+                 max_prefill_tokens, policy="hybrid", prefix_sharing=False, table_cap=64,
+                 nmax_growth=0):
         import numpy as np
         pol = {"constrained": ZP_SCHED_CONSTRAINED, "hybrid": ZP_SCHED_HYBRID}[policy]
         self.cfg = SchedConfig(num_blocks, block_size, window, n_max, num_slots, max_running,
-                               max_prefill_tokens, table_cap, pol, 1 if prefix_sharing else 0)
+                               max_prefill_tokens, table_cap, pol, 1 if prefix_sharing else 0,
+                               nmax_growth)
         self._h = lib().zp_sched_create(C.byref(self.cfg))
         if not self._h:
             raise ZpError(ZP_EINVAL, lib().zp_last_error().decode())

@@ -447,6 +447,8 @@ typedef struct {
   int32_t table_cap;           /* largest block table, >= n_max */
   int32_t policy;              /* ZP_SCHED_CONSTRAINED or ZP_SCHED_HYBRID */
   int32_t prefix_sharing;      /* nonzero: share prefix blocks, preemption rule of Sec. 4.4 */
+  int32_t nmax_growth;         /* adaptive N_max, tokens per extra block (0 = off); see
+                                  zp_sched_add */
 } zp_sched_config;
 
 /* Output of one step. The caller provides every array with the capacity
@@ -505,6 +507,7 @@ typedef struct {
   int32_t slot;        /* -1 = none */
   int32_t compressed;  /* 1 once a compression has committed */
   int32_t ntable;      /* block table length */
+  int32_t n_max;       /* its N_max now (grows with nmax_growth) */
 } zp_sched_req_info;
 
 /* NULL (with zp_last_error) on an invalid configuration. */
@@ -519,6 +522,13 @@ void zp_sched_destroy(zp_sched* s);
  * the N_max of all slot holders sums to at most num_blocks (the
  * per-request form of M <= N_total / N_max, Sec. 4.2; with one N_max and a
  * pool sized by that rule it never binds).
+ * Adaptive N_max (cfg.nmax_growth = A > 0; Zipage, Limitations: N_max set
+ * per request from its actual sequence length): after each step of a
+ * request, its N_max becomes max(current, min(cfg.n_max, n_max_added +
+ * floor(L / A))) with L = prompt_len + outputs so far, before the trigger
+ * check; a slot holder's raise is cut to what keeps the holders' sum within
+ * num_blocks (the remainder is taken at a later step). Compressions report
+ * the N_max they keep (c_nmax).
  * ZP_EINVAL for a repeated rid, bad lengths or n_max, or a prompt longer
  * than table_cap blocks. */
 zp_status zp_sched_add(zp_sched* s, int32_t rid, int32_t prompt_len, int32_t max_new,

@@ -65,6 +65,16 @@ Readings where the pages leave a step open (the product follows the same):
       per-request form of M <= N_total / N_max (Sec. 4.2), so the slot
       holders can always reach their caps. With one N_max for all and a pool
       sized by that rule the reservation never binds.
+  R10 Adaptive N_max (the pages' Limitations section names an N_max set per
+      request from its actual sequence length, with no rule): with a growth
+      step A > 0, a request's N_max is raised, after each of its steps,
+      to min(N_cap, N_base + floor(L / A)), where N_base is the N_max it was
+      added with, N_cap the configured one and L = prompt + outputs so far
+      (its actual sequence length). It never falls. A slot holder's raise is
+      cut so that the slot holders' N_max still sum to at most the pool
+      (R9); the rest of the raise waits for a later step. The raise comes
+      before the trigger check, so a longer request is compressed later and
+      keeps more blocks. A = 0 turns the rule off.
 """
 from __future__ import annotations
 
@@ -80,6 +90,7 @@ class Req:
     def __init__(self, rid, prompt, max_new, group, prefix_len, n_max):
         self.rid = rid
         self.n_max = n_max
+        self.base_n_max = n_max      # R10: the N_max it was added with
         self.prompt = prompt
         self.max_new = max_new
         self.group = group
@@ -97,8 +108,10 @@ class Req:
 
 class Scheduler:
     def __init__(self, num_blocks, block_size, window, n_max, num_slots, max_running,
-                 max_prefill_tokens, policy=HYBRID, prefix_sharing=False, table_cap=None):
-        assert policy in (CONSTRAINED, HYBRID)
+                 max_prefill_tokens, policy=HYBRID, prefix_sharing=False, table_cap=None,
+                 nmax_growth=0):
+        assert policy in (CONSTRAINED, HYBRID) and nmax_growth >= 0
+        self.growth = nmax_growth
         self.b = block_size
         self.w = window
         self.n_max = n_max
@@ -258,10 +271,24 @@ class Scheduler:
         return out
 
     # ---------------------------------------------------------------- steps
+    def _grow(self, r):
+        """R10: raise r's N_max with its actual sequence length."""
+        if not self.growth:
+            return
+        want = min(self.n_max, r.base_n_max + (r.prompt + r.gen) // self.growth)
+        if want <= r.n_max:
+            return
+        if r.slot is not None:
+            held = sum(x.n_max for x in self.running if x.slot is not None)   # r's included
+            want = min(want, r.n_max + self.num_blocks - held)
+        r.n_max = max(r.n_max, want)
+
     def _advance(self, r, out):
         if r.gen >= r.max_new:
             self._finish(r, out)
-        elif self._is_due(r):
+            return
+        self._grow(r)
+        if self._is_due(r):
             r.due = True
 
     def _try_compress(self, r, out):

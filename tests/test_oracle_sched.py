@@ -263,7 +263,10 @@ def _invariants(s, o):
             assert len(e["table"]) == -(-(last + 1) // b)
     for r in s.running:
         if r.compressed and r.state == "running":
-            assert len(r.table) == r.n_max and r.n <= r.n_max * b
+            # the reserved block completes the table, unless N_max has grown
+            # since (R10): the table then grows block by block up to it
+            assert len(r.table) <= r.n_max and r.n <= r.n_max * b
+            assert len(r.table) == r.n_max or r.n_max > r.base_n_max
     for c in o["comp"]:
         nm = c["n_max"]
         assert len(c["dst"]) == nm - 1 and len(c["new"]) == nm and c["slot"] is not None
@@ -357,3 +360,101 @@ def test_constrained_never_preempts_and_hybrid_runs_more_requests():
     assert res[CONSTRAINED][1] == M and res[CONSTRAINED][2] == 0
     assert res[HYBRID][1] > M
     assert res[HYBRID][0] < res[CONSTRAINED][0]
+
+
+# ------------------------------------------------------------ adaptive N_max
+def test_adaptive_n_max_raises_the_cap_with_the_sequence_length():
+    """R10 by hand: b = 16, w = 4, N_cap = 4, growth step A = 24, one request
+    added with N_max 2 (prompt 30, 40 outputs). L = prompt + outputs:
+    after the prefill L = 31 -> N_max 2 + 31 // 24 = 3; at L = 48 (step 18)
+    -> 4, the cap. With N_max 2 it would have been due at n = 32 (step 3);
+    now it is due at n = 64 (step 35, 35 outputs), compressed in step 36 to
+    (4 - 1) * 16 = 48 tokens with its own blocks as targets, and finishes
+    after 5 more outputs in step 41."""
+    s = Scheduler(100, 16, 4, 4, 1, 8, 1000, HYBRID, nmax_growth=24)
+    s.add(0, 30, 40, n_max=2)
+    r = s.reqs[0]
+    nm, comps, fin = [], [], None
+    for t in range(1, 45):
+        o = s.step()
+        nm.append(r.n_max)
+        for c in o["comp"]:
+            comps.append((t, c["n_max"], c["src"], c["dst"], c["new"], r.n))
+            s.compress_done(c["rid"])
+        if o["finished"]:
+            fin = t
+            break
+    assert nm[:17] == [3] * 17 and nm[17:35] == [4] * 18
+    assert comps == [(36, 4, [0, 1, 2, 3], [0, 1, 2], [0, 1, 2, 3], 64)]
+    assert fin == 41 and r.gen == 40
+
+
+def test_adaptive_n_max_raise_is_cut_by_the_slot_reservation():
+    """Pool of 7 blocks, M = 2, N_cap 4, A = 8; two requests added with
+    N_max 2 (prompts 10; 30 and 60 outputs). After the prefill (L = 11) each
+    wants 3: holders' sum 4 -> 5 -> 6 <= 7. At L = 16 (step 6) each wants 4:
+    request 0 gets it (sum 7); request 1 is cut to 3 (7 - 7 leaves no room)
+    and stays there until request 0 finishes in step 30: request 0 comes
+    first in that step's batch, so its slot is free when request 1's raise is
+    taken, in the same step. Request 1 is due at n = 64 (step 55), compressed
+    in step 56 to 48 tokens, and finishes after 5 more outputs (step 61)."""
+    s = Scheduler(7, 16, 4, 4, 2, 8, 1000, HYBRID, nmax_growth=8)
+    s.add(0, 10, 30, n_max=2)
+    s.add(1, 10, 60, n_max=2)
+    r0, r1 = s.reqs[0], s.reqs[1]
+    traj, comps, fin = [], [], {}
+    for t in range(1, 70):
+        o = s.step()
+        traj.append((r0.n_max, r1.n_max))
+        for c in o["comp"]:
+            comps.append((t, c["rid"], c["n_max"], r1.n))
+            s.compress_done(c["rid"])
+        for x in o["finished"]:
+            fin[x] = t
+        assert not o["preempted"]
+        if s.unfinished() == 0:
+            break
+    assert traj[:5] == [(3, 3)] * 5
+    assert traj[5:29] == [(4, 3)] * 24
+    assert traj[29] == (4, 4)
+    assert fin == {0: 30, 1: 61}
+    assert comps == [(56, 1, 4, 64)]
+
+
+def test_adaptive_n_max_off_keeps_the_given_cap():
+    s = Scheduler(100, 16, 4, 4, 1, 8, 1000, HYBRID)
+    s.add(0, 30, 5, n_max=2)
+    for _ in range(5):
+        o = s.step()
+        assert s.reqs[0].n_max == 2 or s.reqs[0].state == "finished"
+        for c in o["comp"]:
+            assert c["n_max"] == 2
+            s.compress_done(c["rid"])
+
+
+@pytest.mark.parametrize("policy", [CONSTRAINED, HYBRID])
+@pytest.mark.parametrize("prefix", [False, True])
+@pytest.mark.parametrize("seed", range(3))
+def test_adaptive_n_max_streams_finish_with_invariants(policy, prefix, seed):
+    """Random streams with N_base in {2, 3} and a growth step of 3 blocks on
+    a pool where the reservation binds: invariants hold at every step, every
+    request finishes, and compressions happen at more than one N_max."""
+    b, nmax, M = 16, 5, 4
+    stream = random_stream(seed, 40, b, short=seed % 2 == 1, nmax_choices=[2, 3])
+    if not prefix:
+        stream = [(r, p, m, -1, 0, nm) for r, p, m, _g, _pl, nm in stream]
+    nb = 14
+    s = Scheduler(nb, b, 4, nmax, M, 8, 256, policy, prefix_sharing=prefix, table_cap=64,
+                  nmax_growth=3 * b)
+
+    def check(s, o):
+        _invariants(s, o)
+        for r in s.reqs.values():
+            assert r.base_n_max <= r.n_max <= s.n_max
+
+    steps = drive(s, stream, seed, check=check)
+    assert {r.rid: r.gen for r in s.reqs.values()} == {x[0]: x[2] for x in stream}
+    assert s.num_free() == nb
+    kept = {c["n_max"] for o in steps for c in o["comp"]}
+    assert len(kept) >= 2
+    assert any(r.n_max > r.base_n_max for r in s.reqs.values())

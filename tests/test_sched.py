@@ -20,11 +20,11 @@ STATE = {"waiting": zp.ZP_REQ_WAITING, "running": zp.ZP_REQ_RUNNING,
          "compressing": zp.ZP_REQ_COMPRESSING, "finished": zp.ZP_REQ_FINISHED}
 
 
-def _pair(num_blocks, b, w, nmax, M, R, max_prefill, policy, prefix=False, cap=64):
+def _pair(num_blocks, b, w, nmax, M, R, max_prefill, policy, prefix=False, cap=64, growth=0):
     o = OracleScheduler(num_blocks, b, w, nmax, M, R, max_prefill, policy,
-                        prefix_sharing=prefix, table_cap=cap)
+                        prefix_sharing=prefix, table_cap=cap, nmax_growth=growth)
     c = zp.Scheduler(num_blocks, b, w, nmax, M, R, max_prefill, policy, prefix_sharing=prefix,
-                     table_cap=cap)
+                     table_cap=cap, nmax_growth=growth)
     return o, c
 
 
@@ -33,7 +33,7 @@ def _same_state(o, c):
         got = c.request(rid)
         want = dict(state=STATE[r.state], n=r.n, gen=r.gen,
                     slot=-1 if r.slot is None else r.slot, compressed=int(r.compressed),
-                    ntable=len(r.table), table=r.table)
+                    ntable=len(r.table), n_max=r.n_max, table=r.table)
         assert got == want, (rid, got, want)
     assert [c.refcount(i) for i in range(len(o.refcount))] == o.refcount
     assert c.unfinished() == o.unfinished()
@@ -108,6 +108,30 @@ def test_per_request_n_max_matches_the_oracle(policy, prefix, seed):
         stream = [(r, p, m, -1, 0, nm) for r, p, m, _g, _pl, nm in stream]
     o, c = _pair(12, b, 4, nmax, M, 8, 256, policy, prefix)
     lockstep(o, c, stream, seed)
+
+
+@pytest.mark.parametrize("policy", ["constrained", "hybrid"])
+@pytest.mark.parametrize("prefix", [False, True])
+@pytest.mark.parametrize("seed", range(3))
+def test_adaptive_n_max_matches_the_oracle(policy, prefix, seed):
+    """Adaptive N_max (growth step 3 blocks, N_base 2 or 3, cap 5) on a pool
+    where the slot reservation cuts raises: same decisions, same caps."""
+    b = 16
+    stream = random_stream(seed, 40, b, short=seed % 2 == 1, nmax_choices=[2, 3])
+    if not prefix:
+        stream = [(r, p, m, -1, 0, nm) for r, p, m, _g, _pl, nm in stream]
+    o, c = _pair(14, b, 4, 5, 4, 8, 256, policy, prefix, growth=3 * b)
+    lockstep(o, c, stream, seed)
+    assert any(r.n_max > r.base_n_max for r in o.reqs.values())
+
+
+def test_adaptive_n_max_hand_scenarios_match():
+    """The two hand-derived traces of the oracle's pins, through the C ABI."""
+    for args, adds in (((100, 16, 4, 4, 1, 8, 1000, "hybrid"), [(0, 30, 40, -1, 0, 2)]),
+                       ((7, 16, 4, 4, 2, 8, 1000, "hybrid"), [(0, 10, 30, -1, 0, 2),
+                                                              (1, 10, 60, -1, 0, 2)])):
+        o, c = _pair(*args, growth=24 if args[0] == 100 else 8)
+        lockstep(o, c, adds, 0, arrivals=False)
 
 
 def test_the_random_streams_reach_every_branch():
