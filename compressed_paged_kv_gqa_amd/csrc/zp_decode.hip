@@ -32,6 +32,7 @@
 //    by the one wavefront that reads that chunk: no other workgroup reads
 //    that slot, so append and attention need no extra launch.
 #include <cmath>
+#include <mutex>
 
 #include "zp_device.h"
 #include "zp_internal.h"
@@ -626,51 +627,51 @@ static size_t decode_ws_layout(const zp_geom* g, int32_t batch, int32_t max_seq_
   return total;
 }
 
-}  // namespace zp
-
-using namespace zp;
-
-extern "C" size_t zp_decode_workspace_size(const zp_geom* geom, int32_t batch,
-                                           int32_t max_seq_len) {
-  if (validate_geom(geom, "zp_decode_workspace_size") != ZP_OK || batch < 0 || max_seq_len < 0)
-    return 0;
-  return decode_ws_layout(geom, batch, max_seq_len, nullptr, nullptr, nullptr, nullptr);
+// Checks the arguments of a decode call and computes its launch shape and
+// the bytes of split partials it needs. No HIP call.
+static zp_status decode_prepare(const zp_geom* geom, const zp_cache* cache, int32_t layer,
+                                int32_t batch, const void* q, const void* k_new,
+                                const void* v_new, const int32_t* block_tables,
+                                int32_t table_stride, const int32_t* seq_lens,
+                                int32_t max_seq_len, const int32_t* qslot, void* out,
+                                const char* who, size_t* need, size_t* p_off,
+                                int32_t* split_tokens, int32_t* max_splits, int32_t* waves) {
+  zp_status st = validate_geom(geom, who);
+  if (st != ZP_OK) return st;
+  if (!cache || !cache->k || !cache->v) return fail(ZP_EINVAL, "%s: cache K/V NULL", who);
+  if (layer < 0 || layer >= geom->num_layers)
+    return fail(ZP_EINVAL, "%s: layer %d out of range", who, layer);
+  if (batch < 0 || table_stride <= 0 || max_seq_len < 0)
+    return fail(ZP_EINVAL, "%s: bad batch/table_stride/max_seq_len", who);
+  if (batch == 0) {
+    *need = 0;
+    return ZP_OK;
+  }
+  if (!q || !k_new || !v_new || !block_tables || !seq_lens || !out)
+    return fail(ZP_EINVAL, "%s: NULL buffer", who);
+  if (qslot && !cache->qwin) return fail(ZP_EINVAL, "%s: qslot given but qwin NULL", who);
+  *need = decode_ws_layout(geom, batch, max_seq_len, p_off, split_tokens, max_splits, waves);
+  return ZP_OK;
 }
 
-extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t layer,
-                                     int32_t batch, const void* q, const void* k_new,
-                                     const void* v_new, const int32_t* block_tables,
-                                     int32_t table_stride, const int32_t* seq_lens,
-                                     int32_t max_seq_len, const int32_t* qslot, void* out,
-                                     float* lse, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
-  zp_status st = validate_geom(geom, "zp_paged_decode");
-  if (st != ZP_OK) return st;
-  if (!cache || !cache->k || !cache->v) return fail(ZP_EINVAL, "zp_paged_decode: cache K/V NULL");
-  if (layer < 0 || layer >= geom->num_layers)
-    return fail(ZP_EINVAL, "zp_paged_decode: layer %d out of range", layer);
-  if (batch < 0 || table_stride <= 0 || max_seq_len < 0)
-    return fail(ZP_EINVAL, "zp_paged_decode: bad batch/table_stride/max_seq_len");
-  if (batch == 0) return ZP_OK;
-  if (!q || !k_new || !v_new || !block_tables || !seq_lens || !out || !workspace)
-    return fail(ZP_EINVAL, "zp_paged_decode: NULL buffer");
-  if (qslot && !cache->qwin) return fail(ZP_EINVAL, "zp_paged_decode: qslot given but qwin NULL");
-  size_t p_off;
-  int32_t split_tokens, max_splits, waves;
-  const size_t need = decode_ws_layout(geom, batch, max_seq_len, &p_off, &split_tokens, &max_splits,
-                                       &waves);
-  if (workspace_bytes < need)
-    return fail(ZP_EINVAL, "zp_paged_decode: workspace %zu bytes, need %zu", workspace_bytes, need);
-
+// Enqueues the decode kernels of one call; partials at `part`, device error
+// bits OR-ed into *err (may be NULL: dropped).
+static zp_status decode_enqueue(const zp_geom* geom, const zp_cache* cache, int32_t layer,
+                                int32_t batch, const void* q, const void* k_new,
+                                const void* v_new, const int32_t* block_tables,
+                                int32_t table_stride, const int32_t* seq_lens,
+                                int32_t max_seq_len, const int32_t* qslot, void* out, float* lse,
+                                float* part, uint32_t* err, int32_t split_tokens,
+                                int32_t max_splits, int32_t waves, void* stream,
+                                const char* who) {
   DecodeParams P{};
   P.q = q; P.k_new = k_new; P.v_new = v_new;
   P.kc = cache->k; P.vc = cache->v; P.qwin = cache->qwin;
   P.qwin_lse = qslot ? cache->qwin_lse : nullptr;
   P.tables = block_tables; P.seq_lens = seq_lens; P.qslot = qslot;
   P.out = out; P.lse = lse;
-  char* ws = static_cast<char*>(workspace);
-  P.err = reinterpret_cast<uint32_t*>(ws);
-  P.part = reinterpret_cast<float*>(ws + p_off);
+  P.err = err;
+  P.part = part;
   const int64_t d = geom->head_dim;
   P.kv_layer_off = int64_t(layer) * geom->num_blocks * geom->num_kv_heads * geom->block_size * d;
   P.qwin_layer_off = int64_t(layer) * geom->max_slots * geom->num_q_heads * geom->window * d;
@@ -692,6 +693,98 @@ extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache,
     else dispatch_group<float, 64>(g, P, batch, s);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(ZP_EHIP, "zp_paged_decode: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(ZP_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ZP_OK;
+}
+
+// Library-owned split partials of zp_paged_decode_noalloc: one array per GPU
+// (each device that loads the library holds its own copy until the process
+// ends). Host code must not pass `scratch` itself to a kernel: its name is a
+// host-side stand-in. The device address comes from hipGetSymbolAddress,
+// taken once per device on that device's first call and kept here.
+static __device__ __align__(256) unsigned char scratch[ZP_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static zp_status scratch_for_current_device(void** ptr, const char* who) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(ZP_EHIP, "%s: no current HIP device", who);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ZP_EHIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", who, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ZP_OK;
+}
+
+}  // namespace zp
+
+using namespace zp;
+
+extern "C" size_t zp_decode_workspace_size(const zp_geom* geom, int32_t batch,
+                                           int32_t max_seq_len) {
+  if (validate_geom(geom, "zp_decode_workspace_size") != ZP_OK || batch < 0 || max_seq_len < 0)
+    return 0;
+  return decode_ws_layout(geom, batch, max_seq_len, nullptr, nullptr, nullptr, nullptr);
+}
+
+extern "C" zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t layer,
+                                     int32_t batch, const void* q, const void* k_new,
+                                     const void* v_new, const int32_t* block_tables,
+                                     int32_t table_stride, const int32_t* seq_lens,
+                                     int32_t max_seq_len, const int32_t* qslot, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  const char* who = "zp_paged_decode";
+  size_t need = 0, p_off = 0;
+  int32_t split_tokens = 0, max_splits = 0, waves = 0;
+  zp_status st = decode_prepare(geom, cache, layer, batch, q, k_new, v_new, block_tables,
+                                table_stride, seq_lens, max_seq_len, qslot, out, who, &need,
+                                &p_off, &split_tokens, &max_splits, &waves);
+  if (st != ZP_OK || batch == 0) return st;
+  if (!workspace) return fail(ZP_EINVAL, "%s: NULL workspace", who);
+  if (workspace_bytes < need)
+    return fail(ZP_EINVAL, "%s: workspace %zu bytes, need %zu", who, workspace_bytes, need);
+  char* ws = static_cast<char*>(workspace);
+  return decode_enqueue(geom, cache, layer, batch, q, k_new, v_new, block_tables, table_stride,
+                        seq_lens, max_seq_len, qslot, out, lse,
+                        reinterpret_cast<float*>(ws + p_off), reinterpret_cast<uint32_t*>(ws),
+                        split_tokens, max_splits, waves, stream, who);
+}
+
+extern "C" zp_status zp_paged_decode_noalloc(const zp_geom* geom, const zp_cache* cache,
+                                             int32_t layer, int32_t batch, const void* q,
+                                             const void* k_new, const void* v_new,
+                                             const int32_t* block_tables, int32_t table_stride,
+                                             const int32_t* seq_lens, int32_t max_seq_len,
+                                             const int32_t* qslot, void* out, float* lse,
+                                             uint32_t* errors, void* stream) {
+  const char* who = "zp_paged_decode_noalloc";
+  size_t need = 0, p_off = 0;
+  int32_t split_tokens = 0, max_splits = 0, waves = 0;
+  zp_status st = decode_prepare(geom, cache, layer, batch, q, k_new, v_new, block_tables,
+                                table_stride, seq_lens, max_seq_len, qslot, out, who, &need,
+                                &p_off, &split_tokens, &max_splits, &waves);
+  if (st != ZP_OK || batch == 0) return st;
+  // the partials need need - p_off bytes (the workspace header is not used:
+  // error bits go to *errors)
+  const size_t part_bytes = need - p_off;
+  if (part_bytes > size_t(ZP_DECODE_SCRATCH_BYTES))
+    return fail(ZP_EINVAL, "%s: this call needs %zu bytes of split partials, more than the "
+                "%d-byte static scratch; use zp_paged_decode with a workspace", who, part_bytes,
+                ZP_DECODE_SCRATCH_BYTES);
+  void* base = nullptr;
+  st = scratch_for_current_device(&base, who);
+  if (st != ZP_OK) return st;
+  return decode_enqueue(geom, cache, layer, batch, q, k_new, v_new, block_tables, table_stride,
+                        seq_lens, max_seq_len, qslot, out, lse, static_cast<float*>(base), errors,
+                        split_tokens, max_splits, waves, stream, who);
 }

@@ -100,6 +100,8 @@ def _declare(lib):
         "zp_decode_workspace_size": (sz, [g, i32, i32]),
         "zp_paged_decode": (C.c_int, [g, c, i32, i32, _P, _P, _P, _P, i32, _P, i32, _P, _P,
                                       _P, _P, sz, _P]),
+        "zp_paged_decode_noalloc": (C.c_int, [g, c, i32, i32, _P, _P, _P, _P, i32, _P, i32, _P,
+                                              _P, _P, _P, _P]),
         "zp_prefill_workspace_size": (sz, [g, i32]),
         "zp_paged_prefill": (C.c_int, [g, c, i32, i32, _P, _P, _P, _P, _P, i32, _P, i32, _P, _P,
                                        _P, _P, sz, _P]),
@@ -303,6 +305,42 @@ def zp_paged_decode(cache: PagedKVCache, layer, q, k_new, v_new, block_tables, s
         v_new.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
         int(max_seq_len), _ptr(qslot), out.data_ptr(), _ptr(lse), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)), "zp_paged_decode")
+
+
+ZP_DECODE_SCRATCH_BYTES = 16 * 1024 * 1024
+
+
+def zp_paged_decode_noalloc(cache: PagedKVCache, layer, q, k_new, v_new, block_tables, seq_lens,
+                            max_seq_len, qslot, out, lse, errors=None, stream=None):
+    """zp_paged_decode with the library's static scratch instead of a
+    workspace; `errors` is an optional zero-filled int32/uint32 device
+    tensor of one element that collects the device error bits."""
+    import torch
+    geom = cache.geom
+    dt = geom.torch_dtype()
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out")):
+        _need(t, dt, n)
+    _need(block_tables, torch.int32, "block_tables")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(qslot, torch.int32, "qslot")
+    _need(lse, torch.float32, "lse")
+    if errors is not None and (errors.dtype not in (torch.int32, torch.uint32)
+                               or errors.numel() < 1 or errors.device.type != "cuda"):
+        raise ValueError("errors must be a device tensor of one 32-bit integer")
+    batch, hq, hkv, d = q.shape[0], geom.num_q_heads, geom.num_kv_heads, geom.head_dim
+    for t, n, h in ((q, "q", hq), (out, "out", hq), (k_new, "k_new", hkv), (v_new, "v_new", hkv)):
+        if tuple(t.shape) != (batch, h, d) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous [{batch}][{h}][{d}] tensor, got {tuple(t.shape)}")
+    if block_tables.shape[0] < batch or seq_lens.shape[0] < batch or (
+            qslot is not None and qslot.shape[0] < batch):
+        raise ValueError("block_tables, seq_lens and qslot need a row per batch entry")
+    if lse is not None and (tuple(lse.shape) != (batch, hq) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous [{batch}][{hq}] tensor")
+    _check(lib().zp_paged_decode_noalloc(
+        C.byref(geom.c()), C.byref(cache.c()), layer, batch, q.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
+        int(max_seq_len), _ptr(qslot), out.data_ptr(), _ptr(lse), _ptr(errors), _stream(stream)),
+        "zp_paged_decode_noalloc")
 
 
 class LayerCalls:

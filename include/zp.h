@@ -151,6 +151,34 @@ zp_status zp_paged_decode(const zp_geom* geom, const zp_cache* cache, int32_t la
                           void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* zp_paged_decode without a workspace, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, serving loops and
+ * harnesses that forbid allocation. Same arguments, semantics and launch as
+ * zp_paged_decode, except:
+ *   - the split partials (needed when a small batch of long sequences is
+ *     split over several workgroups) live in a static device array of
+ *     ZP_DECODE_SCRATCH_BYTES owned by the library; each GPU the library
+ *     runs on holds its own copy until the process ends. Nothing is
+ *     allocated, by the library or through torch;
+ *   - errors [device] uint32, caller-owned, zero-filled by the caller, or
+ *     NULL: device-side ZP_DEVERR_* bits are OR-ed into it (dropped if NULL).
+ * A call whose partials would exceed ZP_DECODE_SCRATCH_BYTES (zp_decode_
+ * workspace_size - 256 bytes) fails with ZP_EINVAL before anything is
+ * enqueued. The scratch of a GPU is shared by every call of this function
+ * on it and keeps the last call's contents (every partial is written before
+ * it is read, so nothing needs clearing): calls that overlap in time on one
+ * GPU (different streams, or several host threads) race and must be
+ * serialised by the caller. The device address of the array is looked up
+ * (hipGetSymbolAddress) on the first call on each device, which can fail
+ * with ZP_EHIP. */
+#define ZP_DECODE_SCRATCH_BYTES (16 * 1024 * 1024)
+zp_status zp_paged_decode_noalloc(const zp_geom* geom, const zp_cache* cache, int32_t layer,
+                                  int32_t batch, const void* q, const void* k_new,
+                                  const void* v_new, const int32_t* block_tables,
+                                  int32_t table_stride, const int32_t* seq_lens,
+                                  int32_t max_seq_len, const int32_t* qslot, void* out,
+                                  float* lse, uint32_t* errors, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Prefill attention (Zipage Sec. 3 block tables; Sec. 4.1 the prompt is     */
 /* written in full and may exceed N_max blocks until its first compression;  */
