@@ -262,7 +262,10 @@ def whole_run_bench(steps, seed=SEED):
             "tokens_per_s": round(tokens / elapsed, 1), "seconds": round(elapsed, 2),
             "output_tokens": tokens, "prompt_tokens": T, "compressions": eng.compressions,
             "final_resident_tokens": [int(min(r.n for r in eng.reqs.values())),
-                                      int(max(r.n for r in eng.reqs.values()))]}
+                                      int(max(r.n for r in eng.reqs.values()))],
+            "decode_steps_of_16384": steps,
+            "cut": (f"each sequence decodes up to 16384 tokens in the full workload; this run "
+                    f"stops after {steps} steps" if steps < 16384 else "full length")}
 
 
 # --------------------------------------------------------------------------
@@ -571,14 +574,29 @@ def _oracle_sequence(sid, phase, steps):
     return time.perf_counter() - t0, comp
 
 
+CPU_SHARE = 16   # host CPUs one GPU's job may keep busy on a shared GPU host
+
+
+def oracle_procs():
+    """Worker processes for the oracle: one per CPU this process may run on
+    (its affinity set), at most the host CPU share of one GPU."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return max(1, min(CPU_SHARE, avail)), avail
+
+
 def cpu_baseline(phases, steps):
     import multiprocessing as mp
-    procs = max(1, min(16, os.cpu_count() or 1))
+    procs, avail = oracle_procs()
     jobs = [(s, int(phases[s]), steps) for s in range(B)]
     t0 = time.perf_counter()
     with mp.get_context("spawn").Pool(procs) as pool:
         res = pool.map(_oracle_worker, jobs, chunksize=1)
-    wall = time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+        log(f"cpu baseline: 36-layer slice done in {wall:.1f} s; 64 x 4096 workload in full")
+        c2 = config2_oracle(pool, procs)
     cpu_s = sum(r[0] for r in res)
     comps = sum(r[1] for r in res)
     tokens_one_layer = B * steps
@@ -586,10 +604,143 @@ def cpu_baseline(phases, steps):
     # token of the workload needs all 36 layers
     value = tokens_one_layer / (cpu_s / procs) / L
     return {"value": round(value, 3), "unit": "tokens/s", "cores": procs, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpus_available": avail,
             "sample": (f"1 of 36 layers x {B} sequences x {steps} decode steps from the same "
-                       f"phases ({comps} compressions), float64 NumPy oracle, one process per "
-                       f"core, {cpu_s:.1f} s of oracle compute ({wall:.1f} s wall with input "
-                       f"generation); rate = tokens / (compute s / cores) / 36 layers")}
+                       f"phases ({comps} compressions), float64 NumPy oracle, one "
+                       f"single-threaded process per core on {procs} cores (the host CPU share "
+                       f"of one GPU; {avail} available to this process, {os.cpu_count()} on the "
+                       f"host), {cpu_s:.1f} s of oracle compute ({wall:.1f} s wall with input "
+                       f"generation); rate = tokens / (compute s / cores) / 36 layers"),
+            "config_64x4096": c2}
+
+
+# 64 prompts of 4096 tokens compressed at once to 1792, then 128 decode steps
+# (one attention layer of the Qwen3-8B shape, bf16 values, 2% heavy keys x4)
+C2_REQ, C2_PROMPT, C2_STEPS = 64, 4096, 128
+
+
+def _oracle_config2_request(r):
+    """One request of the 64 x 4096 workload through the oracle: the
+    compression its prompt triggers (scores, top-k, compaction of every
+    kv-head; first compression, window rows without a log-sum-exp) and 128
+    decode steps. Returns the compute seconds (input generation excluded)."""
+    import threadpoolctl
+    from compressed_paged_kv_gqa_amd import synth
+    from oracle import zipage as Z
+    g = synth.rng(SEED, 2, r, "prompt_k")
+    n = C2_PROMPT
+    cap = n + C2_STEPS
+    K = np.zeros((HKV, cap, D))
+    V = np.zeros((HKV, cap, D))
+    heavy = np.where(g.random((HKV, n)) < 0.02, 4.0, 1.0)[..., None]
+    K[:, :n] = synth.round_bf16((g.standard_normal((HKV, n, D)) * heavy).astype(np.float32))
+    V[:, :n] = synth.round_bf16(g.standard_normal((HKV, n, D)).astype(np.float32))
+    qw = synth.round_bf16(g.standard_normal((HKV, HQ // HKV, W, D)).astype(np.float32))
+    sq = synth.round_bf16(g.standard_normal((C2_STEPS, HQ, D)).astype(np.float32))
+    sk = synth.round_bf16(g.standard_normal((C2_STEPS, HKV, D)).astype(np.float32))
+    sv = synth.round_bf16(g.standard_normal((C2_STEPS, HKV, D)).astype(np.float32))
+    params = Z.ScoreParams()
+    keep = (NMAX - 1) * BS
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        for h in range(HKV):
+            S, _F = Z.score_tokens(qw[h], K[h, :n], None, True, BS, params)
+            kept = Z.topk_keep(S, keep)
+            K[h, :keep] = K[h, kept]
+            V[h, :keep] = V[h, kept]
+        n = keep
+        for s in range(C2_STEPS):
+            K[:, n] = sk[s]
+            V[:, n] = sv[s]
+            n += 1
+            Z.decode_attention(sq[s], K[:, :n], V[:, :n])
+        return time.perf_counter() - t0
+
+
+def config2_oracle(pool, procs):
+    t0 = time.perf_counter()
+    secs = pool.map(_oracle_config2_request, range(C2_REQ), chunksize=1)
+    wall = time.perf_counter() - t0
+    cpu_s = float(sum(secs))
+    tokens = C2_REQ * C2_STEPS
+    return {"value": round(tokens / (cpu_s / procs), 2), "unit": "tokens/s", "cores": procs,
+            "seconds_compute": round(cpu_s, 1), "seconds_wall": round(wall, 1),
+            "sample": (f"the whole workload: {C2_REQ} prompts x {C2_PROMPT} tokens resident, "
+                       f"one compression burst to {(NMAX - 1) * BS} tokens per kv-head, then "
+                       f"{C2_STEPS} decode steps, 1 layer; rate = decode tokens / (compute s / "
+                       f"cores)")}
+
+
+def config2_gpu():
+    """The same 64 x 4096 workload on the GPU: prompts resident in the pages
+    (window rows written without log-sum-exp, so scoring gathers its own
+    softmax statistics), the compression burst they trigger, then 128 decode
+    steps; decode tokens / wall time of both."""
+    import torch
+    from compressed_paged_kv_gqa_amd import zp
+    from compressed_paged_kv_gqa_amd.engine import DecodeEngine
+    nb = C2_PROMPT // BS
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=C2_REQ * nb + 8, block_size=BS,
+                            num_kv_heads=HKV, num_q_heads=HQ, head_dim=D, window=W,
+                            max_slots=C2_REQ, n_max=NMAX, dtype="bf16")
+    eng = DecodeEngine(geom, zp.ScoreParams(), C2_REQ, nb, layer_stride=1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(SEED + 2)
+    c = eng.cache
+    c.k.normal_(generator=g)
+    c.k.mul_(torch.where(torch.rand(c.k.shape[:-1], generator=g, device="cuda") < 0.02, 4.0,
+                         1.0).unsqueeze(-1).to(c.k.dtype))
+    c.v.normal_(generator=g)
+    c.qwin.normal_(generator=g)
+    for r in range(C2_REQ):
+        eng.add_request(r, C2_PROMPT)
+    q = torch.randn((C2_STEPS, 1, C2_REQ, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((C2_STEPS, 1, C2_REQ, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((C2_STEPS, 1, C2_REQ, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((1, C2_REQ, HQ, D), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    eng.compress_due_now()
+    eng.wait_compressions()
+    for i in range(C2_STEPS):
+        eng.step(q[i], k[i], v[i], out)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    assert eng.compressions == C2_REQ and zp.zp_workspace_errors(eng.dec_ws) == 0
+    tokens = eng.decoded_tokens
+    return {"workload": f"{C2_REQ} prompts x {C2_PROMPT} tokens resident, compression burst to "
+                        f"{(NMAX - 1) * BS}, then {C2_STEPS} decode steps, 1 layer, bf16, 2% "
+                        f"heavy keys x4", "tokens_per_s": round(tokens / el, 1),
+            "seconds": round(el, 4), "decode_tokens": tokens}
+
+
+def practical_peak():
+    """Measured bandwidth of plain torch kernels on this GPU, beside the
+    nominal 8 TB/s: a 4 GiB device-to-device copy (read + write) and a sum
+    over 4 GiB of bf16 (read once)."""
+    import torch
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    x = src.view(torch.bfloat16)
+
+    def med(fn):
+        t = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return float(np.median(t))
+    cp = med(lambda: dst.copy_(src))
+    rd = med(lambda: x.sum(dtype=torch.float32))
+    del src, dst, x
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * n / cp / 1e6, 1), "read_sum_gbs": round(n / rd / 1e6, 1),
+            "note": "torch copy_ of 4 GiB (bytes read + written) and torch sum over 4 GiB "
+                    "(bytes read), median of 5"}
 
 
 # --------------------------------------------------------------------------
@@ -659,6 +810,10 @@ def main():
         ck = compress_kernel_bench()
         log("prefill in isolation")
         ck = {"compress": ck, "prefill": prefill_kernel_bench()}
+    log("the 64 x 4096 workload in full")
+    c2 = config2_gpu()
+    log("practical peak: device copy and read")
+    peak = practical_peak()
     whole = None
     if not args.no_whole_run:
         import torch
@@ -696,8 +851,12 @@ def main():
                      "kernel": "paged_decode_kernel<bf16,128,4,4>",
                      "avg_launch_ms": round(r["launch_ms"], 4),
                      "algorithmic_bytes_per_launch": round(r["bytes_per_launch"]),
-                     "timed_launches": len(range(0, r["steps"], EVENT_EVERY)) * L},
+                     "timed_launches": len(range(0, r["steps"], EVENT_EVERY)) * L,
+                     "practical_peak": peak,
+                     "frac_of_copy": round(r["achieved_gbs"] / peak["copy_gbs"], 4),
+                     "frac_of_read": round(r["achieved_gbs"] / peak["read_sum_gbs"], 4)},
         "decode_ms_per_step": round(r["decode_ms_per_step"], 3),
+        "config_64x4096": c2,
     }
     if ck is not None:
         line["compress_kernels"] = ck["compress"]

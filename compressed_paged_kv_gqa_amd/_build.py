@@ -69,5 +69,27 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def build_host_sanitized(out_path):
+    """The host-only part of the library (allocator, planner, capacity,
+    scheduler) as a separate shared library built with g++ under
+    AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests. It
+    holds no GPU entry point. Load it with ZP_LIBRARY=<path> and the ASan
+    runtime preloaded (``sanitizer_runtime()``)."""
+    cxx = shutil.which("g++") or "g++"
+    srcs = [os.path.join(CSRC, s) for s in CXX_SOURCES]
+    _run([cxx, "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+          "-I", INCLUDE, "-I", CSRC, *srcs, "-o", out_path])
+    return out_path
+
+
+def sanitizer_runtime():
+    """Path of g++'s AddressSanitizer runtime (to preload into a Python that
+    loads the sanitized host library)."""
+    cxx = shutil.which("g++") or "g++"
+    return subprocess.run([cxx, "-print-file-name=libasan.so"], capture_output=True,
+                          text=True).stdout.strip()
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -59,6 +59,37 @@ class Compressor:
         self.layer_stride = max(1, min(layer_stride, cache.geom.num_layers))
         self.stream = stream
         self.device = device
+        # Buffers reused by every launch (grown when a launch needs more):
+        # device ones are used in stream order on the compression stream; the
+        # pinned metadata buffers form a ring, each rewritten only after the
+        # copy that last read it has run.
+        self._dev = {}
+        self._ring = [[None, None] for _ in range(4)]
+        self._ring_i = 0
+
+    def _device_buf(self, name, numel, dtype, zero, old):
+        """Flat device buffer of at least numel elements; a replaced one goes
+        to `old` so that it outlives the launches already enqueued on it."""
+        t = self._dev.get(name)
+        if t is None or t.numel() < numel:
+            if t is not None:
+                old.append(t)
+            make = torch.zeros if zero else torch.empty
+            t = make(max(numel, 1), dtype=dtype, device=self.device)
+            self._dev[name] = t
+        return t
+
+    def _pinned_meta(self, numel):
+        slot = self._ring[self._ring_i]
+        self._ring_i = (self._ring_i + 1) % len(self._ring)
+        buf, ev = slot
+        if ev is not None:
+            ev.synchronize()          # the copy that last read this buffer has run
+        if buf is None or buf.numel() < numel:
+            buf = torch.zeros(max(numel, 1), dtype=torch.int32).pin_memory()
+            slot[0] = buf
+        slot[1] = torch.cuda.Event()
+        return buf, slot
 
     def launch(self, src, dst, nblocks, slots, first, lse_ok, record=False, n_max=None):
         """src [nreq][maxb] / dst [nreq][n_max-1] block tables, nblocks, query
@@ -75,7 +106,9 @@ class Compressor:
         assert np.shape(dst) == (nreq, nd)
         # one pinned int32 staging buffer: src tables | dst tables | N | slot |
         # first | window log-sum-exp valid
-        meta = torch.zeros(nreq * (maxb + nd + 4), dtype=torch.int32).pin_memory()
+        nmeta = nreq * (maxb + nd + 4)
+        meta_all, ring_slot = self._pinned_meta(nmeta)
+        meta = meta_all[:nmeta]
         m = meta.numpy()
         m[:nreq * maxb] = np.asarray(src, np.int32).reshape(-1)
         m[nreq * maxb:nreq * (maxb + nd)] = np.asarray(dst, np.int32).reshape(-1)
@@ -87,10 +120,12 @@ class Compressor:
         stream = self.stream or torch.cuda.current_stream()
         ready = torch.cuda.Event()
         ready.record()
-        bufs = [meta]
+        bufs = []
         with torch.cuda.stream(stream):
             stream.wait_event(ready)
-            meta_d = meta.to(self.device, non_blocking=True)
+            meta_d = self._device_buf("meta", nmeta, torch.int32, False, bufs)[:nmeta]
+            meta_d.copy_(meta, non_blocking=True)
+            ring_slot[1].record(stream)
             o = nreq * maxb
             src_d = meta_d[:o].view(nreq, maxb)
             dst_d = meta_d[o:o + nreq * nd].view(nreq, nd)
@@ -101,15 +136,25 @@ class Compressor:
             lse_d = (meta_d[o + 3 * nreq:o + 4 * nreq].to(torch.uint8)
                      if self.cache.qwin_lse is not None else None)
             ls = self.layer_stride
-            nl = G.num_layers if record else ls     # recording keeps every layer
-            scores = torch.empty((nl, nreq, G.num_kv_heads, maxb * b), dtype=torch.float32,
-                                 device=self.device)
             use_f = self.params.use_global and self.cache.gscore is not None
-            f_new = torch.empty_like(scores) if use_f else None
-            kept = (torch.empty((G.num_layers, nreq, G.num_kv_heads, keep), dtype=torch.int32,
-                                device=self.device) if record else None)
-            sws = zp.new_workspace(zp.zp_score_workspace_size(G, ls, nreq, maxb), self.device)
-            cws = zp.new_workspace(zp.zp_select_workspace_size(G, ls, nreq, keep), self.device)
+            shape = (G.num_layers if record else ls, nreq, G.num_kv_heads, maxb * b)
+            if record:
+                # recording keeps every layer's scores and kept lists (read by tests)
+                scores = torch.empty(shape, dtype=torch.float32, device=self.device)
+                f_new = torch.empty_like(scores) if use_f else None
+                kept = torch.empty((G.num_layers, nreq, G.num_kv_heads, keep), dtype=torch.int32,
+                                   device=self.device)
+            else:
+                ns = int(np.prod(shape))
+                scores = self._device_buf("scores", ns, torch.float32, False, bufs)[:ns].view(shape)
+                f_new = (self._device_buf("f_new", ns, torch.float32, False, bufs)[:ns].view(shape)
+                         if use_f else None)
+                kept = None
+            # workspaces: zero-filled once; the kernels leave their counters at zero
+            sws = self._device_buf("score_ws", max(zp.zp_score_workspace_size(G, ls, nreq, maxb),
+                                                   256), torch.uint8, True, bufs)
+            cws = self._device_buf("select_ws", max(zp.zp_select_workspace_size(G, ls, nreq, keep),
+                                                    256), torch.uint8, True, bufs)
             for lb in range(0, G.num_layers, ls):
                 lc = min(ls, G.num_layers - lb)
                 sl = slice(lb, lb + lc) if record else slice(0, lc)
@@ -121,7 +166,9 @@ class Compressor:
                                      stream=stream, f_new=fn)
             done = torch.cuda.Event()
             done.record(stream)
-            bufs += [meta_d, first_d, lse_d, scores, f_new, sws, cws]
+            bufs += [first_d, lse_d]
+            if record:
+                bufs += [scores, f_new, kept]
         return done, bufs, scores, kept
 
 
@@ -398,7 +445,8 @@ class ServingEngine:
 
     def __init__(self, geom: zp.CacheGeometry, params: zp.ScoreParams, max_running, table_cap,
                  max_prefill_tokens, policy="hybrid", prefix_sharing=False, layer_stride=8,
-                 async_compress=True, with_global=True, device="cuda", keep_layer_outputs=False):
+                 async_compress=True, with_global=True, device="cuda", keep_layer_outputs=False,
+                 nmax_growth=0):
         G = geom
         self.geom = G
         self.device = device
@@ -409,7 +457,8 @@ class ServingEngine:
                                      with_window_lse=True)
         self.sched = zp.Scheduler(G.num_blocks, G.block_size, G.window, G.n_max, G.max_slots,
                                   max_running, max_prefill_tokens, policy,
-                                  prefix_sharing=prefix_sharing, table_cap=table_cap)
+                                  prefix_sharing=prefix_sharing, table_cap=table_cap,
+                                  nmax_growth=nmax_growth)
         self.async_compress = async_compress
         self.side = torch.cuda.Stream(device=device)
         self.compressor = Compressor(self.cache, params, layer_stride,
@@ -441,7 +490,8 @@ class ServingEngine:
     # ---------------------------------------------------------------- intake
     def add(self, rid, prompt_len, max_new, prefix_group=-1, prefix_len=0, n_max=0):
         """Queues a request; n_max = its own N_max (0: the geometry's, which
-        is also the largest allowed)."""
+        is also the largest allowed). With nmax_growth > 0 the scheduler
+        raises it as the request's sequence grows (adaptive N_max)."""
         self.sched.add(rid, prompt_len, max_new, prefix_group, prefix_len, n_max)
 
     def unfinished(self):

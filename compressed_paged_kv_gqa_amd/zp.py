@@ -135,7 +135,10 @@ def _declare(lib):
         "zp_sched_unfinished": (i32, [_P]),
         "zp_sched_allocator": (_P, [_P]),
     }
+    host_only = bool(os.environ.get("ZP_LIBRARY"))
     for name, (res, args) in sigs.items():
+        if host_only and not hasattr(lib, name):
+            continue          # a host-only build (see lib()) has no GPU entry points
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
@@ -143,14 +146,19 @@ def _declare(lib):
 
 
 def lib():
-    """The loaded libzp (raises ImportError if it has not been built)."""
+    """The loaded libzp (raises ImportError if it has not been built).
+
+    The environment variable ZP_LIBRARY names another build to load instead,
+    for instance a host-only sanitizer build of the allocator, planner and
+    scheduler (tests); its missing GPU entry points are left undeclared."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        path = os.environ.get("ZP_LIBRARY") or LIB_PATH
+        if not os.path.exists(path):
             raise ImportError(
-                f"{LIB_PATH} is missing: build it with "
+                f"{path} is missing: build it with "
                 "`python -m compressed_paged_kv_gqa_amd._build` (there is no fallback path)")
-        _lib = _declare(C.CDLL(LIB_PATH))
+        _lib = _declare(C.CDLL(path))
     return _lib
 
 

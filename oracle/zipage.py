@@ -244,23 +244,15 @@ def cosine_matrix(Ka, Kb):
     return _unit_rows(Ka) @ _unit_rows(Kb).T
 
 
-def _zero_last_above(C, p, tag=None):
-    """In each column, zero the highest-row entry that exceeds p.
-
-    With ``tag`` (one flag per column) a column whose flag is already set is
-    left alone, and the flag is set wherever an entry is zeroed; this is the
-    zero-out tag of Zipage Alg. 3. Modifies C in place.
-    """
-    rows, cols = C.shape
+def _zero_last_above(C, p):
+    """In each column, zero the entry of the highest row that exceeds p (the
+    newest similar token keeps its similarity, Zipage App. C.5). Modifies C
+    in place."""
     above = C > p
     has = above.any(axis=0)
-    if tag is not None:
-        has &= ~tag
-    last = rows - 1 - np.argmax(above[::-1, :], axis=0)   # highest row above p
+    last = C.shape[0] - 1 - np.argmax(above[::-1, :], axis=0)   # highest row above p
     j = np.nonzero(has)[0]
     C[last[j], j] = 0.0
-    if tag is not None:
-        tag[j] = True
     return C
 
 
@@ -278,29 +270,29 @@ def redundancy_rows_original(K, p):
 
 
 def redundancy_rows_flash(K, b, p):
-    """Row sums by the block-wise flash procedure (Zipage Alg. 3, Fig. 12).
+    """Row sums of the flash redundancy (Zipage App. C.5, Alg. 3, Fig. 12).
 
-    For each column block m a zero-out tag starts clear; row blocks i are
-    visited from the last to the first, each computing the b x b cosine block
-    C(i, m) (diagonal zeroed when i == m), zeroing in each untagged column its
-    last entry above p and tagging it, and storing the block's row sums in the
-    accumulator R'[i][m]. The sum over m of R' gives r: [n].
+    Alg. 3 computes the full similarity matrix of Fig. 11 without holding it:
+    one column block of b keys at a time, against every row block. Its
+    result is the original one: in every column the diagonal and the entry
+    of the highest row whose cosine exceeds p (over the whole sequence) are
+    zeroed, then rows are summed. Here, per column block m, the n x b cosine
+    slab is formed from the b x b blocks, its diagonal entries zeroed, each
+    column's highest row above p located and zeroed, and the slab's row sums
+    added to r. Returns r: [n].
     """
     K = _f64(K)
     n = K.shape[0]
     N = n // b
-    Racc = np.zeros((N, N, b), _F)
+    r = np.zeros(n, _F)
     for m in range(N):
         Km = K[m * b:(m + 1) * b]
-        z = np.zeros(b, bool)
-        for i in range(N - 1, -1, -1):
-            Ki = K[i * b:(i + 1) * b]
-            C = cosine_matrix(Ki, Km)
-            if i == m:
-                np.fill_diagonal(C, 0.0)
-            _zero_last_above(C, p, tag=z)
-            Racc[i, m] = C.sum(axis=1)
-    return Racc.sum(axis=1).reshape(n)
+        slab = np.concatenate([cosine_matrix(K[i * b:(i + 1) * b], Km) for i in range(N)])
+        cols = np.arange(b)
+        slab[m * b + cols, cols] = 0.0            # k_j against itself
+        _zero_last_above(slab, p)
+        r += slab.sum(axis=1)
+    return r
 
 
 def redundancy_rows_lightning(K, b, p):

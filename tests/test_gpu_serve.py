@@ -115,10 +115,11 @@ def _check_outputs(eng, model, st, kind, tol):
     return worst
 
 
-def _check_resident(eng, model):
+def _check_resident(eng, model, last_nmax):
     """Traces every resident K/V row of every running request back to the
     token it came from (rows are matched bit for bit against the request's
-    table rows; seeded normal rows do not repeat)."""
+    table rows; seeded normal rows do not repeat). last_nmax: the N_max each
+    request's last compression kept (N_max - 1 blocks)."""
     G = eng.geom
     b = G.block_size
     Kc = eng.cache.k.float().cpu().numpy()
@@ -143,7 +144,7 @@ def _check_resident(eng, model):
                     # kept rows in token order; the window of the last
                     # compression and every token since are consecutive
                     assert np.all(np.diff(pos) > 0)
-                    tail = pos[(model.n_max[r] - 1) * b - G.window:]
+                    tail = pos[(last_nmax[r] - 1) * b - G.window:]
                     np.testing.assert_array_equal(tail, np.arange(tail[0], tail[0] + len(tail)))
                 np.testing.assert_array_equal(V, model.V[l, idx[pos], h])
         checked += 1
@@ -166,26 +167,29 @@ def _stream(seed, n, b, prefix, nmax_choices=None):
 
 CASES = [
     # dtype, policy, prefix, blocks, async, per-request N_max choices (0 = the
-    # geometry's 3); a request arrives every third step
-    ("f32", "hybrid", True, 14, True, None),
-    ("f32", "hybrid", True, 11, False, None),
-    ("f32", "hybrid", False, 11, True, None),
-    ("f32", "constrained", True, 12, True, None),
-    ("f32", "constrained", False, 9, False, None),
-    ("bf16", "hybrid", True, 14, True, None),
-    ("f32", "hybrid", True, 12, True, [2, 0]),
-    ("bf16", "constrained", False, 8, True, [2, 0]),
+    # geometry's), geometry N_max, adaptive N_max growth step (tokens, 0 = off);
+    # a request arrives every third step
+    ("f32", "hybrid", True, 14, True, None, 3, 0),
+    ("f32", "hybrid", True, 11, False, None, 3, 0),
+    ("f32", "hybrid", False, 11, True, None, 3, 0),
+    ("f32", "constrained", True, 12, True, None, 3, 0),
+    ("f32", "constrained", False, 9, False, None, 3, 0),
+    ("bf16", "hybrid", True, 14, True, None, 3, 0),
+    ("f32", "hybrid", True, 12, True, [2, 0], 3, 0),
+    ("bf16", "constrained", False, 8, True, [2, 0], 3, 0),
+    ("f32", "hybrid", True, 14, True, [2], 4, 24),
+    ("bf16", "constrained", False, 12, True, [2], 4, 24),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[
     f"{c[0]}-{c[1]}-{'prefix' if c[2] else 'noprefix'}-nb{c[3]}{'-nmax' if c[5] else ''}"
-    for c in CASES])
+    f"{'-grow' if c[7] else ''}" for c in CASES])
 def test_serving_loop(case):
-    dtype, policy, prefix, nblocks, async_c, nmax_choices = case
-    b, nmax, M = 16, 3, 3
+    dtype, policy, prefix, nblocks, async_c, nmax_choices, nmax, growth = case
+    b, M = 16, 3
     announce(f"serve dtype={dtype} policy={policy} prefix={prefix} blocks={nblocks} "
-             f"async={async_c} nmax={nmax_choices}")
+             f"async={async_c} nmax={nmax_choices} cap={nmax} growth={growth}")
     geom = zp.CacheGeometry(num_layers=2, num_blocks=nblocks, block_size=b, num_kv_heads=2,
                             num_q_heads=4, head_dim=64, window=8, max_slots=M, n_max=nmax,
                             dtype=dtype)
@@ -193,7 +197,10 @@ def test_serving_loop(case):
     model = TableModel(geom, stream, 3)
     eng = E.ServingEngine(geom, zp.ScoreParams(), max_running=8, table_cap=24,
                           max_prefill_tokens=128, policy=policy, prefix_sharing=prefix,
-                          layer_stride=1, async_compress=async_c, keep_layer_outputs=True)
+                          layer_stride=1, async_compress=async_c, keep_layer_outputs=True,
+                          nmax_growth=growth)
+    last_nmax = {}
+    kept_caps = set()
     tol = tol_for(dtype)
     worst, kinds = 0.0, {}
     n = added = 0
@@ -204,6 +211,9 @@ def test_serving_loop(case):
         st = eng.step(model)
         n += 1
         assert n < 5000
+        for i in range(st.n_comp):
+            last_nmax[int(st.c_rid[i])] = int(st.c_nmax[i])
+            kept_caps.add(int(st.c_nmax[i]))
         torch.cuda.synchronize()
         kinds[st.kind] = kinds.get(st.kind, 0) + 1
         if st.kind in (zp.ZP_STEP_PREFILL, zp.ZP_STEP_DECODE):
@@ -212,10 +222,10 @@ def test_serving_loop(case):
             except AssertionError:
                 print(f"[serve] step {n} kind {st.kind} rids {st.rid.tolist()} "
                       f"ctx {st.ctx.tolist()} pos {st.pos.tolist()} errors {eng.device_errors()}")
-                _check_resident(eng, model)
+                _check_resident(eng, model, last_nmax)
                 raise
         # running requests only: in-flight compactions touch none of their blocks
-        _check_resident(eng, model)
+        _check_resident(eng, model, last_nmax)
     eng.poll(wait=True)
     torch.cuda.synchronize()
     assert eng.device_errors() == 0
@@ -225,4 +235,7 @@ def test_serving_loop(case):
     assert stats["compressions"] > 0
     if policy == "constrained" and not prefix:
         assert stats["preemptions"] == 0
+    if growth:
+        # the caps grew with the sequences: compressions kept more than N_base
+        assert max(kept_caps) > 2, kept_caps
     print(f"[serve] steps={n} kinds={kinds} worst={worst:.3g} stats={stats}")
