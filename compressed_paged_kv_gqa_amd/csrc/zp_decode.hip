@@ -291,8 +291,8 @@ __global__ __launch_bounds__(64 * WAVES, (DecodeCfg<T, D, G>::MIN_WAVES)) void p
         for (int u = 0; u < U; ++u)
           if (!(off >= 0 && base + u * RPW + row < t1)) vr[u] = make_uint4(0u, 0u, 0u, 0u);
       }
-      float cq = max_raw(sj, dpp_z<DPP_QUAD_XOR1>(sj));
-      cq = max_raw(cq, dpp_z<DPP_QUAD_XOR2>(cq));
+      float cq = fmaxf(sj, dpp_z<DPP_QUAD_XOR1>(sj));
+      cq = fmaxf(cq, dpp_z<DPP_QUAD_XOR2>(cq));
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float cm = bcast_row_lane(cq, 4 * h) * sc2;  // head h's chunk max

@@ -125,20 +125,17 @@ __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v
 // (v_permlane16_swap exchanges odd and even 16-lane rows, v_permlane32_swap
 // the wavefront halves), so a symmetric op of the two outputs is the pair's
 // result in both lanes. One VALU op each, no LDS round trip.
-// (v_max_f32 written directly: fmaxf would first quiet both inputs, two
-// more ops, for signalling NaNs that the callers never produce)
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32_e32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+// (fmaxf, not a hand-written v_max_f32: the compiler's hazard checks do not
+// look inside inline asm, and a v_max_f32 issued right after a v_exp_f32 or
+// a lane exchange that produced its operand can read the register's old
+// value)
 __device__ __forceinline__ float xor16_max(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor16_sum(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -30,6 +30,7 @@
 //     sequence, S - lambda R, +inf window -> scores.
 // The window QK^T and the cosine matrices are dense contractions (bf16
 // inputs, fp32 accumulation on MFMA 16x16x32; fp32 inputs use 16x16x4 f32).
+#include <algorithm>
 #include <cmath>
 
 #include "zp_device.h"
@@ -100,8 +101,14 @@ constexpr int kCTW = 4;
 // cosine lies in [-1, 1] and a row collects at most one entry per column, so
 // a sum stays below n * 2^40 < 2^63 for any n < 2^23.
 constexpr double kFixScale = 1099511627776.0;  // 2^40
+// rint(c * 2^40) from exact single-precision steps (|c| < 2^15): c * 2^16
+// splits into its integer part h and a fraction in (-1, 1), which 2^24 turns
+// into an integer after rounding, so the result is h * 2^24 + rint(frac * 2^24).
 __device__ __forceinline__ unsigned long long to_fix(float c) {
-  return static_cast<unsigned long long>(__double2ll_rn(static_cast<double>(c) * kFixScale));
+  const float x = c * 65536.0f;
+  const float h = truncf(x);
+  const int lo = static_cast<int>(rintf((x - h) * 16777216.0f));
+  return static_cast<unsigned long long>((static_cast<long long>(static_cast<int>(h)) << 24) + lo);
 }
 __device__ __forceinline__ float from_fix(unsigned long long v) {
   return static_cast<float>(static_cast<double>(static_cast<long long>(v)) * (1.0 / kFixScale));
@@ -771,11 +778,11 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   float* ptile = lse2 + R;                        // [4][R][16] (general window only)
 
   const int pidx = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
+  const int r = z % P.nreq;
+  if (lse_given(P, r)) return;  // done by phase A (which also flags bad geometry)
   int N, slot;
   const int page = resolve_page(P, pidx, z, &N, &slot);
   if (page < 0) return;
-  const int r = z % P.nreq;
-  if (lse_given(P, r)) return;  // done by phase A
   const int layer = P.layer_begin + z / P.nreq;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int cl = lane & 15;
@@ -811,19 +818,23 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
 // ---------------------------------------------------------------------------
 // Phase C: pooling, redundancy softmax, combination, window.
 // ---------------------------------------------------------------------------
-__device__ float block_reduce(float v, bool is_max, float* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  v = is_max ? group_max<64>(v) : group_sum<64>(v);
-  __syncthreads();
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  float t = red[0];
-  for (int i = 1; i < 4; ++i) t = is_max ? fmaxf(t, red[i]) : t + red[i];
-  return t;
+// (max, sum of exp2(x - max)) pairs merged; an empty pair is (-inf, 0).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
+  m = mn;
 }
 
-__global__ __launch_bounds__(256) void score_finalize_kernel(ScoreParams P) {
-  __shared__ float red[4];
+// One workgroup of kFinThreads per (layer x request, kv-head), 4 tokens per
+// thread per chunk; pooling halves up to kFinHalo are taken from an LDS copy
+// of the chunk.
+constexpr int kFinThreads = 1024, kFinChunk = 4 * kFinThreads, kFinHalo = 64;
+
+__global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams P) {
+  constexpr int NW = kFinThreads / 64;
+  __shared__ float red[2][NW];
+  __shared__ float s1c[kFinChunk + 2 * kFinHalo];
   const int h = blockIdx.x, z = blockIdx.y;
   const int r = z % P.nreq;
   const int N = P.num_blocks[r];
@@ -834,8 +845,8 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(ScoreParams P) {
     const int pg = P.tables[(int64_t)r * P.table_stride + i];
     if (pg < 0 || pg >= P.num_blocks_total) return;  // phases A/B flagged it
   }
-  const int tid = threadIdx.x;
-  const int n = N * P.b;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = N * P.b;  // a multiple of 16
   const int64_t zh = (int64_t)z * P.h_kv + h;
   const float* s1 = P.s1buf + zh * ((int64_t)P.max_blocks * P.b);
   float* rr = P.rbuf + zh * ((int64_t)P.max_blocks * P.b);
@@ -843,38 +854,659 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(ScoreParams P) {
   const bool first = P.first[r] != 0;
   const bool pool = (P.flags & ZP_SCORE_POOL) && (first || !(P.flags & ZP_SCORE_POOL_FIRST_ONLY));
   const bool redun = (P.flags & ZP_SCORE_REDUNDANCY) != 0;
-  const int half = P.pool_kernel / 2;
+  const int half = pool ? P.pool_kernel / 2 : 0;
   const float c2 = P.inv_tau * kLog2e;  // softmax(r / tau) in the exp2 domain
 
-  float mx = -INFINITY, sum = 0.f;
   if (redun && (P.flags & ZP_SCORE_REDUNDANCY_FLASH)) {
     // flash: row sum over the whole sequence minus its zeroed entries, / n
-    // (each thread keeps the same tokens t in every pass below)
+    // (each thread keeps the same tokens in every pass below)
     const unsigned long long* rs = P.rsub + zh * ((int64_t)P.max_blocks * P.b);
-    for (int t = tid; t < n; t += 256) rr[t] = (rr[t] - from_fix(rs[t])) / (float)n;
+    for (int t = 4 * tid; t < n; t += kFinChunk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rr[t + e] = (rr[t + e] - from_fix(rs[t + e])) / (float)n;
   }
+  // softmax statistics of r / tau in one pass: each thread's running
+  // (max, sum), then the wavefront and the workgroup, in a fixed order
+  float mx = -INFINITY, inv_sum = 0.f;
   if (redun) {
-    float m = -INFINITY;
-    for (int t = tid; t < n; t += 256) m = fmaxf(m, rr[t] * c2);
-    mx = block_reduce(m, true, red);
-    float s = 0.f;
-    for (int t = tid; t < n; t += 256) s += exp2f(rr[t] * c2 - mx);
-    sum = block_reduce(s, false, red);
-  }
-  const float inv_sum = redun ? 1.0f / sum : 0.f;
-  for (int t = tid; t < n; t += 256) {
-    float s = s1[t];
-    if (pool) {
-      const int lo = max(0, t - half), hi = min(n - 1, t + half);
-      for (int i = lo; i <= hi; ++i) s = fmaxf(s, s1[i]);
+    float m = -INFINITY, sm = 0.f;
+    for (int t = 4 * tid; t < n; t += kFinChunk) {
+      const float4 x = *reinterpret_cast<const float4*>(rr + t);
+      const float m4 = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)) * c2;
+      const float mn = fmaxf(m, m4);
+      sm = sm * exp2f(m - mn) + exp2f(x.x * c2 - mn) + exp2f(x.y * c2 - mn) +
+           exp2f(x.z * c2 - mn) + exp2f(x.w * c2 - mn);
+      m = mn;
     }
-    if (redun) s -= P.lambda_ * (exp2f(rr[t] * c2 - mx) * inv_sum);
-    if (t >= n - P.w) s = INFINITY;
-    out[t] = s;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lse_merge(m, sm, shfl_xor_f(m, o), shfl_xor_f(sm, o));
+    if (lane == 0) {
+      red[0][wv] = m;
+      red[1][wv] = sm;
+    }
+    __syncthreads();
+    m = red[0][0];
+    sm = red[1][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) lse_merge(m, sm, red[0][i], red[1][i]);
+    mx = m;
+    inv_sum = 1.0f / sm;
+  }
+  const bool lds_pool = pool && half <= kFinHalo;
+  const bool vec_out = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  for (int c0 = 0; c0 < n; c0 += kFinChunk) {
+    if (lds_pool) {  // s1 of [c0 - half, c0 + chunk + half), -inf outside the sequence
+      __syncthreads();
+      for (int i = tid; i < kFinChunk + 2 * half; i += kFinThreads) {
+        const int t = c0 - half + i;
+        s1c[i] = (t >= 0 && t < n) ? s1[t] : -INFINITY;
+      }
+      __syncthreads();
+    }
+    const int t = c0 + 4 * tid;
+    if (t >= n) continue;
+    float v[4];
+    if (lds_pool) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float m = -INFINITY;
+        for (int i = 4 * tid + e; i <= 4 * tid + e + 2 * half; ++i) m = fmaxf(m, s1c[i]);
+        v[e] = m;
+      }
+    } else if (pool) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int lo = max(0, t + e - half), hi = min(n - 1, t + e + half);
+        float m = -INFINITY;
+        for (int i = lo; i <= hi; ++i) m = fmaxf(m, s1[i]);
+        v[e] = m;
+      }
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(s1 + t);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+    if (redun) {
+      const float4 x = *reinterpret_cast<const float4*>(rr + t);
+      const float xr[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] -= P.lambda_ * (exp2f(xr[e] * c2 - mx) * inv_sum);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (t + e >= n - P.w) v[e] = INFINITY;
+    if (vec_out) {
+      *reinterpret_cast<float4*>(out + t) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[t + e] = v[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase A, persistent form for the serving shape (bf16, head_dim 128, blocks
+// of 256 tokens, a 16-token window, g <= 4 query heads per kv-head, lightning
+// redundancy or none): one workgroup of 16 wavefronts per CU walks a
+// contiguous range of the (layer, kv-head, request, block) items. The next
+// item's keys, global-score history and window log-sum-exp are copied
+// HBM -> LDS (global_load_lds, no registers) into the second of two buffers
+// while the current item is scored, so the copy of every block after the
+// first overlaps the work on the one before. Items run in the order
+// (layer, kv-head, request, block), so consecutive items of a workgroup
+// share their window queries, which are copied only when the request or
+// kv-head changes. Per item:
+//   1. MFMA window logits of the wave's column tile against the g*16 window
+//      rows (LDS), giving S0 and the global score from the window
+//      log-sum-exp, or each row's partial (max, sum); key norms, four lanes
+//      per key;
+//   2. MFMA cosine tiles: wave w takes 2 column tiles against 8 of the 16
+//      row tiles and keeps, per column, the sum of k_i . k_j / |k_i| over
+//      its rows and the highest row whose cosine is above p (the Gram
+//      matrix is symmetric, so a column's sum is the row sum of the same
+//      key);
+//   3. per column, the two halves combined and its zeroed entry (one dot
+//      product) added to that entry's row in 64-bit fixed point (exact, so
+//      the same bits in any order);
+//   4. each row's sum minus its zeroed entries, / n: the redundancy row
+//      sums.
+// ---------------------------------------------------------------------------
+// Barrier over LDS traffic only: each wavefront's LDS operations are
+// complete (lgkmcnt 0), its HBM loads and copies into LDS are not waited for.
+// A __syncthreads() (whose fence also waits for copies into LDS) would wait
+// for the next item's copies, which are meant to stay in flight; the LDS
+// they fill is read only after the full wait at the end of the item. The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt and expcnt at their maximum, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Max over lane pairs (l, l ^ 16) / (l, l ^ 32) of an int, with the row swaps.
+__device__ __forceinline__ int xor16_max_i(int v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int xor32_max_i(int v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+
+// 64-bit add to an LDS word, no return value. Written as the instruction
+// itself: the compiler would otherwise wait for every copy into LDS still in
+// flight (vmcnt 0) before an LDS atomic, whatever its address; this one
+// touches only `sub`, which no copy writes. lds_barrier()'s lgkmcnt wait
+// completes it.
+__device__ __forceinline__ void lds_add_u64(unsigned long long* p, unsigned long long v) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned long long*)p;
+  asm volatile("ds_add_u64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lt_lds_ptr;
+typedef __attribute__((address_space(1))) void* lt_gbl_ptr;
+
+constexpr int kLtThreads = 1024;
+
+// Per-request and per-block values the persistent kernel reads (block
+// counts, block ids, slots, flags), through the scalar cache: the address is
+// the same in every lane, and scalar loads are waited for with the LDS /
+// scalar counter, so they never wait behind the in-flight HBM -> LDS copies.
+typedef const __attribute__((address_space(4))) int32_t* lt_const_i32;
+typedef const __attribute__((address_space(4))) uint32_t* lt_const_u32;
+__device__ __forceinline__ int32_t lt_ld(const int32_t* p, int64_t i) {
+  return ((lt_const_i32)p)[i];
+}
+__device__ __forceinline__ uint32_t lt_ld_u8(const uint8_t* p, int64_t i) {
+  // the aligned word holding byte i (allocations are at least 4-byte aligned)
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p) + i;
+  const uint32_t w = *((lt_const_u32)(a & ~uintptr_t(3)));
+  return (w >> (8 * (a & 3))) & 0xffu;
+}
+
+// Cursor over the items of one workgroup, with the values its item needs.
+struct LtItem {
+  int li, h, r, pidx, N;  // layer index in the call, kv-head, request, block, blocks of r
+  int page, slot;
+  bool valid, first, lse;
+};
+
+// Blocks of request r that scoring covers (0 when its geometry is invalid;
+// such a request is flagged once by workgroup 0).
+__device__ __forceinline__ int lt_blocks(const ScoreParams& P, int r) {
+  const int N = lt_ld(P.num_blocks, r);
+  return (N <= 0 || N > P.max_blocks || N > P.table_stride) ? 0 : N;
+}
+
+__device__ __forceinline__ void lt_fill(const ScoreParams& P, LtItem& it) {
+  it.page = lt_ld(P.tables, (int64_t)it.r * P.table_stride + it.pidx);
+  it.slot = lt_ld(P.qslot, it.r);
+  it.first = lt_ld_u8(P.first, it.r) != 0;
+  it.lse = P.lse_ok && P.qwin_lse && lt_ld_u8(P.lse_ok, it.r) != 0;
+}
+
+__device__ __forceinline__ void lt_next_request(const ScoreParams& P, LtItem& it, int layer_count) {
+  // first request (at or after it.r) with blocks, moving to the next kv-head
+  // and layer as needed
+  for (;;) {
+    if (it.r >= P.nreq) {
+      it.r = 0;
+      if (++it.h >= P.h_kv) {
+        it.h = 0;
+        if (++it.li >= layer_count) {
+          it.valid = false;
+          return;
+        }
+      }
+    }
+    it.N = lt_blocks(P, it.r);
+    if (it.N > 0) return;
+    ++it.r;
+  }
+}
+
+__device__ __forceinline__ void lt_advance(const ScoreParams& P, LtItem& it, int layer_count) {
+  if (++it.pidx >= it.N) {
+    it.pidx = 0;
+    ++it.r;
+    lt_next_request(P, it, layer_count);
+  }
+  if (it.valid) lt_fill(P, it);
+}
+
+template <int RT>
+__global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScoreParams P,
+                                                                       int layer_count) {
+  constexpr int R = RT * 16;  // window rows: g query heads x 16 window slots
+  constexpr int D = 128, BT = 256;
+  using L = LdsTile<bf16_t, D>;
+  using M = Mma<bf16_t, D>;
+  __shared__ __align__(16) char Ka[BT * L::ROWB];
+  __shared__ __align__(16) char Kb[BT * L::ROWB];
+  __shared__ __align__(16) char Qs[R * L::ROWB];
+  __shared__ __align__(16) float Fa[BT];
+  __shared__ __align__(16) float Fb[BT];
+  __shared__ __align__(16) float La[R];
+  __shared__ __align__(16) float Lb[R];
+  __shared__ __align__(16) float inv_s[BT];
+  __shared__ __align__(16) float nrm_s[BT];
+  __shared__ __align__(16) unsigned long long sub[BT];
+  __shared__ __align__(16) float csum[2][BT];  // per half of the rows: the column's sum (then csum[0]: the row sum),
+  __shared__ __align__(16) short crow[2][BT];  //   the highest row above p (-1: none)
+  __shared__ __align__(16) float wstat[8][R][2];  // window-row statistics (waves 0..7)
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const bool redun = (P.flags & ZP_SCORE_REDUNDANCY) != 0;
+  const bool glob = (P.flags & ZP_SCORE_GLOBAL) != 0;
+  const float sc2 = P.qk_scale;
+
+  // The workgroup's range of items, in units of the call's valid blocks.
+  int S = 0;
+  for (int r = 0; r < P.nreq; ++r) {
+    const int N = lt_ld(P.num_blocks, r);
+    if (N > P.max_blocks || N > P.table_stride) {
+      if (blockIdx.x == 0 && tid == 0) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
+    } else if (N > 0) {
+      S += N;
+    }
+  }
+  const int64_t V = (int64_t)layer_count * P.h_kv * S;
+  const int64_t v0 = V * blockIdx.x / gridDim.x, v1 = V * (blockIdx.x + 1) / gridDim.x;
+  if (v0 >= v1) return;
+  LtItem cur;
+  {
+    cur.li = (int)(v0 / ((int64_t)P.h_kv * S));
+    const int64_t rem = v0 % ((int64_t)P.h_kv * S);
+    cur.h = (int)(rem / S);
+    int s = (int)(rem % S);
+    cur.r = 0;
+    cur.valid = true;
+    for (;;) {
+      const int N = lt_blocks(P, cur.r);
+      if (s < N) break;
+      s -= N;
+      ++cur.r;
+    }
+    cur.pidx = s;
+    cur.N = lt_blocks(P, cur.r);
+    lt_fill(P, cur);
+  }
+  int left = (int)(v1 - v0);  // items this workgroup still scores, the current one included
+
+  auto item_ok = [&](const LtItem& it) -> bool {
+    return it.page >= 0 && it.page < P.num_blocks_total && it.slot >= 0 && it.slot < P.max_slots;
+  };
+
+  // Copies item `it`'s keys (swizzled tile), history F and window LSE into
+  // (Kd, Fd, Ld): every wavefront 4 KiB of keys; wavefront 0 F, wavefront 1
+  // the LSE.
+  auto issue = [&](const LtItem& it, char* Kd, float* Fd, float* Ld) __attribute__((always_inline)) {
+    if (!item_ok(it)) return;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));  // per item: keeps the addresses out of the loop
+    const int layer = P.layer_begin + it.li;
+    const char* kp = reinterpret_cast<const char*>(
+        reinterpret_cast<const bf16_t*>(P.kc) + layer * P.kv_layer_elems +
+        ((int64_t)it.page * P.h_kv + it.h) * BT * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = (wv * 4 + i) * 64 + lane;      // LDS chunk position
+      const int rr = p >> 4, c = (p & 15) ^ (rr & 15);
+      __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(kp + rr * L::ROWB + c * 16),
+                                       (lt_lds_ptr)(Kd + (wv * 4 + i) * 1024), 16, 0, 0);
+    }
+    if (glob && !it.first && wv == 0) {  // 1 KiB, 16 bytes per lane
+      const float* fp = P.gscore + layer * P.f_layer_elems + ((int64_t)it.page * P.h_kv + it.h) * BT;
+      __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(fp + lane * 4), (lt_lds_ptr)Fd, 16, 0, 0);
+    }
+    if (wv == 1 && it.lse && lane < R / 4) {  // R floats, 16 bytes per lane
+      const float* lp = P.qwin_lse + layer * P.qlse_layer_elems + ((int64_t)it.slot * P.h_kv + it.h) * R;
+      __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(lp + lane * 4), (lt_lds_ptr)Ld, 16, 0, 0);
+    }
+  };
+  // The window queries of item `it` into Qs (R rows, swizzled like K):
+  // R / 4 copies of 1 KiB, one per wavefront.
+  auto issue_q = [&](const LtItem& it) __attribute__((always_inline)) {
+    if (it.slot < 0 || it.slot >= P.max_slots || wv >= R / 4) return;
+    const int layer = P.layer_begin + it.li;
+    const char* qp = reinterpret_cast<const char*>(
+        reinterpret_cast<const bf16_t*>(P.qwin) + layer * P.qwin_layer_elems +
+        ((int64_t)it.slot * P.h_kv + it.h) * R * D);
+    const int p = wv * 64 + lane;
+    const int rr = p >> 4, c = (p & 15) ^ (rr & 15);
+    __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(qp + rr * L::ROWB + c * 16),
+                                     (lt_lds_ptr)(Qs + wv * 1024), 16, 0, 0);
+  };
+
+  // Scores item `it` from (Kt, Ft, Lt); `nx` is the next item (its queries
+  // are copied into Qs once this item's window phase is done).
+  auto process = [&](const LtItem& it, const LtItem& nx, const char* Kt, const float* Ft,
+                     const float* Lt) __attribute__((always_inline)) {
+    // Thread ids laundered once per item: the compiler would otherwise hoist
+    // every lane-dependent LDS address out of the item loop and keep them
+    // all live (register spills).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, q = lane >> 4, cl = lane & 15;
+    const bool ok = item_ok(it);
+    const int z = it.li * P.nreq + it.r;
+    const int64_t zh = (int64_t)z * P.h_kv + it.h;
+    const bool last = it.pidx == it.N - 1;
+    const int n = it.N * BT;
+    if (!ok && tid == 0) {
+      flag_error(P.err, (it.page < 0 || it.page >= P.num_blocks_total) ? ZP_DEVERR_BLOCK_ID
+                                                                        : ZP_DEVERR_SLOT);
+    }
+    // 1. window logits (LSE given: wave w takes column tile w; statistics:
+    // waves 0..7 take column tiles w, w + 8) and key norms (4 lanes per key)
+    if (ok) {
+      if (it.lse) {
+        typename M::op_t bop[M::NKS];
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) bop[ks] = M::lds(Kt, wv * 16 + cl, ks, lane);
+        float pm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          typename M::op_t a[M::NKS];
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks) acc = M::mma(a[ks], bop[ks], acc);
+          const float4 l4 = *reinterpret_cast<const float4*>(Lt + rt * 16 + 4 * q);
+          const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            pm[v] = fmaxf(pm[v], __builtin_amdgcn_exp2f(fmaf(acc[v], sc2, -lv[v])));
+        }
+        const int col = wv * 16 + cl;
+        if (last) {  // causal mask: window slot u = 4q + v sees keys up to BT - 16 + u
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (col > BT - 16 + 4 * q + v) pm[v] = 0.f;
+        }
+        float s = (pm[0] + pm[1]) + (pm[2] + pm[3]);
+        s = xor32_sum(xor16_sum(s));
+        if (q == 0) {
+          const float s0 = s * (1.0f / 16.0f);
+          float s1 = s0;
+          if (glob) {
+            if (!it.first && !last) {
+              const float f = P.alpha * Ft[col];
+              s1 = (P.flags & ZP_SCORE_GLOBAL_SUM) ? f + s0 : fmaxf(f, s0);
+            }
+            P.f_new[zh * P.scores_stride + (int64_t)it.pidx * BT + col] = s1;
+          }
+          P.s1buf[zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT + col] = s1;
+        }
+      } else if (wv < 8) {
+        // partial (max, sum of exp2) of each row over this wave's 32 columns
+        typename M::op_t bop[2][M::NKS];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks) bop[c][ks] = M::lds(Kt, (wv + 8 * c) * 16 + cl, ks, lane);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          typename M::op_t a[M::NKS];
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
+          floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) acc[c] = M::mma(a[ks], bop[c][ks], acc[c]);
+          if (last) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if ((wv + 8 * c) * 16 + cl > BT - 16 + 4 * q + v) acc[c][v] = -INFINITY;
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float Mx = group_max<16>(fmaxf(acc[0][v], acc[1][v]));
+            const float ms = Mx == -INFINITY ? 0.f : Mx * sc2;
+            float sm = __builtin_amdgcn_exp2f(fmaf(acc[0][v], sc2, -ms)) +
+                       __builtin_amdgcn_exp2f(fmaf(acc[1][v], sc2, -ms));
+            sm = group_sum<16>(sm);
+            if (cl == 0) {
+              wstat[wv][rt * 16 + 4 * q + v][0] = Mx == -INFINITY ? -INFINITY : ms;
+              wstat[wv][rt * 16 + 4 * q + v][1] = sm;
+            }
+          }
+        }
+      }
+      if (redun) {  // |k|^2, 4 lanes per key (32 dimensions each)
+        const int row = tid >> 2, part = tid & 3;
+        float ss = 0.f;
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int c = part * 4; c < part * 4 + 4; ++c) {
+          const uint4 u = *reinterpret_cast<const uint4*>(Kt + L::chunk_pos(row, c) * 16);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), __builtin_bit_cast(bf2, u.x), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), __builtin_bit_cast(bf2, u.y), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), __builtin_bit_cast(bf2, u.z), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), __builtin_bit_cast(bf2, u.w), ss, false);
+        }
+        ss += dpp_f<DPP_QUAD_XOR1>(ss);
+        ss += dpp_f<DPP_QUAD_XOR2>(ss);
+        if (part == 0) {
+          inv_s[row] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+          nrm_s[row] = sqrtf(ss);
+        }
+      }
+    }
+    lds_barrier();  // B1: norms and window rows done; Qs free
+    if (nx.valid && (nx.li != it.li || nx.h != it.h || nx.r != it.r)) issue_q(nx);
+    if (ok && !it.lse && tid < R) {
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w2 = 0; w2 < 8; ++w2) Mx = fmaxf(Mx, wstat[w2][tid][0]);
+      float Sm = 0.f;
+      if (Mx != -INFINITY)
+#pragma unroll
+        for (int w2 = 0; w2 < 8; ++w2) Sm += wstat[w2][tid][1] * exp2f(wstat[w2][tid][0] - Mx);
+      float* st = P.stats + ((zh * P.max_blocks + it.pidx) * R + tid) * 2;
+      st[0] = Mx;
+      st[1] = Sm;
+    }
+    if (!ok || !redun) return;
+    // 2. cosine tiles: wave w takes column tiles 2(w % 8), +1 against row
+    // tiles 8(w / 8) .. +7. Per column, over the wave's rows: the highest
+    // row whose entry is above p, and the sum of the entries,
+    // sum_i k_i . k_j / |k_i|, the diagonal left out. The matrix is
+    // symmetric, so column j's sum is row j's. Software-pipelined: the
+    // products of row tile k + 1 are issued before the epilogue of tile k.
+    {
+      const int cg = wv & 7, rh = wv >> 3;
+      const int kd = 2 * cg - 8 * rh;  // local row tile of the diagonal tile of c = 0, if in range
+      const bool has_diag = (cg >> 2) == rh;
+      typename M::op_t bop[2][M::NKS];
+      float pnc[2], cs[2] = {0.f, 0.f};
+      int bk[2] = {-1, -1};  // 4 * local row tile + v of the highest entry above p
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) bop[c][ks] = M::lds(Kt, (2 * cg + c) * 16 + cl, ks, lane);
+        pnc[c] = P.p * nrm_s[(2 * cg + c) * 16 + cl];
+      }
+      bool dg[4];  // this lane's element on the diagonal of a diagonal tile
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dg[v] = 4 * q + v == cl;
+      // this half's rows (row tile 8 rh + k is row tile k from here: the
+      // swizzle depends on the row only modulo 16, so each tile's addresses
+      // are the first's plus a constant)
+      const char* Kh = Kt + rh * 128 * L::ROWB;
+      const float* ivh = inv_s + rh * 128;
+      // Software-pipelined two deep: in step k the operands of tile k + 2
+      // and the inverse norms of tile k + 1 are read from LDS, tile k + 1's
+      // products are issued, and tile k's epilogue runs, so no step waits
+      // on an LDS read or a product issued in the same step.
+      auto load_a = [&](int k, typename M::op_t* a) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Kh, k * 16 + cl, ks, lane);
+      };
+      auto products = [&](const typename M::op_t* a, floatx4* acc) __attribute__((always_inline)) {
+        acc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) acc[c] = M::mma(a[ks], bop[c][ks], acc[c]);
+      };
+      typename M::op_t aA[M::NKS], aB[M::NKS];
+      floatx4 accA[2], accB[2];
+      float4 ivA, ivB;
+      load_a(0, aA);
+      load_a(1, aB);
+      ivA = *reinterpret_cast<const float4*>(ivh + 4 * q);
+      products(aA, accA);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        floatx4* cur = (k & 1) ? accB : accA;
+        floatx4* nxt = (k & 1) ? accA : accB;
+        typename M::op_t* an = (k & 1) ? aA : aB;  // operands of tile k + 1
+        typename M::op_t* af = (k & 1) ? aB : aA;  // free: tile k's, consumed last step
+        const float4 iv = (k & 1) ? ivB : ivA;
+        if (k < 6) load_a(k + 2, af);
+        if (k < 7) {
+          float4& ivn = (k & 1) ? ivA : ivB;
+          ivn = *reinterpret_cast<const float4*>(ivh + (k + 1) * 16 + 4 * q);
+          products(an, nxt);
+        }
+        const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
+        // x = k_i . k_j / |k_i|: summed for the column (the diagonal, k_j
+        // against itself, is taken out after the loop), and above p |k_j|
+        // exactly when the cosine is above p
+        float x[2][4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) x[c][v] = cur[c][v] * ivv[v];
+          cs[c] += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
+        }
+        // the highest row above p, tracked only in tiles that have one (the
+        // test is made for the whole wavefront at once; a diagonal tile
+        // always has one, its diagonal, which is never the entry to zero)
+        const bool any = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])) > pnc[0] ||
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])) > pnc[1];
+        if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const bool isd = has_diag && k == kd + c;  // wave-uniform
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const bool hit = x[c][v] > pnc[c] && !(isd && dg[v]);
+              bk[c] = hit ? 4 * k + v : bk[c];
+            }
+          }
+        }
+        // the epilogue of tile k is made here (not deferred, which would
+        // keep every tile's products live); tile k + 1's products overlap it
+#pragma unroll
+        for (int c = 0; c < 2; ++c) asm volatile("" : "+v"(bk[c]), "+v"(cs[c]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // over the four row groups q of the 16 lanes of each column: the
+      // highest row and the sum, in a fixed order
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = bk[c] < 0 ? -1 : (8 * rh + (bk[c] >> 2)) * 16 + 4 * q + (bk[c] & 3);
+        const int top = xor32_max_i(xor16_max_i(row));
+        const int col = (2 * cg + c) * 16 + cl;
+        float sum = xor32_sum(xor16_sum(cs[c]));
+        // the diagonal entry k_j . k_j / |k_j| = |k_j| out of the sum
+        if (has_diag) sum -= nrm_s[col];
+        if (q == 0) {
+          crow[rh][col] = (short)top;
+          csum[rh][col] = sum;
+        }
+      }
+    }
+    lds_barrier();  // B2
+    // 3. per column j (four threads, 32 dimensions each): its row sum, and
+    // its zeroed entry (the highest row above p over both halves), added to
+    // that row in 64-bit fixed point (the same bits in any order)
+    {
+      const int j = tid >> 2, part = tid & 3;
+      const int r1 = crow[1][j];
+      const int is = r1 >= 0 ? r1 : (int)crow[0][j];  // rows of half 1 are the higher ones
+      float d = 0.f;
+      if (is >= 0) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int c = part * 4; c < part * 4 + 4; ++c) {
+          const uint4 u = *reinterpret_cast<const uint4*>(Kt + L::chunk_pos(is, c) * 16);
+          const uint4 w = *reinterpret_cast<const uint4*>(Kt + L::chunk_pos(j, c) * 16);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), __builtin_bit_cast(bf2, w.x), d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), __builtin_bit_cast(bf2, w.y), d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), __builtin_bit_cast(bf2, w.z), d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), __builtin_bit_cast(bf2, w.w), d, false);
+        }
+      }
+      d += dpp_f<DPP_QUAD_XOR1>(d);
+      d += dpp_f<DPP_QUAD_XOR2>(d);
+      if (part == 0) {
+        const float ivj = inv_s[j];
+        csum[0][j] = (csum[0][j] + csum[1][j]) * ivj;
+        if (is >= 0) lds_add_u64(&sub[is], to_fix(d * inv_s[is] * ivj));
+      }
+    }
+    lds_barrier();  // B3
+    // 4. row i: (row sum - zeroed entries) / n; the fixed-point word is
+    // cleared for the next item
+    if (tid < BT) {
+      const int i = tid;
+      P.rbuf[zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT + i] =
+          (csum[0][i] - from_fix(sub[i])) / (float)n;
+      sub[i] = 0ull;
+    }
+  };
+
+  if (tid < BT) sub[tid] = 0ull;
+  issue(cur, Ka, Fa, La);
+  issue_q(cur);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (;;) {
+    LtItem nx = cur;
+    if (left > 1) lt_advance(P, nx, layer_count); else nx.valid = false;
+    if (nx.valid) issue(nx, Kb, Fb, Lb);
+    process(cur, nx, Ka, Fa, La);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!nx.valid) break;
+    cur = nx;
+    --left;
+    nx = cur;
+    if (left > 1) lt_advance(P, nx, layer_count); else nx.valid = false;
+    if (nx.valid) issue(nx, Ka, Fa, La);
+    process(cur, nx, Kb, Fb, Lb);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!nx.valid) break;
+    cur = nx;
+    --left;
   }
 }
 
 constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
+
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 template <typename T, int D, int R>
 static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
@@ -902,10 +1534,22 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
                           hipFuncAttributeMaxDynamicSharedMemorySize, int(smemB)) != hipSuccess)
     return fail(ZP_EHIP, "zp_score_tokens: cannot reserve %zu bytes of LDS", smemA);
   dim3 gridP(P.max_blocks, P.h_kv, items);
-  hipLaunchKernelGGL(kA, gridP, dim3(256), smemA, s, P);
+  bool persistent = false;
+  if constexpr (sizeof(T) == 2 && D == 128 && R <= 64) {
+    // the serving shape: bf16 keys of head_dim 128 in blocks of 256, a
+    // 16-token window, g <= 4, lightning redundancy or none
+    if (P.b == 256 && P.w == 16 && !flash) {
+      const int64_t work = int64_t(items) * P.h_kv * P.max_blocks;
+      const int grid = int(std::min<int64_t>(work, device_cus()));
+      hipLaunchKernelGGL(score_lightning_kernel<R / 16>, dim3(grid), dim3(kLtThreads), 0, s, P,
+                         items / P.nreq);
+      persistent = true;
+    }
+  }
+  if (!persistent) hipLaunchKernelGGL(kA, gridP, dim3(256), smemA, s, P);
   if (flash) hipLaunchKernelGGL(kF, gridP, dim3(256), smemF, s, P);
   hipLaunchKernelGGL(kB, gridP, dim3(256), smemB, s, P);
-  hipLaunchKernelGGL(score_finalize_kernel, dim3(P.h_kv, items), dim3(256), 0, s, P);
+  hipLaunchKernelGGL(score_finalize_kernel, dim3(P.h_kv, items), dim3(kFinThreads), 0, s, P);
   return ZP_OK;
 }
 

@@ -183,6 +183,14 @@ def test_score_flag_combinations(flags):
          layer_count=2)
 
 
+@pytest.mark.parametrize("p", [0.0, 0.5])
+def test_score_redundancy_threshold_planted_serving_shape(p):
+    """Planted clusters in blocks of 256 (d 128, g 4, w 16: the persistent
+    kernel), first and later compressions, several requests per workgroup."""
+    sp = zp.ScoreParams(p=p, pool_first_only=False)
+    _run("bf16", 128, 32, 8, 256, 16, [5, 3, 7], lambda r: r != 1, sp, planted=True, heavy=False)
+
+
 @pytest.mark.parametrize("p", [0.0, 0.1, 0.5])
 def test_score_redundancy_threshold_sweep_planted(p):
     sp = zp.ScoreParams(p=p, use_global=False, use_pool=False)
