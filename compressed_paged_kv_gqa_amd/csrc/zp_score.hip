@@ -1204,7 +1204,9 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
         typename M::op_t bop[M::NKS];
 #pragma unroll
         for (int ks = 0; ks < M::NKS; ++ks) bop[ks] = M::lds(Kt, wv * 16 + cl, ks, lane);
-        float pm[4] = {0.f, 0.f, 0.f, 0.f};
+        // the group max of P = exp2(logit - lse) is exp2 of the group max
+        // of (logit - lse): one exp2 per window slot
+        float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           typename M::op_t a[M::NKS];
@@ -1216,9 +1218,10 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
           const float4 l4 = *reinterpret_cast<const float4*>(Lt + rt * 16 + 4 * q);
           const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            pm[v] = fmaxf(pm[v], __builtin_amdgcn_exp2f(fmaf(acc[v], sc2, -lv[v])));
+          for (int v = 0; v < 4; ++v) pm[v] = fmaxf(pm[v], fmaf(acc[v], sc2, -lv[v]));
         }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) pm[v] = __builtin_amdgcn_exp2f(pm[v]);
         const int col = wv * 16 + cl;
         if (last) {  // causal mask: window slot u = 4q + v sees keys up to BT - 16 + u
 #pragma unroll
@@ -1292,8 +1295,9 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
         ss += dpp_f<DPP_QUAD_XOR1>(ss);
         ss += dpp_f<DPP_QUAD_XOR2>(ss);
         if (part == 0) {
-          inv_s[row] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-          nrm_s[row] = sqrtf(ss);
+          const float nr = sqrtf(ss);
+          inv_s[row] = ss > 0.f ? __builtin_amdgcn_rcpf(nr) : 0.f;  // v_rcp_f32, 1 ulp
+          nrm_s[row] = nr;
         }
       }
     }
