@@ -681,9 +681,9 @@ __global__ __launch_bounds__(256, 2) void score_block_kernel(ScoreParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Flash redundancy (Zipage Alg. 3): one workgroup per column block m. Every
-// row block i is staged in turn and its cosines against the columns of m are
-// formed; each column keeps its highest row above p over the whole sequence
+// Flash redundancy (Zipage Alg. 3), shapes other than the serving one: one
+// workgroup per column block m. Every row block i is staged in turn and its
+// cosines against the columns of m are formed; each column keeps its highest row above p over the whole sequence
 // (the entry Alg. 3 zeroes when it scans the row blocks from the last one
 // with a zero-out tag per column). Row i's sum over the whole sequence is
 // khat_i . (sum of all unit keys) minus its diagonal; the zeroed entries are
@@ -1496,6 +1496,263 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
   }
 }
 
+// ---------------------------------------------------------------------------
+// Flash redundancy, persistent form for the serving shape (bf16, head_dim
+// 128, blocks of 256): one workgroup of 16 wavefronts per CU walks a
+// contiguous range of (layer, kv-head, request, column block m) items. The
+// column block's MFMA operands are read once per item into registers (wave
+// w: column tiles 2(w % 8), +1); the request's row blocks i = 0 .. N - 1
+// stream through two LDS buffers (keys and their inverse norms, copied
+// HBM -> LDS with global_load_lds while the previous row block is used;
+// the copy of the next item's first row block overlaps the current item's
+// last). Per row block the wavefront forms the cosine tiles of its 8 row
+// tiles (half w / 8 of the block) against its 2 column tiles, exactly as
+// the lightning kernel does, and keeps per column, over the whole sequence:
+// the sum of k_i . k_j / |k_i| and the highest row whose cosine is above p
+// (rows run in ascending order, so the last hit is the highest). The
+// diagonal (block m against itself) is left out. At the end of the item,
+// per column j: the row sum of cosines of key j (the matrix is symmetric),
+// and its zeroed entry added to that entry's row in 64-bit fixed point
+// (global atomics: other items hold other columns of the same rows; exact,
+// so the same bits in any order). The score finalize subtracts them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(ScoreParams P,
+                                                                           int layer_count) {
+  constexpr int D = 128, BT = 256;
+  using L = LdsTile<bf16_t, D>;
+  using M = Mma<bf16_t, D>;
+  __shared__ __align__(16) char Ka[BT * L::ROWB];
+  __shared__ __align__(16) char Kb[BT * L::ROWB];
+  __shared__ __align__(16) float Ia[BT];
+  __shared__ __align__(16) float Ib[BT];
+  __shared__ __align__(16) float csum[2][BT];  // per half of the rows: the column's sum,
+  __shared__ __align__(16) int crow[2][BT];    //   the highest row above p (-1: none)
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  int S = 0;
+  for (int r = 0; r < P.nreq; ++r) S += lt_blocks(P, r);
+  const int64_t V = (int64_t)layer_count * P.h_kv * S;
+  const int64_t v0 = V * blockIdx.x / gridDim.x, v1 = V * (blockIdx.x + 1) / gridDim.x;
+  if (v0 >= v1) return;
+  LtItem cur;
+  {
+    cur.li = (int)(v0 / ((int64_t)P.h_kv * S));
+    const int64_t rem = v0 % ((int64_t)P.h_kv * S);
+    cur.h = (int)(rem / S);
+    int s2 = (int)(rem % S);
+    cur.r = 0;
+    cur.valid = true;
+    for (;;) {
+      const int N = lt_blocks(P, cur.r);
+      if (s2 < N) break;
+      s2 -= N;
+      ++cur.r;
+    }
+    cur.pidx = s2;
+    cur.N = lt_blocks(P, cur.r);
+    lt_fill(P, cur);
+  }
+  int left = (int)(v1 - v0);
+
+  // Copies row block i of item `it` (its keys, swizzled; its inverse norms)
+  // into (Kd, Id): every wavefront 4 KiB of keys, wavefront 0 the norms.
+  auto issue = [&](const LtItem& it, int i, char* Kd, float* Id) __attribute__((always_inline)) {
+    int ln = threadIdx.x & 63;
+    asm volatile("" : "+v"(ln));
+    const int page = lt_ld(P.tables, (int64_t)it.r * P.table_stride + i);
+    if (page < 0 || page >= P.num_blocks_total) return;  // flagged by phase A
+    const int layer = P.layer_begin + it.li;
+    const char* kp = reinterpret_cast<const char*>(
+        reinterpret_cast<const bf16_t*>(P.kc) + layer * P.kv_layer_elems +
+        ((int64_t)page * P.h_kv + it.h) * BT * D);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int pch = (wv * 4 + c4) * 64 + ln;
+      const int rr = pch >> 4, c = (pch & 15) ^ (rr & 15);
+      __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(kp + rr * L::ROWB + c * 16),
+                                       (lt_lds_ptr)(Kd + (wv * 4 + c4) * 1024), 16, 0, 0);
+    }
+    if (wv == 0) {
+      const int64_t zh = (int64_t)(it.li * P.nreq + it.r) * P.h_kv + it.h;
+      const float* ip = P.inv + zh * ((int64_t)P.max_blocks * BT) + (int64_t)i * BT;
+      __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(ip + ln * 4), (lt_lds_ptr)Id, 16, 0, 0);
+    }
+  };
+  auto item_ok = [&](const LtItem& it) -> bool {
+    return it.page >= 0 && it.page < P.num_blocks_total && it.slot >= 0 && it.slot < P.max_slots;
+  };
+
+  issue(cur, 0, Ka, Ia);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int buf = 0;  // the buffer that holds the current row block
+  for (;;) {
+    LtItem nx = cur;
+    if (left > 1) lt_advance(P, nx, layer_count); else nx.valid = false;
+    int tid2 = threadIdx.x;
+    asm volatile("" : "+v"(tid2));
+    const int ln = tid2 & 63, q = ln >> 4, cl = ln & 15;
+    const bool ok = item_ok(cur);
+    const int z = cur.li * P.nreq + cur.r;
+    const int64_t zh = (int64_t)z * P.h_kv + cur.h;
+    const int m = cur.pidx, N = cur.N, n = N * BT;
+    const int layer = P.layer_begin + cur.li;
+    const bf16_t* kbase = reinterpret_cast<const bf16_t*>(P.kc) + layer * P.kv_layer_elems;
+    const float* invz = P.inv + zh * ((int64_t)P.max_blocks * BT);
+    const float* nrmz = P.nrm + zh * ((int64_t)P.max_blocks * BT);
+    const int cg = wv & 7, rh = wv >> 3;
+    const int kd = 2 * cg - 8 * rh;  // local row tile of the diagonal tile of c = 0 (block m)
+    const bool has_diag = (cg >> 2) == rh;
+    // the column block's operands and thresholds, from global memory
+    typename M::op_t bop[2][M::NKS];
+    float pnc[2], cs[2] = {0.f, 0.f};
+    int bk[2] = {-1, -1};  // 32 * row block + 4 * local row tile + v of the highest entry above p
+    if (ok) {
+      const bf16_t* kpm = kbase + ((int64_t)cur.page * P.h_kv + cur.h) * BT * D;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int col = (2 * cg + c) * 16 + cl;
+#pragma unroll
+        for (int ks = 0; ks < M::NKS; ++ks) bop[c][ks] = M::glb(kpm + (int64_t)col * D, ks, ln);
+        pnc[c] = P.p * nrmz[(int64_t)m * BT + col];
+      }
+    }
+    bool dg[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dg[v] = 4 * q + v == cl;
+    // Row block i from (Kt, It) while the next one is copied into (Kn, In).
+    // Called with the two buffers in either order as distinct LDS arrays, so
+    // the compiler sees that the copies in flight never alias the reads.
+    auto row_block = [&](int i, const char* Kt, const float* It, char* Kn, float* In)
+                         __attribute__((always_inline)) {
+      if (i + 1 < N) issue(cur, i + 1, Kn, In);
+      else if (nx.valid) issue(nx, 0, Kn, In);
+      if (ok) {
+        const char* Kh = Kt + rh * 128 * L::ROWB;
+        const float* ivh = It + rh * 128;
+        const bool dblk = i == m;
+        auto load_a = [&](int k, typename M::op_t* a) __attribute__((always_inline)) {
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Kh, k * 16 + cl, ks, ln);
+        };
+        auto products = [&](const typename M::op_t* a, floatx4* acc) __attribute__((always_inline)) {
+          acc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+          acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) acc[c] = M::mma(a[ks], bop[c][ks], acc[c]);
+        };
+        typename M::op_t aA[M::NKS], aB[M::NKS];
+        floatx4 accA[2], accB[2];
+        float4 ivA, ivB;
+        load_a(0, aA);
+        load_a(1, aB);
+        ivA = *reinterpret_cast<const float4*>(ivh + 4 * q);
+        products(aA, accA);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          floatx4* curc = (k & 1) ? accB : accA;
+          floatx4* nxt = (k & 1) ? accA : accB;
+          typename M::op_t* an = (k & 1) ? aA : aB;
+          typename M::op_t* af = (k & 1) ? aB : aA;
+          const float4 iv = (k & 1) ? ivB : ivA;
+          if (k < 6) load_a(k + 2, af);
+          if (k < 7) {
+            float4& ivn = (k & 1) ? ivA : ivB;
+            ivn = *reinterpret_cast<const float4*>(ivh + (k + 1) * 16 + 4 * q);
+            products(an, nxt);
+          }
+          const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
+          float x[2][4];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[c][v] = curc[c][v] * ivv[v];
+            cs[c] += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
+          }
+          const bool any = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])) > pnc[0] ||
+                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])) > pnc[1];
+          if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const bool isd = dblk && has_diag && k == kd + c;  // wave-uniform
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const bool hit = x[c][v] > pnc[c] && !(isd && dg[v]);
+                bk[c] = hit ? 32 * i + 4 * k + v : bk[c];
+              }
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) asm volatile("" : "+v"(bk[c]), "+v"(cs[c]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int i = 0; i < N; ++i) {
+      if (buf == 0) row_block(i, Ka, Ia, Kb, Ib);
+      else row_block(i, Kb, Ib, Ka, Ia);
+      buf ^= 1;
+    }
+    // per column: over the four row groups, then the two halves of the rows
+    if (ok) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int kk = bk[c];
+        const int row = kk < 0 ? -1 : (kk >> 5) * BT + (8 * rh + ((kk >> 2) & 7)) * 16 + 4 * q + (kk & 3);
+        const int top = xor32_max_i(xor16_max_i(row));
+        const int col = (2 * cg + c) * 16 + cl;
+        float sum = xor32_sum(xor16_sum(cs[c]));
+        // the diagonal entry k_j . k_j / |k_j| = |k_j| out of the sum
+        if (has_diag) sum -= nrmz[(int64_t)m * BT + col];
+        if (q == 0) {
+          crow[rh][col] = top;
+          csum[rh][col] = sum;
+        }
+      }
+    }
+    __syncthreads();
+    if (ok) {  // per column j, four threads of 32 dimensions each
+      const int j = tid2 >> 2, part = tid2 & 3;
+      const int is = max(crow[0][j], crow[1][j]);
+      float d = 0.f;
+      if (is >= 0) {
+        const int pg = lt_ld(P.tables, (int64_t)cur.r * P.table_stride + is / BT);
+        const bf16_t* ki = kbase + ((int64_t)pg * P.h_kv + cur.h) * BT * D + (int64_t)(is % BT) * D;
+        const bf16_t* kj = kbase + ((int64_t)cur.page * P.h_kv + cur.h) * BT * D + (int64_t)j * D;
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int c = part * 4; c < part * 4 + 4; ++c) {
+          const uint4 u = ld16(ki + c * 8), w = ld16(kj + c * 8);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), __builtin_bit_cast(bf2, w.x), d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), __builtin_bit_cast(bf2, w.y), d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), __builtin_bit_cast(bf2, w.z), d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), __builtin_bit_cast(bf2, w.w), d, false);
+        }
+      }
+      d += dpp_f<DPP_QUAD_XOR1>(d);
+      d += dpp_f<DPP_QUAD_XOR2>(d);
+      if (part == 0) {
+        const float ivj = invz[(int64_t)m * BT + j];
+        P.rbuf[zh * ((int64_t)P.max_blocks * BT) + (int64_t)m * BT + j] = (csum[0][j] + csum[1][j]) * ivj;
+        if (is >= 0) {
+          unsigned long long* rs = P.rsub + zh * ((int64_t)P.max_blocks * BT);
+          atomicAdd(rs + is, to_fix(d * invz[is] * ivj));
+        }
+      }
+    }
+    __syncthreads();  // csum / crow reused by the next item
+    (void)n;
+    if (!nx.valid) break;
+    cur = nx;
+    --left;
+  }
+}
+
 constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
 
 // Compute units of the current device (queried once per device).
@@ -1551,7 +1808,19 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
     }
   }
   if (!persistent) hipLaunchKernelGGL(kA, gridP, dim3(256), smemA, s, P);
-  if (flash) hipLaunchKernelGGL(kF, gridP, dim3(256), smemF, s, P);
+  if (flash) {
+    bool flash_persistent = false;
+    if constexpr (sizeof(T) == 2 && D == 128) {
+      if (P.b == 256) {
+        const int64_t work = int64_t(items) * P.h_kv * P.max_blocks;
+        const int grid = int(std::min<int64_t>(work, device_cus()));
+        hipLaunchKernelGGL(score_flash_persist_kernel, dim3(grid), dim3(kLtThreads), 0, s, P,
+                           items / P.nreq);
+        flash_persistent = true;
+      }
+    }
+    if (!flash_persistent) hipLaunchKernelGGL(kF, gridP, dim3(256), smemF, s, P);
+  }
   hipLaunchKernelGGL(kB, gridP, dim3(256), smemB, s, P);
   hipLaunchKernelGGL(score_finalize_kernel, dim3(P.h_kv, items), dim3(kFinThreads), 0, s, P);
   return ZP_OK;

@@ -211,6 +211,7 @@ class DecodeEngine:
                                      self.side if async_compress else None, device)
         self.pending: list[_Pending] = []
         self.compressions = 0
+        self.compressions_lse = 0   # of which the window rows carried their log-sum-exp
         self.decoded_tokens = 0
         # optional per-layer timing of the decode kernel (start, end) events
         self.layer_events = None
@@ -390,6 +391,7 @@ class DecodeEngine:
             self.log.append((list(ok), np.array(first, np.uint8), scores, kept))
         self.pending.append(_Pending(ok, plans, done, bufs))
         self.compressions += nreq
+        self.compressions_lse += sum(1 for f in lse_ok if f)
         if not self.async_compress:
             self.poll(wait=True)
 

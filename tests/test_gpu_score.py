@@ -228,6 +228,15 @@ def test_score_flash_redundancy_planted_clusters_across_blocks(p):
          planted=True, heavy=False)
 
 
+@pytest.mark.parametrize("p", [0.0, 0.5])
+def test_score_flash_redundancy_planted_serving_shape(p):
+    """Planted clusters over blocks of 256 (d 128, g 4: the persistent flash
+    kernel), so each column's highest row above p can lie in any row block;
+    several column blocks per workgroup, ragged requests."""
+    sp = zp.ScoreParams(p=p, pool_first_only=False, redundancy="flash")
+    _run("bf16", 128, 32, 8, 256, 16, [5, 3, 7], lambda r: r != 1, sp, planted=True, heavy=False)
+
+
 @pytest.mark.parametrize("red", ["lightning", "flash"])
 def test_score_with_window_lse_qwen_shape(red):
     # requests 0 and 2 bring their window rows' log-sum-exp: one pass over K
