@@ -945,8 +945,8 @@ __global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams
 
 // ---------------------------------------------------------------------------
 // Phase A, persistent form for the serving shape (bf16, head_dim 128, blocks
-// of 256 tokens, a 16-token window, g <= 4 query heads per kv-head, lightning
-// redundancy or none): one workgroup of 16 wavefronts per CU walks a
+// of 256 tokens, a 16-token window, g <= 4 query heads per kv-head): one
+// workgroup of 16 wavefronts per CU walks a
 // contiguous range of the (layer, kv-head, request, block) items. The next
 // item's keys, global-score history and window log-sum-exp are copied
 // HBM -> LDS (global_load_lds, no registers) into the second of two buffers
@@ -969,6 +969,8 @@ __global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams
 //      the same bits in any order);
 //   4. each row's sum minus its zeroed entries, / n: the redundancy row
 //      sums.
+// With flash redundancy, steps 2-4 belong to score_flash_persist_kernel: the
+// item writes its key norms for it and clears its fixed-point words.
 // ---------------------------------------------------------------------------
 // Barrier over LDS traffic only: each wavefront's LDS operations are
 // complete (lgkmcnt 0), its HBM loads and copies into LDS are not waited for.
@@ -1097,6 +1099,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
 
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const bool redun = (P.flags & ZP_SCORE_REDUNDANCY) != 0;
+  const bool flash = redun && (P.flags & ZP_SCORE_REDUNDANCY_FLASH) != 0;
   const bool glob = (P.flags & ZP_SCORE_GLOBAL) != 0;
   const float sc2 = P.qk_scale;
 
@@ -1314,6 +1317,15 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
       float* st = P.stats + ((zh * P.max_blocks + it.pidx) * R + tid) * 2;
       st[0] = Mx;
       st[1] = Sm;
+    }
+    if (ok && flash) {  // flash: the norms for its own kernel, its fixed-point words cleared
+      if (tid < BT) {
+        const int64_t o = zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT + tid;
+        P.inv[o] = inv_s[tid];
+        P.nrm[o] = nrm_s[tid];
+        P.rsub[o] = 0ull;
+      }
+      return;
     }
     if (!ok || !redun) return;
     // 2. cosine tiles: wave w takes column tiles 2(w % 8), +1 against row
@@ -1798,8 +1810,9 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
   bool persistent = false;
   if constexpr (sizeof(T) == 2 && D == 128 && R <= 64) {
     // the serving shape: bf16 keys of head_dim 128 in blocks of 256, a
-    // 16-token window, g <= 4, lightning redundancy or none
-    if (P.b == 256 && P.w == 16 && !flash) {
+    // 16-token window, g <= 4 (with flash redundancy: the window scores and
+    // the key norms only)
+    if (P.b == 256 && P.w == 16) {
       const int64_t work = int64_t(items) * P.h_kv * P.max_blocks;
       const int grid = int(std::min<int64_t>(work, device_cus()));
       hipLaunchKernelGGL(score_lightning_kernel<R / 16>, dim3(grid), dim3(kLtThreads), 0, s, P,
