@@ -775,7 +775,7 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the hot path has no "
-              "inter-GPU exchange and this build runs no multi-GPU configuration.",
+              "inter-GPU exchange and the library runs on one GPU.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

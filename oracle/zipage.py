@@ -8,8 +8,7 @@ Source of every definition: "Zipage: Maintain High Request Concurrency for LLM
 Reasoning through Compressed PagedAttention" (Liao et al., arXiv 2603.08743),
 cited below as "Zipage" with the section, algorithm, equation or figure.
 
-Readings taken where the paper is silent or garbled (each is also listed in
-DESIGN.md):
+Readings taken where the paper is silent or garbled:
   * causal mask of the window logits: a window query never sees a key that
     comes after it (the printed inequality of Alg. 1 is inverted);
   * GQA grouping is contiguous: query head j belongs to kv-head j // g;
