@@ -1041,10 +1041,18 @@ __device__ __forceinline__ int lt_blocks(const ScoreParams& P, int r) {
 }
 
 __device__ __forceinline__ void lt_fill(const ScoreParams& P, LtItem& it) {
-  it.page = lt_ld(P.tables, (int64_t)it.r * P.table_stride + it.pidx);
-  it.slot = lt_ld(P.qslot, it.r);
-  it.first = lt_ld_u8(P.first, it.r) != 0;
-  it.lse = P.lse_ok && P.qwin_lse && lt_ld_u8(P.lse_ok, it.r) != 0;
+  // four independent loads, no branch between them (one wait): without a
+  // window-LSE flag array the first-flag word is read in its place and
+  // ignored
+  const uint8_t* lp = P.lse_ok ? P.lse_ok : P.first;
+  const int32_t page = lt_ld(P.tables, (int64_t)it.r * P.table_stride + it.pidx);
+  const int32_t slot = lt_ld(P.qslot, it.r);
+  const uint32_t f = lt_ld_u8(P.first, it.r);
+  const uint32_t l = lt_ld_u8(lp, it.r);
+  it.page = page;
+  it.slot = slot;
+  it.first = f != 0;
+  it.lse = P.lse_ok != nullptr && P.qwin_lse != nullptr && l != 0;
 }
 
 __device__ __forceinline__ void lt_next_request(const ScoreParams& P, LtItem& it, int layer_count) {
@@ -1072,8 +1080,10 @@ __device__ __forceinline__ void lt_advance(const ScoreParams& P, LtItem& it, int
     it.pidx = 0;
     ++it.r;
     lt_next_request(P, it, layer_count);
+    if (it.valid) lt_fill(P, it);
+  } else {  // same request: only the block id changes
+    it.page = lt_ld(P.tables, (int64_t)it.r * P.table_stride + it.pidx);
   }
-  if (it.valid) lt_fill(P, it);
 }
 
 template <int RT>
@@ -1151,13 +1161,16 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     const char* kp = reinterpret_cast<const char*>(
         reinterpret_cast<const bf16_t*>(P.kc) + layer * P.kv_layer_elems +
         ((int64_t)it.page * P.h_kv + it.h) * BT * D);
+    // Byte offsets, inside the block, of the four 16-byte chunks this lane
+    // copies: LDS chunk p = (4 wv + i) 64 + lane of the swizzled tile holds
+    // row p / 16 = 16 wv + 4 i + lane / 16 and chunk (p % 16) ^ (row % 16)
+    // = (lane % 16) ^ (lane / 16) ^ 4 i, so chunk i sits at
+    // kb + 1024 i + (kc ^ 64 i).
+    const int kb = (16 * wv + (lane >> 4)) * L::ROWB, kc = ((lane & 15) ^ (lane >> 4)) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = (wv * 4 + i) * 64 + lane;      // LDS chunk position
-      const int rr = p >> 4, c = (p & 15) ^ (rr & 15);
-      __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(kp + rr * L::ROWB + c * 16),
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(kp + kb + 1024 * i + (kc ^ (64 * i))),
                                        (lt_lds_ptr)(Kd + (wv * 4 + i) * 1024), 16, 0, 0);
-    }
     if (glob && !it.first && wv == 0) {  // 1 KiB, 16 bytes per lane
       const float* fp = P.gscore + layer * P.f_layer_elems + ((int64_t)it.page * P.h_kv + it.h) * BT;
       __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(fp + lane * 4), (lt_lds_ptr)Fd, 16, 0, 0);
