@@ -152,6 +152,10 @@ constexpr int kPKT = 64;                 // keys per tile
 constexpr float kPLazy = 8.0f;           // lazy rescale threshold (log2 units)
 constexpr int kPRows = 128;              // query rows (token, head) per workgroup
 constexpr int kPfTabLds = 2048;          // block ids staged in LDS (tables up to this wide)
+#ifndef ZP_PF_DMA_KT
+#define ZP_PF_DMA_KT 32
+#endif
+constexpr int kPfDmaKT = ZP_PF_DMA_KT;   // keys per tile of the LDS-copy kernel
 constexpr int kVtStride = kPKT + 4;      // bf16 per row of the transposed V tile
 // Key slot of key `key` in row d of the transposed V tile: XOR with a
 // multiple of 4 keyed by d / 8, so the dword writes of lanes that hold
@@ -422,50 +426,76 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 
 // ---------------------------------------------------------------------------
 // 2a'. bf16 attention with K/V tiles copied straight into LDS (blocks of at
-// least 64 tokens, block table staged in LDS).
+// least KT tokens, block table staged in LDS).
 //
 // The loads of a tile go from HBM to LDS without registers
-// (global_load_lds): K as 16-byte chunks, XOR-swizzled like the register
-// path; V one 4-byte word per lane, one key row per instruction, into rows
-// padded to 2D + 32 bytes. The Vᵀ operand of the PV product is then read
+// (global_load_lds, 16 bytes per lane): K in 16-byte chunks XOR-swizzled
+// like the register path; V with each row's 32-byte segments permuted by
+// the row index (vseg), the lanes of one copy fetching whichever chunk its
+// destination slot holds. The V^T operand of the PV product is then read
 // with the transposing LDS load (ds_read_b64_tr_b16): within each group of
 // 16 lanes, lane l receives element l % 4 of the 8-byte pieces addressed by
 // lanes l / 4, l / 4 + 4, l / 4 + 8, l / 4 + 12. Lane (cl, q) addresses row
 // 4q + cl / 4 (plus the tile's key offset), columns d = 16dt + 4(cl % 4) ..
-// +3, and so receives V[4 consecutive keys][16dt + cl]: the A operand of Oᵀ
-// += Vᵀ·Pᵀ in the key order of the P registers. With the 32-byte pad the 16
-// rows one read touches fall in 8 distinct bank windows.
+// +3, and so receives V[4 consecutive keys][16dt + cl]: the A operand of O^T
+// += V^T P^T in the key order of the P registers. The 16 rows one read
+// touches fall evenly on the four 128-byte bank windows.
 //
 // Two LDS buffers alternate: tile t + 1 is in flight while tile t is used,
 // and one barrier per tile both retires the copies (the barrier waits for
 // them) and frees the buffer the next copy overwrites.
+//
+// Key tiles of 32 (KT): a workgroup then needs 40 KB of LDS and 168 VGPRs
+// per lane, so three workgroups share a CU (three wavefronts per SIMD). On
+// this kernel MFMA and VALU time add up on a SIMD, and the third wavefront
+// hides more of the LDS and copy latency than the extra per-tile work of the
+// shorter tile costs (64-key tiles fit two workgroups per CU).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* gbl_void_ptr;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 
-template <int D>
+template <int D, int KT>
 struct PfDma {
   static constexpr int CH = D * 2 / 16;          // 16-byte chunks per key row
-  static constexpr int KB = kPKT * D * 2;        // bytes of a K tile
-  static constexpr int KI = KB / 1024 / 4;       // 1 KiB K copies per wavefront per tile
-  static constexpr int VS = D * 2 + 32;          // bytes per padded V row
-  static constexpr int VB = kPKT * VS;           // bytes of a V tile
-  static constexpr int VL = D / 2;               // lanes that copy a V row (4 bytes each)
+  static constexpr int KB = KT * D * 2;          // bytes of a K (or V) tile
+  static constexpr int KI = KB / 1024 / 4;       // 1 KiB copies per wavefront per tile
+  static constexpr int VS = D * 2;               // bytes per V row
+  static constexpr int NSEG = D * 2 / 32;        // 32-byte segments per V row
   __device__ static int chunk_pos(int r, int c) { return r * CH + (c ^ (r % CH)); }
+  // 32-byte segment s of V row r sits at segment s ^ (r mod NSEG): the 16
+  // rows one transposing read touches then spread evenly over the banks.
+  __device__ static int vseg(int r, int s) { return s ^ (r & (NSEG - 1)); }
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams P) {
-  using L = PfDma<D>;
+// IEEE maximum (gfx950 v_maximum3_f32): unlike fmaxf it needs no quieting
+// of its inputs, so a max over raw MFMA results costs one instruction per
+// two values. Masked keys are -inf by selection, never NaN, so the rows it
+// sees hold no NaN unless the inputs do.
+__device__ __forceinline__ float max_nq(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float row16_max_nq(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_nq(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row32_max_nq(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_nq(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int D, int G, int KT>
+__global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel(PrefillParams P) {
+  static_assert(KT == 32 || KT == 64, "key tile of 32 or 64");
+  using L = PfDma<D, KT>;
   constexpr int QT = kPRows / G;   // query tokens per workgroup
   constexpr int NDT = D / 16;      // output column tiles (head dims)
   constexpr int NKS = D / 32;      // k-steps of the logits
+  constexpr int NCT = KT / 16;     // 16-key column tiles of the logits
+  constexpr int NST = KT / 32;     // k-steps of the PV product
   __shared__ __align__(16) char Ks0[L::KB];
   __shared__ __align__(16) char Ks1[L::KB];
-  __shared__ __align__(16) char Vs0[L::VB];
-  __shared__ __align__(16) char Vs1[L::VB];
+  __shared__ __align__(16) char Vs0[L::KB];
+  __shared__ __align__(16) char Vs1[L::KB];
   __shared__ int32_t s_tab[kPfTabLds];
 
   const int r = blockIdx.z, h = blockIdx.y;
@@ -480,7 +510,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams 
   const int q = lane >> 4, cl = lane & 15;
   const int q_last = min(qlen, q0 + QT) - 1;
   const int n_keys = ctx + q_last + 1;             // keys any row of the tile may see
-  const int ntiles = (n_keys + kPKT - 1) / kPKT;
+  const int ntiles = (n_keys + KT - 1) / KT;
   const int32_t* tab = P.tables + (int64_t)r * P.table_stride;
   const bf16_t* kcache = reinterpret_cast<const bf16_t*>(P.kc) + P.kv_layer_off;
   const bf16_t* vcache = reinterpret_cast<const bf16_t*>(P.vc) + P.kv_layer_off;
@@ -511,55 +541,55 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams 
   __syncthreads();
 
   bool bad = false;  // a needed tile sits on an out-of-range block id
-  // Byte offset, inside a tile of K rows, of the 16-byte chunk this lane
-  // copies in each of its KI copies (LDS chunk p holds row p / CH, chunk
-  // (p % CH) ^ (row % CH)).
-  int koff[L::KI];
+  // Byte offsets, inside a tile of K (V) rows, of the 16-byte chunk this
+  // lane copies in each of its KI copies: LDS chunk p holds row p / CH and,
+  // for K, chunk (p % CH) ^ (row % CH); for V, the chunk whose 32-byte
+  // segment vseg places there.
+  int koff[L::KI], voff[L::KI], vrow[L::KI];
 #pragma unroll
   for (int i = 0; i < L::KI; ++i) {
     const int pidx = (wv * L::KI + i) * 64 + lane;
     const int kr = pidx / L::CH, pc = pidx % L::CH;
     koff[i] = (kr * D + (pc ^ (kr % L::CH)) * 8) * 2;
+    voff[i] = kr * D * 2 + L::vseg(kr, pc >> 1) * 32 + (pc & 1) * 16;
+    vrow[i] = kr;
   }
-  // Copy tile t into (Kb, Vb): K rows whole, V rows of existing keys; a bad
-  // block or keys past n_keys are written as zeros instead. Wavefront wv
-  // copies V rows 16wv .. 16wv + 15.
+  // Copy tile t into (Kb, Vb), 16 bytes per lane and copy: K rows whole, V
+  // rows of existing keys; a bad block or keys past n_keys are written as
+  // zeros instead (their weights are 0, and 0 x garbage must not reach O).
   auto issue = [&](int t, char* Kb, char* Vb) __attribute__((always_inline)) {
-    const int page = s_tab[(t * kPKT) >> P.log2b];
+    const int page = s_tab[(t * KT) >> P.log2b];
     const bool ok = page >= 0 && page < P.num_blocks;
     bad |= !ok;
-    const int row0 = ((page * P.h_kv + h) * P.b) + ((t * kPKT) & (P.b - 1));
-    const int vrow0 = wv * (kPKT / 4);
+    const int row0 = ((page * P.h_kv + h) * P.b) + ((t * KT) & (P.b - 1));
     if (ok) {
       const char* kt = reinterpret_cast<const char*>(kcache + (int64_t)row0 * D);
+      const char* vt = reinterpret_cast<const char*>(vcache + (int64_t)row0 * D);
 #pragma unroll
       for (int i = 0; i < L::KI; ++i)
         __builtin_amdgcn_global_load_lds((gbl_void_ptr)(kt + koff[i]),
                                          (lds_void_ptr)(Kb + (wv * L::KI + i) * 1024), 16, 0, 0);
-      const char* vt = reinterpret_cast<const char*>(vcache + (int64_t)(row0 + vrow0) * D) + 4 * lane;
-      if (t * kPKT + vrow0 + kPKT / 4 <= n_keys) {  // all 16 rows exist
+      if (t * KT + KT <= n_keys) {  // every row of the tile exists
 #pragma unroll
-        for (int i = 0; i < kPKT / 4; ++i)
-          if (lane < L::VL)
-            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(vt + i * D * 2),
-                                             (lds_void_ptr)(Vb + (vrow0 + i) * L::VS), 4, 0, 0);
+        for (int i = 0; i < L::KI; ++i)
+          __builtin_amdgcn_global_load_lds((gbl_void_ptr)(vt + voff[i]),
+                                           (lds_void_ptr)(Vb + (wv * L::KI + i) * 1024), 16, 0, 0);
       } else {
-        for (int i = 0; i < kPKT / 4; ++i) {
-          if (lane < L::VL) {
-            if (t * kPKT + vrow0 + i < n_keys)
-              __builtin_amdgcn_global_load_lds((gbl_void_ptr)(vt + i * D * 2),
-                                               (lds_void_ptr)(Vb + (vrow0 + i) * L::VS), 4, 0, 0);
-            else
-              *reinterpret_cast<uint32_t*>(Vb + (vrow0 + i) * L::VS + 4 * lane) = 0u;
-          }
+#pragma unroll
+        for (int i = 0; i < L::KI; ++i) {
+          if (t * KT + vrow[i] < n_keys)
+            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(vt + voff[i]),
+                                             (lds_void_ptr)(Vb + (wv * L::KI + i) * 1024), 16, 0, 0);
+          else
+            *reinterpret_cast<uint4*>(Vb + ((wv * L::KI + i) * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
         }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < L::KI; ++i)
+      for (int i = 0; i < L::KI; ++i) {
         *reinterpret_cast<uint4*>(Kb + ((wv * L::KI + i) * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
-      for (int i = 0; i < kPKT / 4; ++i)
-        if (lane < L::VL) *reinterpret_cast<uint32_t*>(Vb + (vrow0 + i) * L::VS + 4 * lane) = 0u;
+        *reinterpret_cast<uint4*>(Vb + ((wv * L::KI + i) * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
 
@@ -572,21 +602,22 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams 
   int qpos[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) qpos[k] = ctx + q0 + ti0_of[k] + cl;  // this lane's query position
-  const int vbase = (4 * q + (cl >> 2)) * L::VS + 8 * (cl & 3);       // Vᵀ read, key row 4q + cl/4
+  const int vrr = 4 * q + (cl >> 2);                                  // Vᵀ read, key row 4q + cl/4
+  const int vbase = vrr * L::VS + 8 * (cl & 3);
 
   auto tile = [&](int t, const char* Kb, const char* Vb, char* Kn, char* Vn) __attribute__((always_inline)) {
     if (t + 1 < ntiles) issue(t + 1, Kn, Vn);  // in flight while this tile is used
-    const bool diag = t * kPKT + kPKT - 1 > ctx + q0;  // some key may follow some query
-    bf16x8_t pop[2][2];
-    floatx4 sk[2][4];
+    const bool diag = t * KT + KT - 1 > ctx + q0;  // some key may follow some query
+    bf16x8_t pop[2][NST];
+    floatx4 sk[2][NCT];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) sk[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < NCT; ++ct) sk[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         const bf16x8_t kop = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const uint4*>(Kb + L::chunk_pos(ct * 16 + cl, ks * 4 + q) * 16));
         sk[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[0][ks], sk[0][ct], 0, 0, 0);
@@ -599,21 +630,21 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams 
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      floatx4 (&s)[4] = sk[k];
-      if (diag) {  // one branch, taken on the last tile or two only
-        const int lim = qpos[k] - t * kPKT - 4 * q;  // last visible key offset
+      floatx4 (&s)[NCT] = sk[k];
+      if (diag) {  // one branch, taken on the last tile or few only
+        const int lim = qpos[k] - t * KT - 4 * q;  // last visible key offset
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             if (ct * 16 + v > lim) s[ct][v] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[ct][v]);
-      mx = xor32_max(xor16_max(mx));
+        for (int v = 0; v < 4; v += 2) mx = max_nq(mx, max_nq(s[ct][v], s[ct][v + 1]));
+      mx = row32_max_nq(row16_max_nq(mx));
       mx *= P.qk_scale;
       if (__builtin_amdgcn_read_exec() & __ballot(mx > m[k] + kPLazy)) {  // any lane: rescale
         const float mn = fmaxf(m[k], mx);
@@ -624,9 +655,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams 
         for (int dt = 0; dt < NDT; ++dt) o[k][dt] *= alpha;
       }
       float ps = 0.f;
-      float p[4][4];
+      float p[NCT][4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
@@ -635,7 +666,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams 
       l[k] += ps;
       // P operands: k-step st holds keys {32st + 4q + v} and {32st + 16 + 4q + v}
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < NST; ++st) {
         typedef float f2 __attribute__((ext_vector_type(2)));
         typedef __bf16 b2 __attribute__((ext_vector_type(2)));
         b2 x0 = __builtin_convertvector(f2{p[2 * st][0], p[2 * st][1]}, b2);
@@ -653,8 +684,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_dma_kernel(PrefillParams 
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const char* va = Vb + vbase + 32 * st * L::VS + 32 * dt;
+      for (int st = 0; st < NST; ++st) {
+        const char* va = Vb + vbase + 32 * st * L::VS + 32 * L::vseg(vrr, dt);  // rows + 32st keep vseg
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(va));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(va + 16 * L::VS));
         typedef short v8i16_t __attribute__((ext_vector_type(8)));
@@ -785,8 +816,8 @@ static void launch_prefill(const PrefillParams& P, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     constexpr int QT = kPRows / G;
     dim3 g((P.max_q_len + QT - 1) / QT, P.h_kv, P.nreq);
-    if (P.b >= kPKT && P.table_stride <= kPfTabLds)
-      hipLaunchKernelGGL((prefill_attn_dma_kernel<D, G>), g, dim3(256), 0, s, P);
+    if (P.b >= kPfDmaKT && P.table_stride <= kPfTabLds)
+      hipLaunchKernelGGL((prefill_attn_dma_kernel<D, G, kPfDmaKT>), g, dim3(256), 0, s, P);
     else
       hipLaunchKernelGGL((prefill_attn_kernel<D, G>), g, dim3(256), 0, s, P);
   } else {
