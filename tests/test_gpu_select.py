@@ -92,6 +92,12 @@ def test_select_fresh_targets_prefix_like():
          use_f_new=True)
 
 
+def test_select_mid_length_ragged_with_ties():
+    # 4352..8192 tokens per unit (up to 32 keys per thread in the selection)
+    _run("bf16", 128, 2, 256, 16, [17, 32, 20], 7 * 256, lambda r, i: r == 1 and i % 3 == 0,
+         levels=3, layer_count=1)
+
+
 def test_select_long_context_to_budget():
     _run("bf16", 128, 2, 256, 16, [64, 128, 20], 7 * 256, lambda r, i: r == 2 and i % 2 == 0,
          levels=3, layer_count=1)
