@@ -56,13 +56,14 @@ struct PrefillParams {
   float qk_scale;  // log2(e) / sqrt(d)
 };
 
-// Chunk geometry of request r; false (and an error bit) when it does not fit.
+// Chunk geometry of request r; false (and an error bit, set by the
+// workgroups with `lead`) when it does not fit.
 __device__ __forceinline__ bool chunk_of(const PrefillParams& P, int r, int* c0, int* qlen,
-                                         int* ctx) {
+                                         int* ctx, bool lead) {
   const int a = P.cu[r], e = P.cu[r + 1], cx = P.ctx[r];
   if (e < a || e - a > P.max_q_len || cx < 0 ||
       (int64_t)cx + (e - a) > (int64_t)P.table_stride * P.b) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
+    if (threadIdx.x == 0 && lead) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
     return false;
   }
   *c0 = a;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillParams P) {
   constexpr int RPP = 256 / LPR;  // rows per pass
   const int r = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * 64;
   int c0, qlen, ctx;
-  if (!chunk_of(P, r, &c0, &qlen, &ctx) || i0 >= qlen) return;
+  if (!chunk_of(P, r, &c0, &qlen, &ctx, blockIdx.x == 0) || i0 >= qlen) return;
   const int tid = threadIdx.x, sub = tid % LPR;
   const int32_t* tab = P.tables + (int64_t)r * P.table_stride;
   const int last = ctx + qlen - 1;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
 
   const int r = blockIdx.z, h = blockIdx.y;
   int c0, qlen, ctx;
-  if (!chunk_of(P, r, &c0, &qlen, &ctx)) return;
+  if (!chunk_of(P, r, &c0, &qlen, &ctx, blockIdx.x == 0)) return;
   const int ntq = (P.max_q_len + QT - 1) / QT;
   const int qt = ntq - 1 - blockIdx.x;            // heavy (late) tiles first
   const int q0 = qt * QT;
@@ -498,11 +499,24 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
   __shared__ __align__(16) char Vs1[L::KB];
   __shared__ int32_t s_tab[kPfTabLds];
 
-  const int r = blockIdx.z, h = blockIdx.y;
-  int c0, qlen, ctx;
-  if (!chunk_of(P, r, &c0, &qlen, &ctx)) return;
+  // Workgroups go to the 8 XCDs round-robin in id order. Renumber them so
+  // the query tiles of one (request, kv-head) run on one XCD, back to back:
+  // its K/V tiles, re-read by every query tile, then stay in that XCD's L2.
+  // Within a unit, heavy (late) tiles first.
   const int ntq = (P.max_q_len + QT - 1) / QT;
-  const int qt = ntq - 1 - blockIdx.x;            // heavy (late) tiles first
+  int r, h, qt;
+  {
+    const uint32_t W = gridDim.x * gridDim.y * gridDim.z;
+    const uint32_t w = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t x = w & 7, q8 = W >> 3, rem = W & 7;
+    const uint32_t L = x * q8 + min(x, rem) + (w >> 3);
+    const uint32_t unit = L / (uint32_t)ntq;
+    qt = ntq - 1 - (int)(L - unit * (uint32_t)ntq);
+    h = (int)(unit % (uint32_t)P.h_kv);
+    r = (int)(unit / (uint32_t)P.h_kv);
+  }
+  int c0, qlen, ctx;
+  if (!chunk_of(P, r, &c0, &qlen, &ctx, qt == ntq - 1)) return;
   const int q0 = qt * QT;
   if (q0 >= qlen) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -739,7 +753,7 @@ __global__ __launch_bounds__(256) void prefill_simple_kernel(PrefillParams P) {
   __shared__ float sm_o[4 * RPW][G][D];
   const int r = blockIdx.z, h = blockIdx.y, i = blockIdx.x;
   int c0, qlen, ctx;
-  if (!chunk_of(P, r, &c0, &qlen, &ctx) || i >= qlen) return;
+  if (!chunk_of(P, r, &c0, &qlen, &ctx, blockIdx.x == 0) || i >= qlen) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int grp = wv * RPW + lane / LPR, sub = lane % LPR;  // row group, lane in row
   const int pos = ctx + i;
