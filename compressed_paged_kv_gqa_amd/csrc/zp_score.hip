@@ -1075,6 +1075,23 @@ __device__ __forceinline__ void lt_next_request(const ScoreParams& P, LtItem& it
   }
 }
 
+// Moves the cursor k >= 1 items on (the next item is k = 1), then loads
+// the new item's block id, slot and flags once.
+__device__ __forceinline__ void lt_skip(const ScoreParams& P, LtItem& it, int k, int layer_count) {
+  for (;;) {
+    const int room = it.N - 1 - it.pidx;  // items after this one in the same request
+    if (k <= room) {
+      it.pidx += k;
+      break;
+    }
+    k -= room + 1;
+    it.pidx = 0;
+    ++it.r;
+    lt_next_request(P, it, layer_count);
+    if (!it.valid) return;
+  }
+  lt_fill(P, it);
+}
 __device__ __forceinline__ void lt_advance(const ScoreParams& P, LtItem& it, int layer_count) {
   if (++it.pidx >= it.N) {
     it.pidx = 0;
@@ -1556,9 +1573,19 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   int S = 0;
   for (int r = 0; r < P.nreq; ++r) S += lt_blocks(P, r);
+  // Items (layer, kv-head, request, column block) in order, a unit's column
+  // blocks adjacent. Workgroups reach the 8 XCDs round-robin; each XCD gets
+  // a contiguous share of the items, which its Gx workgroups take in stride,
+  // so at any time they work on the column blocks of one or two units and
+  // the row blocks every column block streams come from that XCD's L2.
   const int64_t V = (int64_t)layer_count * P.h_kv * S;
-  const int64_t v0 = V * blockIdx.x / gridDim.x, v1 = V * (blockIdx.x + 1) / gridDim.x;
-  if (v0 >= v1) return;
+  const int G = gridDim.x, xcd = blockIdx.x & 7, l8 = blockIdx.x >> 3;
+  const int g8 = G >> 3, gr = G & 7;
+  const int cw0 = xcd * g8 + min(xcd, gr), cw1 = (xcd + 1) * g8 + min(xcd + 1, gr);
+  const int Gx = cw1 - cw0;  // workgroups on this XCD, l8 < Gx
+  const int64_t xe = V * cw1 / G;
+  const int64_t v0 = V * cw0 / G + l8;
+  if (v0 >= xe) return;
   LtItem cur;
   {
     cur.li = (int)(v0 / ((int64_t)P.h_kv * S));
@@ -1577,7 +1604,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
     cur.N = lt_blocks(P, cur.r);
     lt_fill(P, cur);
   }
-  int left = (int)(v1 - v0);
+  int left = (int)((xe - v0 + Gx - 1) / Gx);
 
   // Copies row block i of item `it` (its keys, swizzled; its inverse norms)
   // into (Kd, Id): every wavefront 4 KiB of keys, wavefront 0 the norms.
@@ -1613,7 +1640,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
   int buf = 0;  // the buffer that holds the current row block
   for (;;) {
     LtItem nx = cur;
-    if (left > 1) lt_advance(P, nx, layer_count); else nx.valid = false;
+    if (left > 1) lt_skip(P, nx, Gx, layer_count); else nx.valid = false;
     int tid2 = threadIdx.x;
     asm volatile("" : "+v"(tid2));
     const int ln = tid2 & 63, q = ln >> 4, cl = ln & 15;
