@@ -350,6 +350,7 @@ def compress_kernel_bench(iters=20):
     sws = zp.new_workspace(zp.zp_score_workspace_size(geom, 1, R, NB))
     cws = zp.new_workspace(zp.zp_select_workspace_size(geom, 1, R, keep))
     stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())  # the inputs above are filled on that stream
     units = R * HKV
     out = {"workload": f"{R} requests x {n} tokens ({NB} full blocks) compressing at once, "
                        f"1 layer, bf16, first compression, keep {keep}",
@@ -424,6 +425,7 @@ def prefill_kernel_bench(iters=5):
     qslot = torch.arange(R, dtype=torch.int32, device="cuda")
     ws = zp.new_workspace(zp.zp_prefill_workspace_size(geom, R))
     stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())  # the inputs above are filled on that stream
     with torch.cuda.stream(stream):
         ms = _time_calls(lambda: zp.zp_paged_prefill(cache, 0, q, k, v, cu, ctx, T, tables, qslot,
                                                      out, lse, ws, stream=stream), iters, stream)
