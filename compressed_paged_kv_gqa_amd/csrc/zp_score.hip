@@ -990,6 +990,19 @@ __device__ __forceinline__ int xor16_max_i(int v) {
   const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return max((int)r[0], (int)r[1]);
 }
+// IEEE maximum (gfx950 v_maximum3_f32): fmaxf must first quiet inputs the
+// compiler cannot prove canonical (MFMA results, LDS loads, DPP moves), one
+// v_max_f32 each; this needs none. The values it sees carry no NaN unless
+// the inputs do (masked logits are -inf by selection).
+__device__ __forceinline__ float max_nq(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+template <int LANES>
+__device__ __forceinline__ float group_max_nq(float v) {
+  static_assert(LANES == 16, "16-lane rows");
+  v = max_nq(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = max_nq(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = max_nq(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  return max_nq(v, dpp_f<DPP_ROW_MIRROR>(v));
+}
 __device__ __forceinline__ int xor32_max_i(int v) {
   const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return max((int)r[0], (int)r[1]);
@@ -1251,7 +1264,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
           const float4 l4 = *reinterpret_cast<const float4*>(Lt + rt * 16 + 4 * q);
           const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) pm[v] = fmaxf(pm[v], fmaf(acc[v], sc2, -lv[v]));
+          for (int v = 0; v < 4; ++v) pm[v] = max_nq(pm[v], fmaf(acc[v], sc2, -lv[v]));
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) pm[v] = __builtin_amdgcn_exp2f(pm[v]);
@@ -1301,7 +1314,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
           }
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float Mx = group_max<16>(fmaxf(acc[0][v], acc[1][v]));
+            const float Mx = group_max_nq<16>(max_nq(acc[0][v], acc[1][v]));
             const float ms = Mx == -INFINITY ? 0.f : Mx * sc2;
             float sm = __builtin_amdgcn_exp2f(fmaf(acc[0][v], sc2, -ms)) +
                        __builtin_amdgcn_exp2f(fmaf(acc[1][v], sc2, -ms));
@@ -1339,7 +1352,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     if (ok && !it.lse && tid < R) {
       float Mx = -INFINITY;
 #pragma unroll
-      for (int w2 = 0; w2 < 8; ++w2) Mx = fmaxf(Mx, wstat[w2][tid][0]);
+      for (int w2 = 0; w2 < 8; ++w2) Mx = max_nq(Mx, wstat[w2][tid][0]);
       float Sm = 0.f;
       if (Mx != -INFINITY)
 #pragma unroll
@@ -1436,8 +1449,8 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
         // the highest row above p, tracked only in tiles that have one (the
         // test is made for the whole wavefront at once; a diagonal tile
         // always has one, its diagonal, which is never the entry to zero)
-        const bool any = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])) > pnc[0] ||
-                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])) > pnc[1];
+        const bool any = max_nq(max_nq(x[0][0], x[0][1]), max_nq(x[0][2], x[0][3])) > pnc[0] ||
+                         max_nq(max_nq(x[1][0], x[1][1]), max_nq(x[1][2], x[1][3])) > pnc[1];
         if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
