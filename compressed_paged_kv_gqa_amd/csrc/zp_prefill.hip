@@ -559,7 +559,9 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
   // lane copies in each of its KI copies: LDS chunk p holds row p / CH and,
   // for K, chunk (p % CH) ^ (row % CH); for V, the chunk whose 32-byte
   // segment vseg places there.
-  int koff[L::KI], voff[L::KI], vrow[L::KI];
+  // unsigned: the copies then take a scalar base plus a 32-bit lane offset
+  uint32_t koff[L::KI], voff[L::KI];
+  int vrow[L::KI];
 #pragma unroll
   for (int i = 0; i < L::KI; ++i) {
     const int pidx = (wv * L::KI + i) * 64 + lane;
@@ -668,15 +670,14 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[k][dt] *= alpha;
       }
-      float ps = 0.f;
       float p[NCT][4];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
-          ps += p[ct][v];
-        }
+        for (int v = 0; v < 4; ++v) p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
+      float ps = p[0][0];
+#pragma unroll
+      for (int e = 1; e < 4 * NCT; ++e) ps += p[e >> 2][e & 3];
       l[k] += ps;
       // P operands: k-step st holds keys {32st + 4q + v} and {32st + 16 + 4q + v}
 #pragma unroll
