@@ -1253,8 +1253,12 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
         // the group max of P = exp2(logit - lse) is exp2 of the group max
         // of (logit - lse): one exp2 per window slot
         float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        __builtin_amdgcn_s_setprio(3);  // stepped down per row tile, as in the cosine phase
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
+          if (rt == 1) __builtin_amdgcn_s_setprio(2);
+          if (rt == 2) __builtin_amdgcn_s_setprio(1);
+          if (rt == 3) __builtin_amdgcn_s_setprio(0);
           typename M::op_t a[M::NKS];
 #pragma unroll
           for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Qs, rt * 16 + cl, ks, lane);
@@ -1266,6 +1270,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
 #pragma unroll
           for (int v = 0; v < 4; ++v) pm[v] = max_nq(pm[v], fmaf(acc[v], sc2, -lv[v]));
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int v = 0; v < 4; ++v) pm[v] = __builtin_amdgcn_exp2f(pm[v]);
         const int col = wv * 16 + cl;
@@ -1417,6 +1422,11 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
       typename M::op_t aA[M::NKS], aB[M::NKS];
       floatx4 accA[2], accB[2];
       float4 ivA, ivB;
+      // The four wavefronts of a SIMD would otherwise finish this phase
+      // apart (the oldest issues first) and wait for the last at the next
+      // barrier: a wavefront's priority steps down as its tiles are done,
+      // so the ones behind get the issue slots.
+      __builtin_amdgcn_s_setprio(3);
       load_a(0, aA);
       load_a(1, aB);
       ivA = *reinterpret_cast<const float4*>(ivh + 4 * q);
@@ -1424,6 +1434,9 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
+        if (k == 2) __builtin_amdgcn_s_setprio(2);
+        if (k == 4) __builtin_amdgcn_s_setprio(1);
+        if (k == 6) __builtin_amdgcn_s_setprio(0);
         floatx4* cur = (k & 1) ? accB : accA;
         floatx4* nxt = (k & 1) ? accA : accB;
         typename M::op_t* an = (k & 1) ? aA : aB;  // operands of tile k + 1
@@ -1711,6 +1724,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
         typename M::op_t aA[M::NKS], aB[M::NKS];
         floatx4 accA[2], accB[2];
         float4 ivA, ivB;
+        __builtin_amdgcn_s_setprio(3);  // stepped down as the tiles are done (see the lightning kernel)
         load_a(0, aA);
         load_a(1, aB);
         ivA = *reinterpret_cast<const float4*>(ivh + 4 * q);
@@ -1718,6 +1732,9 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
+          if (k == 2) __builtin_amdgcn_s_setprio(2);
+          if (k == 4) __builtin_amdgcn_s_setprio(1);
+          if (k == 6) __builtin_amdgcn_s_setprio(0);
           floatx4* curc = (k & 1) ? accB : accA;
           floatx4* nxt = (k & 1) ? accA : accB;
           typename M::op_t* an = (k & 1) ? aA : aB;
