@@ -1596,7 +1596,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
   __shared__ __align__(16) float csum[2][BT];  // per half of the rows: the column's sum,
   __shared__ __align__(16) int crow[2][BT];    //   the highest row above p (-1: none)
 
-  const int tid = threadIdx.x, wv = wave_id();
+  const int wv = wave_id();
   int S = 0;
   for (int r = 0; r < P.nreq; ++r) S += lt_blocks(P, r);
   // Items (layer, kv-head, request, column block) in order, a unit's column
