@@ -360,9 +360,12 @@ def compress_kernel_bench(iters=20):
                                ("score_lightning_stats", "lightning", None),
                                ("score_flash", "flash", lse_ok)):
             sp = zp.ScoreParams(redundancy=red)
+            # all window rows carry their log-sum-exp: the engine then passes
+            # window_lse_all as well, and so does this leg
             ms = _time_calls(lambda: zp.zp_score_tokens(cache, sp, 0, 1, tables, nblk, NB, qslot,
                                                         first, scores, f_new, sws, stream=stream,
-                                                        window_lse_valid=lse),
+                                                        window_lse_valid=lse,
+                                                        window_lse_all=lse is not None),
                              iters if red == "lightning" else max(3, iters // 4), stream)
             fl, by = score_unit_cost(n, red, True)
             tf = units * fl / (ms * 1e-3) / 1e12

@@ -456,7 +456,8 @@ __device__ __forceinline__ void s0_columns(const ScoreParams& P, const ColOps<T,
 
 // Whether request r's window rows come with their log-sum-exp.
 __device__ __forceinline__ bool lse_given(const ScoreParams& P, int r) {
-  return P.lse_ok && P.qwin_lse && P.lse_ok[r] != 0;
+  if (!P.qwin_lse) return false;
+  return (P.flags & ZP_SCORE_WINDOW_LSE_ALL) || (P.lse_ok && P.lse_ok[r] != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -826,52 +827,119 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 
+// Per-request and per-block values (block counts, block ids, slots, flags)
+// read through the scalar cache: the address is the same in every lane, and
+// scalar loads are waited for with the LDS / scalar counter, so in the
+// persistent kernels they never wait behind the in-flight HBM -> LDS copies.
+typedef const __attribute__((address_space(4))) int32_t* lt_const_i32;
+typedef const __attribute__((address_space(4))) uint32_t* lt_const_u32;
+__device__ __forceinline__ int32_t lt_ld(const int32_t* p, int64_t i) {
+  return ((lt_const_i32)p)[i];
+}
+__device__ __forceinline__ uint32_t lt_ld_u8(const uint8_t* p, int64_t i) {
+  // the aligned word holding byte i (allocations are at least 4-byte aligned)
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p) + i;
+  const uint32_t w = *((lt_const_u32)(a & ~uintptr_t(3)));
+  return (w >> (8 * (a & 3))) & 0xffu;
+}
+
 // One workgroup of kFinThreads per (layer x request, kv-head), 4 tokens per
 // thread per chunk; pooling halves up to kFinHalo are taken from an LDS copy
-// of the chunk.
+// of the chunk. The workgroups are all resident at once at the serving
+// shapes, so the kernel takes about one workgroup's chain of dependent
+// memory round trips: the request's fields are requested together, the
+// block ids are checked one per thread, and the first chunk's loads (row
+// sums, S1 window) all go out before the one barrier that merges the
+// softmax statistics and the block-id check.
 constexpr int kFinThreads = 1024, kFinChunk = 4 * kFinThreads, kFinHalo = 64;
 
 __global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams P) {
   constexpr int NW = kFinThreads / 64;
   __shared__ float red[2][NW];
+  __shared__ int badw[NW];
   __shared__ float s1c[kFinChunk + 2 * kFinHalo];
   const int h = blockIdx.x, z = blockIdx.y;
   const int r = z % P.nreq;
-  const int N = P.num_blocks[r];
+  const int N = lt_ld(P.num_blocks, r);
+  const int slot = lt_ld(P.qslot, r);
+  const uint32_t first_w = lt_ld_u8(P.first, r);
+  asm volatile("" ::"s"(N), "s"(slot), "s"(first_w));  // the three loads before any test
   if (N <= 0 || N > P.max_blocks || N > P.table_stride) return;
-  const int slot = P.qslot[r];
   if (slot < 0 || slot >= P.max_slots) return;
-  for (int i = 0; i < N; ++i) {
-    const int pg = P.tables[(int64_t)r * P.table_stride + i];
-    if (pg < 0 || pg >= P.num_blocks_total) return;  // phases A/B flagged it
-  }
+  const bool first = first_w != 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = N * P.b;  // a multiple of 16
+  // A bad block id (flagged by the scoring kernels) leaves the unit's
+  // scores unwritten. The ids are loaded here, one per thread, and tested
+  // at the barrier below, so the loads in between are not held up.
+  const int* trow = P.tables + (int64_t)r * P.table_stride;
+  const int pg = tid < N ? trow[tid] : 0;
+  int bad = 0;
+  for (int i = tid + kFinThreads; i < N; i += kFinThreads)
+    bad |= (trow[i] < 0 || trow[i] >= P.num_blocks_total) ? 1 : 0;
   const int64_t zh = (int64_t)z * P.h_kv + h;
   const float* s1 = P.s1buf + zh * ((int64_t)P.max_blocks * P.b);
-  float* rr = P.rbuf + zh * ((int64_t)P.max_blocks * P.b);
+  const float* rr = P.rbuf + zh * ((int64_t)P.max_blocks * P.b);
+  const unsigned long long* rs = P.rsub + zh * ((int64_t)P.max_blocks * P.b);
   float* out = P.scores + zh * P.scores_stride;
-  const bool first = P.first[r] != 0;
   const bool pool = (P.flags & ZP_SCORE_POOL) && (first || !(P.flags & ZP_SCORE_POOL_FIRST_ONLY));
   const bool redun = (P.flags & ZP_SCORE_REDUNDANCY) != 0;
+  const bool flash = redun && (P.flags & ZP_SCORE_REDUNDANCY_FLASH);
   const int half = pool ? P.pool_kernel / 2 : 0;
+  const bool lds_pool = pool && half <= kFinHalo;
   const float c2 = P.inv_tau * kLog2e;  // softmax(r / tau) in the exp2 domain
 
-  if (redun && (P.flags & ZP_SCORE_REDUNDANCY_FLASH)) {
-    // flash: row sum over the whole sequence minus its zeroed entries, / n
-    // (each thread keeps the same tokens in every pass below)
-    const unsigned long long* rs = P.rsub + zh * ((int64_t)P.max_blocks * P.b);
-    for (int t = 4 * tid; t < n; t += kFinChunk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rr[t + e] = (rr[t + e] - from_fix(rs[t + e])) / (float)n;
-  }
+  // Redundancy row values of tokens t .. t + 3; with flash redundancy the
+  // row sum over the whole sequence minus its zeroed entries, / n.
+  auto row4 = [&](int t) __attribute__((always_inline)) -> float4 {
+    float4 x = *reinterpret_cast<const float4*>(rr + t);
+    if (flash) {
+      x.x = (x.x - from_fix(rs[t])) / (float)n;
+      x.y = (x.y - from_fix(rs[t + 1])) / (float)n;
+      x.z = (x.z - from_fix(rs[t + 2])) / (float)n;
+      x.w = (x.w - from_fix(rs[t + 3])) / (float)n;
+    }
+    return x;
+  };
+  // S1 of [c0 - half, c0 + chunk + half) into s1c, -inf outside the
+  // sequence: each thread its own four tokens (one 16-byte load; n is a
+  // multiple of 4), the first `half` threads the halos, all loads issued
+  // before any is waited for
+  struct Win {
+    float4 x;
+    float lo, hi;
+  };
+  auto fill_load = [&](int c0) __attribute__((always_inline)) -> Win {
+    Win f{make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY), -INFINITY, -INFINITY};
+    const int t = c0 + 4 * tid;
+    if (t < n) f.x = *reinterpret_cast<const float4*>(s1 + t);
+    if (tid < half) {
+      const int tl = c0 - half + tid, tr = c0 + kFinChunk + tid;
+      if (tl >= 0) f.lo = s1[tl];
+      if (tr < n) f.hi = s1[tr];
+    }
+    return f;
+  };
+  auto fill_store = [&](const Win& f) __attribute__((always_inline)) {
+    float* d = s1c + half + 4 * tid;
+    d[0] = f.x.x; d[1] = f.x.y; d[2] = f.x.z; d[3] = f.x.w;
+    if (tid < half) {
+      s1c[tid] = f.lo;
+      s1c[half + kFinChunk + tid] = f.hi;
+    }
+  };
+
   // softmax statistics of r / tau in one pass: each thread's running
-  // (max, sum), then the wavefront and the workgroup, in a fixed order
-  float mx = -INFINITY, inv_sum = 0.f;
+  // (max, sum), then the wavefront and the workgroup, in a fixed order;
+  // chunk 0's row values stay in registers for the output pass
+  float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float m = -INFINITY, sm = 0.f;
+  Win w0{};
+  if (lds_pool) w0 = fill_load(0);  // in flight with the row sums
   if (redun) {
-    float m = -INFINITY, sm = 0.f;
     for (int t = 4 * tid; t < n; t += kFinChunk) {
-      const float4 x = *reinterpret_cast<const float4*>(rr + t);
+      const float4 x = row4(t);
+      if (t < kFinChunk) x0 = x;
       const float m4 = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)) * c2;
       const float mn = fmaxf(m, m4);
       sm = sm * exp2f(m - mn) + exp2f(x.x * c2 - mn) + exp2f(x.y * c2 - mn) +
@@ -880,11 +948,22 @@ __global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) lse_merge(m, sm, shfl_xor_f(m, o), shfl_xor_f(sm, o));
-    if (lane == 0) {
-      red[0][wv] = m;
-      red[1][wv] = sm;
-    }
-    __syncthreads();
+  }
+  if (lds_pool) fill_store(w0);
+  bad |= (pg < 0 || pg >= P.num_blocks_total) ? 1 : 0;
+  const bool wbad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  if (lane == 0) {
+    red[0][wv] = m;
+    red[1][wv] = sm;
+    badw[wv] = wbad ? 1 : 0;
+  }
+  __syncthreads();
+  int anybad = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) anybad |= badw[i];
+  if (anybad) return;  // the same for every thread
+  float mx = -INFINITY, inv_sum = 0.f;
+  if (redun) {
     m = red[0][0];
     sm = red[1][0];
 #pragma unroll
@@ -892,15 +971,11 @@ __global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams
     mx = m;
     inv_sum = 1.0f / sm;
   }
-  const bool lds_pool = pool && half <= kFinHalo;
   const bool vec_out = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   for (int c0 = 0; c0 < n; c0 += kFinChunk) {
-    if (lds_pool) {  // s1 of [c0 - half, c0 + chunk + half), -inf outside the sequence
+    if (lds_pool && c0 > 0) {  // chunk 0's copy was made before the barrier above
       __syncthreads();
-      for (int i = tid; i < kFinChunk + 2 * half; i += kFinThreads) {
-        const int t = c0 - half + i;
-        s1c[i] = (t >= 0 && t < n) ? s1[t] : -INFINITY;
-      }
+      fill_store(fill_load(c0));
       __syncthreads();
     }
     const int t = c0 + 4 * tid;
@@ -909,24 +984,24 @@ __global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams
     if (lds_pool) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float m = -INFINITY;
-        for (int i = 4 * tid + e; i <= 4 * tid + e + 2 * half; ++i) m = fmaxf(m, s1c[i]);
-        v[e] = m;
+        float mm = -INFINITY;
+        for (int i = 4 * tid + e; i <= 4 * tid + e + 2 * half; ++i) mm = fmaxf(mm, s1c[i]);
+        v[e] = mm;
       }
     } else if (pool) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int lo = max(0, t + e - half), hi = min(n - 1, t + e + half);
-        float m = -INFINITY;
-        for (int i = lo; i <= hi; ++i) m = fmaxf(m, s1[i]);
-        v[e] = m;
+        float mm = -INFINITY;
+        for (int i = lo; i <= hi; ++i) mm = fmaxf(mm, s1[i]);
+        v[e] = mm;
       }
     } else {
       const float4 x = *reinterpret_cast<const float4*>(s1 + t);
       v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     }
     if (redun) {
-      const float4 x = *reinterpret_cast<const float4*>(rr + t);
+      const float4 x = c0 == 0 ? x0 : row4(t);
       const float xr[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] -= P.lambda_ * (exp2f(xr[e] * c2 - mx) * inv_sum);
@@ -1023,22 +1098,6 @@ typedef __attribute__((address_space(1))) void* lt_gbl_ptr;
 
 constexpr int kLtThreads = 1024;
 
-// Per-request and per-block values the persistent kernel reads (block
-// counts, block ids, slots, flags), through the scalar cache: the address is
-// the same in every lane, and scalar loads are waited for with the LDS /
-// scalar counter, so they never wait behind the in-flight HBM -> LDS copies.
-typedef const __attribute__((address_space(4))) int32_t* lt_const_i32;
-typedef const __attribute__((address_space(4))) uint32_t* lt_const_u32;
-__device__ __forceinline__ int32_t lt_ld(const int32_t* p, int64_t i) {
-  return ((lt_const_i32)p)[i];
-}
-__device__ __forceinline__ uint32_t lt_ld_u8(const uint8_t* p, int64_t i) {
-  // the aligned word holding byte i (allocations are at least 4-byte aligned)
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p) + i;
-  const uint32_t w = *((lt_const_u32)(a & ~uintptr_t(3)));
-  return (w >> (8 * (a & 3))) & 0xffu;
-}
-
 // Cursor over the items of one workgroup, with the values its item needs.
 struct LtItem {
   int li, h, r, pidx, N;  // layer index in the call, kv-head, request, block, blocks of r
@@ -1065,7 +1124,8 @@ __device__ __forceinline__ void lt_fill(const ScoreParams& P, LtItem& it) {
   it.page = page;
   it.slot = slot;
   it.first = f != 0;
-  it.lse = P.lse_ok != nullptr && P.qwin_lse != nullptr && l != 0;
+  it.lse = P.qwin_lse != nullptr &&
+           ((P.flags & ZP_SCORE_WINDOW_LSE_ALL) || (P.lse_ok != nullptr && l != 0));
 }
 
 __device__ __forceinline__ void lt_next_request(const ScoreParams& P, LtItem& it, int layer_count) {
@@ -1856,7 +1916,8 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
   using L = LdsTile<T, D>;
   const int b = P.b;
   const bool w16 = P.w == 16;
-  const size_t ptileA = (P.lse_ok && !w16) ? size_t(4) * R * 16 : 0;
+  const bool lse_all = (P.flags & ZP_SCORE_WINDOW_LSE_ALL) != 0;
+  const size_t ptileA = ((P.lse_ok || lse_all) && !w16) ? size_t(4) * R * 16 : 0;
   const size_t smemA = size_t(b) * L::ROWB +
                        sizeof(float) * (2 * b + D + 4 * R * 2 + 3 * b + R + ptileA);
   const size_t smemF = size_t(b) * L::ROWB + sizeof(float) * D;
@@ -1904,7 +1965,7 @@ static zp_status launch_score(const ScoreParams& P, int items, hipStream_t s) {
     }
     if (!flash_persistent) hipLaunchKernelGGL(kF, gridP, dim3(256), smemF, s, P);
   }
-  hipLaunchKernelGGL(kB, gridP, dim3(256), smemB, s, P);
+  if (!lse_all) hipLaunchKernelGGL(kB, gridP, dim3(256), smemB, s, P);  // else nothing to gather
   hipLaunchKernelGGL(score_finalize_kernel, dim3(P.h_kv, items), dim3(kFinThreads), 0, s, P);
   return ZP_OK;
 }
@@ -1989,10 +2050,13 @@ extern "C" zp_status zp_score_tokens(const zp_geom* geom, const zp_cache* cache,
   const zp_score_params& sp = *params;
   if (window_lse_valid && !cache->qwin_lse)
     return fail(ZP_EINVAL, "zp_score_tokens: window_lse_valid needs cache->qwin_lse");
+  if ((sp.flags & ZP_SCORE_WINDOW_LSE_ALL) && !cache->qwin_lse)
+    return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_WINDOW_LSE_ALL needs cache->qwin_lse");
   if ((sp.flags & ZP_SCORE_GLOBAL) && (!cache->gscore || !f_new))
     return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL needs cache->gscore and f_new");
   if (sp.flags & ~uint32_t(ZP_SCORE_GLOBAL | ZP_SCORE_POOL | ZP_SCORE_POOL_FIRST_ONLY |
-                           ZP_SCORE_REDUNDANCY | ZP_SCORE_REDUNDANCY_FLASH | ZP_SCORE_GLOBAL_SUM))
+                           ZP_SCORE_REDUNDANCY | ZP_SCORE_REDUNDANCY_FLASH | ZP_SCORE_GLOBAL_SUM |
+                           ZP_SCORE_WINDOW_LSE_ALL))
     return fail(ZP_EINVAL, "zp_score_tokens: unknown flags 0x%x", sp.flags);
   if ((sp.flags & ZP_SCORE_GLOBAL_SUM) && !(sp.flags & ZP_SCORE_GLOBAL))
     return fail(ZP_EINVAL, "zp_score_tokens: ZP_SCORE_GLOBAL_SUM needs ZP_SCORE_GLOBAL");

@@ -135,6 +135,9 @@ class Compressor:
             first_d = meta_d[o + 2 * nreq:o + 3 * nreq].to(torch.uint8)
             lse_d = (meta_d[o + 3 * nreq:o + 4 * nreq].to(torch.uint8)
                      if self.cache.qwin_lse is not None else None)
+            # every request's window rows carry their log-sum-exp: the scoring
+            # call skips its statistics pass altogether
+            lse_all = lse_d is not None and all(bool(f) for f in lse_ok)
             ls = self.layer_stride
             use_f = self.params.use_global and self.cache.gscore is not None
             shape = (G.num_layers if record else ls, nreq, G.num_kv_heads, maxb * b)
@@ -160,7 +163,8 @@ class Compressor:
                 sl = slice(lb, lb + lc) if record else slice(0, lc)
                 sc, fn = scores[sl], (f_new[sl] if use_f else None)
                 zp.zp_score_tokens(self.cache, self.params, lb, lc, src_d, nblk_d, maxb, qslot_d,
-                                   first_d, sc, fn, sws, stream=stream, window_lse_valid=lse_d)
+                                   first_d, sc, fn, sws, stream=stream, window_lse_valid=lse_d,
+                                   window_lse_all=lse_all)
                 zp.zp_select_compact(self.cache, lb, lc, sc, src_d, nblk_d, maxb, dst_d, keep,
                                      kept[sl] if kept is not None else None, cws,
                                      stream=stream, f_new=fn)

@@ -23,6 +23,7 @@ ZP_DEVERR_BLOCK_ID, ZP_DEVERR_SEQ_LEN, ZP_DEVERR_SLOT, ZP_DEVERR_KEEP = 1, 2, 4,
 ZP_SCORE_GLOBAL, ZP_SCORE_POOL, ZP_SCORE_POOL_FIRST_ONLY, ZP_SCORE_REDUNDANCY = 1, 2, 4, 8
 ZP_SCORE_REDUNDANCY_FLASH = 0x10
 ZP_SCORE_GLOBAL_SUM = 0x20
+ZP_SCORE_WINDOW_LSE_ALL = 0x40
 ZP_SELECT_NO_COMPACT = 1
 
 
@@ -502,7 +503,9 @@ class ScoreParams:
 
 def zp_score_tokens(cache: PagedKVCache, params: ScoreParams, layer_begin, layer_count,
                     block_tables, num_blocks, max_blocks, qslot, first_compression, scores,
-                    f_new, workspace, stream=None, window_lse_valid=None):
+                    f_new, workspace, stream=None, window_lse_valid=None, window_lse_all=False):
+    """window_lse_all: every request's window rows carry their log-sum-exp
+    (window_lse_valid is then not read); the statistics pass is skipped."""
     import torch
     _need(block_tables, torch.int32, "block_tables")
     _need(num_blocks, torch.int32, "num_blocks")
@@ -514,8 +517,11 @@ def zp_score_tokens(cache: PagedKVCache, params: ScoreParams, layer_begin, layer
     if f_new is not None and f_new.shape != scores.shape:
         raise ValueError("f_new must have the shape of scores")
     nreq = block_tables.shape[0]
+    pc = params.c()
+    if window_lse_all:
+        pc.flags |= ZP_SCORE_WINDOW_LSE_ALL
     _check(lib().zp_score_tokens(
-        C.byref(cache.geom.c()), C.byref(cache.c()), C.byref(params.c()), layer_begin,
+        C.byref(cache.geom.c()), C.byref(cache.c()), C.byref(pc), layer_begin,
         layer_count, nreq, block_tables.data_ptr(), block_tables.shape[1],
         num_blocks.data_ptr(), int(max_blocks), qslot.data_ptr(), first_compression.data_ptr(),
         _ptr(window_lse_valid), scores.data_ptr(), _ptr(f_new), scores.shape[-1],

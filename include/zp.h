@@ -243,6 +243,12 @@ zp_status zp_paged_prefill(const zp_geom* geom, const zp_cache* cache, int32_t l
                                          alpha*F + S, instead of Alg. 2's
                                          max(alpha*F, S) (App. C.3 names both);
                                          invalid without ZP_SCORE_GLOBAL             */
+#define ZP_SCORE_WINDOW_LSE_ALL 0x40u /* every request's window rows carry their
+                                         log-sum-exp in cache->qwin_lse, as if
+                                         window_lse_valid[r] != 0 for all r (the
+                                         array is then not read and may be NULL); the
+                                         statistics pass is not launched at all.
+                                         Needs cache->qwin_lse                       */
 
 typedef struct zp_score_params {
   float alpha;         /* decay of the global score                          */

@@ -102,6 +102,22 @@ def test_score_global_reduce_is_validated():
     assert st == zp.ZP_EINVAL and "GLOBAL_SUM" in zp.lib().zp_last_error().decode()
 
 
+def test_score_window_lse_all_needs_the_lse_table():
+    # the flag promises every window row's log-sum-exp: refused on the host
+    # when the cache has no log-sum-exp table, and unknown bits stay refused
+    g = _geom().c()
+    cache = zp.Cache(1, 1, 1, None, None)
+    sp = zp.ScoreParams(use_global=False).c()
+    sp.flags |= zp.ZP_SCORE_WINDOW_LSE_ALL
+    st = zp.lib().zp_score_tokens(C.byref(g), C.byref(cache), C.byref(sp), 0, 1, 1, 1, 4, 1, 4, 1,
+                                  1, None, 1, None, 64, 1, 1 << 20, None)
+    assert st == zp.ZP_EINVAL and "WINDOW_LSE_ALL" in zp.lib().zp_last_error().decode()
+    sp.flags = zp.ZP_SCORE_WINDOW_LSE_ALL << 1
+    st = zp.lib().zp_score_tokens(C.byref(g), C.byref(cache), C.byref(sp), 0, 1, 1, 1, 4, 1, 4, 1,
+                                  1, None, 1, None, 64, 1, 1 << 20, None)
+    assert st == zp.ZP_EINVAL and "unknown flags" in zp.lib().zp_last_error().decode()
+
+
 # --- allocator ------------------------------------------------------------
 
 def test_alloc_all_or_nothing_and_conservation():

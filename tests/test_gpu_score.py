@@ -57,7 +57,7 @@ def _window_lse(Qw, K, b):
 
 
 def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, layer_count=2,
-         seed=11, planted=False, heavy=True, lse=None, repeat=1):
+         seed=11, planted=False, heavy=True, lse=None, repeat=1, lse_all=False):
     announce(f"score dtype={dtype} d={d} g={h_q // h_kv} b={b} w={w} N={nblocks} first={first} "
              f"sp={sp}")
     nreq = len(nblocks)
@@ -108,9 +108,12 @@ def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, laye
         sc2 = torch.full_like(scores, -7.0)
         fn2 = torch.full_like(f_new, -5.0) if f_new is not None else None
         ws2 = zp.new_workspace(ws.numel())
+        # with lse_all the repeats say "every request has it" by the call
+        # flag instead of the per-request array (which is then not passed)
         zp.zp_score_tokens(hc.dev, sp, layer_begin, layer_count, dev_i32(tab), dev_i32(nblocks),
                            max_blocks, dev_i32(qslot), torch.from_numpy(firsts).cuda(), sc2, fn2,
-                           ws2, window_lse_valid=lse_valid)
+                           ws2, window_lse_valid=None if lse_all else lse_valid,
+                           window_lse_all=lse_all)
         torch.cuda.synchronize()
         assert torch.equal(sc2.view(torch.int32), scores.view(torch.int32))
         if f_new is not None:
@@ -242,6 +245,17 @@ def test_score_with_window_lse_qwen_shape(red):
     # requests 0 and 2 bring their window rows' log-sum-exp: one pass over K
     sp = zp.ScoreParams(redundancy=red)
     _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, sp, lse=lambda r: r != 1)
+
+
+@pytest.mark.parametrize("red", ["lightning", "flash"])
+def test_score_window_lse_all_flag_same_bits(red):
+    # every request carries its window log-sum-exp: the call flag (no
+    # statistics launch, no flag array) gives the bits of the per-request flags
+    sp = zp.ScoreParams(redundancy=red)
+    _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, sp, lse=lambda r: True,
+         repeat=2, lse_all=True)
+    _run("bf16", 128, 16, 2, 64, 8, [3, 5], lambda r: 1, sp, L=1, layer_begin=0, layer_count=1,
+         lse=lambda r: True, repeat=2, lse_all=True)
 
 
 def test_score_global_sum_reduce_every_path():
