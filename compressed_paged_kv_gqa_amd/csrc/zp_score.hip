@@ -1331,9 +1331,30 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
           for (int v = 0; v < 4; ++v) pm[v] = max_nq(pm[v], fmaf(acc[v], sc2, -lv[v]));
         }
         __builtin_amdgcn_s_setprio(0);
+        const int col = wv * 16 + cl;
+        if (redun) {
+          // |k|^2 of the wavefront's 16 keys from its operand registers:
+          // lanes cl, cl + 16, cl + 32, cl + 48 hold the 128 dimensions of
+          // key cl (no second LDS pass over the block)
+          typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+          float ss = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < M::NKS; ++ks) {
+            const uint4 u = __builtin_bit_cast(uint4, bop[ks]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), __builtin_bit_cast(bf2, u.x), ss, false);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), __builtin_bit_cast(bf2, u.y), ss, false);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), __builtin_bit_cast(bf2, u.z), ss, false);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), __builtin_bit_cast(bf2, u.w), ss, false);
+          }
+          ss = xor32_sum(xor16_sum(ss));
+          if (q == 0) {
+            const float nr = sqrtf(ss);
+            inv_s[col] = ss > 0.f ? __builtin_amdgcn_rcpf(nr) : 0.f;  // v_rcp_f32, 1 ulp
+            nrm_s[col] = nr;
+          }
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) pm[v] = __builtin_amdgcn_exp2f(pm[v]);
-        const int col = wv * 16 + cl;
         if (last) {  // causal mask: window slot u = 4q + v sees keys up to BT - 16 + u
 #pragma unroll
           for (int v = 0; v < 4; ++v)
@@ -1391,7 +1412,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
           }
         }
       }
-      if (redun) {  // |k|^2, 4 lanes per key (32 dimensions each)
+      if (redun && !it.lse) {  // |k|^2, 4 lanes per key (32 dimensions each)
         const int row = tid >> 2, part = tid & 3;
         float ss = 0.f;
         typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
