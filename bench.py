@@ -301,12 +301,27 @@ def select_unit_bytes(n, keep):
     return 4 * n + 4 * keep * D * ELEM + 8 * keep
 
 
-def _time_calls(fn, iters, stream):
+def _time_calls(fn, iters, stream, warm_ms=200.0):
+    """HIP-event time per call of fn (ms) over `iters` calls, after untimed
+    calls that fill at least warm_ms of GPU time: from idle the clocks take
+    ~100 ms of steady work to settle, and calls timed before that ran up to
+    25% slower (lightning scoring: 0.311 -> 0.244 ms over its first 120
+    calls, then 0.240-0.245)."""
     import torch
-    fn()
-    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    spent, k = 0.0, 1
+    while spent < warm_ms:  # back-to-back batches, doubled while short
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1)
+        spent += t
+        if t < 25.0:
+            k *= 2
+    torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(iters):
         fn()

@@ -1043,7 +1043,8 @@ __global__ __launch_bounds__(kFinThreads) void score_finalize_kernel(ScoreParams
 //      product) added to that entry's row in 64-bit fixed point (exact, so
 //      the same bits in any order);
 //   4. each row's sum minus its zeroed entries, / n: the redundancy row
-//      sums.
+//      sums (made at the start of the next item, so that no barrier of its
+//      own is needed).
 // With flash redundancy, steps 2-4 belong to score_flash_persist_kernel: the
 // item writes its key norms for it and clears its fixed-point words.
 // ---------------------------------------------------------------------------
@@ -1284,6 +1285,21 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
                                      (lt_lds_ptr)(Qs + wv * 1024), 16, 0, 0);
   };
 
+  // 4. of the previous item, row i: (row sum - zeroed entries) / n, and its
+  // fixed-point word cleared. Run before this item's first barrier: csum
+  // and sub are written again only after it, and the barrier that ended
+  // the previous item retired its LDS adds.
+  bool pend = false;
+  int64_t pend_off = 0;
+  float pend_n = 1.f;
+  auto flush_rows = [&](int t) __attribute__((always_inline)) {
+    if (pend && t < BT) {
+      P.rbuf[pend_off + t] = (csum[0][t] - from_fix(sub[t])) / pend_n;
+      sub[t] = 0ull;
+    }
+    pend = false;
+  };
+
   // Scores item `it` from (Kt, Ft, Lt); `nx` is the next item (its queries
   // are copied into Qs once this item's window phase is done).
   auto process = [&](const LtItem& it, const LtItem& nx, const char* Kt, const float* Ft,
@@ -1294,6 +1310,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, q = lane >> 4, cl = lane & 15;
+    flush_rows(tid);
     const bool ok = item_ok(it);
     const int z = it.li * P.nreq + it.r;
     const int64_t zh = (int64_t)z * P.h_kv + it.h;
@@ -1607,15 +1624,11 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
         if (is >= 0) lds_add_u64(&sub[is], to_fix(d * inv_s[is] * ivj));
       }
     }
-    lds_barrier();  // B3
-    // 4. row i: (row sum - zeroed entries) / n; the fixed-point word is
-    // cleared for the next item
-    if (tid < BT) {
-      const int i = tid;
-      P.rbuf[zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT + i] =
-          (csum[0][i] - from_fix(sub[i])) / (float)n;
-      sub[i] = 0ull;
-    }
+    // 4. is left to the start of the next item (or the end of the loop),
+    // after the barrier that ends this one
+    pend = true;
+    pend_off = zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT;
+    pend_n = (float)n;
   };
 
   if (tid < BT) sub[tid] = 0ull;
@@ -1643,6 +1656,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     cur = nx;
     --left;
   }
+  flush_rows(tid);
 }
 
 // ---------------------------------------------------------------------------
