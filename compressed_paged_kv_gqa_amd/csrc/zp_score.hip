@@ -1547,28 +1547,30 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
           products(an, nxt);
         }
         const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
-        // x = k_i . k_j / |k_i|: summed for the column (the diagonal, k_j
-        // against itself, is taken out after the loop), and above p |k_j|
+        // x = k_i . k_j / |k_i| is summed for the column (the diagonal, k_j
+        // against itself, is taken out after the loop), and is above p |k_j|
         // exactly when the cosine is above p
-        float x[2][4];
+        float cmx[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) x[c][v] = cur[c][v] * ivv[v];
-          cs[c] += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
+          cs[c] = fmaf(cur[c][3], ivv[3], fmaf(cur[c][2], ivv[2], fmaf(cur[c][1], ivv[1], fmaf(cur[c][0], ivv[0], cs[c]))));
+          cmx[c] = max_nq(max_nq(cur[c][0], cur[c][1]), max_nq(cur[c][2], cur[c][3]));
         }
         // the highest row above p, tracked only in tiles that have one (the
         // test is made for the whole wavefront at once; a diagonal tile
-        // always has one, its diagonal, which is never the entry to zero)
-        const bool any = max_nq(max_nq(x[0][0], x[0][1]), max_nq(x[0][2], x[0][3])) > pnc[0] ||
-                         max_nq(max_nq(x[1][0], x[1][1]), max_nq(x[1][2], x[1][3])) > pnc[1];
+        // always has one, its diagonal, which is never the entry to zero).
+        // An entry above p |k_j| >= 0 has a positive product, so the
+        // column's largest product times the tile's largest 1/|k_i| bounds
+        // every entry (rounding is monotone); NaN passes to the exact test.
+        const float ivm = max_nq(max_nq(ivv[0], ivv[1]), max_nq(ivv[2], ivv[3]));
+        const bool any = !(cmx[0] * ivm <= pnc[0]) || !(cmx[1] * ivm <= pnc[1]);
         if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const bool isd = has_diag && k == kd + c;  // wave-uniform
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const bool hit = x[c][v] > pnc[c] && !(isd && dg[v]);
+              const bool hit = cur[c][v] * ivv[v] > pnc[c] && !(isd && dg[v]);
               bk[c] = hit ? 4 * k + v : bk[c];
             }
           }
@@ -1842,22 +1844,23 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
             products(an, nxt);
           }
           const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
-          float x[2][4];
+          // as in the lightning kernel: the column sums by FMA, the test
+          // for an entry above p first against a bound of the tile
+          float cmx[2];
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) x[c][v] = curc[c][v] * ivv[v];
-            cs[c] += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
+            cs[c] = fmaf(curc[c][3], ivv[3], fmaf(curc[c][2], ivv[2], fmaf(curc[c][1], ivv[1], fmaf(curc[c][0], ivv[0], cs[c]))));
+            cmx[c] = max_nq(max_nq(curc[c][0], curc[c][1]), max_nq(curc[c][2], curc[c][3]));
           }
-          const bool any = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])) > pnc[0] ||
-                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])) > pnc[1];
+          const float ivm = max_nq(max_nq(ivv[0], ivv[1]), max_nq(ivv[2], ivv[3]));
+          const bool any = !(cmx[0] * ivm <= pnc[0]) || !(cmx[1] * ivm <= pnc[1]);
           if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
               const bool isd = dblk && has_diag && k == kd + c;  // wave-uniform
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
-                const bool hit = x[c][v] > pnc[c] && !(isd && dg[v]);
+                const bool hit = curc[c][v] * ivv[v] > pnc[c] && !(isd && dg[v]);
                 bk[c] = hit ? 32 * i + 4 * k + v : bk[c];
               }
             }
