@@ -185,3 +185,68 @@ def test_prefill_reports_bad_block_ids_without_faulting(b):
                         dev_i32([[0, 1, 2, 3]]), None, out, None, ws)
     torch.cuda.synchronize()
     assert zp.zp_workspace_errors(ws) & zp.ZP_DEVERR_SEQ_LEN
+
+
+def test_prefill_bench_launch_sampled():
+    """The launch bench.py times: 64 prompts of 4096 tokens in one call, the
+    Qwen3-8B attention shape (32 query / 8 kv heads, d 128, bf16, blocks of
+    256), so the LDS-copy kernel runs with its workgroups renumbered over
+    the 8 XCDs. The inputs are too large for the host generator; they come
+    from torch's seeded generator on the device, and the oracle gets the
+    same values. Checked on three requests (first, middle, last, so on
+    different XCD slots): sampled rows in every head against the float64
+    oracle, every appended K/V block bit-exact, the final block's window
+    queries and log-sum-exp."""
+    R, T, b, NB = 64, 4096, 256, 16
+    h_q, h_kv, d, w = 32, 8, 128, 16
+    g = h_q // h_kv
+    announce(f"prefill bench launch {R} x {T}")
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=R * NB + 8, block_size=b, num_kv_heads=h_kv,
+                            num_q_heads=h_q, head_dim=d, window=w, max_slots=R, n_max=8,
+                            dtype="bf16")
+    cache = zp.PagedKVCache(geom, with_global=False, with_window_lse=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(41)
+    q = torch.randn((R * T, h_q, d), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((R * T, h_kv, d), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((R * T, h_kv, d), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.full_like(q, 7.0)
+    lse = torch.zeros((R * T, h_q), dtype=torch.float32, device="cuda")
+    tables = torch.randperm(R * NB, generator=gen, device="cuda").to(torch.int32).view(R, NB)
+    cu = torch.arange(0, (R + 1) * T, T, dtype=torch.int32, device="cuda")
+    ctx = torch.zeros(R, dtype=torch.int32, device="cuda")
+    qslot = torch.arange(R, dtype=torch.int32, device="cuda")
+    ws = zp.new_workspace(zp.zp_prefill_workspace_size(geom, R))
+    zp.zp_paged_prefill(cache, 0, q, k, v, cu, ctx, T, tables.contiguous(), qslot, out, lse, ws)
+    torch.cuda.synchronize()
+    assert zp.zp_workspace_errors(ws) == 0
+    tab = tables.cpu().numpy()
+    srng = np.random.default_rng(41)
+    worst = 0.0
+    for r in (0, 37, R - 1):
+        c0 = r * T
+        # appended K/V: every block of the request, bit-exact
+        for blk in range(NB):
+            rows = slice(c0 + blk * b, c0 + (blk + 1) * b)
+            assert torch.equal(cache.k[0, tab[r, blk]], k[rows].transpose(0, 1))
+            assert torch.equal(cache.v[0, tab[r, blk]], v[rows].transpose(0, 1))
+        qf = q[c0:c0 + T].float().cpu().numpy()
+        K = k[c0:c0 + T].float().cpu().numpy().transpose(1, 0, 2)
+        V = v[c0:c0 + T].float().cpu().numpy().transpose(1, 0, 2)
+        rows = _sample_rows(srng, T, b, w, 0, k=8)
+        O, L = Z.prefill_attention(qf, K, V, 0, rows=rows)
+        out_h = out[c0:c0 + T].float().cpu().numpy()
+        lse_h = lse[c0:c0 + T].cpu().numpy()
+        for x, i in enumerate(rows):
+            for j in range(h_q):
+                err = np.abs(out_h[i, j] - O[x, j]).max() / np.abs(O[x, j]).max()
+                worst = max(worst, err)
+                assert err <= 2e-2, f"req {r} row {i} head {j}: {err}"
+            np.testing.assert_allclose(lse_h[i], L[x], rtol=0, atol=2e-3)
+        # the final block's 16 window rows: queries and log-sum-exp captured
+        for u in range(w):
+            i = T - w + u
+            assert torch.equal(cache.qwin[0, r, :, :, u], q[c0 + i].view(h_kv, g, d))
+            np.testing.assert_array_equal(cache.qwin_lse[0, r, :, :, u].cpu().numpy(),
+                                          lse_h[i].reshape(h_kv, g))
+    print(f"[prefill bench launch] worst relative error {worst:.3g}")
