@@ -14,7 +14,8 @@ Sampled units (requests spread over every workgroup range of the persistent
 scoring kernel, two of them through the window log-sum-exp path, two
 through the statistics pass, three kv-heads each): the scores against the
 float64 oracle, and the kept set against the oracle's scores under the 1e-6
-tie rule.
+tie rule. A third case gives every request its window log-sum-exp and says
+so by the call flag, as the timed compression leg does.
 """
 import numpy as np
 import pytest
@@ -35,10 +36,13 @@ SAMPLE_HEADS = [0, 3, 7]
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("redundancy", ["lightning", "flash"])
-def test_burst_full_width_compression_chain(redundancy):
+@pytest.mark.parametrize("redundancy,all_lse", [("lightning", False), ("flash", False),
+                                               ("lightning", True)],
+                         ids=["lightning", "flash", "lightning-all-lse"])
+def test_burst_full_width_compression_chain(redundancy, all_lse):
     announce(f"burst full width: {R} requests x {NB * BS} tokens, {redundancy}, "
-             f"keep {(NMAX - 1) * BS}")
+             f"keep {(NMAX - 1) * BS}, all window lse {all_lse}")
+    sample = {r: True for r in SAMPLE_REQ} if all_lse else SAMPLE_REQ
     n, keep, g = NB * BS, (NMAX - 1) * BS, HQ // HKV
     pool = R * NB + 4
     geom = zp.CacheGeometry(num_layers=1, num_blocks=pool, block_size=BS, num_kv_heads=HKV,
@@ -58,7 +62,10 @@ def test_burst_full_width_compression_chain(redundancy):
     # window log-sum-exp from the oracle for the requests that take that path
     tbl = np.zeros((1, R, HKV, g, W), np.float32)
     Kseq = {}
-    for r, given in SAMPLE_REQ.items():
+    for r in range(R):
+        given = sample.get(r, False) or all_lse
+        if r not in sample and not all_lse:
+            continue
         for h in range(HKV):
             if given or h in SAMPLE_HEADS:
                 Kseq[r, h] = Z.gather_sequence(hc.K[0, :, h], tab[r], n, BS)
@@ -74,7 +81,8 @@ def test_burst_full_width_compression_chain(redundancy):
     tab_d, nblk_d = dev_i32(tab), dev_i32(np.full(R, NB, np.int32))
     zp.zp_score_tokens(hc.dev, sp, 0, 1, tab_d, nblk_d, NB, dev_i32(qslot),
                        torch.from_numpy(first).cuda(), scores, f_new, sws,
-                       window_lse_valid=torch.from_numpy(lse_ok).cuda())
+                       window_lse_valid=None if all_lse else torch.from_numpy(lse_ok).cuda(),
+                       window_lse_all=all_lse)
     kept = torch.full((1, R, HKV, keep), -1, dtype=torch.int32, device="cuda")
     cws = zp.new_workspace(zp.zp_select_workspace_size(geom, 1, R, keep))
     zp.zp_select_compact(hc.dev, 0, 1, scores, tab_d, nblk_d, NB, dev_i32(dst), keep, kept, cws,
@@ -105,7 +113,7 @@ def test_burst_full_width_compression_chain(redundancy):
                                           err_msg=f"F request {r} head {h}")
     # sampled units against the oracle
     worst = 0.0
-    for r in SAMPLE_REQ:
+    for r in sample:
         for h in SAMPLE_HEADS:
             Fo = Z.gather_sequence(F0[0, :, h], tab[r], n, BS)
             S_ref, _ = Z.score_tokens(hc.Q[0, r, h], Kseq[r, h], Fo, True, BS, op)
@@ -115,7 +123,7 @@ def test_burst_full_width_compression_chain(redundancy):
             worst = max(worst, err)
             assert err <= SCORE_TOL, (r, h, err)
             chk = check_kept(kept_h[r, h], S_ref, keep)
-            print(f"request {r} head {h} (lse {SAMPLE_REQ[r]}): score err {err:.2e}; kept "
+            print(f"request {r} head {h} (lse {sample[r]}): score err {err:.2e}; kept "
                   f"{'same' if chk.same else chk.describe()}")
             assert chk.ok, (r, h, chk.describe())
     print(f"burst full width: 512 units top-k + move bit-exact; sampled worst score error {worst:.2e}")
