@@ -151,6 +151,12 @@ __device__ __forceinline__ void emit_lse(const PrefillParams& P, int r, int c0, 
 // ---------------------------------------------------------------------------
 constexpr int kPKT = 64;                 // keys per tile
 constexpr float kPLazy = 8.0f;           // lazy rescale threshold (log2 units)
+// The LDS-copy kernel forms a tile's weights with the running maximum as it
+// stands and moves the maximum only when a lane's partial sum of its
+// weights exceeds kPSumCap: every weight then stays below 2^11 (fp32 sums
+// and bf16 weights hold that), and with 32-key tiles (8 weights per lane)
+// the maximum moves at latest when some weight would pass 2^kPLazy.
+constexpr float kPSumCap = 2048.0f;
 constexpr int kPRows = 128;              // query rows (token, head) per workgroup
 constexpr int kPfTabLds = 2048;          // block ids staged in LDS (tables up to this wide)
 #ifndef ZP_PF_DMA_KT
@@ -655,21 +661,7 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
           for (int v = 0; v < 4; ++v)
             if (ct * 16 + v > lim) s[ct][v] = -INFINITY;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int v = 0; v < 4; v += 2) mx = max_nq(mx, max_nq(s[ct][v], s[ct][v + 1]));
-      mx = row32_max_nq(row16_max_nq(mx));
-      mx *= P.qk_scale;
-      if (__builtin_amdgcn_read_exec() & __ballot(mx > m[k] + kPLazy)) {  // any lane: rescale
-        const float mn = fmaxf(m[k], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
-        m[k] = mn;
-        l[k] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[k][dt] *= alpha;
-      }
+      // weights against the running maximum as it stands
       float p[NCT][4];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -678,6 +670,31 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
       float ps = p[0][0];
 #pragma unroll
       for (int e = 1; e < 4 * NCT; ++e) ps += p[e >> 2][e & 3];
+      if (__builtin_amdgcn_read_exec() & __ballot(!(ps <= kPSumCap))) {
+        // some weight too large (the first tile, whose running maximum is
+        // -1e30, or a new maximum; NaN lands here too): the rows' maxima,
+        // the rescale, and the weights again
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; v += 2) mx = max_nq(mx, max_nq(s[ct][v], s[ct][v + 1]));
+        mx = row32_max_nq(row16_max_nq(mx));
+        mx *= P.qk_scale;
+        const float mn = fmaxf(m[k], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
+        m[k] = mn;
+        l[k] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[k][dt] *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
+        ps = p[0][0];
+#pragma unroll
+        for (int e = 1; e < 4 * NCT; ++e) ps += p[e >> 2][e & 3];
+      }
       l[k] += ps;
       // P operands: k-step st holds keys {32st + 4q + v} and {32st + 16 + 4q + v}
 #pragma unroll
