@@ -51,7 +51,7 @@ def _sample_rows(rng, qlen, b, w, ctx, k=24):
 
 
 def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24, noslot=None,
-         min_stride=0):
+         min_stride=0, k_ramp=0.0):
     announce(f"prefill dtype={dtype} d={d} hq={h_q} hkv={h_kv} b={b} w={w} q={q_lens} ctx={ctx_lens}")
     nreq = len(q_lens)
     g = h_q // h_kv
@@ -69,7 +69,12 @@ def _run(dtype, d, h_q, h_kv, b, w, q_lens, ctx_lens, seed=5, layer=1, sample=24
     T = sum(q_lens)
     gen = synth.rng(seed, 2, layer, "prompt_q")
     q = synth.cast(gen.standard_normal((T, h_q, d)), dtype)
-    kn = synth.cast(gen.standard_normal((T, h_kv, d)) * np.where(gen.random((T, h_kv)) < 0.02, 4.0, 1.0)[..., None], dtype)
+    kn = gen.standard_normal((T, h_kv, d)) * np.where(gen.random((T, h_kv)) < 0.02, 4.0, 1.0)[..., None]
+    if k_ramp:
+        # every key dimension grows with the position: the logits of queries
+        # with a positive coordinate sum climb from tile to tile
+        kn = kn + k_ramp * (np.arange(T) / 64.0)[:, None, None]
+    kn = synth.cast(kn, dtype)
     vn = synth.cast(gen.standard_normal((T, h_kv, d)), dtype)
     cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     qslot = np.arange(nreq, dtype=np.int32) + 1
@@ -149,6 +154,14 @@ def test_prefill_parity(case):
 @pytest.mark.parametrize("b", [16, 256])   # register-staged and LDS-copy kernels
 def test_prefill_empty_chunks_in_a_batch(b):
     _run("bf16", 128, 16, 2, b, 8, [70, 0, 300, 0], [0, 0, 40, 0])
+
+
+def test_prefill_rising_logits_move_the_maximum_every_tile():
+    # keys ramped so some rows' logits rise ~11 (log2 units) per 32-key
+    # tile: the running maximum moves on almost every tile, through the
+    # path that takes the row maxima, rescales and forms the weights again
+    _run("bf16", 128, 16, 2, 256, 16, [1500, 700], [0, 300], k_ramp=16.0)
+    _run("bf16", 128, 32, 8, 256, 16, [600], [0], k_ramp=16.0)
 
 
 def test_prefill_wide_table_big_blocks():
