@@ -626,6 +626,15 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
   for (int k = 0; k < 2; ++k) qpos[k] = ctx + q0 + ti0_of[k] + cl;  // this lane's query position
   const int vrr = 4 * q + (cl >> 2);                                  // Vᵀ read, key row 4q + cl/4
   const int vbase = vrr * L::VS + 8 * (cl & 3);
+  // This lane's Vᵀ read offset within a V tile, per 16 head dims dt. Kept
+  // opaque, so that each read adds the tile's LDS base (a constant of the
+  // unrolled loop) as its immediate offset instead of a VALU add per read.
+  uint32_t vro[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    vro[dt] = (uint32_t)(vbase + 32 * L::vseg(vrr, dt));
+    asm volatile("" : "+v"(vro[dt]));
+  }
 
   auto tile = [&](int t, const char* Kb, const char* Vb, char* Kn, char* Vn) __attribute__((always_inline)) {
     if (t + 1 < ntiles) issue(t + 1, Kn, Vn);  // in flight while this tile is used
@@ -717,7 +726,7 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        const char* va = Vb + vbase + 32 * st * L::VS + 32 * L::vseg(vrr, dt);  // rows + 32st keep vseg
+        const char* va = Vb + 32 * st * L::VS + vro[dt];  // rows + 32st keep vseg
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(va));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(va + 16 * L::VS));
         typedef short v8i16_t __attribute__((ext_vector_type(8)));
