@@ -151,12 +151,13 @@ __device__ __forceinline__ void emit_lse(const PrefillParams& P, int r, int c0, 
 // ---------------------------------------------------------------------------
 constexpr int kPKT = 64;                 // keys per tile
 constexpr float kPLazy = 8.0f;           // lazy rescale threshold (log2 units)
-// The LDS-copy kernel forms a tile's weights with the running maximum as it
-// stands and moves the maximum only when a lane's partial sum of its
-// weights exceeds kPSumCap: every weight then stays below 2^11 (fp32 sums
-// and bf16 weights hold that), and with 32-key tiles (8 weights per lane)
-// the maximum moves at latest when some weight would pass 2^kPLazy.
-constexpr float kPSumCap = 2048.0f;
+// The bf16 kernels form a tile's weights with the running maximum as it
+// stands and move the maximum only when a lane's partial sum of its n
+// weights exceeds n * 2^kPLazy, i.e. at latest when some weight would pass
+// 2^kPLazy; every weight stays below n * 2^kPLazy (2^11 with 32-key tiles,
+// 2^12 with 64), which fp32 sums and bf16 weights hold.
+constexpr float psum_cap(int weights_per_lane) { return 256.0f * weights_per_lane; }  // 2^kPLazy
+static_assert(kPLazy == 8.0f, "psum_cap assumes 2^kPLazy = 256");
 constexpr int kPRows = 128;              // query rows (token, head) per workgroup
 constexpr int kPfTabLds = 2048;          // block ids staged in LDS (tables up to this wide)
 #ifndef ZP_PF_DMA_KT
@@ -338,9 +339,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
       floatx4 (&s)[4] = sk[k];
       // s[ct][v] = raw logit of key t*64 + ct*16 + 4q + v for this lane's
       // query; softmax in the exp2 domain with the scale folded into an FMA.
-      // m is the running max of the scaled logits; it is raised (and O, l
-      // rescaled) only when a tile's max exceeds it by more than kLazy, so
-      // the weights exp2(x - m) stay below 2^kLazy.
+      // m is the running max of the scaled logits, raised (and O, l
+      // rescaled) only when a weight exp2(x - m) would grow too large.
       if (diag) {  // one branch, taken on the last tile or two only
         const int lim = qpos[k] - t * kPKT - 4 * q;  // last visible key offset
 #pragma unroll
@@ -349,21 +349,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           for (int v = 0; v < 4; ++v)
             if (ct * 16 + v > lim) s[ct][v] = -INFINITY;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[ct][v]);
-      mx = xor32_max(xor16_max(mx));
-      mx *= P.qk_scale;
-      if (__builtin_amdgcn_read_exec() & __ballot(mx > m[k] + kPLazy)) {  // any lane: rescale
-        const float mn = fmaxf(m[k], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
-        m[k] = mn;
-        l[k] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[k][dt] *= alpha;
-      }
+      // weights against the running maximum as it stands; the tile's row
+      // maxima only when a weight would pass 2^kPLazy (see psum_cap)
       float ps = 0.f;
       float p[4][4];
 #pragma unroll
@@ -373,6 +360,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams P) {
           p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
           ps += p[ct][v];
         }
+      if (__builtin_amdgcn_read_exec() & __ballot(!(ps <= psum_cap(16)))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[ct][v]);
+        mx = xor32_max(xor16_max(mx));
+        mx *= P.qk_scale;
+        const float mn = fmaxf(m[k], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
+        m[k] = mn;
+        l[k] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[k][dt] *= alpha;
+        ps = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
+            ps += p[ct][v];
+          }
+      }
       l[k] += ps;
       // P operands: k-step st holds keys {32st + 4q + v} and {32st + 16 + 4q + v}
 #pragma unroll
@@ -679,7 +689,7 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
       float ps = p[0][0];
 #pragma unroll
       for (int e = 1; e < 4 * NCT; ++e) ps += p[e >> 2][e & 3];
-      if (__builtin_amdgcn_read_exec() & __ballot(!(ps <= kPSumCap))) {
+      if (__builtin_amdgcn_read_exec() & __ballot(!(ps <= psum_cap(4 * NCT)))) {
         // some weight too large (the first tile, whose running maximum is
         // -1e30, or a new maximum; NaN lands here too): the rows' maxima,
         // the rescale, and the weights again
