@@ -500,6 +500,19 @@ __device__ __forceinline__ float row32_max_nq(float v) {
   return max_nq(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Sum of a lane's NCT x 4 weights as a balanced tree, in a fixed order.
+template <int NCT>
+__device__ __forceinline__ float tree_sum(const float (&p)[NCT][4]) {
+  float q[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) q[ct] = (p[ct][0] + p[ct][1]) + (p[ct][2] + p[ct][3]);
+#pragma unroll
+  for (int w = 1; w < NCT; w *= 2)
+#pragma unroll
+    for (int ct = 0; ct + w < NCT; ct += 2 * w) q[ct] += q[ct + w];
+  return q[0];
+}
+
 template <int D, int G, int KT>
 __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel(PrefillParams P) {
   static_assert(KT == 32 || KT == 64, "key tile of 32 or 64");
@@ -686,9 +699,9 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int v = 0; v < 4; ++v) p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
-      float ps = p[0][0];
-#pragma unroll
-      for (int e = 1; e < 4 * NCT; ++e) ps += p[e >> 2][e & 3];
+      // a tree (depth log2 of the weights), not a chain: the compare that
+      // follows waits on it
+      float ps = tree_sum<NCT>(p);
       if (__builtin_amdgcn_read_exec() & __ballot(!(ps <= psum_cap(4 * NCT)))) {
         // some weight too large (the first tile, whose running maximum is
         // -1e30, or a new maximum; NaN lands here too): the rows' maxima,
@@ -710,9 +723,7 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void prefill_attn_dma_kernel
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
           for (int v = 0; v < 4; ++v) p[ct][v] = __builtin_amdgcn_exp2f(fmaf(s[ct][v], P.qk_scale, -m[k]));
-        ps = p[0][0];
-#pragma unroll
-        for (int e = 1; e < 4 * NCT; ++e) ps += p[e >> 2][e & 3];
+        ps = tree_sum<NCT>(p);
       }
       l[k] += ps;
       // P operands: k-step st holds keys {32st + 4q + v} and {32st + 16 + 4q + v}
