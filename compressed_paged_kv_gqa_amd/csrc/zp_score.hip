@@ -1079,6 +1079,25 @@ __device__ __forceinline__ float group_max_nq(float v) {
   v = max_nq(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
   return max_nq(v, dpp_f<DPP_ROW_MIRROR>(v));
 }
+// IEEE maximum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_max_nq(float v) {
+  v = group_max_nq<16>(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max_nq(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_nq(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+// Per column, the largest raw product of a tile above which an entry
+// k_i . k_j / |k_i| of it may exceed p |k_j| (pnc): pnc / (the largest 1/|k_i|
+// over the rows, ivx), less 1e-5 relative so that rounding can only let more
+// tiles through to the exact test (an entry above pnc >= 0 has a positive
+// product, and product * 1/|k_i| <= largest product * ivx). ivx = 0 (no
+// norm) gives +inf (no entry can pass), pnc = 0 with it NaN (every tile
+// passes to the exact test).
+__device__ __forceinline__ float product_threshold(float pnc, float ivx) {
+  return pnc * __builtin_amdgcn_rcpf(ivx) * (1.0f - 1.0e-5f);
+}
+
 __device__ __forceinline__ int xor32_max_i(int v) {
   const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return max((int)r[0], (int)r[1]);
@@ -1501,6 +1520,8 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
       // are the first's plus a constant)
       const char* Kh = Kt + rh * 128 * L::ROWB;
       const float* ivh = inv_s + rh * 128;
+      const float ivx = wave_max_nq(max_nq(ivh[lane], ivh[lane + 64]));  // over this half's rows
+      const float thr[2] = {product_threshold(pnc[0], ivx), product_threshold(pnc[1], ivx)};
       // Software-pipelined two deep: in step k the operands of tile k + 2
       // and the inverse norms of tile k + 1 are read from LDS, tile k + 1's
       // products are issued, and tile k's epilogue runs, so no step waits
@@ -1558,12 +1579,10 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
         }
         // the highest row above p, tracked only in tiles that have one (the
         // test is made for the whole wavefront at once; a diagonal tile
-        // always has one, its diagonal, which is never the entry to zero).
-        // An entry above p |k_j| >= 0 has a positive product, so the
-        // column's largest product times the tile's largest 1/|k_i| bounds
-        // every entry (rounding is monotone); NaN passes to the exact test.
-        const float ivm = max_nq(max_nq(ivv[0], ivv[1]), max_nq(ivv[2], ivv[3]));
-        const bool any = !(cmx[0] * ivm <= pnc[0]) || !(cmx[1] * ivm <= pnc[1]);
+        // always has one, its diagonal, which is never the entry to zero):
+        // a tile whose largest product per column stays at or below that
+        // column's threshold has none; NaN passes to the exact test
+        const bool any = !(cmx[0] <= thr[0]) || !(cmx[1] <= thr[1]);
         if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
@@ -1806,6 +1825,8 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
         const char* Kh = Kt + rh * 128 * L::ROWB;
         const float* ivh = It + rh * 128;
         const bool dblk = i == m;
+        const float ivx = wave_max_nq(max_nq(ivh[ln], ivh[ln + 64]));  // over this half's rows
+        const float thr[2] = {product_threshold(pnc[0], ivx), product_threshold(pnc[1], ivx)};
         auto load_a = [&](int k, typename M::op_t* a) __attribute__((always_inline)) {
 #pragma unroll
           for (int ks = 0; ks < M::NKS; ++ks) a[ks] = M::lds(Kh, k * 16 + cl, ks, ln);
@@ -1845,15 +1866,14 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
           }
           const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
           // as in the lightning kernel: the column sums by FMA, the test
-          // for an entry above p first against a bound of the tile
+          // for an entry above p first against the column's threshold
           float cmx[2];
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             cs[c] = fmaf(curc[c][3], ivv[3], fmaf(curc[c][2], ivv[2], fmaf(curc[c][1], ivv[1], fmaf(curc[c][0], ivv[0], cs[c]))));
             cmx[c] = max_nq(max_nq(curc[c][0], curc[c][1]), max_nq(curc[c][2], curc[c][3]));
           }
-          const float ivm = max_nq(max_nq(ivv[0], ivv[1]), max_nq(ivv[2], ivv[3]));
-          const bool any = !(cmx[0] * ivm <= pnc[0]) || !(cmx[1] * ivm <= pnc[1]);
+          const bool any = !(cmx[0] <= thr[0]) || !(cmx[1] <= thr[1]);
           if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
