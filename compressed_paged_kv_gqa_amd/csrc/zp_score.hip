@@ -769,6 +769,14 @@ __global__ __launch_bounds__(256, 2) void score_flash_kernel(ScoreParams P) {
 // Phase B (requests without window log-sum-exp): merges the per-block row
 // statistics into log-sum-exp, recomputes the logits, S0 and global score.
 // ---------------------------------------------------------------------------
+// (max, sum of exp2(x - max)) pairs merged; an empty pair is (-inf, 0).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
+  m = mn;
+}
+
 template <typename T, int D, int R, bool W16>
 __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   using L = LdsTile<T, D>;
@@ -800,12 +808,24 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
   B.from_global(kpage, CT, wv, lane);
   stage_rows<T, D>(Qs, qrows, R, tid);
   if (tid < R) {
-    const float* st = P.stats + (zh * P.max_blocks) * R * 2 + tid * 2;
-    float Mx = -INFINITY;
-    for (int i = 0; i < N; ++i) Mx = fmaxf(Mx, st[(int64_t)i * R * 2]);
-    float S = 0.f;
-    for (int i = 0; i < N; ++i) S += st[(int64_t)i * R * 2 + 1] * exp2f(st[(int64_t)i * R * 2] - Mx);
-    lse2[tid] = Mx + log2f(S);
+    // this window row's per-block (max, sum) pairs merged in block order,
+    // four 8-byte loads in flight at a time (a loop of single loads waits
+    // for each in turn)
+    const float2* st = reinterpret_cast<const float2*>(P.stats + (zh * P.max_blocks) * R * 2) + tid;
+    float m = -INFINITY, sm = 0.f;
+    int i = 0;
+    for (; i + 4 <= N; i += 4) {
+      float2 a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = st[(int64_t)(i + j) * R];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lse_merge(m, sm, a[j].x, a[j].y);
+    }
+    for (; i < N; ++i) {
+      const float2 a = st[(int64_t)i * R];
+      lse_merge(m, sm, a.x, a.y);
+    }
+    lse2[tid] = m + log2f(sm);
   }
   __syncthreads();
   auto qop = [&](int rt, typename M::op_t* a) {
@@ -819,14 +839,6 @@ __global__ __launch_bounds__(256, 2) void score_s0_kernel(ScoreParams P) {
 // ---------------------------------------------------------------------------
 // Phase C: pooling, redundancy softmax, combination, window.
 // ---------------------------------------------------------------------------
-// (max, sum of exp2(x - max)) pairs merged; an empty pair is (-inf, 0).
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-  const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) return;
-  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
-  m = mn;
-}
-
 // Per-request and per-block values (block counts, block ids, slots, flags)
 // read through the scalar cache: the address is the same in every lane, and
 // scalar loads are waited for with the LDS / scalar counter, so in the
