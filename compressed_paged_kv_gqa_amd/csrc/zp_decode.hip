@@ -565,14 +565,33 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams P) {
   T* out = reinterpret_cast<T*>(P.out);
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int h = i / D, e = i % D;
-    float M = kNoMax;
-    for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, parts[(s2 * G + h) * (D + 2)]);
-    float L = 0.f, O = 0.f;
-    for (int s2 = 0; s2 < nsplit; ++s2) {
+    // the splits' (max, sum, output) merged online in split order, four
+    // splits' loads in flight at a time (two passes of single loads would
+    // wait for each in turn)
+    float M = kNoMax, L = 0.f, O = 0.f;
+    auto merge = [&](float pm, float pl, float po) __attribute__((always_inline)) {
+      const float mn = fmaxf(M, pm);
+      const float a = __builtin_amdgcn_exp2f(M - mn), c = __builtin_amdgcn_exp2f(pm - mn);
+      L = L * a + pl * c;
+      O = O * a + po * c;
+      M = mn;
+    };
+    int s2 = 0;
+    for (; s2 + 4 <= nsplit; s2 += 4) {
+      float pm[4], pl[4], po[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* pp = parts + ((s2 + j) * G + h) * (D + 2);
+        pm[j] = pp[0];
+        pl[j] = pp[1];
+        po[j] = pp[2 + e];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) merge(pm[j], pl[j], po[j]);
+    }
+    for (; s2 < nsplit; ++s2) {
       const float* pp = parts + (s2 * G + h) * (D + 2);
-      const float sc = __builtin_amdgcn_exp2f(pp[0] - M);
-      L += pp[1] * sc;
-      O += pp[2 + e] * sc;
+      merge(pp[0], pp[1], pp[2 + e]);
     }
     out[(out_row + h) * D + e] = from_f32<T>(O / L);
     if (e == 0) {
