@@ -1208,6 +1208,65 @@ __device__ __forceinline__ void lt_advance(const ScoreParams& P, LtItem& it, int
   }
 }
 
+// Blocks of request r, one request per lane, read with a vector load: every
+// lane's load is in flight at once (0 past the last request and for a
+// request whose geometry is invalid, which `flag` reports).
+__device__ __forceinline__ int lt_lane_blocks(const ScoreParams& P, int r, bool flag) {
+  int N = 0;
+  if (r < P.nreq) {
+    N = P.num_blocks[r];
+    if (N > P.max_blocks || N > P.table_stride) {
+      if (flag) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
+      N = 0;
+    } else if (N < 0) {
+      N = 0;
+    }
+  }
+  return N;
+}
+
+// Inclusive prefix sum over the 64 lanes of the wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// The call's valid blocks over all requests, 64 requests per step (the
+// same value in every wavefront).
+__device__ __forceinline__ int lt_total_blocks(const ScoreParams& P, bool flag) {
+  int S = 0;
+  for (int r0 = 0; r0 < P.nreq; r0 += 64) {
+    const int inc = wave_incl_scan(lt_lane_blocks(P, r0 + (threadIdx.x & 63), flag));
+    S += __builtin_amdgcn_readlane(inc, 63);
+  }
+  return S;
+}
+
+// Places the cursor on the call's valid block s (0 <= s < the total): the
+// first request whose running block count exceeds s, found with a prefix
+// sum and a ballot over 64 requests per step. False if s is past the end.
+__device__ __forceinline__ bool lt_locate(const ScoreParams& P, int s, LtItem& it) {
+  for (int r0 = 0; r0 < P.nreq; r0 += 64) {
+    const int N = lt_lane_blocks(P, r0 + (threadIdx.x & 63), false);
+    const int inc = wave_incl_scan(N);
+    const unsigned long long hit = __ballot(inc > s);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      it.r = r0 + l;
+      it.N = __builtin_amdgcn_readlane(N, l);
+      it.pidx = s - (__builtin_amdgcn_readlane(inc, l) - it.N);
+      return true;
+    }
+    s -= __builtin_amdgcn_readlane(inc, 63);
+  }
+  return false;
+}
+
 template <int RT>
 __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScoreParams P,
                                                                        int layer_count) {
@@ -1236,15 +1295,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
   const float sc2 = P.qk_scale;
 
   // The workgroup's range of items, in units of the call's valid blocks.
-  int S = 0;
-  for (int r = 0; r < P.nreq; ++r) {
-    const int N = lt_ld(P.num_blocks, r);
-    if (N > P.max_blocks || N > P.table_stride) {
-      if (blockIdx.x == 0 && tid == 0) flag_error(P.err, ZP_DEVERR_SEQ_LEN);
-    } else if (N > 0) {
-      S += N;
-    }
-  }
+  const int S = lt_total_blocks(P, blockIdx.x == 0 && wv == 0);
   const int64_t V = (int64_t)layer_count * P.h_kv * S;
   const int64_t v0 = V * blockIdx.x / gridDim.x, v1 = V * (blockIdx.x + 1) / gridDim.x;
   if (v0 >= v1) return;
@@ -1253,17 +1304,8 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     cur.li = (int)(v0 / ((int64_t)P.h_kv * S));
     const int64_t rem = v0 % ((int64_t)P.h_kv * S);
     cur.h = (int)(rem / S);
-    int s = (int)(rem % S);
-    cur.r = 0;
     cur.valid = true;
-    for (;;) {
-      const int N = lt_blocks(P, cur.r);
-      if (s < N) break;
-      s -= N;
-      ++cur.r;
-    }
-    cur.pidx = s;
-    cur.N = lt_blocks(P, cur.r);
+    if (!lt_locate(P, (int)(rem % S), cur)) return;
     lt_fill(P, cur);
   }
   int left = (int)(v1 - v0);  // items this workgroup still scores, the current one included
@@ -1725,8 +1767,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
   __shared__ __align__(16) int crow[2][BT];    //   the highest row above p (-1: none)
 
   const int wv = wave_id();
-  int S = 0;
-  for (int r = 0; r < P.nreq; ++r) S += lt_blocks(P, r);
+  const int S = lt_total_blocks(P, false);
   // Items (layer, kv-head, request, column block) in order, a unit's column
   // blocks adjacent. Workgroups reach the 8 XCDs round-robin; each XCD gets
   // a contiguous share of the items, which its Gx workgroups take in stride,
@@ -1745,17 +1786,8 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_flash_persist_kernel(Scor
     cur.li = (int)(v0 / ((int64_t)P.h_kv * S));
     const int64_t rem = v0 % ((int64_t)P.h_kv * S);
     cur.h = (int)(rem / S);
-    int s2 = (int)(rem % S);
-    cur.r = 0;
     cur.valid = true;
-    for (;;) {
-      const int N = lt_blocks(P, cur.r);
-      if (s2 < N) break;
-      s2 -= N;
-      ++cur.r;
-    }
-    cur.pidx = s2;
-    cur.N = lt_blocks(P, cur.r);
+    if (!lt_locate(P, (int)(rem % S), cur)) return;
     lt_fill(P, cur);
   }
   int left = (int)((xe - v0 + Gx - 1) / Gx);

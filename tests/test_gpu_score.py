@@ -210,6 +210,17 @@ def test_score_other_shapes():
 FLASH = zp.ScoreParams(redundancy="flash")
 
 
+@pytest.mark.parametrize("sp", [DEFAULT, zp.ScoreParams(redundancy="flash", pool_first_only=False)],
+                         ids=["lightning", "flash"])
+def test_score_more_requests_than_a_wavefront(sp):
+    """70 requests of 1-3 blocks on the persistent kernels' shape: each
+    workgroup places its first item with 64 requests per step, so items of
+    requests 64..69 are found on the second step."""
+    nb = [1 + (r * 7) % 3 for r in range(70)]
+    _run("bf16", 128, 8, 2, 256, 16, nb, lambda r: r % 3 != 0, sp, L=1, layer_begin=0,
+         layer_count=1)
+
+
 def test_score_flash_redundancy_qwen_shape_bf16():
     _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, FLASH)
 
@@ -283,3 +294,37 @@ def test_score_bit_reproducible(redundancy):
     _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, sp, repeat=4)
     sp = zp.ScoreParams(p=0.5, redundancy=redundancy, use_global=False)
     _run("bf16", 128, 16, 4, 64, 16, [6, 3], lambda r: 1, sp, planted=True, heavy=False, repeat=4)
+
+
+@pytest.mark.parametrize("red", ["lightning", "flash"])
+def test_score_request_past_max_blocks_is_flagged_and_skipped(red):
+    """A request whose block count exceeds max_blocks raises the sequence-length
+    error and is left unwritten; the other requests score as they do when it
+    has no blocks at all."""
+    announce(f"score past-max-blocks red={red}")
+    b, nb, maxb = 256, [2, 5, 3], 3
+    geom = zp.CacheGeometry(num_layers=1, num_blocks=sum(nb) + 2, block_size=b, num_kv_heads=2,
+                            num_q_heads=8, head_dim=128, window=16, max_slots=4, n_max=2,
+                            dtype="bf16")
+    hc = HostCache(geom, 5, 2)
+    hc.plant_heavy(5, 2)
+    hc.upload()
+    tab = dev_i32(random_tables(5, 2, nb, geom.num_blocks, max(nb)))
+    qslot = dev_i32(np.array([1, 2, 3], np.int32))
+    first = torch.ones(3, dtype=torch.uint8, device="cuda")
+    sp = zp.ScoreParams(redundancy=red)
+    out = []
+    for counts in ([2, 5, 3], [2, 0, 3]):
+        sc = torch.full((1, 3, 2, maxb * b), -7.0, device="cuda")
+        fn = torch.full_like(sc, -5.0)
+        ws = zp.new_workspace(zp.zp_score_workspace_size(geom, 1, 3, maxb))
+        zp.zp_score_tokens(hc.dev, sp, 0, 1, tab, dev_i32(np.array(counts, np.int32)), maxb,
+                           qslot, first, sc, fn, ws)
+        torch.cuda.synchronize()
+        out.append((sc.cpu().numpy(), fn.cpu().numpy(), zp.zp_workspace_errors(ws)))
+    (s_bad, f_bad, e_bad), (s_ok, f_ok, e_ok) = out
+    assert e_bad & zp.ZP_DEVERR_SEQ_LEN and e_ok == 0
+    assert np.all(s_bad[:, 1] == -7.0) and np.all(f_bad[:, 1] == -5.0)
+    for r in (0, 2):
+        np.testing.assert_allclose(s_bad[:, r], s_ok[:, r], rtol=1e-6, atol=0)
+        np.testing.assert_allclose(f_bad[:, r], f_ok[:, r], rtol=1e-6, atol=0)
