@@ -1197,15 +1197,23 @@ __device__ __forceinline__ void lt_skip(const ScoreParams& P, LtItem& it, int k,
   }
   lt_fill(P, it);
 }
-__device__ __forceinline__ void lt_advance(const ScoreParams& P, LtItem& it, int layer_count) {
+// Moves the cursor to the next item. `next_page` holds the block id after
+// the current item in its request, read by the previous call (an item
+// ahead, so its wait falls behind that item's work); the call reads the one
+// after the new item the same way (the index is clamped to the request's
+// last block, whose id is then not used).
+__device__ __forceinline__ void lt_advance(const ScoreParams& P, LtItem& it, int layer_count,
+                                           int& next_page) {
   if (++it.pidx >= it.N) {
     it.pidx = 0;
     ++it.r;
     lt_next_request(P, it, layer_count);
     if (it.valid) lt_fill(P, it);
   } else {  // same request: only the block id changes
-    it.page = lt_ld(P.tables, (int64_t)it.r * P.table_stride + it.pidx);
+    it.page = next_page;
   }
+  if (it.valid)
+    next_page = lt_ld(P.tables, (int64_t)it.r * P.table_stride + min(it.pidx + 1, it.N - 1));
 }
 
 // Blocks of request r, one request per lane, read with a vector load: every
@@ -1707,13 +1715,14 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
   };
 
   if (tid < BT) sub[tid] = 0ull;
+  int next_page = lt_ld(P.tables, (int64_t)cur.r * P.table_stride + min(cur.pidx + 1, cur.N - 1));
   issue(cur, Ka, Fa, La);
   issue_q(cur);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (;;) {
     LtItem nx = cur;
-    if (left > 1) lt_advance(P, nx, layer_count); else nx.valid = false;
+    if (left > 1) lt_advance(P, nx, layer_count, next_page); else nx.valid = false;
     if (nx.valid) issue(nx, Kb, Fb, Lb);
     process(cur, nx, Ka, Fa, La);
     __builtin_amdgcn_s_waitcnt(0);
@@ -1722,7 +1731,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     cur = nx;
     --left;
     nx = cur;
-    if (left > 1) lt_advance(P, nx, layer_count); else nx.valid = false;
+    if (left > 1) lt_advance(P, nx, layer_count, next_page); else nx.valid = false;
     if (nx.valid) issue(nx, Ka, Fa, La);
     process(cur, nx, Kb, Fb, Lb);
     __builtin_amdgcn_s_waitcnt(0);
