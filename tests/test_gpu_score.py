@@ -89,7 +89,7 @@ def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, laye
         for li in range(layer_count):
             l = layer_begin + li
             for r in range(nreq):
-                if flags[r]:
+                if flags[r] and nblocks[r] > 0:
                     for h in range(h_kv):
                         K = Z.gather_sequence(hc.K[l, :, h], tab[r], nblocks[r] * b, b)
                         tbl[l, qslot[r], h] = _window_lse(hc.Q[l, qslot[r], h], K, b)
@@ -126,6 +126,10 @@ def _run(dtype, d, h_q, h_kv, b, w, nblocks, first, sp, L=3, layer_begin=1, laye
         l = layer_begin + li
         for r in range(nreq):
             n = nblocks[r] * b
+            if n == 0:  # a request without blocks is skipped: nothing written
+                assert np.all(S_gpu[li, r] == -7.0)
+                assert Fn_gpu is None or np.all(Fn_gpu[li, r] == -5.0)
+                continue
             for h in range(h_kv):
                 K = Z.gather_sequence(hc.K[l, :, h], tab[r], n, b)
                 Fo = Z.gather_sequence(hc.F[l, :, h], tab[r], n, b)
@@ -219,6 +223,18 @@ def test_score_more_requests_than_a_wavefront(sp):
     nb = [1 + (r * 7) % 3 for r in range(70)]
     _run("bf16", 128, 8, 2, 256, 16, nb, lambda r: r % 3 != 0, sp, L=1, layer_begin=0,
          layer_count=1)
+
+
+@pytest.mark.parametrize("sp", [DEFAULT, zp.ScoreParams(redundancy="flash")],
+                         ids=["lightning", "flash"])
+@pytest.mark.parametrize("with_lse", [False, True], ids=["stats", "lse"])
+def test_score_requests_without_blocks_among_many(sp, with_lse):
+    """130 requests over three 64-request steps of the persistent kernels'
+    cursor, a fifth of them with no blocks (first, last and runs of them):
+    those are skipped and left unwritten, the rest score as the oracle."""
+    nb = [0 if (r % 5 == 0 or r in (1, 2, 129)) else 1 + (r % 2) for r in range(130)]
+    _run("bf16", 128, 8, 2, 256, 16, nb, lambda r: r % 2, sp, L=1, layer_begin=0, layer_count=1,
+         lse=(lambda r: r % 3 != 1) if with_lse else None)
 
 
 def test_score_flash_redundancy_qwen_shape_bf16():
