@@ -1318,8 +1318,22 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
   }
   int left = (int)(v1 - v0);  // items this workgroup still scores, the current one included
 
+  // The item loop reads the call's parameters through `pq`, the kernel
+  // argument segment (P is its first argument, at offset 0), re-read from
+  // an opaque copy of its address at each item. The compiler then reloads a
+  // field with a scalar load where the item uses it, instead of holding ~60
+  // parameter registers across the item's straight-line body and spilling
+  // them to VGPR lanes (84 spilled SGPRs, ~200 `v_readlane` per item, before).
+  typedef const __attribute__((address_space(4))) ScoreParams* kp_t;
+  const kp_t kp0 = (kp_t)__builtin_amdgcn_kernarg_segment_ptr();
+  const ScoreParams* pq = (const ScoreParams*)kp0;
+  auto relaunder = [&]() __attribute__((always_inline)) {
+    uint64_t u = (uint64_t)kp0;
+    asm volatile("" : "+s"(u));
+    pq = (const ScoreParams*)(kp_t)u;
+  };
   auto item_ok = [&](const LtItem& it) -> bool {
-    return it.page >= 0 && it.page < P.num_blocks_total && it.slot >= 0 && it.slot < P.max_slots;
+    return it.page >= 0 && it.page < pq->num_blocks_total && it.slot >= 0 && it.slot < pq->max_slots;
   };
 
   // Copies item `it`'s keys (swizzled tile), history F and window LSE into
@@ -1329,10 +1343,10 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     if (!item_ok(it)) return;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));  // per item: keeps the addresses out of the loop
-    const int layer = P.layer_begin + it.li;
+    const int layer = pq->layer_begin + it.li;
     const char* kp = reinterpret_cast<const char*>(
-        reinterpret_cast<const bf16_t*>(P.kc) + layer * P.kv_layer_elems +
-        ((int64_t)it.page * P.h_kv + it.h) * BT * D);
+        reinterpret_cast<const bf16_t*>(pq->kc) + layer * pq->kv_layer_elems +
+        ((int64_t)it.page * pq->h_kv + it.h) * BT * D);
     // Byte offsets, inside the block, of the four 16-byte chunks this lane
     // copies: LDS chunk p = (4 wv + i) 64 + lane of the swizzled tile holds
     // row p / 16 = 16 wv + 4 i + lane / 16 and chunk (p % 16) ^ (row % 16)
@@ -1344,22 +1358,22 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
       __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(kp + kb + 1024 * i + (kc ^ (64 * i))),
                                        (lt_lds_ptr)(Kd + (wv * 4 + i) * 1024), 16, 0, 0);
     if (glob && !it.first && wv == 0) {  // 1 KiB, 16 bytes per lane
-      const float* fp = P.gscore + layer * P.f_layer_elems + ((int64_t)it.page * P.h_kv + it.h) * BT;
+      const float* fp = pq->gscore + layer * pq->f_layer_elems + ((int64_t)it.page * pq->h_kv + it.h) * BT;
       __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(fp + lane * 4), (lt_lds_ptr)Fd, 16, 0, 0);
     }
     if (wv == 1 && it.lse && lane < R / 4) {  // R floats, 16 bytes per lane
-      const float* lp = P.qwin_lse + layer * P.qlse_layer_elems + ((int64_t)it.slot * P.h_kv + it.h) * R;
+      const float* lp = pq->qwin_lse + layer * pq->qlse_layer_elems + ((int64_t)it.slot * pq->h_kv + it.h) * R;
       __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(lp + lane * 4), (lt_lds_ptr)Ld, 16, 0, 0);
     }
   };
   // The window queries of item `it` into Qs (R rows, swizzled like K):
   // R / 4 copies of 1 KiB, one per wavefront.
   auto issue_q = [&](const LtItem& it) __attribute__((always_inline)) {
-    if (it.slot < 0 || it.slot >= P.max_slots || wv >= R / 4) return;
-    const int layer = P.layer_begin + it.li;
+    if (it.slot < 0 || it.slot >= pq->max_slots || wv >= R / 4) return;
+    const int layer = pq->layer_begin + it.li;
     const char* qp = reinterpret_cast<const char*>(
-        reinterpret_cast<const bf16_t*>(P.qwin) + layer * P.qwin_layer_elems +
-        ((int64_t)it.slot * P.h_kv + it.h) * R * D);
+        reinterpret_cast<const bf16_t*>(pq->qwin) + layer * pq->qwin_layer_elems +
+        ((int64_t)it.slot * pq->h_kv + it.h) * R * D);
     const int p = wv * 64 + lane;
     const int rr = p >> 4, c = (p & 15) ^ (rr & 15);
     __builtin_amdgcn_global_load_lds((lt_gbl_ptr)(qp + rr * L::ROWB + c * 16),
@@ -1375,7 +1389,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
   float pend_n = 1.f;
   auto flush_rows = [&](int t) __attribute__((always_inline)) {
     if (pend && t < BT) {
-      P.rbuf[pend_off + t] = (csum[0][t] - from_fix(sub[t])) / pend_n;
+      pq->rbuf[pend_off + t] = (csum[0][t] - from_fix(sub[t])) / pend_n;
       sub[t] = 0ull;
     }
     pend = false;
@@ -1393,12 +1407,12 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     const int lane = tid & 63, q = lane >> 4, cl = lane & 15;
     flush_rows(tid);
     const bool ok = item_ok(it);
-    const int z = it.li * P.nreq + it.r;
-    const int64_t zh = (int64_t)z * P.h_kv + it.h;
+    const int z = it.li * pq->nreq + it.r;
+    const int64_t zh = (int64_t)z * pq->h_kv + it.h;
     const bool last = it.pidx == it.N - 1;
     const int n = it.N * BT;
     if (!ok && tid == 0) {
-      flag_error(P.err, (it.page < 0 || it.page >= P.num_blocks_total) ? ZP_DEVERR_BLOCK_ID
+      flag_error(pq->err, (it.page < 0 || it.page >= pq->num_blocks_total) ? ZP_DEVERR_BLOCK_ID
                                                                         : ZP_DEVERR_SLOT);
     }
     // 1. window logits (LSE given: wave w takes column tile w; statistics:
@@ -1465,12 +1479,12 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
           float s1 = s0;
           if (glob) {
             if (!it.first && !last) {
-              const float f = P.alpha * Ft[col];
-              s1 = (P.flags & ZP_SCORE_GLOBAL_SUM) ? f + s0 : fmaxf(f, s0);
+              const float f = pq->alpha * Ft[col];
+              s1 = (pq->flags & ZP_SCORE_GLOBAL_SUM) ? f + s0 : fmaxf(f, s0);
             }
-            P.f_new[zh * P.scores_stride + (int64_t)it.pidx * BT + col] = s1;
+            pq->f_new[zh * pq->scores_stride + (int64_t)it.pidx * BT + col] = s1;
           }
-          P.s1buf[zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT + col] = s1;
+          pq->s1buf[zh * ((int64_t)pq->max_blocks * BT) + (int64_t)it.pidx * BT + col] = s1;
         }
       } else if (wv < 8) {
         // partial (max, sum of exp2) of each row over this wave's 32 columns
@@ -1541,16 +1555,16 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
       if (Mx != -INFINITY)
 #pragma unroll
         for (int w2 = 0; w2 < 8; ++w2) Sm += wstat[w2][tid][1] * exp2f(wstat[w2][tid][0] - Mx);
-      float* st = P.stats + ((zh * P.max_blocks + it.pidx) * R + tid) * 2;
+      float* st = pq->stats + ((zh * pq->max_blocks + it.pidx) * R + tid) * 2;
       st[0] = Mx;
       st[1] = Sm;
     }
     if (ok && flash) {  // flash: the norms for its own kernel, its fixed-point words cleared
       if (tid < BT) {
-        const int64_t o = zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT + tid;
-        P.inv[o] = inv_s[tid];
-        P.nrm[o] = nrm_s[tid];
-        P.rsub[o] = 0ull;
+        const int64_t o = zh * ((int64_t)pq->max_blocks * BT) + (int64_t)it.pidx * BT + tid;
+        pq->inv[o] = inv_s[tid];
+        pq->nrm[o] = nrm_s[tid];
+        pq->rsub[o] = 0ull;
       }
       return;
     }
@@ -1572,7 +1586,7 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int ks = 0; ks < M::NKS; ++ks) bop[c][ks] = M::lds(Kt, (2 * cg + c) * 16 + cl, ks, lane);
-        pnc[c] = P.p * nrm_s[(2 * cg + c) * 16 + cl];
+        pnc[c] = pq->p * nrm_s[(2 * cg + c) * 16 + cl];
       }
       bool dg[4];  // this lane's element on the diagonal of a diagonal tile
 #pragma unroll
@@ -1710,19 +1724,20 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     // 4. is left to the start of the next item (or the end of the loop),
     // after the barrier that ends this one
     pend = true;
-    pend_off = zh * ((int64_t)P.max_blocks * BT) + (int64_t)it.pidx * BT;
+    pend_off = zh * ((int64_t)pq->max_blocks * BT) + (int64_t)it.pidx * BT;
     pend_n = (float)n;
   };
 
   if (tid < BT) sub[tid] = 0ull;
-  int next_page = lt_ld(P.tables, (int64_t)cur.r * P.table_stride + min(cur.pidx + 1, cur.N - 1));
+  int next_page = lt_ld(pq->tables, (int64_t)cur.r * pq->table_stride + min(cur.pidx + 1, cur.N - 1));
   issue(cur, Ka, Fa, La);
   issue_q(cur);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (;;) {
+    relaunder();
     LtItem nx = cur;
-    if (left > 1) lt_advance(P, nx, layer_count, next_page); else nx.valid = false;
+    if (left > 1) lt_advance(*pq, nx, layer_count, next_page); else nx.valid = false;
     if (nx.valid) issue(nx, Kb, Fb, Lb);
     process(cur, nx, Ka, Fa, La);
     __builtin_amdgcn_s_waitcnt(0);
@@ -1730,8 +1745,9 @@ __global__ __launch_bounds__(kLtThreads, 1) void score_lightning_kernel(ScorePar
     if (!nx.valid) break;
     cur = nx;
     --left;
+    relaunder();
     nx = cur;
-    if (left > 1) lt_advance(P, nx, layer_count, next_page); else nx.valid = false;
+    if (left > 1) lt_advance(*pq, nx, layer_count, next_page); else nx.valid = false;
     if (nx.valid) issue(nx, Ka, Fa, La);
     process(cur, nx, Kb, Fb, Lb);
     __builtin_amdgcn_s_waitcnt(0);
