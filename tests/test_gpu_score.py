@@ -237,6 +237,22 @@ def test_score_requests_without_blocks_among_many(sp, with_lse):
          lse=(lambda r: r % 3 != 1) if with_lse else None)
 
 
+@pytest.mark.parametrize("sp", [DEFAULT, zp.ScoreParams(redundancy="flash")],
+                         ids=["lightning", "flash"])
+def test_score_cursor_wraps_layers_past_empty_requests(sp):
+    """Three layers of a four-layer cache, 3 kv-heads, the first and last
+    two requests without blocks. 9 x 59 = 531 items over 256 workgroups
+    give each workgroup two or three consecutive items; the (layer, kv-head)
+    boundaries at items 59, 177 (a layer change), 295 and 413 fall inside a
+    workgroup's range, so that workgroup steps across the empty requests at
+    both ends (the lightning kernel one item at a time, the flash kernel in
+    strides). With 2 kv-heads and 2 layers every boundary would fall on the
+    start of a range."""
+    nb = [0, 10, 9, 11, 10, 9, 10, 0, 0]
+    _run("bf16", 128, 12, 3, 256, 16, nb, lambda r: r % 2, sp, L=4, layer_begin=1,
+         layer_count=3, lse=lambda r: r != 3)
+
+
 def test_score_flash_redundancy_qwen_shape_bf16():
     _run("bf16", 128, 32, 8, 256, 16, [8, 16, 9], lambda r: r % 2, FLASH)
 
